@@ -1,0 +1,438 @@
+"""Pins of the f64 oracle against things other than itself (CPU only).
+
+Each test ties the oracle to a fact the pages or plain mathematics fix:
+brute force with textbook softmax (no max shift) and an mpmath referee, closed
+forms (all-zero keys, a single key, one-hot scores, constant values), the
+invariants the tang paper proves (probability rows sum to one, shift
+invariance, the online-softmax combine equals two-pass softmax under any
+split/merge order, §2.5 and §6), grouped-query heads equal to repeated
+multi-head keys, and torch's own float64 CPU attention as a library special
+case. Together they fail on a dropped term, a wrong sign, a wrong index or
+mask bound, or a transposed operand anywhere in the oracle.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import monoid
+from online_softmax_monoid_amd import inputs
+from tests import brute
+
+RTOL_EXACT = 1e-13
+
+
+def _rand_bits(rng, shape, std=1.0):
+    x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
+    return inputs.bf16_bits(x)
+
+
+def _close(a, b, rtol=RTOL_EXACT, atol=1e-300):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape
+    same_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    fa, fb = np.where(same_inf, 0, a), np.where(same_inf, 0, b)
+    err = np.abs(fa - fb)
+    bound = atol + rtol * np.maximum(np.abs(fa), np.abs(fb))
+    assert np.all(err <= bound), f"max err {err.max()} (bound {bound[err.argmax()]})"
+
+
+# --------------------------------------------------------------------- T1 --
+TINY_CASES = [
+    # B, Hq, Hkv, Sq, Sk, d, causal
+    (1, 1, 1, 1, 1, 1, False),
+    (1, 2, 2, 5, 7, 3, False),
+    (2, 2, 1, 6, 6, 4, True),
+    (1, 2, 1, 3, 8, 4, True),    # Sq < Sk: bottom-right causal alignment
+    (2, 1, 1, 7, 4, 2, True),    # Sq > Sk: the first rows see no key at all
+    (1, 2, 2, 8, 8, 4, False),
+    (2, 2, 2, 4, 0, 3, False),   # Sk = 0: every row is empty
+]
+
+
+@pytest.mark.parametrize("case", TINY_CASES)
+def test_brute_force_tiny(case):
+    B, Hq, Hkv, Sq, Sk, d, causal = case
+    rng = np.random.Generator(np.random.PCG64(hash(case) % (2 ** 32)))
+    q = _rand_bits(rng, (B, Hq, Sq, d))
+    k = _rand_bits(rng, (B, Hkv, Sk, d))
+    v = _rand_bits(rng, (B, Hkv, Sk, d))
+    scale = 0.5
+    o, lse = oracle.attn_fwd(q, k, v, causal, scale)
+    bo, blse = brute.attention(q.tolist(), k.tolist(), v.tolist(), causal, scale)
+    _close(o, np.array(bo, dtype=np.float64).reshape(o.shape))
+    _close(lse, np.array(blse, dtype=np.float64))
+    mo, mlse = brute.mp_attention(q.tolist(), k.tolist(), v.tolist(), causal, scale)
+    _close(o, np.array([[[[float(x) for x in r] for r in h] for h in b] for b in mo],
+                       dtype=np.float64).reshape(o.shape))
+    _close(lse, np.array([[[float(x) for x in h] for h in b] for b in mlse]))
+    # empty rows: O = +0 exactly and LSE = -inf
+    if causal:
+        for i in range(Sq):
+            if i + Sk - Sq + 1 <= 0:
+                assert np.all(o[:, :, i] == 0) and np.all(np.isneginf(lse[:, :, i]))
+
+
+# --------------------------------------------------------------------- T2 --
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_keys_give_uniform_weights(causal):
+    """K = 0: every score is 0, so LSE = ln |J_i| and O is the mean of V over J_i."""
+    rng = np.random.Generator(np.random.PCG64(2))
+    B, H, S, d = 2, 3, 37, 8
+    q = _rand_bits(rng, (B, H, S, d))
+    k = np.zeros((B, H, S, d), dtype=np.uint16)
+    v = _rand_bits(rng, (B, H, S, d))
+    o, lse = oracle.attn_fwd(q, k, v, causal, 0.125)
+    vf = inputs.bf16_to_f32(v).astype(np.float64)
+    for i in range(S):
+        n = i + 1 if causal else S
+        _close(lse[:, :, i], np.full((B, H), math.log(n)), rtol=1e-15)
+        _close(o[:, :, i], vf[:, :, :n].sum(axis=2) / n, rtol=1e-13, atol=1e-15)
+
+
+# --------------------------------------------------------------------- T3 --
+def test_single_key_and_causal_first_row():
+    rng = np.random.Generator(np.random.PCG64(3))
+    # Sk = 1: O = V_0, LSE = s_0
+    q = _rand_bits(rng, (1, 2, 5, 16))
+    k = _rand_bits(rng, (1, 2, 1, 16))
+    v = _rand_bits(rng, (1, 2, 1, 16))
+    o, lse = oracle.attn_fwd(q, k, v, False, 0.25)
+    qf = inputs.bf16_to_f32(q).astype(np.float64)
+    kf = inputs.bf16_to_f32(k).astype(np.float64)
+    vf = inputs.bf16_to_f32(v).astype(np.float64)
+    assert np.array_equal(o, np.broadcast_to(vf[:, :, :1], o.shape))
+    s0 = 0.25 * np.einsum("bhid,bhd->bhi", qf, kf[:, :, 0])
+    _close(lse, s0, rtol=1e-15)
+    # causal with Sq = Sk: row 0 sees only key 0
+    q = _rand_bits(rng, (1, 2, 9, 16))
+    k = _rand_bits(rng, (1, 2, 9, 16))
+    v = _rand_bits(rng, (1, 2, 9, 16))
+    o, lse = oracle.attn_fwd(q, k, v, True, 0.25)
+    assert np.array_equal(o[:, :, 0], inputs.bf16_to_f32(v[:, :, 0]).astype(np.float64))
+
+
+# --------------------------------------------------------------------- T4 --
+def test_one_hot_scores():
+    """Orthogonal keys: q.k_j* = 4 and q.k_j = 0 otherwise, scale 0.5, so the
+    scores are L = 2 at j* and 0 elsewhere: p_j* = e^2 / (e^2 + n - 1)."""
+    n, d, jstar = 6, 8, 4
+    one = inputs.f32_to_bf16_bits_scalar(1.0)
+    four = inputs.f32_to_bf16_bits_scalar(4.0)
+    k = np.zeros((1, 1, n, d), dtype=np.uint16)
+    for j in range(n):
+        k[0, 0, j, j] = one
+    q = np.zeros((1, 1, 1, d), dtype=np.uint16)
+    q[0, 0, 0, jstar] = four
+    rng = np.random.Generator(np.random.PCG64(4))
+    v = _rand_bits(rng, (1, 1, n, d))
+    o, lse = oracle.attn_fwd(q, k, v, False, 0.5)
+    L = 2.0
+    pstar = math.exp(L) / (math.exp(L) + n - 1)
+    pother = 1.0 / (math.exp(L) + n - 1)
+    vf = inputs.bf16_to_f32(v[0, 0]).astype(np.float64)
+    expect = pstar * vf[jstar] + pother * (vf.sum(axis=0) - vf[jstar])
+    _close(o[0, 0, 0], expect, rtol=1e-14, atol=1e-16)
+    _close(lse[0, 0, 0], math.log(math.exp(L) + n - 1), rtol=1e-15)
+    p = oracle.attn_probs(q, k, False, 0.5, 0)
+    _close(p[jstar], pstar, rtol=1e-15)
+    _close(np.delete(p, jstar), np.full(n - 1, pother), rtol=1e-15)
+
+
+# --------------------------------------------------------------------- T5 --
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_values(causal):
+    rng = np.random.Generator(np.random.PCG64(5))
+    q = _rand_bits(rng, (2, 2, 33, 16), std=2.0)
+    k = _rand_bits(rng, (2, 2, 33, 16), std=2.0)
+    c = inputs.f32_to_bf16_bits_scalar(-1.71875)
+    v = np.full((2, 2, 33, 16), c, dtype=np.uint16)
+    o, _ = oracle.attn_fwd(q, k, v, causal, 0.25)
+    _close(o, np.full(o.shape, -1.71875), rtol=1e-15)
+
+
+# --------------------------------------------------------------------- T6 --
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows(causal):
+    rng = np.random.Generator(np.random.PCG64(6))
+    q = _rand_bits(rng, (1, 2, 20, 32))
+    k = _rand_bits(rng, (1, 2, 20, 32))
+    for row in range(0, 40, 3):
+        p = oracle.attn_probs(q, k, causal, 0.2, row)
+        i = row % 20
+        assert np.all(p >= 0) and np.all(p <= 1)
+        _close(p.sum(), 1.0, rtol=1e-15)
+        if causal:
+            assert np.all(p[i + 1:] == 0) and np.all(p[: i + 1] > 0)
+
+
+# --------------------------------------------------------------------- T7 --
+@pytest.mark.parametrize("causal", [False, True])
+def test_shift_invariance(causal):
+    """Append q' = [q, 1], k'_j = [k_j, c]: every score shifts by scale*c, so O
+    is unchanged and LSE moves by exactly scale*c (theorem listed in §6)."""
+    rng = np.random.Generator(np.random.PCG64(7))
+    B, H, S, d = 1, 2, 24, 15
+    q = _rand_bits(rng, (B, H, S, d))
+    k = _rand_bits(rng, (B, H, S, d))
+    v = _rand_bits(rng, (B, H, S, d + 1))
+    c = 3.5
+    q2 = np.concatenate([q, np.full((B, H, S, 1), inputs.f32_to_bf16_bits_scalar(1.0),
+                                    dtype=np.uint16)], axis=3)
+    k2 = np.concatenate([k, np.full((B, H, S, 1), inputs.f32_to_bf16_bits_scalar(c),
+                                    dtype=np.uint16)], axis=3)
+    scale = 0.375
+    # pad q/k with a zero coordinate so both runs use d + 1 columns
+    q1 = np.concatenate([q, np.zeros((B, H, S, 1), dtype=np.uint16)], axis=3)
+    k1 = np.concatenate([k, np.zeros((B, H, S, 1), dtype=np.uint16)], axis=3)
+    o1, lse1 = oracle.attn_fwd(q1, k1, v, causal, scale)
+    o2, lse2 = oracle.attn_fwd(q2, k2, v, causal, scale)
+    _close(o2, o1, rtol=1e-12, atol=1e-14)
+    _close(lse2, lse1 + scale * c, rtol=1e-13)
+
+
+# --------------------------------------------------------------------- T8 --
+@pytest.mark.parametrize("causal", [False, True])
+def test_monoid_any_split_order_equals_two_pass(causal):
+    rng = np.random.Generator(np.random.PCG64(8))
+    B, H, Sq, Sk, d = 1, 2, 12, 19, 8
+    q = _rand_bits(rng, (B, H, Sq, d), std=1.5)
+    k = _rand_bits(rng, (B, H, Sk, d), std=1.5)
+    v = _rand_bits(rng, (B, H, Sk, d))
+    scale = 0.5
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal, scale)
+    for h in range(H):
+        for i in range(Sq):
+            n = min(Sk, max(0, i + Sk - Sq + 1)) if causal else Sk
+            leaves = monoid.row_leaves(q[0, h, i], k[0, h], v[0, h], n, scale)
+            for trial in range(3):
+                perm = rng.permutation(len(leaves))
+                st = monoid.fold_tree([leaves[j] for j in perm], d, rng)
+                # the identity on either side changes nothing
+                st = monoid.combine(monoid.identity(d), monoid.combine(st, monoid.identity(d)))
+                o, lse = monoid.finish(st)
+                _close(o, o_ref[0, h, i], rtol=1e-12, atol=1e-14)
+                _close(lse, lse_ref[0, h, i], rtol=1e-12)
+
+
+def test_monoid_laws_on_states():
+    rng = np.random.Generator(np.random.PCG64(81))
+    d = 5
+
+    def rand_state():
+        return (float(rng.normal() * 3), float(rng.uniform(0.5, 4)), rng.normal(size=d))
+
+    for _ in range(50):
+        x, y, z = rand_state(), rand_state(), rand_state()
+        a = monoid.combine(monoid.combine(x, y), z)
+        b = monoid.combine(x, monoid.combine(y, z))
+        c = monoid.combine(y, x)
+        xy = monoid.combine(x, y)
+        for u, w in ((a[0], b[0]), (xy[0], c[0])):
+            assert u == w
+        _close(a[1], b[1], rtol=1e-14)
+        _close(a[2], b[2], rtol=1e-13, atol=1e-15)
+        _close(xy[1], c[1], rtol=1e-15)
+        _close(xy[2], c[2], rtol=1e-15, atol=1e-16)
+    e = monoid.identity(d)
+    x = rand_state()
+    for st in (monoid.combine(e, x), monoid.combine(x, e)):
+        assert st[0] == x[0] and st[1] == x[1] and np.array_equal(st[2], x[2])
+    o, lse = monoid.finish(e)
+    assert np.all(o == 0) and lse == -math.inf
+
+
+# --------------------------------------------------------------------- T9 --
+def test_key_permutation_invariance():
+    rng = np.random.Generator(np.random.PCG64(9))
+    q = _rand_bits(rng, (2, 2, 10, 16))
+    k = _rand_bits(rng, (2, 2, 31, 16))
+    v = _rand_bits(rng, (2, 2, 31, 16))
+    o, lse = oracle.attn_fwd(q, k, v, False, 0.25)
+    perm = rng.permutation(31)
+    o2, lse2 = oracle.attn_fwd(q, k[:, :, perm], v[:, :, perm], False, 0.25)
+    _close(o2, o, rtol=1e-13, atol=1e-15)
+    _close(lse2, lse, rtol=1e-14)
+    # and the mask really excludes keys: perturbing a later key leaves earlier rows
+    o_c, lse_c = oracle.attn_fwd(q[:, :, :, :], k[:, :, :10], v[:, :, :10], True, 0.25)
+    k3, v3 = k[:, :, :10].copy(), v[:, :, :10].copy()
+    k3[:, :, 7] ^= np.uint16(0x1234)
+    v3[:, :, 7] ^= np.uint16(0x0F0F)
+    o_p, lse_p = oracle.attn_fwd(q, k3, v3, True, 0.25)
+    assert np.array_equal(o_p[:, :, :7], o_c[:, :, :7])
+    assert np.array_equal(lse_p[:, :, :7], lse_c[:, :, :7])
+    assert not np.array_equal(o_p[:, :, 7:], o_c[:, :, 7:])
+
+
+# -------------------------------------------------------------------- T10 --
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_equals_repeated_mha(causal):
+    rng = np.random.Generator(np.random.PCG64(10))
+    B, Hq, Hkv, S, d = 2, 8, 2, 21, 16
+    q = _rand_bits(rng, (B, Hq, S, d))
+    k = _rand_bits(rng, (B, Hkv, S, d))
+    v = _rand_bits(rng, (B, Hkv, S, d))
+    o, lse = oracle.attn_fwd(q, k, v, causal, 0.25)
+    # contiguous groups: query head h reads kv-head h // (Hq // Hkv)
+    kr = np.repeat(k, Hq // Hkv, axis=1)
+    vr = np.repeat(v, Hq // Hkv, axis=1)
+    o2, lse2 = oracle.attn_fwd(q, kr, vr, causal, 0.25)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    # and a different grouping would not match
+    kw = np.tile(k, (1, Hq // Hkv, 1, 1))
+    vw = np.tile(v, (1, Hq // Hkv, 1, 1))
+    o3, _ = oracle.attn_fwd(q, kw, vw, causal, 0.25)
+    assert not np.allclose(o, o3)
+
+
+# -------------------------------------------------------------------- T11 --
+def _torch_reference(q, k, v, causal, scale):
+    import torch
+    qf = torch.from_numpy(inputs.bf16_to_f32(q).astype(np.float64))
+    kf = torch.from_numpy(inputs.bf16_to_f32(k).astype(np.float64))
+    vf = torch.from_numpy(inputs.bf16_to_f32(v).astype(np.float64))
+    G = qf.shape[1] // kf.shape[1]
+    kf = kf.repeat_interleave(G, dim=1)
+    vf = vf.repeat_interleave(G, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(qf, kf, vf, is_causal=causal,
+                                                         scale=scale)
+    s = scale * (qf @ kf.transpose(-1, -2).contiguous())
+    if causal:
+        Sq, Sk = s.shape[-2], s.shape[-1]
+        mask = torch.ones(Sq, Sk, dtype=torch.bool).tril(diagonal=Sk - Sq)
+        s = s.masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return o.numpy(), lse.numpy()
+
+
+@pytest.mark.parametrize("wid,causal,sl", [
+    (1, False, None),
+    (2, True, (slice(0, 1), slice(0, 2))),
+    (2, False, (slice(3, 4), slice(14, 16))),
+    (3, True, (slice(1, 2), slice(5, 6))),
+])
+def test_torch_f64_sdpa(wid, causal, sl):
+    w = inputs.WORKLOADS[wid]
+    q, k, v = inputs.prefill_inputs(w)
+    if sl is not None:
+        q, k, v = q[sl], k[sl], v[sl]
+    o, lse = oracle.attn_fwd(q, k, v, causal, w.scale)
+    to, tlse = _torch_reference(q, k, v, causal, w.scale)
+    _close(o, to, rtol=1e-11, atol=1e-13)
+    _close(lse, tlse, rtol=1e-12)
+
+
+def test_torch_f64_gqa_ragged():
+    rng = np.random.Generator(np.random.PCG64(11))
+    q = _rand_bits(rng, (1, 8, 77, 64))
+    k = _rand_bits(rng, (1, 2, 77, 64))
+    v = _rand_bits(rng, (1, 2, 77, 64))
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd(q, k, v, causal, 0.125)
+        to, tlse = _torch_reference(q, k, v, causal, 0.125)
+        _close(o, to, rtol=1e-11, atol=1e-13)
+        _close(lse, tlse, rtol=1e-12)
+
+
+def test_row_subset_matches_full():
+    rng = np.random.Generator(np.random.PCG64(12))
+    q = _rand_bits(rng, (2, 4, 50, 32))
+    k = _rand_bits(rng, (2, 2, 50, 32))
+    v = _rand_bits(rng, (2, 2, 50, 32))
+    o, lse = oracle.attn_fwd(q, k, v, True, 0.2)
+    rows = np.array([0, 49, 50, 123, 399, 251], dtype=np.int64)
+    os_, lses = oracle.attn_fwd(q, k, v, True, 0.2, rows=rows)
+    assert np.array_equal(os_, o.reshape(-1, 32)[rows])
+    assert np.array_equal(lses, lse.reshape(-1)[rows])
+
+
+# -------------------------------------------------------------------- T12 --
+def test_decode_split_combine_equals_whole():
+    rng = np.random.Generator(np.random.PCG64(13))
+    B, Hq, Hkv, d, S_cap = 6, 8, 2, 16, 40
+    lens = np.array([0, 1, 5, 16, 37, 40], dtype=np.int32)
+    lens_, q, kc, vc = inputs.draw_decode_bits(1234, B, Hq, Hkv, d, 0, 0, S_cap, lens=lens,
+                                               pad_bits=int(inputs.BF16_NAN))
+    o, lse = oracle.attn_decode(q, kc, vc, lens, 0.25)
+    assert np.all(np.isfinite(o))
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+    for ns in (1, 3, 16):
+        om, lsem = monoid.decode_split(q, kc, vc, lens, 0.25, ns)
+        _close(om, o, rtol=1e-12, atol=1e-14)
+        _close(lsem, lse, rtol=1e-13)
+    # decode is the prefill definition with Sq = 1 over the valid prefix
+    for b in range(1, B):
+        n = int(lens[b])
+        op, lsep = oracle.attn_fwd(q[b][None, :, None, :], kc[b][None, :, :n], vc[b][None, :, :n],
+                                   False, 0.25)
+        assert np.array_equal(op[0, :, 0], o[b]) and np.array_equal(lsep[0, :, 0], lse[b])
+
+
+def test_decode_ignores_padding_bits():
+    lens = np.array([3, 9, 2], dtype=np.int32)
+    args = (77, 3, 4, 2, 8, 0, 0, 12)
+    _, q, kc0, vc0 = inputs.draw_decode_bits(*args, lens=lens, pad_bits=0)
+    _, q2, kcn, vcn = inputs.draw_decode_bits(*args, lens=lens, pad_bits=int(inputs.BF16_NAN))
+    assert np.array_equal(q, q2)
+    o0, l0 = oracle.attn_decode(q, kc0, vc0, lens, 0.3)
+    on, ln = oracle.attn_decode(q, kcn, vcn, lens, 0.3)
+    assert np.array_equal(o0, on) and np.array_equal(l0, ln)
+
+
+# ------------------------------------------------------------- shared bits --
+def test_bf16_rounding_matches_torch():
+    import torch
+    rng = np.random.Generator(np.random.PCG64(14))
+    x = np.concatenate([rng.standard_normal(100000, dtype=np.float32) * 7,
+                        np.array([0.0, -0.0, 1e-40, -3e-39, np.inf, -np.inf, 3.4e38,
+                                  1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8], dtype=np.float32)])
+    ours = inputs.bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert inputs.bf16_bits(np.array([np.nan], dtype=np.float32))[0] == 0x7FC0
+    assert np.array_equal(inputs.bf16_to_f32(ref), torch.from_numpy(ref.view(np.int16)).view(
+        torch.bfloat16).float().numpy())
+
+
+def test_workload_recipe_is_deterministic():
+    w = inputs.WORKLOADS[1]
+    a = inputs.prefill_inputs(w)
+    b = inputs.prefill_inputs(w)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    f = inputs.prefill_inputs_f32(w)
+    for x, y in zip(a, f):
+        assert np.array_equal(x, inputs.bf16_bits(y))
+
+
+# ------------------------------------------------------- the pages' tables --
+def _golden_rows():
+    path = os.path.join(os.path.dirname(__file__), "golden", "h200_d256_attention_fwd.txt")
+    rows = []
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([float(x) for x in line.split()])
+    return rows
+
+
+def test_flop_convention_reproduces_the_pages_tables():
+    """Table 10's TFLOP/s follow from Table 11's times under 4*B*H*N^2*d (halved
+    when causal) with B*H*N = 2^17: the convention the bench reports in."""
+    rows = _golden_rows()
+    assert len(rows) == 5
+    for N, causal, tang_tf, sdpa_tf, tang_ms, fa3_ms, sdpa_ms in rows:
+        N = int(N)
+        BH = 2 ** 17 // N
+        w = inputs.Prefill(0, "h200", 1, BH, BH, N, N, 256, (bool(causal),))
+        for tf, ms in ((tang_tf, tang_ms), (sdpa_tf, sdpa_ms)):
+            got = w.flops(bool(causal)) / (ms * 1e-3) / 1e12
+            assert abs(got - tf) / tf < 0.02, (N, causal, got, tf)
+        # tang forward runs at 0.43-0.54 of FA3's speed (abstract, Table 11)
+        assert 0.42 <= fa3_ms / tang_ms <= 0.545

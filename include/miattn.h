@@ -1,0 +1,147 @@
+/*
+ * miattn.h -- C ABI of libmiattn, the fused softmax-attention forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is O = softmax(scale * Q K^T + mask) V together with the
+ * per-row log-sum-exp, computed as one tiled reduction under the
+ * online-softmax monoid: the state of a row is (running max m, running sum l
+ * rescaled to m, value accumulator rescaled to m), two states combine by
+ * rescaling both to the larger max and adding (the tang paper,
+ * muni.works/research/tang, §2.2 "Comprehensions and monoids" and §2.3
+ * "Rewrites": the max and both exponential sums of softmax merge into this
+ * one reduction, so the score matrix is never materialised). The final map
+ * O = acc / l runs on the thread that holds the accumulator (§2.3, epilogues
+ * run on the reducing thread), and LSE = m + ln l is the same monoid's
+ * logsumexp.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers into caller-owned memory; the
+ *     library allocates nothing and keeps no state between calls, apart from
+ *     a thread-local copy of the last error message.
+ *   - Tensors are dense, row-major, contiguous. bf16 tensors are raw IEEE
+ *     bfloat16 bit patterns (uint16); q, k, v, o and the workspace must be
+ *     16-byte aligned, lse and kv_lens 4-byte aligned.
+ *   - Work is enqueued on `stream` and the call returns without waiting;
+ *     nothing is synchronised. Calls on different streams are independent.
+ *   - Every logical output element is written (including rows that see no
+ *     key), and nothing outside the logical outputs is written.
+ *   - A row with no visible key gets O = +0.0 and LSE = -inf: the finished
+ *     identity of the monoid (§2.1 "Views": a guarded read yields the
+ *     reduction's identity). Masked keys are excluded by a select, never by
+ *     an additive bias, so values stored at masked or out-of-range positions
+ *     cannot reach any output -- with one caveat for causal prefill: a key
+ *     that lies in a partially visible tile and is masked for some rows is
+ *     multiplied by an exact zero weight, so its V row must hold finite
+ *     values (NaN/inf there would propagate as 0 * NaN).
+ *   - Accumulation is float32: scores and the monoid state in f32. In the
+ *     prefill kernel the probabilities are rounded to bf16 (round to nearest
+ *     even) before the value contraction; O is normalised by the sum of
+ *     exactly those rounded values, LSE uses the sum of the unrounded f32
+ *     probabilities. Decode keeps the probabilities in f32. O is rounded to
+ *     bf16 (RNE) and LSE is stored as f32.
+ *   - Return value: MIATTN_OK, or an error code with the message available
+ *     from miattn_last_error(). Argument checks happen on the host before
+ *     anything is enqueued; on error nothing is launched.
+ */
+#ifndef MIATTN_H
+#define MIATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__)
+#define MIATTN_API __attribute__((visibility("default")))
+#else
+#define MIATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MIATTN_OK = 0,
+    MIATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad scale */
+    MIATTN_ERR_UNSUPPORTED = 2, /* head dimension not in {64, 128, 256} */
+    MIATTN_ERR_HIP = 3          /* the HIP runtime reported a launch error */
+} miattn_status;
+
+/*
+ * Prefill / full attention forward.
+ *
+ *   q   bf16 [B, Hq,  Sq, d]       queries
+ *   k   bf16 [B, Hkv, Sk, d]       keys
+ *   v   bf16 [B, Hkv, Sk, d]       values
+ *   o   bf16 [B, Hq,  Sq, d]       output (written)
+ *   lse f32  [B, Hq,  Sq]          natural-log log-sum-exp of the scaled,
+ *                                  masked scores of each row (written)
+ *
+ * Query head h reads kv-head h / (Hq / Hkv): grouped-query attention as two
+ * head dimensions (kv-head, group), §2.1 "Views". `causal` != 0 applies the
+ * bottom-right aligned mask: key j is visible to query i iff
+ * j <= i + (Sk - Sq); for Sq == Sk this is the usual lower-triangular
+ * (upper-triangle-masked) pattern. scale multiplies Q K^T before the mask and
+ * must be finite and > 0.
+ *
+ * Sizes: B, Sq, Sk >= 0 (B == 0 or Sq == 0: nothing to do, pointers unused;
+ * Sk == 0: every row is empty, k and v unused); Hq, Hkv >= 1 with
+ * Hq % Hkv == 0; d in {64, 128, 256}. Offsets are 64-bit, so any size that
+ * fits device memory is accepted.
+ */
+MIATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
+             float scale, hipStream_t stream);
+
+/*
+ * Bytes of workspace attn_fwd_decode needs: B * Hq * num_splits * (d + 2) * 4
+ * (one f32 partial state (m, l, acc[d]) per stream, head and split).
+ * Returns 0 for invalid arguments.
+ */
+MIATTN_API size_t attn_fwd_decode_workspace_size(int B, int Hq, int d, int num_splits);
+
+/*
+ * Decode forward (one query row per stream and head) with split-KV.
+ *
+ *   q        bf16  [B, Hq, d]
+ *   k_cache  bf16  [B, Hkv, S_cap, d]   rows >= kv_lens[b] are never read
+ *   v_cache  bf16  [B, Hkv, S_cap, d]
+ *   kv_lens  int32 [B]  DEVICE array of valid cache lengths; values are not
+ *                        inspected on the host and are clamped to [0, S_cap]
+ *                        on the device
+ *   o        bf16  [B, Hq, d]           (written)
+ *   lse      f32   [B, Hq]              (written)
+ *   workspace         device scratch of at least
+ *                     attn_fwd_decode_workspace_size(B, Hq, d, num_splits)
+ *                     bytes; its contents on entry do not matter and are
+ *                     overwritten.
+ *
+ * Attention is non-causal over keys [0, kv_lens[b]). The keys of each stream
+ * are cut into num_splits balanced ranges, split s covering
+ * [floor(s*len/num_splits), floor((s+1)*len/num_splits)). A first kernel
+ * reduces each range to a partial monoid state (one read of each K/V row
+ * serves all Hq/Hkv query heads of its kv-head); a second kernel folds the
+ * partials with the monoid's combine and finishes O and LSE. The split is
+ * the paper's split schedule, valid for any associative monoid (§2.5
+ * "Schedules"). Two calls sharing one workspace must be ordered (same stream
+ * or synchronised).
+ *
+ * Sizes: B >= 0 (0: nothing to do); Hq, Hkv >= 1, Hq % Hkv == 0; S_cap >= 0;
+ * d in {64, 128, 256}; num_splits >= 1.
+ */
+MIATTN_API int attn_fwd_decode(const void *q, const void *k_cache, const void *v_cache,
+                    const int *kv_lens, void *o, float *lse, int B, int Hq,
+                    int Hkv, int S_cap, int d, int num_splits, float scale,
+                    void *workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* Message for the last non-OK status returned on the calling thread. */
+MIATTN_API const char *miattn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+MIATTN_API int miattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIATTN_H */

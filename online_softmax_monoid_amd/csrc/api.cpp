@@ -1,0 +1,165 @@
+// api.cpp -- the C ABI of libmiattn: argument validation, error reporting and
+// dispatch to the kernel launchers. Nothing here allocates or synchronises.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string>
+
+#include "launch.h"
+#include "miattn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_ptr(const void *p, const char *name, uintptr_t align)
+{
+    if (p == nullptr)
+        return fail(MIATTN_ERR_INVALID_ARG, "%s is NULL", name);
+    if (!aligned(p, align))
+        return fail(MIATTN_ERR_INVALID_ARG, "%s is not %u-byte aligned", name, (unsigned)align);
+    return MIATTN_OK;
+}
+
+int check_heads_dim(int Hq, int Hkv, int d)
+{
+    if (Hq < 1 || Hkv < 1)
+        return fail(MIATTN_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", Hq, Hkv);
+    if (Hq % Hkv != 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (d != 64 && d != 128 && d != 256)
+        return fail(MIATTN_ERR_UNSUPPORTED, "head dimension %d not supported (64, 128, 256)", d);
+    return MIATTN_OK;
+}
+
+int check_scale(float scale)
+{
+    if (!(scale > 0.f) || !isfinite(scale))
+        return fail(MIATTN_ERR_INVALID_ARG, "scale must be finite and > 0 (got %g)", (double)scale);
+    return MIATTN_OK;
+}
+
+int hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess)
+        return MIATTN_OK;
+    return fail(MIATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+#define MIATTN_TRY(expr)                 \
+    do {                                 \
+        int rc_ = (expr);                \
+        if (rc_ != MIATTN_OK)            \
+            return rc_;                  \
+    } while (0)
+
+extern "C" {
+
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq,
+             int Hkv, int Sq, int Sk, int d, int causal, float scale, hipStream_t stream)
+{
+    if (B < 0 || Sq < 0 || Sk < 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d, Sq=%d, Sk=%d)", B, Sq, Sk);
+    MIATTN_TRY(check_heads_dim(Hq, Hkv, d));
+    MIATTN_TRY(check_scale(scale));
+    if (B == 0 || Sq == 0)
+        return MIATTN_OK;
+    MIATTN_TRY(check_ptr(q, "q", 16));
+    MIATTN_TRY(check_ptr(o, "o", 16));
+    MIATTN_TRY(check_ptr(lse, "lse", 4));
+    if (Sk > 0) {
+        MIATTN_TRY(check_ptr(k, "k", 16));
+        MIATTN_TRY(check_ptr(v, "v", 16));
+    }
+    miattn::FwdArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.o = static_cast<uint16_t *>(o);
+    a.lse = lse;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Sq = Sq;
+    a.Sk = Sk;
+    a.scale = scale;
+    return hip_status(miattn::launch_fwd(a, d, causal != 0, stream), "attn_fwd launch");
+}
+
+size_t attn_fwd_decode_workspace_size(int B, int Hq, int d, int num_splits)
+{
+    if (B < 0 || Hq < 1 || d < 1 || num_splits < 1)
+        return 0;
+    return (size_t)B * (size_t)Hq * (size_t)num_splits * (size_t)(d + 2) * sizeof(float);
+}
+
+int attn_fwd_decode(const void *q, const void *k_cache, const void *v_cache, const int *kv_lens,
+                    void *o, float *lse, int B, int Hq, int Hkv, int S_cap, int d,
+                    int num_splits, float scale, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream)
+{
+    if (B < 0 || S_cap < 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d, S_cap=%d)", B, S_cap);
+    MIATTN_TRY(check_heads_dim(Hq, Hkv, d));
+    MIATTN_TRY(check_scale(scale));
+    if (num_splits < 1)
+        return fail(MIATTN_ERR_INVALID_ARG, "num_splits must be >= 1 (got %d)", num_splits);
+    if (B == 0)
+        return MIATTN_OK;
+    MIATTN_TRY(check_ptr(q, "q", 16));
+    MIATTN_TRY(check_ptr(o, "o", 16));
+    MIATTN_TRY(check_ptr(lse, "lse", 4));
+    MIATTN_TRY(check_ptr(kv_lens, "kv_lens", 4));
+    if (S_cap > 0) {
+        MIATTN_TRY(check_ptr(k_cache, "k_cache", 16));
+        MIATTN_TRY(check_ptr(v_cache, "v_cache", 16));
+    }
+    MIATTN_TRY(check_ptr(workspace, "workspace", 16));
+    const size_t need = attn_fwd_decode_workspace_size(B, Hq, d, num_splits);
+    if (workspace_bytes < need)
+        return fail(MIATTN_ERR_INVALID_ARG, "workspace too small: %zu bytes, need %zu",
+                    workspace_bytes, need);
+    miattn::DecodeArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k_cache);
+    a.v = static_cast<const uint16_t *>(v_cache);
+    a.lens = kv_lens;
+    a.o = static_cast<uint16_t *>(o);
+    a.lse = lse;
+    // workspace layout: acc partials [B,Hq,S,d] first (16-byte aligned rows),
+    // then (m, l) pairs [B,Hq,S,2]
+    a.part_acc = static_cast<float *>(workspace);
+    a.part_ml = a.part_acc + (size_t)B * Hq * num_splits * d;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.S_cap = S_cap;
+    a.splits = num_splits;
+    a.scale = scale;
+    return hip_status(miattn::launch_decode(a, d, stream), "attn_fwd_decode launch");
+}
+
+const char *miattn_last_error(void) { return g_last_error.c_str(); }
+
+int miattn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// launch.h -- internal interface between the C-ABI layer (api.cpp) and the
+// kernel translation units. Arguments are already validated when these run.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace miattn {
+
+struct FwdArgs {
+    const uint16_t *q;
+    const uint16_t *k;
+    const uint16_t *v;
+    uint16_t *o;
+    float *lse;
+    int B, Hq, Hkv, Sq, Sk;
+    float scale;
+};
+
+struct DecodeArgs {
+    const uint16_t *q;
+    const uint16_t *k;
+    const uint16_t *v;
+    const int *lens;
+    uint16_t *o;
+    float *lse;
+    float *part_acc;  // [B, Hq, splits, d]
+    float *part_ml;   // [B, Hq, splits, 2]  (m in log2 units, l)
+    int B, Hq, Hkv, S_cap, splits;
+    float scale;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t stream);
+
+}  // namespace miattn

@@ -1,0 +1,401 @@
+// prefill.hip -- fused attention forward on gfx950 MFMA.
+//
+// One workgroup owns BM = 32*NW query rows of one (batch, query head) and
+// streams the keys of that head's kv-head in tiles of BN keys. Per tile:
+//
+//   (a2) stage the K tile into LDS (row-major, 16-byte chunks XOR-swizzled)
+//        and the V tile transposed (V^T, key order permuted to match the
+//        score accumulator), double-buffered so the next tile's global loads
+//        are in flight while this tile computes;
+//   (a2) S^T = K Q^T with v_mfma_f32_32x32x16_bf16: each lane owns one query
+//        column and 16 key rows of every 32x32 score block;
+//   (a3) scale and mask by select (masked key -> -inf, the identity of max);
+//   (a4) the online-softmax monoid update (tang paper, §2.2): new running
+//        max, rescale factor exp2((m_old - m_new)*c), probabilities
+//        exp2(s*c - m_new*c) with c = scale*log2(e), rounded to bf16; two row
+//        sums: the rounded P exactly as P.V consumes them (v_dot2 with ones;
+//        normalises O, so constant V gives exactly that constant) and the
+//        unrounded f32 P (gives LSE, free of the bf16 rounding of P);
+//   (a5) O^T += V^T P^T with the same MFMA, P used straight from registers as
+//        the B operand. The score accumulator holds keys
+//        {4g..4g+3, 8+4g..8+4g+3} of each 16-key chunk in lane half g; V^T is
+//        stored with exactly that key order, so no data moves between the two
+//        contractions (legal because the sum over keys is commutative and
+//        associative -- the paper's §5 "Lowering" makes the same move with
+//        permuted keys on another ISA);
+//   (a6) epilogue on the reducing lanes (§2.3): O = acc / l, LSE = m*scale +
+//        ln l; rows with no visible key get O = +0 and LSE = -inf.
+//
+// The score matrix never leaves registers. Workgroups are ordered so that
+// all tiles of one (batch, kv-head) run back to back on one XCD
+// (workgroups are dispatched round-robin over the 8 XCDs), heaviest causal
+// tiles first, and the query heads of one GQA group sharing a kv-head are
+// adjacent.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace miattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr int kXcds = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+
+union Frag8 {
+    bf16x8 v;
+    uint4 u;
+    uint32_t w[4];
+};
+
+// Combine a per-lane value with the one in lane l ^ 32 (the other half of the
+// wave). v_permlane32_swap exchanges the two halves; its two results hold the
+// values of lanes l % 32 and l % 32 + 32 (in some order), so a symmetric
+// combine of the pair gives both lanes bit-identical results.
+__device__ __forceinline__ float halves_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                              false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                              false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);  // IEEE add commutes
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2 p;
+    p[0] = (__bf16)lo;
+    p[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// Physical tile index -> logical tile index. Consecutive logical tiles land on
+// one XCD: physical id x runs on XCD x % 8.
+__device__ __forceinline__ int xcd_remap(int id, int n)
+{
+    const int per = n / kXcds;
+    if (id < per * kXcds)
+        return (id % kXcds) * per + id / kXcds;
+    return id;
+}
+
+template <int D, int BN, int NW>
+struct Cfg {
+    static constexpr int NT = NW * 64;
+    static constexpr int BM = NW * 32;
+    static constexpr int KCH = D / 8;                      // 16-byte chunks per K row
+    static constexpr int SWZ = (KCH < 16 ? KCH : 16) - 1;  // XOR mask on the chunk index
+    static constexpr int VTS = BN + 8;                     // V^T row stride (elements)
+    static constexpr int K_TILE = BN * D;
+    static constexpr int VT_TILE = D * VTS;
+    static constexpr int KPT = BN * KCH / NT;              // K chunks per thread
+    static constexpr int VUNITS = (BN / 4) * (D / 8);      // 4-key x 8-dim units
+    static constexpr int VPT = (VUNITS + NT - 1) / NT;
+    static_assert(BN % 32 == 0, "BN must be a multiple of 32");
+    static_assert((BN * KCH) % NT == 0, "K tile must split evenly over threads");
+};
+
+template <int D, int BN, int NW, bool CAUSAL>
+__global__ void __launch_bounds__(NW * 64)
+fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
+{
+    using C = Cfg<D, BN, NW>;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][C::K_TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t sVT[2][C::VT_TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+
+    // ---- work decomposition ---------------------------------------------
+    const int G = a.Hq / a.Hkv;
+    const int t = xcd_remap((int)blockIdx.x, n_tiles);
+    const int per_unit = G * n_qtiles;
+    const int unit = t / per_unit;
+    const int rem = t - unit * per_unit;
+    const int rank = rem / G;
+    const int gq = rem - rank * G;
+    const int qtile = CAUSAL ? (n_qtiles - 1 - rank) : rank;
+    const int b = unit / a.Hkv;
+    const int kvh = unit - b * a.Hkv;
+    const int hq = kvh * G + gq;
+
+    const int Sq = a.Sq, Sk = a.Sk;
+    const int diag = Sk - Sq;  // key j is visible to query i iff j <= i + diag
+    const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
+    const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
+    const uint16_t *__restrict__ Kp = a.k + krow0 * D;
+    const uint16_t *__restrict__ Vp = a.v + krow0 * D;
+
+    const int q_wg = qtile * C::BM;
+    const int q_wg_last = min(q_wg + C::BM, Sq) - 1;
+    const int q0 = q_wg + wave * 32;
+    const int my_q = q0 + l32;
+    const bool wave_live = q0 < Sq;
+
+    int kv_end = Sk;
+    int wave_end = wave_live ? Sk : 0;
+    if (CAUSAL) {
+        kv_end = min(Sk, max(0, q_wg_last + diag + 1));
+        if (wave_live)
+            wave_end = min(Sk, max(0, min(q0 + 31, Sq - 1) + diag + 1));
+    }
+    const int nblk = (kv_end + BN - 1) / BN;
+
+    // ---- Q fragment: B operand of S^T = K Q^T (a1) ------------------------
+    bf16x8 qf[D / 16];
+    {
+        const bool ok = my_q < Sq;
+        const uint16_t *qr = a.q + (qrow0 + (ok ? my_q : 0)) * D + 8 * g;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+            Frag8 f;
+            f.u = ok ? *(const uint4 *)(qr + 16 * kk) : make_uint4(0, 0, 0, 0);
+            qf[kk] = f.v;
+        }
+    }
+
+    // ---- staging helpers (a2) -------------------------------------------
+    uint4 kreg[C::KPT];
+    uint4 vreg[C::VPT][4];
+
+    auto load_tile = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < C::KPT; ++u) {
+            const int ci = tid + C::NT * u;
+            const int key = ci / C::KCH, c = ci % C::KCH;
+            kreg[u] = (j0 + key < Sk)
+                ? *(const uint4 *)(Kp + (int64_t)(j0 + key) * D + 8 * c)
+                : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int w = 0; w < C::VPT; ++w) {
+            const int un = tid + C::NT * w;
+            const int kg = un % (BN / 4), dc = un / (BN / 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = j0 + 4 * kg + i;
+                vreg[w][i] = (un < C::VUNITS && key < Sk)
+                    ? *(const uint4 *)(Vp + (int64_t)key * D + 8 * dc)
+                    : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < C::KPT; ++u) {
+            const int ci = tid + C::NT * u;
+            const int key = ci / C::KCH, c = ci % C::KCH;
+            *(uint4 *)(&sK[buf][key * D + 8 * (c ^ (key & C::SWZ))]) = kreg[u];
+        }
+#pragma unroll
+        for (int w = 0; w < C::VPT; ++w) {
+            const int un = tid + C::NT * w;
+            if (un < C::VUNITS) {
+                const int kg = un % (BN / 4), dc = un / (BN / 4);
+                const int gam = kg & 3;
+                const int col = 16 * (kg >> 2) + 8 * (gam & 1) + 4 * (gam >> 1);
+                const uint32_t *r0 = (const uint32_t *)&vreg[w][0];
+                const uint32_t *r1 = (const uint32_t *)&vreg[w][1];
+                const uint32_t *r2 = (const uint32_t *)&vreg[w][2];
+                const uint32_t *r3 = (const uint32_t *)&vreg[w][3];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int wd = jj >> 1;
+                    uint32_t lo, hi;
+                    if (jj & 1) {
+                        lo = (r0[wd] >> 16) | (r1[wd] & 0xffff0000u);
+                        hi = (r2[wd] >> 16) | (r3[wd] & 0xffff0000u);
+                    } else {
+                        lo = (r0[wd] & 0xffffu) | (r1[wd] << 16);
+                        hi = (r2[wd] & 0xffffu) | (r3[wd] << 16);
+                    }
+                    *(uint2 *)(&sVT[buf][(8 * dc + jj) * C::VTS + col]) = make_uint2(lo, hi);
+                }
+            }
+        }
+    };
+
+    // ---- running monoid state of this lane's query row (a4) ---------------
+    const float c = a.scale * kLog2e;
+    float m_run = -INFINITY;  // running max of raw scores q.k
+    float l_half = 0.f;       // running sum of the bf16-rounded P of this lane half
+    float lx_half = 0.f;      // running sum of the unrounded P (for LSE)
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[db][r] = 0.f;
+
+    if (nblk > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int buf = blk & 1;
+        const int j0 = blk * BN;
+        const bool has_next = blk + 1 < nblk;
+        if (has_next)
+            load_tile(j0 + BN);
+
+        if (j0 < wave_end) {
+            // S^T = K Q^T
+            f32x16 s[BN / 32];
+#pragma unroll
+            for (int bb = 0; bb < BN / 32; ++bb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    s[bb][r] = 0.f;
+                const int key = 32 * bb + l32;
+                const uint16_t *krow = &sK[buf][key * D];
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk) {
+                    Frag8 f;
+                    f.u = *(const uint4 *)(krow + 8 * ((2 * kk + g) ^ (key & C::SWZ)));
+                    s[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.v, qf[kk], s[bb], 0, 0, 0);
+                }
+            }
+
+            // mask by select (a3)
+            const bool full = (j0 + BN <= Sk) && (!CAUSAL || j0 + BN - 1 <= q0 + diag);
+            if (!full) {
+                const int lim = CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1;
+#pragma unroll
+                for (int bb = 0; bb < BN / 32; ++bb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = j0 + 32 * bb + 8 * (r >> 2) + 4 * g + (r & 3);
+                        s[bb][r] = (key <= lim) ? s[bb][r] : -INFINITY;
+                    }
+            }
+
+            // online-softmax update (a4)
+            float mx = -INFINITY;
+#pragma unroll
+            for (int bb = 0; bb < BN / 32; ++bb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    mx = fmaxf(mx, s[bb][r]);
+            mx = halves_max(mx);
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
+            const float mc = m_use * c;
+
+            Frag8 pf[BN / 16];
+            float rs = 0.f, rx = 0.f;
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+            for (int bb = 0; bb < BN / 32; ++bb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][8 * h + 2 * w], c, -mc));
+                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][8 * h + 2 * w + 1], c, -mc));
+                        const uint32_t pk = pack_bf16x2(p0, p1);
+                        pf[2 * bb + h].w[w] = pk;
+                        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, rs, false);
+                        rx += p0 + p1;
+                    }
+            l_half = l_half * alpha + rs;
+            lx_half = lx_half * alpha + rx;
+            if (__any(m_new > m_run)) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[db][r] *= alpha;
+            }
+            m_run = m_new;
+
+            // O^T += V^T P^T (a5)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const uint16_t *vrow = &sVT[buf][(32 * db + l32) * C::VTS + 8 * g];
+#pragma unroll
+                for (int kc = 0; kc < BN / 16; ++kc) {
+                    Frag8 f;
+                    f.u = *(const uint4 *)(vrow + 16 * kc);
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.v, pf[kc].v, acc[db], 0, 0, 0);
+                }
+            }
+        }
+
+        if (has_next)
+            store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue (a6) ----------------------------------------------------
+    const float l_tot = halves_sum(l_half);
+    const float lx_tot = halves_sum(lx_half);
+    if (my_q < Sq) {
+        const bool empty = !(l_tot > 0.f);
+        const float inv = empty ? 0.f : 1.f / l_tot;
+        uint16_t *orow = a.o + (qrow0 + my_q) * D + 4 * g;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int rho = 0; rho < 4; ++rho) {
+                uint2 w;
+                if (empty) {
+                    w = make_uint2(0, 0);
+                } else {
+                    w.x = pack_bf16x2(acc[db][4 * rho] * inv, acc[db][4 * rho + 1] * inv);
+                    w.y = pack_bf16x2(acc[db][4 * rho + 2] * inv, acc[db][4 * rho + 3] * inv);
+                }
+                *(uint2 *)(orow + 32 * db + 8 * rho) = w;
+            }
+        if (g == 0)
+            a.lse[qrow0 + my_q] = empty ? -INFINITY : m_run * a.scale + logf(lx_tot);
+    }
+}
+
+template <int D, int BN, int NW, bool CAUSAL>
+hipError_t launch(const FwdArgs &a, hipStream_t stream)
+{
+    constexpr int BM = NW * 32;
+    const int n_qtiles = (a.Sq + BM - 1) / BM;
+    const long long n_tiles = (long long)a.B * a.Hq * n_qtiles;
+    if (n_tiles > 0x7fffffffLL)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_kernel<D, BN, NW, CAUSAL>), dim3((unsigned)n_tiles), dim3(NW * 64),
+                       0, stream, a, n_qtiles, (int)n_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
+{
+    switch (d) {
+    case 64:
+        return causal ? launch<64, 64, 4, true>(a, stream) : launch<64, 64, 4, false>(a, stream);
+    case 128:
+        return causal ? launch<128, 64, 4, true>(a, stream) : launch<128, 64, 4, false>(a, stream);
+    case 256:
+        return causal ? launch<256, 64, 4, true>(a, stream) : launch<256, 64, 4, false>(a, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace miattn

@@ -1,0 +1,109 @@
+"""ctypes binding of libmiattn (argument marshalling only).
+
+Every entry point has the name and argument order of its C declaration in
+``include/miattn.h``. Tensor arguments may be torch tensors (their
+``data_ptr()`` is passed) or raw integer device addresses; ``stream`` may be a
+``torch.cuda.Stream``, a raw ``hipStream_t`` integer, or None for torch's
+current stream. A non-OK status raises :class:`MiattnError` carrying the
+library's message. All compute happens in the HIP library; when it is not
+built or cannot be loaded, every call fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("MIATTN_LIB", os.path.join(_PKG, "libmiattn.so"))
+
+MIATTN_OK = 0
+MIATTN_ERR_INVALID_ARG = 1
+MIATTN_ERR_UNSUPPORTED = 2
+MIATTN_ERR_HIP = 3
+
+EXPORTS = ("attn_fwd", "attn_fwd_decode_workspace_size", "attn_fwd_decode",
+           "miattn_last_error", "miattn_version")
+
+
+class MiattnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libmiattn status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the library (building it first if no build exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        from . import build as _build
+        _build.build(out=path)
+    L = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    L.attn_fwd.restype = i
+    L.attn_fwd_decode_workspace_size.argtypes = [i, i, i, i]
+    L.attn_fwd_decode_workspace_size.restype = ctypes.c_size_t
+    L.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp,
+                                  ctypes.c_size_t, vp]
+    L.attn_fwd_decode.restype = i
+    L.miattn_last_error.argtypes = []
+    L.miattn_last_error.restype = ctypes.c_char_p
+    L.miattn_version.argtypes = []
+    L.miattn_version.restype = i
+    _lib = L
+    return L
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(rc: int):
+    if rc != MIATTN_OK:
+        raise MiattnError(rc, miattn_last_error())
+
+
+def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, scale, stream=None):
+    _check(load().attn_fwd(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), int(B),
+                           int(Hq), int(Hkv), int(Sq), int(Sk), int(d), int(bool(causal)),
+                           float(scale), _stream(stream)))
+
+
+def attn_fwd_decode_workspace_size(B, Hq, d, num_splits) -> int:
+    return int(load().attn_fwd_decode_workspace_size(int(B), int(Hq), int(d), int(num_splits)))
+
+
+def attn_fwd_decode(q, k_cache, v_cache, kv_lens, o, lse, B, Hq, Hkv, S_cap, d, num_splits,
+                    scale, workspace, workspace_bytes, stream=None):
+    _check(load().attn_fwd_decode(_addr(q), _addr(k_cache), _addr(v_cache), _addr(kv_lens),
+                                  _addr(o), _addr(lse), int(B), int(Hq), int(Hkv), int(S_cap),
+                                  int(d), int(num_splits), float(scale), _addr(workspace),
+                                  int(workspace_bytes), _stream(stream)))
+
+
+def miattn_last_error() -> str:
+    msg = load().miattn_last_error()
+    return msg.decode() if msg else ""
+
+
+def miattn_version() -> int:
+    return int(load().miattn_version())

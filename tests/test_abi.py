@@ -1,0 +1,129 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+entry point include/miattn.h declares, and rejects bad arguments with the
+documented status before anything is launched."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from online_softmax_monoid_amd import miattn as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "miattn.h")).read()
+    return sorted(set(re.findall(r"^MIATTN_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(M.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(M.LIB_PATH if os.path.exists(M.LIB_PATH) else M.load()._name)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_workspace_size():
+    assert M.miattn_version() == 100
+    assert M.attn_fwd_decode_workspace_size(32, 32, 128, 16) == 32 * 32 * 16 * 130 * 4
+    assert M.attn_fwd_decode_workspace_size(0, 32, 128, 16) == 0
+    assert M.attn_fwd_decode_workspace_size(1, 0, 128, 16) == 0
+    assert M.attn_fwd_decode_workspace_size(1, 1, 128, 0) == 0
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _fwd(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=2, Hkv=2, Sq=8, Sk=8, d=64,
+                causal=0, scale=0.125, stream=0)
+    args.update(kw)
+    return M.load().attn_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                             args["B"], args["Hq"], args["Hkv"], args["Sq"], args["Sk"],
+                             args["d"], args["causal"], args["scale"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=0), M.MIATTN_ERR_INVALID_ARG, "q is NULL"),
+    (dict(k=0), M.MIATTN_ERR_INVALID_ARG, "k is NULL"),
+    (dict(v=0), M.MIATTN_ERR_INVALID_ARG, "v is NULL"),
+    (dict(o=0), M.MIATTN_ERR_INVALID_ARG, "o is NULL"),
+    (dict(lse=0), M.MIATTN_ERR_INVALID_ARG, "lse is NULL"),
+    (dict(q=FAKE + 8), M.MIATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(lse=FAKE + 2), M.MIATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(Hq=3, Hkv=2), M.MIATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(Hkv=0), M.MIATTN_ERR_INVALID_ARG, "head counts"),
+    (dict(B=-1), M.MIATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(Sk=-1), M.MIATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(d=96), M.MIATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(d=32), M.MIATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(scale=0.0), M.MIATTN_ERR_INVALID_ARG, "scale"),
+    (dict(scale=-1.0), M.MIATTN_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("inf")), M.MIATTN_ERR_INVALID_ARG, "scale"),
+    (dict(scale=float("nan")), M.MIATTN_ERR_INVALID_ARG, "scale"),
+])
+def test_attn_fwd_rejects(kw, status, needle):
+    assert _fwd(**kw) == status
+    assert needle in M.miattn_last_error()
+
+
+def test_attn_fwd_empty_is_a_no_op():
+    assert _fwd(B=0, q=0, k=0, v=0, o=0, lse=0) == M.MIATTN_OK
+    assert _fwd(Sq=0, q=0, k=0, v=0, o=0, lse=0) == M.MIATTN_OK
+
+
+def test_binding_raises_with_message():
+    with pytest.raises(M.MiattnError) as e:
+        M.attn_fwd(0, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 8, 8, 64, False, 0.125, stream=0)
+    assert e.value.status == M.MIATTN_ERR_INVALID_ARG and "q is NULL" in e.value.message
+
+
+def _dec(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, o=FAKE, lse=FAKE, B=2, Hq=4, Hkv=2, S_cap=16,
+                d=128, ns=4, scale=0.1, ws=FAKE, wsb=None, stream=0)
+    args.update(kw)
+    if args["wsb"] is None:
+        args["wsb"] = M.attn_fwd_decode_workspace_size(args["B"], args["Hq"], args["d"],
+                                                       max(args["ns"], 1))
+    return M.load().attn_fwd_decode(args["q"], args["k"], args["v"], args["lens"], args["o"],
+                                    args["lse"], args["B"], args["Hq"], args["Hkv"],
+                                    args["S_cap"], args["d"], args["ns"], args["scale"],
+                                    args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=0), M.MIATTN_ERR_INVALID_ARG, "q is NULL"),
+    (dict(lens=0), M.MIATTN_ERR_INVALID_ARG, "kv_lens is NULL"),
+    (dict(k=0), M.MIATTN_ERR_INVALID_ARG, "k_cache is NULL"),
+    (dict(ws=0), M.MIATTN_ERR_INVALID_ARG, "workspace is NULL"),
+    (dict(ws=FAKE + 4), M.MIATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(wsb=100), M.MIATTN_ERR_INVALID_ARG, "workspace too small"),
+    (dict(ns=0), M.MIATTN_ERR_INVALID_ARG, "num_splits"),
+    (dict(Hq=5), M.MIATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(d=80), M.MIATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(scale=0.0), M.MIATTN_ERR_INVALID_ARG, "scale"),
+    (dict(S_cap=-1), M.MIATTN_ERR_INVALID_ARG, "sizes"),
+])
+def test_attn_fwd_decode_rejects(kw, status, needle):
+    assert _dec(**kw) == status
+    assert needle in M.miattn_last_error()
+
+
+def test_decode_empty_batch_is_a_no_op():
+    assert _dec(B=0, q=0, k=0, v=0, lens=0, o=0, lse=0, ws=0, wsb=0) == M.MIATTN_OK
+
+
+def test_product_path_does_not_import_the_oracle():
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from online_softmax_monoid_amd import miattn, inputs\n"
+            "miattn.load()\n"
+            "assert 'oracle' not in sys.modules, sorted(sys.modules)\n") % ROOT
+    subprocess.run([sys.executable, "-c", code], check=True)

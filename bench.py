@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark of libmiattn's hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * attn_fwd on the Llama-class causal prefill workload
+    (B=2, Hq=Hkv=32, Sq=Sk=4096, d=128, bf16, N(0,1)*0.5), and
+  * attn_fwd_decode on the batched decode workload (32 streams, Hq=32, Hkv=8,
+    d=128, lengths U[1024, 8192], 16 splits; split kernel + combine kernel).
+
+`value` is the prefill throughput in TFLOP/s (4*B*Hq*Sq*Sk*d, halved for
+causal) from HIP events recorded around every prefill launch on its stream;
+the decode HBM throughput and the long-context GQA workload (B=1, Hq=16,
+Hkv=2, S=44032, d=256, causal) are reported beside it. Inputs are resident in
+HBM before the timed region starts. The f64 oracle, timed on a bounded row
+sample of the prefill workload on the host cores, is reported as a baseline.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --profile-pass   # short fixed launch sequence for rocprofv3
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (fraction of bf16 MFMA peak); decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU * 4096 flop/clk * 2.4 GHz
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PREFILL_WID, LONG_WID, DECODE_WID = 3, 4, 5
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_b2_h32_s4096_d128_causal_traffic.txt")
+KERNEL_SOURCES = ("online_softmax_monoid_amd/csrc/prefill.hip",)
+
+
+def dev_bits(bits):
+    """uint16 host bits -> int16 device tensor with the same bits."""
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per prefill launch from the committed counter summary, or None
+    when it is missing or was taken on a different kernel source."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+class Prefill:
+    def __init__(self, w, torch):
+        from online_softmax_monoid_amd import inputs
+        self.w = w
+        q, k, v = inputs.prefill_inputs(w)
+        self.q, self.k, self.v = dev_bits(q), dev_bits(k), dev_bits(v)
+        n = w.B * w.Hq * w.Sq
+        self.o = torch.empty(n * w.d, dtype=torch.int16, device="cuda")
+        self.lse = torch.empty(n, dtype=torch.float32, device="cuda")
+        self.causal = w.causal[0]
+        self.flops = w.flops(self.causal)
+
+    def __call__(self, stream):
+        from online_softmax_monoid_amd import miattn
+        w = self.w
+        miattn.attn_fwd(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Sq, w.Sk,
+                        w.d, self.causal, w.scale, stream)
+
+
+class Decode:
+    """Two independent KV-cache copies, used alternately, so consecutive steps
+    cannot serve K/V from the 256 MB last-level cache."""
+
+    def __init__(self, w, torch):
+        import numpy as np
+        from online_softmax_monoid_amd import inputs, miattn
+        self.w = w
+        lens, q, kc, vc = inputs.decode_inputs(w)
+        self.lens_host = lens
+        self.q = dev_bits(q)
+        self.caches = [(dev_bits(kc), dev_bits(vc))]
+        self.caches.append((self.caches[0][0].clone(), self.caches[0][1].clone()))
+        self.lens = torch.from_numpy(lens.astype(np.int32)).to("cuda")
+        self.o = torch.empty(w.B * w.Hq * w.d, dtype=torch.int16, device="cuda")
+        self.lse = torch.empty(w.B * w.Hq, dtype=torch.float32, device="cuda")
+        self.ws_bytes = miattn.attn_fwd_decode_workspace_size(w.B, w.Hq, w.d, w.num_splits)
+        self.ws = torch.empty(self.ws_bytes // 4, dtype=torch.float32, device="cuda")
+        self.i = 0
+        # algorithmic HBM bytes: every valid K and V row once, Q in, O and LSE out
+        self.bytes = (2 * int(lens.sum()) * w.Hkv * w.d * 2 + 2 * w.B * w.Hq * w.d * 2
+                      + 4 * w.B * w.Hq)
+
+    def __call__(self, stream):
+        from online_softmax_monoid_amd import miattn
+        w = self.w
+        kc, vc = self.caches[self.i & 1]
+        self.i += 1
+        miattn.attn_fwd_decode(self.q, kc, vc, self.lens, self.o, self.lse, w.B, w.Hq, w.Hkv,
+                               w.S_cap, w.d, w.num_splits, w.scale, self.ws, self.ws_bytes,
+                               stream)
+
+
+def time_launches(fn, stream, torch, n):
+    """Per-launch durations (ms) from HIP events recorded on the launch stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            a.record(stream)
+            fn(stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(target_seconds: float = 12.0):
+    """The f64 oracle on a bounded random row sample of the prefill workload."""
+    import numpy as np
+    import oracle
+    from online_softmax_monoid_amd import inputs
+    w = inputs.WORKLOADS[PREFILL_WID]
+    q, k, v = inputs.prefill_inputs(w)
+    causal = w.causal[0]
+    total_rows = w.B * w.Hq * w.Sq
+    rng = np.random.Generator(np.random.PCG64(w.seed + 7))
+    threads = oracle.max_threads()
+
+    def row_flops(rows):
+        i = rows % w.Sq
+        keys = np.minimum(w.Sk, i + (w.Sk - w.Sq) + 1) if causal else np.full(rows.shape, w.Sk)
+        return float(np.sum(4.0 * w.d * keys))
+
+    probe = np.sort(rng.choice(total_rows, size=2048, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, causal, w.scale, rows=probe)
+    dt = time.perf_counter() - t0
+    rate = row_flops(probe) / dt
+    n = int(min(total_rows, max(2048, target_seconds * rate / (row_flops(probe) / 2048))))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attn_fwd(q, k, v, causal, w.scale, rows=rows)
+    dt = time.perf_counter() - t0
+    fl = row_flops(rows)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {total_rows} query rows (uniform random, seed {w.seed + 7}) of "
+                      f"the B2 H32 S4096 d128 causal prefill, f64 two-pass, {dt:.1f} s, "
+                      f"{fl / 1e9:.1f} GFLOP"}
+
+
+def profile_pass():
+    """A short fixed sequence for rocprofv3: a plain 1 GiB device copy (the
+    counter calibration), 3 prefill launches, 3 decode launches."""
+    import torch
+    from online_softmax_monoid_amd import inputs
+    stream = torch.cuda.current_stream()
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    pre = Prefill(inputs.WORKLOADS[PREFILL_WID], torch)
+    dec = Decode(inputs.WORKLOADS[DECODE_WID], torch)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        pre(stream)
+    for _ in range(3):
+        dec(stream)
+    torch.cuda.synchronize()
+    log("profile pass done")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--long-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    if args.profile_pass:
+        profile_pass()
+        return
+
+    import torch
+    from online_softmax_monoid_amd import inputs, miattn
+    miattn.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    log("bench: drawing inputs")
+    pre = Prefill(inputs.WORKLOADS[PREFILL_WID], torch)
+    dec = Decode(inputs.WORKLOADS[DECODE_WID], torch)
+    torch.cuda.synchronize()
+
+    def step(s):
+        pre(s)
+        dec(s)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(stream)
+    torch.cuda.synchronize()
+
+    log(f"bench: timing {args.steps} steps")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        pre(stream)
+        e[1].record(stream)
+        dec(stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    dec_ms = [b.elapsed_time(c) for _, b, c in ev]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    tflops = pre.flops / (pre_avg * 1e-3) / 1e12
+    dec_gbs = dec.bytes / (dec_avg * 1e-3) / 1e9
+    log(f"bench: prefill {pre_avg:.4f} ms ({tflops:.1f} TFLOP/s), decode {dec_avg:.4f} ms "
+        f"({dec_gbs:.0f} GB/s)")
+    del pre
+    torch.cuda.empty_cache()
+
+    log("bench: long-context GQA workload")
+    lw = inputs.WORKLOADS[LONG_WID]
+    lng = Prefill(lw, torch)
+    time_launches(lng, stream, torch, 1)
+    lms = time_launches(lng, stream, torch, args.long_steps)
+    l_avg = sum(lms) / len(lms)
+    l_tflops = lng.flops / (l_avg * 1e-3) / 1e12
+    log(f"bench: long-context {l_avg:.3f} ms ({l_tflops:.1f} TFLOP/s)")
+    del lng
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (f64 oracle on a row sample)")
+        cpu = cpu_baseline()
+
+    traffic = measured_traffic()
+    pw, dw = inputs.WORKLOADS[PREFILL_WID], inputs.WORKLOADS[DECODE_WID]
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-class causal prefill B=2 Hq=Hkv=32 Sq=Sk=4096 d=128 bf16 "
+                        "+ batched split-KV decode B=32 Hq=32 Hkv=8 d=128 len U[1024,8192] "
+                        "16 splits",
+            "prefill": {"B": pw.B, "Hq": pw.Hq, "Hkv": pw.Hkv, "Sq": pw.Sq, "Sk": pw.Sk,
+                        "d": pw.d, "causal": True, "flops": pw.flops(True)},
+            "decode": {"B": dw.B, "Hq": dw.Hq, "Hkv": dw.Hkv, "d": dw.d,
+                       "kv_len_sum": int(dec.lens_host.sum()), "splits": dw.num_splits},
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "prefill_ms": round(pre_avg, 4),
+        "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "ms": round(dec_avg, 4),
+                   "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "bound": "hbm",
+                   "algorithmic_bytes": dec.bytes},
+        "long_context_gqa_d256": {"value": round(l_tflops, 2), "unit": "TFLOP/s",
+                                  "ms": round(l_avg, 3),
+                                  "frac": round(l_tflops / PEAK_BF16_TFLOPS, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,6 +31,9 @@ def hipcc() -> str:
 def flags(extra=()):
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in VGPRs: the online-softmax rescale and the
+            # epilogue touch them with VALU ops, which cannot address AGPRs
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-fvisibility=hidden", "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC, *extra]
 
 

@@ -80,6 +80,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, p);
 }
 
+// Raw buffer resource over [base, base + bytes): loads past the end return 0,
+// which is how ragged tails and rows beyond Sq/Sk are read without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // Physical tile index -> logical tile index. Consecutive logical tiles land on
 // one XCD: physical id x runs on XCD x % 8.
 __device__ __forceinline__ int xcd_remap(int id, int n)
@@ -116,7 +129,7 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int l32 = lane & 31;
     const int g = lane >> 5;
 
@@ -158,12 +171,12 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
     // ---- Q fragment: B operand of S^T = K Q^T (a1) ------------------------
     bf16x8 qf[D / 16];
     {
-        const bool ok = my_q < Sq;
-        const uint16_t *qr = a.q + (qrow0 + (ok ? my_q : 0)) * D + 8 * g;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0 * D, (uint32_t)Sq * D * 2);
+        const uint32_t off = (uint32_t)my_q * D * 2 + 16 * g;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             Frag8 f;
-            f.u = ok ? *(const uint4 *)(qr + 16 * kk) : make_uint4(0, 0, 0, 0);
+            f.u = buf_load16(rq, off + 32 * kk);  // rows >= Sq read as 0
             qf[kk] = f.v;
         }
     }
@@ -172,26 +185,25 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
     uint4 kreg[C::KPT];
     uint4 vreg[C::VPT][4];
 
+    // keys at or beyond Sk read as 0 (buffer range check)
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kp, (uint32_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vp, (uint32_t)Sk * D * 2);
     auto load_tile = [&](int j0) {
+        const uint32_t base = (uint32_t)j0 * D * 2;
 #pragma unroll
         for (int u = 0; u < C::KPT; ++u) {
-            const int ci = tid + C::NT * u;
-            const int key = ci / C::KCH, c = ci % C::KCH;
-            kreg[u] = (j0 + key < Sk)
-                ? *(const uint4 *)(Kp + (int64_t)(j0 + key) * D + 8 * c)
-                : make_uint4(0, 0, 0, 0);
+            const int ci = tid + C::NT * u;  // 16-byte chunk ci of the tile, row-major
+            kreg[u] = buf_load16(rk, base + 16 * ci);
         }
 #pragma unroll
         for (int w = 0; w < C::VPT; ++w) {
             const int un = tid + C::NT * w;
             const int kg = un % (BN / 4), dc = un / (BN / 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = j0 + 4 * kg + i;
-                vreg[w][i] = (un < C::VUNITS && key < Sk)
-                    ? *(const uint4 *)(Vp + (int64_t)key * D + 8 * dc)
+            for (int i = 0; i < 4; ++i)
+                vreg[w][i] = (C::VUNITS % C::NT == 0 || un < C::VUNITS)
+                    ? buf_load16(rv, base + (uint32_t)(4 * kg + i) * D * 2 + 16 * dc)
                     : make_uint4(0, 0, 0, 0);
-            }
         }
     };
 
@@ -242,10 +254,13 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
         for (int r = 0; r < 16; ++r)
             acc[db][r] = 0.f;
 
-    if (nblk > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
+    // Stage tile 0 on every path (an empty key range reads zeros) and drain
+    // all global loads, so no load issued before the loop is still in flight
+    // when it starts: the prefetch issued inside the loop is then waited on
+    // only where its registers are consumed.
+    load_tile(0);
+    store_tile(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
     for (int blk = 0; blk < nblk; ++blk) {

@@ -119,7 +119,7 @@ struct Cfg {
     static_assert((BN * KCH) % NT == 0, "K tile must split evenly over threads");
 };
 
-template <int D, int BN, int NW, bool CAUSAL>
+template <int D, int BN, int NW, bool PIPE, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64)
 fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
 {
@@ -181,20 +181,27 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
         }
     }
 
-    // ---- staging helpers (a2) -------------------------------------------
+    // ---- staging (a2) -----------------------------------------------------
+    // K runs one tile ahead of V: while tile j's softmax runs on the VALU, the
+    // MFMAs already compute tile j+1's scores. LDS holds K tiles j+1 (being
+    // read) and V tile j; the global loads of K tile j+2 and V tile j+1 are in
+    // flight in registers meanwhile and land in the buffers freed by tile j-1.
     uint4 kreg[C::KPT];
     uint4 vreg[C::VPT][4];
 
     // keys at or beyond Sk read as 0 (buffer range check)
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kp, (uint32_t)Sk * D * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vp, (uint32_t)Sk * D * 2);
-    auto load_tile = [&](int j0) {
-        const uint32_t base = (uint32_t)j0 * D * 2;
+    auto load_k = [&](int blk) {
+        const uint32_t base = (uint32_t)blk * BN * D * 2;
 #pragma unroll
         for (int u = 0; u < C::KPT; ++u) {
             const int ci = tid + C::NT * u;  // 16-byte chunk ci of the tile, row-major
             kreg[u] = buf_load16(rk, base + 16 * ci);
         }
+    };
+    auto load_v = [&](int blk) {
+        const uint32_t base = (uint32_t)blk * BN * D * 2;
 #pragma unroll
         for (int w = 0; w < C::VPT; ++w) {
             const int un = tid + C::NT * w;
@@ -206,14 +213,15 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
                     : make_uint4(0, 0, 0, 0);
         }
     };
-
-    auto store_tile = [&](int buf) {
+    auto store_k = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < C::KPT; ++u) {
             const int ci = tid + C::NT * u;
             const int key = ci / C::KCH, c = ci % C::KCH;
             *(uint4 *)(&sK[buf][key * D + 8 * (c ^ (key & C::SWZ))]) = kreg[u];
         }
+    };
+    auto store_v = [&](int buf) {
 #pragma unroll
         for (int w = 0; w < C::VPT; ++w) {
             const int un = tid + C::NT * w;
@@ -242,11 +250,35 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
         }
     };
 
+    // S^T = K Q^T for the tile in K buffer `buf` (a2)
+    auto scores = [&](int buf, f32x16 (&s)[BN / 32]) {
+#pragma unroll
+        for (int bb = 0; bb < BN / 32; ++bb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[bb][r] = 0.f;
+            const int key = 32 * bb + l32;
+            const uint16_t *krow = &sK[buf][key * D];
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) {
+                Frag8 f;
+                f.u = *(const uint4 *)(krow + 8 * ((2 * kk + g) ^ (key & C::SWZ)));
+                s[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.v, qf[kk], s[bb], 0, 0, 0);
+            }
+        }
+    };
+
     // ---- running monoid state of this lane's query row (a4) ---------------
+    // m_ref is a reference maximum: probabilities are exp2((s - m_ref) * c).
+    // It moves (and the state is rescaled) only when a tile's maximum exceeds
+    // it by more than kLazy in log2 units, so p stays below 2^kLazy; O = acc/l
+    // and LSE = m_ref*scale + ln(l) are the same for any reference.
+    constexpr float kLazy = 8.f;
     const float c = a.scale * kLog2e;
-    float m_run = -INFINITY;  // running max of raw scores q.k
-    float l_half = 0.f;       // running sum of the bf16-rounded P of this lane half
-    float lx_half = 0.f;      // running sum of the unrounded P (for LSE)
+    const float thr = kLazy / c;  // in raw score units
+    float m_ref = -INFINITY;
+    float l_half = 0.f;   // running sum of the bf16-rounded P of this lane half
+    float lx_half = 0.f;  // running sum of the unrounded P (for LSE)
     f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -254,110 +286,131 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
         for (int r = 0; r < 16; ++r)
             acc[db][r] = 0.f;
 
-    // Stage tile 0 on every path (an empty key range reads zeros) and drain
-    // all global loads, so no load issued before the loop is still in flight
-    // when it starts: the prefetch issued inside the loop is then waited on
-    // only where its registers are consumed.
-    load_tile(0);
-    store_tile(0);
+    // mask (a3), monoid update (a4) and value contraction (a5) of tile blk
+    auto softmax_pv = [&](int blk, f32x16 (&s)[BN / 32]) {
+        const int j0 = blk * BN;
+        const bool full = (j0 + BN <= Sk) && (!CAUSAL || j0 + BN - 1 <= q0 + diag);
+        if (!full) {
+            const int lim = CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1;
+#pragma unroll
+            for (int bb = 0; bb < BN / 32; ++bb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = j0 + 32 * bb + 8 * (r >> 2) + 4 * g + (r & 3);
+                    s[bb][r] = (key <= lim) ? s[bb][r] : -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int bb = 0; bb < BN / 32; ++bb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                mx = fmaxf(mx, s[bb][r]);
+        mx = halves_max(mx);
+        if (__any(mx > m_ref + thr)) {  // rare after the first tile
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);  // 0 if m_ref = -inf
+            l_half *= alpha;
+            lx_half *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[db][r] *= alpha;
+            m_ref = m_new;
+        }
+        const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
+
+        Frag8 pf[BN / 16];
+        float rs = 0.f, rx = 0.f;
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int bb = 0; bb < BN / 32; ++bb)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][8 * h + 2 * w], c, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][8 * h + 2 * w + 1], c, -mc));
+                    const uint32_t pk = pack_bf16x2(p0, p1);
+                    pf[2 * bb + h].w[w] = pk;
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, rs, false);
+                    rx += p0 + p1;
+                }
+        l_half += rs;
+        lx_half += rx;
+
+        // O^T += V^T P^T (a5)
+        const int vb = blk & 1;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const uint16_t *vrow = &sVT[vb][(32 * db + l32) * C::VTS + 8 * g];
+#pragma unroll
+            for (int kc = 0; kc < BN / 16; ++kc) {
+                Frag8 f;
+                f.u = *(const uint4 *)(vrow + 16 * kc);
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.v, pf[kc].v, acc[db], 0, 0, 0);
+            }
+        }
+    };
+
+    // Blocks this wave computes (the workgroup iterates over nblk for the
+    // barriers; fully masked tiles of a wave are skipped).
+    const int nwb = (wave_end + BN - 1) / BN;
+
+    // ---- prologue: K tiles 0 and 1, V tile 0; scores of tile 0 -------------
+    // Staged on every path (an empty key range reads zeros), then all global
+    // loads are drained, so none issued before the loop is still in flight in
+    // it: the prefetch issued inside the loop is waited on only where its
+    // registers are consumed.
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
+    if (PIPE && nblk > 1) {
+        load_k(1);
+        store_k(1);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int buf = blk & 1;
-        const int j0 = blk * BN;
-        const bool has_next = blk + 1 < nblk;
-        if (has_next)
-            load_tile(j0 + BN);
+    f32x16 sa[BN / 32], sb[BN / 32];
+    if (PIPE && nwb > 0)
+        scores(0, sa);
 
-        if (j0 < wave_end) {
-            // S^T = K Q^T
-            f32x16 s[BN / 32];
-#pragma unroll
-            for (int bb = 0; bb < BN / 32; ++bb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    s[bb][r] = 0.f;
-                const int key = 32 * bb + l32;
-                const uint16_t *krow = &sK[buf][key * D];
-#pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    Frag8 f;
-                    f.u = *(const uint4 *)(krow + 8 * ((2 * kk + g) ^ (key & C::SWZ)));
-                    s[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.v, qf[kk], s[bb], 0, 0, 0);
-                }
+    // one pipelined step: softmax + PV of tile j (scores in `cur`) while the
+    // MFMAs compute tile j+1's scores into `nxt`; then restage and sync.
+    // Without PIPE, K and V tiles travel together and the scores of tile j
+    // are computed at the start of step j.
+    auto step = [&](int j, f32x16 (&cur)[BN / 32], f32x16 (&nxt)[BN / 32]) {
+        constexpr int KA = PIPE ? 2 : 1;  // how far K is staged ahead
+        if (j + KA < nblk)
+            load_k(j + KA);
+        if (j + 1 < nblk)
+            load_v(j + 1);
+        if (j < nwb) {
+            if (PIPE) {
+                if (j + 1 < nwb)
+                    scores((j + 1) & 1, nxt);
+            } else {
+                scores(j & 1, cur);
             }
-
-            // mask by select (a3)
-            const bool full = (j0 + BN <= Sk) && (!CAUSAL || j0 + BN - 1 <= q0 + diag);
-            if (!full) {
-                const int lim = CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1;
-#pragma unroll
-                for (int bb = 0; bb < BN / 32; ++bb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = j0 + 32 * bb + 8 * (r >> 2) + 4 * g + (r & 3);
-                        s[bb][r] = (key <= lim) ? s[bb][r] : -INFINITY;
-                    }
-            }
-
-            // online-softmax update (a4)
-            float mx = -INFINITY;
-#pragma unroll
-            for (int bb = 0; bb < BN / 32; ++bb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    mx = fmaxf(mx, s[bb][r]);
-            mx = halves_max(mx);
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
-            const float mc = m_use * c;
-
-            Frag8 pf[BN / 16];
-            float rs = 0.f, rx = 0.f;
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int bb = 0; bb < BN / 32; ++bb)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][8 * h + 2 * w], c, -mc));
-                        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][8 * h + 2 * w + 1], c, -mc));
-                        const uint32_t pk = pack_bf16x2(p0, p1);
-                        pf[2 * bb + h].w[w] = pk;
-                        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, rs, false);
-                        rx += p0 + p1;
-                    }
-            l_half = l_half * alpha + rs;
-            lx_half = lx_half * alpha + rx;
-            if (__any(m_new > m_run)) {
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[db][r] *= alpha;
-            }
-            m_run = m_new;
-
-            // O^T += V^T P^T (a5)
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const uint16_t *vrow = &sVT[buf][(32 * db + l32) * C::VTS + 8 * g];
-#pragma unroll
-                for (int kc = 0; kc < BN / 16; ++kc) {
-                    Frag8 f;
-                    f.u = *(const uint4 *)(vrow + 16 * kc);
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.v, pf[kc].v, acc[db], 0, 0, 0);
-                }
-            }
+            softmax_pv(j, cur);
         }
-
-        if (has_next)
-            store_tile(buf ^ 1);
+        if (j + KA < nblk)
+            store_k((j + KA) & 1);
+        if (j + 1 < nblk)
+            store_v((j + 1) & 1);
         __syncthreads();
+    };
+
+    int j = 0;
+    for (; j + 1 < nblk; j += 2) {
+        step(j, sa, sb);
+        step(j + 1, sb, sa);
     }
+    if (j < nblk)
+        step(j, sa, sb);
 
     // ---- epilogue (a6) ----------------------------------------------------
     const float l_tot = halves_sum(l_half);
@@ -380,11 +433,11 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
                 *(uint2 *)(orow + 32 * db + 8 * rho) = w;
             }
         if (g == 0)
-            a.lse[qrow0 + my_q] = empty ? -INFINITY : m_run * a.scale + logf(lx_tot);
+            a.lse[qrow0 + my_q] = empty ? -INFINITY : m_ref * a.scale + logf(lx_tot);
     }
 }
 
-template <int D, int BN, int NW, bool CAUSAL>
+template <int D, int BN, int NW, bool PIPE, bool CAUSAL>
 hipError_t launch(const FwdArgs &a, hipStream_t stream)
 {
     constexpr int BM = NW * 32;
@@ -392,22 +445,37 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream)
     const long long n_tiles = (long long)a.B * a.Hq * n_qtiles;
     if (n_tiles > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_kernel<D, BN, NW, CAUSAL>), dim3((unsigned)n_tiles), dim3(NW * 64),
+    hipLaunchKernelGGL((fwd_kernel<D, BN, NW, PIPE, CAUSAL>), dim3((unsigned)n_tiles), dim3(NW * 64),
                        0, stream, a, n_qtiles, (int)n_tiles);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// Tile configuration per head dimension: <BN keys per tile, NW waves,
+// K staged one tile ahead of V>.
+#ifndef MIATTN_FWD_D64
+#define MIATTN_FWD_D64 64, 4, false
+#endif
+#ifndef MIATTN_FWD_D128
+#define MIATTN_FWD_D128 64, 4, false
+#endif
+#ifndef MIATTN_FWD_D256
+#define MIATTN_FWD_D256 64, 4, false
+#endif
+
 hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
 {
     switch (d) {
     case 64:
-        return causal ? launch<64, 64, 4, true>(a, stream) : launch<64, 64, 4, false>(a, stream);
+        return causal ? launch<64, MIATTN_FWD_D64, true>(a, stream)
+                      : launch<64, MIATTN_FWD_D64, false>(a, stream);
     case 128:
-        return causal ? launch<128, 64, 4, true>(a, stream) : launch<128, 64, 4, false>(a, stream);
+        return causal ? launch<128, MIATTN_FWD_D128, true>(a, stream)
+                      : launch<128, MIATTN_FWD_D128, false>(a, stream);
     case 256:
-        return causal ? launch<256, 64, 4, true>(a, stream) : launch<256, 64, 4, false>(a, stream);
+        return causal ? launch<256, MIATTN_FWD_D256, true>(a, stream)
+                      : launch<256, MIATTN_FWD_D256, false>(a, stream);
     default:
         return hipErrorInvalidValue;
     }

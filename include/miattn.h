@@ -35,10 +35,10 @@
  *     values (NaN/inf there would propagate as 0 * NaN).
  *   - Accumulation is float32: scores and the monoid state in f32. In the
  *     prefill kernel the probabilities are rounded to bf16 (round to nearest
- *     even) before the value contraction; O is normalised by the sum of
- *     exactly those rounded values, LSE uses the sum of the unrounded f32
- *     probabilities. Decode keeps the probabilities in f32. O is rounded to
- *     bf16 (RNE) and LSE is stored as f32.
+ *     even) before the value contraction, while the row sum l that
+ *     normalises O and gives LSE adds the unrounded f32 probabilities.
+ *     Decode keeps the probabilities in f32. O is rounded to bf16 (RNE) and
+ *     LSE is stored as f32.
  *   - Return value: MIATTN_OK, or an error code with the message available
  *     from miattn_last_error(). Argument checks happen on the host before
  *     anything is enqueued; on error nothing is launched.

@@ -10,12 +10,11 @@
 //   (a2) S^T = K Q^T with v_mfma_f32_32x32x16_bf16: each lane owns one query
 //        column and 16 key rows of every 32x32 score block;
 //   (a3) scale and mask by select (masked key -> -inf, the identity of max);
-//   (a4) the online-softmax monoid update (tang paper, §2.2): new running
-//        max, rescale factor exp2((m_old - m_new)*c), probabilities
-//        exp2(s*c - m_new*c) with c = scale*log2(e), rounded to bf16; two row
-//        sums: the rounded P exactly as P.V consumes them (v_dot2 with ones;
-//        normalises O, so constant V gives exactly that constant) and the
-//        unrounded f32 P (gives LSE, free of the bf16 rounding of P);
+//   (a4) the online-softmax monoid update (tang paper, §2.2): reference max
+//        (moved lazily, see below), probabilities exp2(s*c - m*c) with
+//        c = scale*log2(e), rounded to bf16 for the value contraction, and
+//        their f32 row sum (plain adds: the packed bf16 dot instruction
+//        shares the matrix pipe on gfx950 and would stall the MFMAs);
 //   (a5) O^T += V^T P^T with the same MFMA, P used straight from registers as
 //        the B operand. The score accumulator holds keys
 //        {4g..4g+3, 8+4g..8+4g+3} of each 16-key chunk in lane half g; V^T is
@@ -277,8 +276,7 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
     const float c = a.scale * kLog2e;
     const float thr = kLazy / c;  // in raw score units
     float m_ref = -INFINITY;
-    float l_half = 0.f;   // running sum of the bf16-rounded P of this lane half
-    float lx_half = 0.f;  // running sum of the unrounded P (for LSE)
+    float l_half = 0.f;   // running sum of P over this lane half's keys (f32)
     f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -311,7 +309,6 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
             const float m_new = fmaxf(m_ref, mx);
             const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);  // 0 if m_ref = -inf
             l_half *= alpha;
-            lx_half *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -322,8 +319,7 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
         const float mc = (m_ref == -INFINITY) ? 0.f : m_ref * c;
 
         Frag8 pf[BN / 16];
-        float rs = 0.f, rx = 0.f;
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float rs = 0.f;
 #pragma unroll
         for (int bb = 0; bb < BN / 32; ++bb)
 #pragma unroll
@@ -334,11 +330,9 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
                     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][8 * h + 2 * w + 1], c, -mc));
                     const uint32_t pk = pack_bf16x2(p0, p1);
                     pf[2 * bb + h].w[w] = pk;
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, rs, false);
-                    rx += p0 + p1;
+                    rs += p0 + p1;
                 }
         l_half += rs;
-        lx_half += rx;
 
         // O^T += V^T P^T (a5)
         const int vb = blk & 1;
@@ -414,7 +408,6 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
 
     // ---- epilogue (a6) ----------------------------------------------------
     const float l_tot = halves_sum(l_half);
-    const float lx_tot = halves_sum(lx_half);
     if (my_q < Sq) {
         const bool empty = !(l_tot > 0.f);
         const float inv = empty ? 0.f : 1.f / l_tot;
@@ -433,7 +426,7 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
                 *(uint2 *)(orow + 32 * db + 8 * rho) = w;
             }
         if (g == 0)
-            a.lse[qrow0 + my_q] = empty ? -INFINITY : m_ref * a.scale + logf(lx_tot);
+            a.lse[qrow0 + my_q] = empty ? -INFINITY : m_ref * a.scale + logf(l_tot);
     }
 }
 
@@ -471,8 +464,12 @@ hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
         return causal ? launch<64, MIATTN_FWD_D64, true>(a, stream)
                       : launch<64, MIATTN_FWD_D64, false>(a, stream);
     case 128:
+#ifdef MIATTN_D128_PINGPONG
+        return launch_fwd_pp(a, causal, stream);
+#else
         return causal ? launch<128, MIATTN_FWD_D128, true>(a, stream)
                       : launch<128, MIATTN_FWD_D128, false>(a, stream);
+#endif
     case 256:
         return causal ? launch<256, MIATTN_FWD_D256, true>(a, stream)
                       : launch<256, MIATTN_FWD_D256, false>(a, stream);

@@ -146,12 +146,20 @@ def test_causal_first_row_and_masked_key_exactness(d):
 
 @pytest.mark.parametrize("d,causal", [(64, False), (128, True), (256, True)])
 def test_constant_values_give_that_constant(d, causal):
+    """Constant V: O equals the constant up to the bf16 rounding of P (the
+    value contraction sums bf16 probabilities, the normaliser their f32 sum):
+    within one bf16 ulp everywhere, exactly where a row sees a single key."""
     q = _rand_bits(41, (2, 2, 150, d), std=2.0)
     k = _rand_bits(42, (2, 2, 150, d), std=2.0)
-    c = inputs.f32_to_bf16_bits_scalar(-1.71875)
+    cval = -1.71875
+    c = inputs.f32_to_bf16_bits_scalar(cval)
     v = np.full((2, 2, 150, d), c, dtype=np.uint16)
     o, _, _ = H.run_fwd(q, k, v, causal, inputs.default_scale(d))
-    assert np.all(o == c)
+    of = inputs.bf16_to_f32(o).astype(np.float64)
+    assert np.max(np.abs(of - cval)) <= 2.0 ** -7 * 2  # one bf16 ulp at |c| in [1, 2)
+    assert np.mean(o == c) > 0.9
+    if causal:
+        assert np.all(o[:, :, 0] == c)
 
 
 def test_zero_keys_give_uniform_average():

@@ -464,8 +464,10 @@ hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
         return causal ? launch<64, MIATTN_FWD_D64, true>(a, stream)
                       : launch<64, MIATTN_FWD_D64, false>(a, stream);
     case 128:
-#ifdef MIATTN_D128_PINGPONG
+#if defined(MIATTN_D128_PINGPONG)
         return launch_fwd_pp(a, causal, stream);
+#elif defined(MIATTN_D128_Q64)
+        return launch_fwd_q64(a, causal, stream);
 #else
         return causal ? launch<128, MIATTN_FWD_D128, true>(a, stream)
                       : launch<128, MIATTN_FWD_D128, false>(a, stream);

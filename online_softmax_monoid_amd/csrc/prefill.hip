@@ -25,17 +25,22 @@
 //   (a6) epilogue on the reducing lanes (§2.3): O = acc / l, LSE = m*scale +
 //        ln l; rows with no visible key get O = +0 and LSE = -inf.
 //
-// The score matrix never leaves registers. Workgroups are ordered so that
-// all tiles of one (batch, kv-head) run back to back on one XCD
-// (workgroups are dispatched round-robin over the 8 XCDs), heaviest causal
-// tiles first, and the query heads of one GQA group sharing a kv-head are
-// adjacent.
+// The score matrix never leaves registers. Workgroups take their tiles in
+// the order of tile_order.h: each XCD owns a set of (batch, kv-head) units,
+// whose K and V then stay in its L2, and walks them heaviest causal tile
+// first; the query heads of one GQA group sharing a kv-head are adjacent.
+//
+// Head dimensions 64 and 256 use this kernel; head dimension 128 uses the
+// 64-rows-per-wave kernel of prefill_q64.hip (this one with
+// -DMIATTN_D128_SIMPLE, the two-group kernel of prefill_pp.hip with
+// -DMIATTN_D128_PINGPONG).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "launch.h"
+#include "tile_order.h"
 
 namespace miattn {
 namespace {
@@ -44,7 +49,6 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
-constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 
 union Frag8 {
@@ -94,14 +98,6 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 
 // Physical tile index -> logical tile index. Consecutive logical tiles land on
 // one XCD: physical id x runs on XCD x % 8.
-__device__ __forceinline__ int xcd_remap(int id, int n)
-{
-    const int per = n / kXcds;
-    if (id < per * kXcds)
-        return (id % kXcds) * per + id / kXcds;
-    return id;
-}
-
 template <int D, int BN, int NW>
 struct Cfg {
     static constexpr int NT = NW * 64;
@@ -120,7 +116,7 @@ struct Cfg {
 
 template <int D, int BN, int NW, bool PIPE, bool CAUSAL>
 __global__ void __launch_bounds__(NW * 64)
-fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
+fwd_kernel(FwdArgs a, int n_qtiles)
 {
     using C = Cfg<D, BN, NW>;
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][C::K_TILE];
@@ -134,13 +130,8 @@ fwd_kernel(FwdArgs a, int n_qtiles, int n_tiles)
 
     // ---- work decomposition ---------------------------------------------
     const int G = a.Hq / a.Hkv;
-    const int t = xcd_remap((int)blockIdx.x, n_tiles);
-    const int per_unit = G * n_qtiles;
-    const int unit = t / per_unit;
-    const int rem = t - unit * per_unit;
-    const int rank = rem / G;
-    const int gq = rem - rank * G;
-    const int qtile = CAUSAL ? (n_qtiles - 1 - rank) : rank;
+    const TileOrder to = tile_order((int)blockIdx.x, a.B * a.Hkv, G, n_qtiles, CAUSAL);
+    const int unit = to.unit, gq = to.gq, qtile = to.qtile;
     const int b = unit / a.Hkv;
     const int kvh = unit - b * a.Hkv;
     const int hq = kvh * G + gq;
@@ -439,7 +430,7 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream)
     if (n_tiles > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((fwd_kernel<D, BN, NW, PIPE, CAUSAL>), dim3((unsigned)n_tiles), dim3(NW * 64),
-                       0, stream, a, n_qtiles, (int)n_tiles);
+                       0, stream, a, n_qtiles);
     return hipGetLastError();
 }
 
@@ -466,11 +457,11 @@ hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
     case 128:
 #if defined(MIATTN_D128_PINGPONG)
         return launch_fwd_pp(a, causal, stream);
-#elif defined(MIATTN_D128_Q64)
-        return launch_fwd_q64(a, causal, stream);
-#else
+#elif defined(MIATTN_D128_SIMPLE)
         return causal ? launch<128, MIATTN_FWD_D128, true>(a, stream)
                       : launch<128, MIATTN_FWD_D128, false>(a, stream);
+#else
+        return launch_fwd_q64(a, causal, stream);
 #endif
     case 256:
         return causal ? launch<256, MIATTN_FWD_D256, true>(a, stream)

@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include "launch.h"
+#include "tile_order.h"
 
 namespace miattn {
 namespace {
@@ -45,7 +46,6 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int N>
@@ -107,14 +107,6 @@ __device__ __forceinline__ int opaque_lane()
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
 
-__device__ __forceinline__ int xcd_remap(int id, int n)
-{
-    const int per = n / kXcds;
-    if (id < per * kXcds)
-        return (id % kXcds) * per + id / kXcds;
-    return id;
-}
-
 // V rows: 16-byte chunk c of row r sits at chunk c ^ vswz(r). With this
 // pattern the four rows x four 8-byte column blocks addressed by one 16-lane
 // group of a transposing read land in distinct banks (32 or 64 banks).
@@ -125,7 +117,7 @@ __device__ __forceinline__ int vswz(int r)
 
 template <bool CAUSAL>
 __global__ void __launch_bounds__(512)
-fwd_pp_kernel(FwdArgs a, int n_qtiles, int n_tiles)
+fwd_pp_kernel(FwdArgs a, int n_qtiles)
 {
     constexpr int D = 128;
     constexpr int BN = 32;            // keys per tile
@@ -155,13 +147,8 @@ fwd_pp_kernel(FwdArgs a, int n_qtiles, int n_tiles)
 
     // ---- work decomposition (same order as prefill.hip) ---------------------
     const int G = a.Hq / a.Hkv;
-    const int t = xcd_remap((int)blockIdx.x, n_tiles);
-    const int per_unit = G * n_qtiles;
-    const int unit = t / per_unit;
-    const int rem = t - unit * per_unit;
-    const int rank = rem / G;
-    const int gq = rem - rank * G;
-    const int qtile = CAUSAL ? (n_qtiles - 1 - rank) : rank;
+    const TileOrder to = tile_order((int)blockIdx.x, a.B * a.Hkv, G, n_qtiles, CAUSAL);
+    const int unit = to.unit, gq = to.gq, qtile = to.qtile;
     const int b = unit / a.Hkv;
     const int kvh = unit - b * a.Hkv;
     const int hq = kvh * G + gq;
@@ -543,10 +530,10 @@ hipError_t launch_fwd_pp(const FwdArgs &a, bool causal, hipStream_t stream)
         return hipErrorInvalidConfiguration;
     if (causal)
         hipLaunchKernelGGL(fwd_pp_kernel<true>, dim3((unsigned)n_tiles), dim3(512), 0, stream, a,
-                           n_qtiles, (int)n_tiles);
+                           n_qtiles);
     else
         hipLaunchKernelGGL(fwd_pp_kernel<false>, dim3((unsigned)n_tiles), dim3(512), 0, stream, a,
-                           n_qtiles, (int)n_tiles);
+                           n_qtiles);
     return hipGetLastError();
 }
 

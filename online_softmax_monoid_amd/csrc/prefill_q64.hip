@@ -1,33 +1,48 @@
 // prefill_q64.hip -- fused attention forward on gfx950, head dimension 128,
-// 64 query rows per wave.
+// 64 query rows per wave, hand-placed instruction schedule.
 //
-// Same operation and online-softmax monoid as prefill.hip. The schedule is
-// shaped by the gfx950 LDS read bandwidth (about 150-200 bytes per ns per
-// CU): with 32 query rows per wave every 16-byte K or V fragment read from LDS
-// feeds one 32x32x16 MFMA, and the fragment traffic alone takes longer than
-// the MFMAs. Here each wave owns two 32-row query blocks (64 rows), so every
-// fragment feeds two MFMAs, halving LDS bytes per flop. The register file
-// then holds one wave per SIMD (four waves, 256 query rows per workgroup),
-// and each wave hides its own latencies by software pipelining:
+// Same operation and online-softmax monoid as prefill.hip. The design answers
+// two gfx950 limits measured on the simpler kernel:
 //
-//   stage A of tile j: S_{j+1} = K_{j+1} Q^T (16 MFMAs)  interleaved with
-//       the second key chunk of tile j's probabilities (exp2, bf16 rounding,
-//       row sums) and the transposing LDS reads of V_j's fragments;
-//   stage B of tile j: O^T += V_j^T P_j (16 MFMAs)  interleaved with mask,
-//       row max and lazy reference update of tile j+1, the first key chunk of
-//       its probabilities, and the LDS reads of K_{j+2}'s fragments.
+//  * LDS read bandwidth (about 150-200 bytes/ns per CU): with 32 query rows
+//    per wave every 16-byte K or V fragment read from LDS feeds one
+//    32x32x16 MFMA, which needs more LDS bandwidth than the CU has at full
+//    MFMA rate. Here a wave owns two 32-row query blocks (64 rows) and every
+//    fragment feeds two MFMAs.
+//  * VALU issue: the softmax costs about four VALU instructions and one
+//    v_exp_f32 per score, roughly what the score's MFMA share takes on the
+//    matrix unit. A wave can issue independent VALU work while its own MFMA
+//    runs, so the softmax of one tile is spread between the MFMAs of another.
 //
-// K and V tiles of 32 keys go global -> LDS with range-checked buffer DMA
-// (rows past Sk arrive as zeros) into four-deep rings, each buffer its own LDS
-// array; one workgroup barrier per tile orders the rings. K rows carry a
-// 16-byte-chunk XOR swizzle by row, V rows the swizzle that keeps the
-// transposing reads free of bank conflicts (both as in prefill_pp.hip).
+// The register file then holds one wave per SIMD (four waves, 256 query rows
+// per workgroup); each wave runs a two-stage software pipeline per 32-key
+// tile j, and every stage is laid out slot by slot (one MFMA per slot, the
+// VALU and LDS work of the slot after it, a scheduling barrier between
+// slots):
+//
+//   stage A: S_{j+1} = K_{j+1} Q^T (16 MFMAs)       | exp/pack/row-sum of the
+//            second 16 keys of tile j; row max of S_{j+1} for query block 0;
+//            transposing LDS reads of V_j
+//   stage B: O^T += V_j^T P_j (16 MFMAs)             | row max of S_{j+1} for
+//            query block 1; exp/pack/row-sum of the first 16 keys of tile
+//            j+1; LDS reads of K_{j+2}
+//
+// K and V tiles of 32 keys go global -> LDS by range-checked buffer DMA (keys
+// past Sk arrive as zeros) into four-deep rings, one barrier per tile. Both
+// are stored fragment-major: each LDS read instruction of a wave reads one
+// contiguous 1 KB (K, ds_read_b128) or 512 B (V, ds_read_b64_tr_b16) block,
+// which is free of bank conflicts and needs no address arithmetic.
+//
+// The running maximum moves lazily (only when a tile's row maximum exceeds it
+// by more than 8 in log2 units), so probabilities stay below 2^8 and the
+// accumulator is rescaled only on the rare tiles that move it.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "launch.h"
+#include "tile_order.h"
 
 namespace miattn {
 namespace {
@@ -40,7 +55,6 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int N>
@@ -54,10 +68,14 @@ union Frag8 {
     uint32_t w[4];
 };
 
+// IEEE maximum (NaN-propagating): on gfx950 it maps to v_maximum3_f32 and,
+// unlike fmaxf, needs no quieting of its operands first
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float halves_max(float x)
 {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return fmax_ieee(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float halves_sum(float x)
@@ -85,34 +103,23 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-// keeps a value's computation before this point (see prefill_pp.hip)
+__device__ __forceinline__ void slot_end() { __builtin_amdgcn_sched_barrier(0); }
+
+// Keep a value's computation inside its slot: an input pinned here cannot be
+// consumed earlier, an output pinned here cannot be computed later (the
+// compiler would otherwise sink work towards its uses across slots).
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
 
-__device__ __forceinline__ int xcd_remap(int id, int n)
-{
-    const int per = n / kXcds;
-    if (id < per * kXcds)
-        return (id % kXcds) * per + id / kXcds;
-    return id;
-}
-
-// V rows: 16-byte chunk c of row r sits at chunk c ^ vswz(r)
-__device__ __forceinline__ int vswz(int r)
-{
-    return (0xEA40 >> (4 * (r & 3))) & 15;  // 0, 4, 10, 14 for r % 4 = 0..3
-}
-
 template <bool CAUSAL>
 __global__ void __launch_bounds__(256, 1)
-fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_tiles)
+fwd_q64_kernel(FwdArgs a, int n_qtiles)
 {
     constexpr int D = 128;
-    constexpr int QB = 2;             // 32-row query blocks per wave
-    constexpr int BN = 32;            // keys per tile
-    constexpr int BM = 4 * 32 * QB;   // query rows per workgroup
-    constexpr int KCH = D / 8;        // 16-byte chunks per row
-    constexpr int TILE_CH = BN * KCH; // 512 chunks = 8 KB = 8 DMA instructions
+    constexpr int QB = 2;            // 32-row query blocks per wave
+    constexpr int BN = 32;           // keys per tile
+    constexpr int BM = 4 * 32 * QB;  // query rows per workgroup
+    constexpr int TILE_CH = BN * D / 8;     // 16-byte chunks per tile (512)
 
     __shared__ __attribute__((aligned(16))) uint4 sK0[TILE_CH];
     __shared__ __attribute__((aligned(16))) uint4 sK1[TILE_CH];
@@ -131,13 +138,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_tiles)
 
     // ---- work decomposition (same order as prefill.hip) ---------------------
     const int G = a.Hq / a.Hkv;
-    const int t = xcd_remap((int)blockIdx.x, n_tiles);
-    const int per_unit = G * n_qtiles;
-    const int unit = t / per_unit;
-    const int rem = t - unit * per_unit;
-    const int rank = rem / G;
-    const int gq = rem - rank * G;
-    const int qtile = CAUSAL ? (n_qtiles - 1 - rank) : rank;
+    const TileOrder to = tile_order((int)blockIdx.x, a.B * a.Hkv, G, n_qtiles, CAUSAL);
+    const int unit = to.unit, gq = to.gq, qtile = to.qtile;
     const int b = unit / a.Hkv;
     const int kvh = unit - b * a.Hkv;
     const int hq = kvh * G + gq;
@@ -178,74 +180,76 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_tiles)
         }
     }
 
-    // ---- global -> LDS copies: each wave issues 2 of a tile's 8 instructions --
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + krow0 * D, (uint32_t)Sk * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + krow0 * D, (uint32_t)Sk * D * 2);
-    auto dma_k = [&](uint4 *buf, int tile) __attribute__((always_inline)) {
+    // ---- global -> LDS copies ---------------------------------------------------
+    // A tile takes 8 DMA instructions (1 KB each) for K and 8 for V; wave w
+    // issues instructions 2w and 2w+1 of each. Every copy gets a buffer
+    // resource covering just its tile, so keys at or past Sk read as zero.
+    //
+    // K layout: block kk (1 KB) holds lane L's A fragment for dims
+    // 16kk + 8(L/32) .. +7 of key L%32, at byte 16L.
+    // V layout: block r = (2 db + kc) * 2 + hh (512 B) holds, at byte 8L for
+    // L = 16G + 4jj + q, the four values V[16kc + 8hh + 4(G/2) + jj]
+    // [32db + 16(G%2) + 4q .. +3]; a transposing 8-byte read of the block
+    // gives lane L the values of dim 32db + L%32 at four consecutive keys.
+    uint32_t koff[2], voff[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int i = 2 * wave + h;
-            const int r = 4 * i + (lane >> 4);
-            const int c = (lane & 15) ^ (r & 15);
-            const uint32_t off = ((uint32_t)(tile * BN + r) * D + 8 * c) * 2;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(buf + 64 * i), 16, (int)off,
-                                                     0, 0, 0);
-        }
+    for (int h = 0; h < 2; ++h) {
+        const int i = 2 * wave + h;
+        koff[h] = (uint32_t)(l32 * D + 16 * i + 8 * g) * 2;
+        const int db = i >> 1, kc = i & 1, tt = l32;
+        const int G4 = tt >> 3, jj = (tt >> 1) & 3, qh = tt & 1;
+        const int key = 16 * kc + 8 * g + 4 * (G4 >> 1) + jj;
+        const int dim = 32 * db + 16 * (G4 & 1) + 8 * qh;
+        voff[h] = (uint32_t)(key * D + dim) * 2;
+    }
+    const uint16_t *const kbase = a.k + krow0 * D;
+    const uint16_t *const vbase = a.v + krow0 * D;
+    auto tile_rsrc = [&](const uint16_t *base, int tile) __attribute__((always_inline)) {
+        const int keys = __builtin_amdgcn_readfirstlane(min(max(Sk - tile * BN, 0), BN));  // below Sk
+        return make_rsrc(base + (int64_t)tile * (BN * D), (uint32_t)keys * (D * 2));
+    };
+    auto dma_k = [&](uint4 *buf, int tile) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase, tile);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(buf + 64 * (2 * wave + h)), 16,
+                                                     (int)koff[h], 0, 0, 0);
     };
     auto dma_v = [&](uint4 *buf, int tile) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, tile);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int i = 2 * wave + h;
-            const int r = 4 * i + (lane >> 4);
-            const int c = (lane & 15) ^ vswz(r);
-            const uint32_t off = ((uint32_t)(tile * BN + r) * D + 8 * c) * 2;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(buf + 64 * i), 16, (int)off,
-                                                     0, 0, 0);
-        }
+        for (int h = 0; h < 2; ++h)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(buf + 64 * (2 * wave + h)), 16,
+                                                     (int)voff[h], 0, 0, 0);
     };
 
-    // ---- fragments from LDS ---------------------------------------------------
-    Frag8 kf[D / 16];   // K rows l32 of the tile, per 16-dim step
-    bf16x8 vf[4][2];    // V^T rows 32 db + l32, per (d-block, 16-key chunk)
-    auto read_k = [&](const uint4 *buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            kf[kk].u = buf[l32 * KCH + ((2 * kk + g) ^ (l32 & 15))];
+    // ---- fragments from LDS -------------------------------------------------------
+    Frag8 kf[D / 16];  // A fragments of the K tile the next QK uses
+    bf16x8 vf[4][2];   // A fragments of V^T: [d-block][16-key chunk]
+    auto read_k = [&](const uint4 *buf, int kk) __attribute__((always_inline)) {
+        kf[kk].u = buf[64 * kk + lane];
     };
-    // transposing reads: lane L = 16 G + 4 jr + q addresses row
-    // 16 kc + 8 hh + 4 (G / 2) + jr at column 32 db + 16 (G % 2) + 4 q
-    auto read_v = [&](const uint4 *buf) __attribute__((always_inline)) {
-        const int G4 = lane >> 4, i = lane & 15;
-        const int jr = i >> 2, q = i & 3;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                i16x4 half[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int row = 16 * kc + 8 * hh + 4 * (G4 >> 1) + jr;
-                    const int c = 4 * db + 2 * (G4 & 1) + (q >> 1);
-                    const char *p = (const char *)buf + row * (D * 2) + 16 * (c ^ vswz(row)) +
-                                    8 * (q & 1);
-                    half[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)(const_cast<char *>(p)));
-                }
-                const i16x8 both = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                vf[db][kc] = __builtin_bit_cast(bf16x8, both);
-            }
+    auto read_v = [&](const uint4 *buf, int db, int kc) __attribute__((always_inline)) {
+        const char *base = (const char *)buf + 8 * lane;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)(const_cast<char *>(base + ((2 * db + kc) * 2 + 0) * 512)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4 *)(const_cast<char *>(base + ((2 * db + kc) * 2 + 1) * 512)));
+        const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        vf[db][kc] = __builtin_bit_cast(bf16x8, both);
     };
 
-    // ---- monoid state per query block -----------------------------------------
+    // ---- monoid state per query block -------------------------------------------
     constexpr float kLazy = 8.f;
     const float c = a.scale * kLog2e;
     const float thr = kLazy / c;
-    float m_ref[QB], mc[QB], alpha_acc[QB], l_half[QB];
+    float m_ref[QB], nmc[QB], m_thr[QB], alpha_acc[QB], l_half[QB];  // nmc = -m_ref * c
     f32x16 acc[QB][D / 32];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         m_ref[qb] = -INFINITY;
-        mc[qb] = 0.f;
+        nmc[qb] = 0.f;
+        m_thr[qb] = -INFINITY;
         alpha_acc[qb] = 1.f;
         l_half[qb] = 0.f;
 #pragma unroll
@@ -256,84 +260,81 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_tiles)
     }
 
     using Sc = f32x16[QB];
-    using Pc = Frag8[QB];
-    auto qk = [&](Sc &s) __attribute__((always_inline)) {
-        // Q fragments stay in AGPRs, read there directly by the MFMAs (else
-        // the allocator parks them in AGPRs and copies them back every tile)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk)
-                asm volatile("" : "+a"(qf[qb][kk]));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                s[qb][r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[qb][kk], s[qb], 0, 0, 0);
-    };
-    // probabilities of key chunk h (scores s[8h .. 8h+7]) -> bf16 fragments
-    auto probs = [&](const Sc &s, int h, Pc &p) __attribute__((always_inline)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float rs = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * h + 2 * w], c, -mc[qb]));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * h + 2 * w + 1], c, -mc[qb]));
-                p[qb].w[w] = pack_bf16x2(p0, p1);
-                rs += p0 + p1;
-            }
-            l_half[qb] += rs;
+    using Pc = Frag8[QB][2];  // [query block][16-key chunk]
+    auto qk_mfma = [&](Sc &s, int qb, int kk) __attribute__((always_inline)) {
+        // Q fragments stay in AGPRs and are read there by the MFMA (else the
+        // allocator parks them in AGPRs and copies them back every tile)
+        asm volatile("" : "+a"(qf[qb][kk]));
+        if (kk == 0) {
+            const f32x16 zero = {};
+            s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[qb][kk], zero, 0, 0, 0);
+        } else {
+            s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[qb][kk], s[qb], 0, 0, 0);
         }
     };
-    // last key of tile j this row may see; -1 when the wave computes nothing
-    // for tile j (all of its probabilities are then exactly 0)
-    auto mask_lim = [&](int j, int qb) __attribute__((always_inline)) {
-        const int my_q = q0 + 32 * qb + l32;
-        const int lim = CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1;
-        return j < nwb ? lim : -1;
+    auto pv_mfma = [&](const Pc &p, int qb, int db, int kc) __attribute__((always_inline)) {
+        acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][kc], p[qb][kc].v, acc[qb][db],
+                                                              0, 0, 0);
     };
-    // mask (MASK), row max and lazy update of the reference for tile j
-    auto row_stats = [&](Sc &s, int j, auto MASKc) __attribute__((always_inline)) {
+
+    // Softmax work, in pieces placed between the MFMAs. Scores of a query
+    // block: s[qb][r], key 8(r/4) + 4g + r%4 of the tile; chunk h = keys
+    // 16h .. 16h+15 = r in [8h, 8h+8). Every piece pins     // its outputs at the end of its group of MFMAs (else the compiler sinks
+    // them towards their uses); inside the group its independent chains
+    // overlap one another.
+    //
+    // probabilities of scores r = 8h + 4quad .. +3 -> two packed bf16 pairs
+    auto probs_quad = [&](const Sc &s, Pc &p, int qb, int h, int quad)
+        __attribute__((always_inline)) {
+        float e[4];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            if (decltype(MASKc)::value) {
-                const int j0 = j * BN;
-                const int lim = mask_lim(j, qb);
+        for (int i = 0; i < 4; ++i)
+            e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * h + 4 * quad + i], c, nmc[qb]));
+        p[qb][h].w[2 * quad] = pack_bf16x2(e[0], e[1]);
+        p[qb][h].w[2 * quad + 1] = pack_bf16x2(e[2], e[3]);
+        l_half[qb] += (e[0] + e[1]) + (e[2] + e[3]);
+        pin(p[qb][h].w[2 * quad]);
+        pin(p[qb][h].w[2 * quad + 1]);
+        pin(l_half[qb]);
+    };
+    // row maximum in three parts (scores 0-7, scores 8-15, both halves of the
+    // wave); a masked tile first selects hidden keys to -inf
+    float mxa[QB], mxb[QB];
+    auto row_max = [&](Sc &s, int qb, int part, int j, bool masked) __attribute__((always_inline)) {
+        if (part < 2) {
+            if (masked) {
+                const int my_q = q0 + 32 * qb + l32;
+                const int lim = j < nwb ? (CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1) : -1;
+                const int rel = lim - j * BN - 4 * g;  // key r visible iff offset(r) <= rel
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    s[qb][r] = (key <= lim) ? s[qb][r] : -INFINITY;
-                }
+                for (int r = 8 * part; r < 8 * part + 8; ++r)
+                    s[qb][r] = (8 * (r >> 2) + (r & 3) <= rel) ? s[qb][r] : -INFINITY;
             }
-            float mx = s[qb][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r)
-                mx = fmaxf(mx, s[qb][r]);
-            mx = halves_max(mx);
-            const bool move = __any(mx > m_ref[qb] + thr);
-            const float m_new = move ? fmaxf(m_ref[qb], mx) : m_ref[qb];
+            const int r0 = 8 * part;
+            float m = fmax_ieee(fmax_ieee(s[qb][r0], s[qb][r0 + 1]), s[qb][r0 + 2]);
+            m = fmax_ieee(fmax_ieee(m, s[qb][r0 + 3]), s[qb][r0 + 4]);
+            m = fmax_ieee(fmax_ieee(m, s[qb][r0 + 5]), s[qb][r0 + 6]);
+            m = fmax_ieee(m, s[qb][r0 + 7]);
+            pin(m);
+            (part == 0 ? mxa[qb] : mxb[qb]) = m;
+        } else {
+            mxa[qb] = halves_max(fmax_ieee(mxa[qb], mxb[qb]));
+            pin(mxa[qb]);
+        }
+    };
+    // lazy reference update of a query block, taken only when some row of
+    // the wave exceeds its reference by more than the threshold
+    auto move_ref = [&](int qb) __attribute__((always_inline)) {
+        if (__any(mxa[qb] > m_thr[qb])) {
+            const float m_new = fmax_ieee(m_ref[qb], mxa[qb]);
             const float alpha =
                 (m_new == m_ref[qb]) ? 1.f : __builtin_amdgcn_exp2f((m_ref[qb] - m_new) * c);
             l_half[qb] *= alpha;
             alpha_acc[qb] *= alpha;
             m_ref[qb] = m_new;
-            mc[qb] = (m_new == -INFINITY) ? 0.f : m_new * c;
+            nmc[qb] = (m_new == -INFINITY) ? 0.f : -(m_new * c);
+            m_thr[qb] = m_new + thr;
         }
-    };
-    auto pv = [&](const Pc &p0, const Pc &p1) __attribute__((always_inline)) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][0], p0[qb].v, acc[qb][db], 0, 0, 0);
-                acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][1], p1[qb].v, acc[qb][db], 0, 0, 0);
-            }
     };
     auto apply_alpha = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -344,30 +345,14 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_tiles)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         acc[qb][db][r] *= alpha_acc[qb];
+                alpha_acc[qb] = 1.f;
             }
-            alpha_acc[qb] = 1.f;
-        }
-    };
-    auto pin_p = [&](Pc &p) __attribute__((always_inline)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                pin(p[qb].w[w]);
-    };
-    auto pin_stats = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            pin(l_half[qb]);
-            pin(m_ref[qb]);
-            pin(mc[qb]);
-            pin(alpha_acc[qb]);
         }
     };
 
-    // ---- prologue ---------------------------------------------------------------
-    // Copies of K tiles 0-3 and V tiles 0-2, drained; every wave computes S_0,
-    // its statistics and P_0's first key chunk, then reads K tile 1.
+    // ---- prologue -------------------------------------------------------------------
+    // Copies of K tiles 0-3 and V tiles 0-2, drained. Then S_0, its statistics
+    // and the first chunk of P_0 without overlap, and K tile 1 into registers.
     dma_k(sK0, 0);
     dma_k(sK1, 1);
     dma_k(sK2, 2);
@@ -377,59 +362,115 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_tiles)
     dma_v(sV2, 2);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the copies
     __syncthreads();
-    Sc sA, sB;            // scores of tiles j (even) and j+1
-    Pc pA, pA2, pB, pB2;  // probabilities: key chunks 0 and 1 of each tile
-    read_k(sK0);
-    qk(sA);
-    row_stats(sA, 0, IntC<1>{});
-    probs(sA, 0, pA);
-    read_k(sK1);
-    __syncthreads();      // everyone has read K tile 0 before K tile 4 replaces it
+    Sc sA, sB;      // scores of the even / odd tile in flight
+    Pc pA, pB;      // probabilities of the even / odd tile
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        read_k(sK0, kk);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+        qk_mfma(sA, 0, kk);
+        qk_mfma(sA, 1, kk);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        row_max(sA, qb, 0, 0, true);
+        row_max(sA, qb, 1, 0, true);
+        row_max(sA, qb, 2, 0, true);
+        move_ref(qb);
+        probs_quad(sA, pA, qb, 0, 0);
+        probs_quad(sA, pA, qb, 0, 1);
+    }
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        read_k(sK1, kk);
+    __syncthreads();  // every wave has read K tile 0 before K tile 4 replaces it
 
-    // ---- one tile step ------------------------------------------------------------
-    // Tile m's K lives in buffer m % 4, its V likewise. Step j: copies of K tile
-    // j+4 (into tile j's K buffer, last read in step j-2) and V tile j+3 (into
-    // tile j-1's V buffer, last read in step j-1); stage A; stage B; wait until
-    // the copies the next step reads (K tile j+3, V tile j+1) are complete --
-    // the six newer copy instructions of this wave may still fly; barrier.
-    auto step = [&](auto PI, auto MASKc, int j, Sc &sc, Sc &sn, Pc &pc0, Pc &pc1, Pc &pn0)
+    // ---- one tile step ------------------------------------------------------------------
+    // Tile m's K and V live in buffer m % 4. Step j: copies of K tile j+4 (into
+    // tile j's K buffer, last read in step j-2) and V tile j+3 (into tile j-1's
+    // V buffer, last read in step j-1); stage A; stage B; wait until the copies
+    // the next step reads (V tile j+1, K tile j+3) are complete -- the six
+    // newer copy instructions of this wave may still fly -- and barrier.
+    auto step = [&](auto PI, auto MASKc, int j, Sc &sc, Sc &sn, Pc &pc, Pc &pn)
         __attribute__((always_inline)) {
         constexpr int P = decltype(PI)::value;  // j % 4
+        constexpr bool MASK = decltype(MASKc)::value;
         uint4 *const kb[4] = {sK0, sK1, sK2, sK3};
         uint4 *const vb[4] = {sV0, sV1, sV2, sV3};
         dma_k(kb[P], j + 4);
         dma_v(vb[(P + 3) & 3], j + 3);
-        // stage A
         apply_alpha();
-        qk(sn);
-        read_v(vb[P]);
-        probs(sc, 1, pc1);
+        slot_end();
+
+        // Stage A, four groups of four MFMAs (QK of tile j+1, query block 0
+        // then 1). Groups 0-1 read V_j; the groups compute chunk 1 of tile
+        // j's probabilities (block 0, then block 1) and, in groups 2-3, the
+        // row maximum of block 0 of tile j+1 (its MFMAs finished in group 1).
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
-        }
-        pin_p(pc1);
-        pin_stats();
-        // stage B
-        pv(pc0, pc1);
-        read_k(kb[(P + 2) & 3]);
-        row_stats(sn, j + 1, MASKc);
-        probs(sn, 0, pn0);
+        for (int grp = 0; grp < 4; ++grp) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            if (i < 8)
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+            for (int i = 0; i < 4; ++i) {
+                const int sl = 4 * grp + i;
+                qk_mfma(sn, sl >> 3, sl & 7);
+                if (grp < 2)
+                    read_v(vb[P], 2 * grp + (i >> 1), i & 1);
+            }
+            probs_quad(sc, pc, grp >> 1, 1, grp & 1);
+            if (grp == 2)
+                row_max(sn, 0, 0, j + 1, MASK);
+            if (grp == 3) {
+                row_max(sn, 0, 1, j + 1, MASK);
+                row_max(sn, 0, 2, j + 1, MASK);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                if (grp < 2)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+            }
+            slot_end();
         }
-        pin_p(pn0);
-        pin_stats();
+        move_ref(0);
+        slot_end();
+
+        // Stage B, four groups of four MFMAs (PV of tile j). Each group reads
+        // two K_{j+2} fragments; groups 0-1 compute chunk 0 of tile j+1 for
+        // block 0 and the row maximum of block 1, groups 2-3 chunk 0 for
+        // block 1 after its reference update.
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sl = 4 * grp + i;
+                pv_mfma(pc, sl & 1, (sl >> 1) & 3, sl >> 3);
+                if (i < 2)
+                    read_k(kb[(P + 2) & 3], 2 * grp + i);
+            }
+            probs_quad(sn, pn, grp >> 1, 0, grp & 1);
+            if (grp == 0)
+                row_max(sn, 1, 0, j + 1, MASK);
+            if (grp == 1) {
+                row_max(sn, 1, 1, j + 1, MASK);
+                row_max(sn, 1, 2, j + 1, MASK);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                if (i < 2)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+            }
+            slot_end();
+            if (grp == 1) {
+                move_ref(1);
+                slot_end();
+            }
+        }
         __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
-        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+        slot_end();
     };
 
     // Leading steps of this wave that need no mask (a multiple of 4): tile j+1
@@ -446,23 +487,23 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_tiles)
 
     int j = 0;
     for (; j < n_fast; j += 4) {
-        step(IntC<0>{}, IntC<0>{}, j, sA, sB, pA, pA2, pB);
-        step(IntC<1>{}, IntC<0>{}, j + 1, sB, sA, pB, pB2, pA);
-        step(IntC<2>{}, IntC<0>{}, j + 2, sA, sB, pA, pA2, pB);
-        step(IntC<3>{}, IntC<0>{}, j + 3, sB, sA, pB, pB2, pA);
+        step(IntC<0>{}, IntC<0>{}, j, sA, sB, pA, pB);
+        step(IntC<1>{}, IntC<0>{}, j + 1, sB, sA, pB, pA);
+        step(IntC<2>{}, IntC<0>{}, j + 2, sA, sB, pA, pB);
+        step(IntC<3>{}, IntC<0>{}, j + 3, sB, sA, pB, pA);
     }
     for (; j + 3 < nblk; j += 4) {
-        step(IntC<0>{}, IntC<1>{}, j, sA, sB, pA, pA2, pB);
-        step(IntC<1>{}, IntC<1>{}, j + 1, sB, sA, pB, pB2, pA);
-        step(IntC<2>{}, IntC<1>{}, j + 2, sA, sB, pA, pA2, pB);
-        step(IntC<3>{}, IntC<1>{}, j + 3, sB, sA, pB, pB2, pA);
+        step(IntC<0>{}, IntC<1>{}, j, sA, sB, pA, pB);
+        step(IntC<1>{}, IntC<1>{}, j + 1, sB, sA, pB, pA);
+        step(IntC<2>{}, IntC<1>{}, j + 2, sA, sB, pA, pB);
+        step(IntC<3>{}, IntC<1>{}, j + 3, sB, sA, pB, pA);
     }
     if (j < nblk)
-        step(IntC<0>{}, IntC<1>{}, j, sA, sB, pA, pA2, pB);
+        step(IntC<0>{}, IntC<1>{}, j, sA, sB, pA, pB);
     if (j + 1 < nblk)
-        step(IntC<1>{}, IntC<1>{}, j + 1, sB, sA, pB, pB2, pA);
+        step(IntC<1>{}, IntC<1>{}, j + 1, sB, sA, pB, pA);
     if (j + 2 < nblk)
-        step(IntC<2>{}, IntC<1>{}, j + 2, sA, sB, pA, pA2, pB);
+        step(IntC<2>{}, IntC<1>{}, j + 2, sA, sB, pA, pB);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy may still target LDS
     apply_alpha();
 
@@ -505,10 +546,10 @@ hipError_t launch_fwd_q64(const FwdArgs &a, bool causal, hipStream_t stream)
         return hipErrorInvalidConfiguration;
     if (causal)
         hipLaunchKernelGGL(fwd_q64_kernel<true>, dim3((unsigned)n_tiles), dim3(256), 0, stream, a,
-                           n_qtiles, (int)n_tiles);
+                           n_qtiles);
     else
         hipLaunchKernelGGL(fwd_q64_kernel<false>, dim3((unsigned)n_tiles), dim3(256), 0, stream,
-                           a, n_qtiles, (int)n_tiles);
+                           a, n_qtiles);
     return hipGetLastError();
 }
 

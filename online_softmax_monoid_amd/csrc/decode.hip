@@ -1,16 +1,13 @@
 // decode.hip -- split-KV decode attention on gfx950: a bandwidth-bound split
 // kernel and a small combine kernel, both the online-softmax monoid.
 //
-// Split kernel (a7): one workgroup per (stream b, kv-head, group of GH query
-// heads, split s). The split covers keys [floor(s*len/S), floor((s+1)*len/S))
-// of the stream's cache. LPK = d/8 lanes share one key row (16 bytes each), so
-// a 256-thread workgroup reads 256/LPK whole key rows per load instruction;
-// each row of K and V is read from HBM exactly once and serves all GH query
-// heads (the paper's decode kernel shares one set of probabilities across the
-// GQA heads, §7.4 / appendix). Every lane group runs the monoid over its own
-// keys, U keys per step with one rescale per step; the lane groups' states
-// are then folded through LDS, and the unnormalised partial state
-// (m, l, acc[d]) goes to the workspace.
+// Split kernel (a7): one workgroup per (stream b, kv-head, chunk of up to 16
+// query heads, split s). The split covers keys [floor(s*len/S),
+// floor((s+1)*len/S)) of the stream's cache. Every row of K and V is read
+// from HBM once and serves all query heads of its kv-head: the heads are the
+// columns of the MFMA tiles (the paper's decode kernel likewise shares one
+// pass over K and V between the GQA heads, §7.4). The unnormalised partial
+// state (m, l, acc[d]) of the split goes to the workspace.
 //
 // Combine kernel (a8): one wave per (b, query head) folds the S partial states
 // with the monoid combine (rescale to the largest max, add) and finishes
@@ -18,8 +15,8 @@
 // Splitting is valid because the combine is associative (§2.5 "Schedules":
 // split on any associative monoid).
 //
-// Scores are kept in log2 units (q is pre-multiplied by scale*log2(e)) so
-// every exponential is one v_exp_f32. Decode keeps the probabilities in f32.
+// Partial maxima are kept in log2 units (scores times scale*log2(e)), so every
+// exponential is one v_exp_f32.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -33,9 +30,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
     typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
@@ -45,39 +39,49 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, p);
 }
 
-// Sum over the LPK lanes of a key group (aligned groups of LPK lanes).
-template <int LPK>
-__device__ __forceinline__ float group_sum(float x)
+// ---- split kernel on MFMA ----------------------------------------------------
+// One workgroup of NW waves per (stream b, kv-head, chunk of up to 16 query
+// heads, split). The split's keys go in blocks of 32, block n to wave n % NW,
+// so no wave walks more than a quarter of a split (the long streams' splits
+// would otherwise leave a tail of lone waves). Per block:
+//   * K rows load straight into the A operands of v_mfma_f32_16x16x32_bf16
+//     (lane l holds dims 8(l/16)..+7 of key l%16 of a 32-dim slice), and
+//     S^T = K Q^T puts the query heads in the 16 columns, so the dot
+//     products need no cross-lane sums; columns past the chunk's heads see
+//     zero queries and are never written out.
+//   * V rows go global -> LDS by buffer DMA, fragment-major: a transposing
+//     8-byte read of one 512-byte block gives lane l four consecutive keys of
+//     dim l%16 (+16 per d-block), the A operand of O^T += V^T P^T.
+//   * The probabilities stay in registers as the B operand: lane l's eight
+//     keys are 4(l/16)+{0..3} of both 16-key halves, exactly the rows its
+//     score accumulators hold, and V^T is read with the same key order.
+// K and V of a wave's next block are in flight while a block computes. The
+// reference maximum moves lazily (only past a margin of 8 in log2 units), as
+// in the prefill kernels. At the end the NW waves' states are folded through
+// LDS with the monoid combine and written as the split's partial state.
+template <int D, int NW>
+__global__ void __launch_bounds__(64 * NW)
+decode_mfma_kernel(DecodeArgs a, int hchunks)
 {
-#pragma unroll
-    for (int off = 1; off < LPK; off <<= 1)
-        x += __shfl_xor(x, off, 64);
-    return x;
-}
+    constexpr int KK = D / 32;  // 32-dim slices of a key row
+    constexpr int DB = D / 16;  // 16-dim blocks of the output = V DMA instructions per block
+    constexpr int BK = 32;      // keys per block
+    typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+    typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) void lds_void;
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <int D, int GH, int U>
-struct DecCfg {
-    static constexpr int NT = 256;
-    static constexpr int LPK = D / 8;        // lanes per key row
-    static constexpr int NKG = NT / LPK;     // key groups per workgroup
-    static constexpr int STEP = NKG * U;     // keys per loop step
-};
+    // per wave: one V block (32 keys x D bf16), reused at the end for the
+    // wave's accumulator (16 columns x D f32 -- the same 64 D bytes)
+    __shared__ __attribute__((aligned(16))) uint4 sVall[NW][BK * D / 8];
+    __shared__ float s_mc[NW][16], s_l[NW][16];
 
-template <int D, int GH, int U>
-__global__ void __launch_bounds__(256)
-decode_split_kernel(DecodeArgs a)
-{
-    using C = DecCfg<D, GH, U>;
-    __shared__ float s_m[C::NKG][GH];
-    __shared__ float s_l[C::NKG][GH];
-    __shared__ __attribute__((aligned(16))) float s_acc[C::NKG][GH][D];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l16 = lane & 15, r4 = lane >> 4;
+    uint4 *const sV = sVall[wave];
 
-    const int tid = threadIdx.x;
-    const int kgrp = tid / C::LPK;
-    const int dl = tid % C::LPK;  // this lane's 8 dims: [8*dl, 8*dl + 8)
-
-    const int G = a.Hq / a.Hkv;
-    const int hchunks = G / GH;
     int id = blockIdx.x;
     const int split = id % a.splits;
     id /= a.splits;
@@ -85,167 +89,289 @@ decode_split_kernel(DecodeArgs a)
     id /= hchunks;
     const int kvh = id % a.Hkv;
     const int b = id / a.Hkv;
-    const int h0 = kvh * G + hc * GH;
+    const int G = a.Hq / a.Hkv;
+    const int h0 = kvh * G + 16 * hc;
+    const int GH = min(16, G - 16 * hc);  // query heads of this chunk
 
     int len = a.lens[b];
     len = len < 0 ? 0 : (len > a.S_cap ? a.S_cap : len);
+    len = __builtin_amdgcn_readfirstlane(len);
     const int k_lo = (int)(((int64_t)split * len) / a.splits);
     const int k_hi = (int)(((int64_t)(split + 1) * len) / a.splits);
+    const int nb = (k_hi - k_lo + BK - 1) / BK;
 
-    const float c = a.scale * kLog2e;
-    float q[GH][8];
+    // Q^T fragments (B operand): column l%16 is query head h0 + l%16
+    bf16x8 qf[KK];
+    {
+        const bool live = l16 < GH;
+        const uint16_t *qrow = a.q + ((int64_t)b * a.Hq + h0 + (live ? l16 : 0)) * D + 8 * r4;
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
-        const uint4 w = *(const uint4 *)(a.q + ((int64_t)b * a.Hq + h0 + h) * D + 8 * dl);
-        q[h][0] = bf16_lo(w.x) * c; q[h][1] = bf16_hi(w.x) * c;
-        q[h][2] = bf16_lo(w.y) * c; q[h][3] = bf16_hi(w.y) * c;
-        q[h][4] = bf16_lo(w.z) * c; q[h][5] = bf16_hi(w.z) * c;
-        q[h][6] = bf16_lo(w.w) * c; q[h][7] = bf16_hi(w.w) * c;
-    }
-
-    float m[GH], l[GH], acc[GH][8];
-#pragma unroll
-    for (int h = 0; h < GH; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc[h][i] = 0.f;
+        for (int kk = 0; kk < KK; ++kk) {
+            const uint4 w = live ? *(const uint4 *)(qrow + 32 * kk) : make_uint4(0, 0, 0, 0);
+            qf[kk] = __builtin_bit_cast(bf16x8, w);
+        }
     }
 
     const int64_t row0 = ((int64_t)b * a.Hkv + kvh) * a.S_cap;
-    const uint16_t *Kp = a.k + row0 * D + 8 * dl;
-    const uint16_t *Vp = a.v + row0 * D + 8 * dl;
+    const uint16_t *const kbase = a.k + row0 * D;
+    const uint16_t *const vbase = a.v + row0 * D;
+    auto block_rsrc = [&](const uint16_t *base, int kb) __attribute__((always_inline)) {
+        const int keys = __builtin_amdgcn_readfirstlane(min(k_hi - kb, BK));
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base + (int64_t)kb * D),
+                                                 (short)0, keys * (D * 2), 0x00020000);
+    };
+    // K: lane l loads dims 32kk + 8(l/16) .. +7 of key 16*half + l%16
+    const uint32_t koff0 = (uint32_t)(l16 * D + 8 * r4) * 2;
+    const uint32_t koff1 = koff0 + 16 * D * 2;
+    uint4 kf[2][KK];
+    auto load_k = [&](int kb) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = block_rsrc(kbase, kb);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            kf[0][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(koff0 + 64 * kk), 0, 0));
+            kf[1][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(koff1 + 64 * kk), 0, 0));
+        }
+    };
+    // V DMA: instruction i fills LDS bytes [1024 i, 1024 i + 1024) = read
+    // blocks (d-block i, half 0) and (d-block i, half 1); lane l copies the
+    // 16 bytes V[16 hh + 4 rr + jj][16 i + 8 qh .. +7] with hh = l/32,
+    // t = l%32, rr = t/8, jj = (t/2)%4, qh = t%2
+    uint32_t voff;
+    {
+        const int hh = lane >> 5, t = lane & 31;
+        const int key = 16 * hh + 4 * (t >> 3) + ((t >> 1) & 3);
+        voff = (uint32_t)(key * D + 8 * (t & 1)) * 2;
+    }
+    auto dma_v = [&](int kb) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = block_rsrc(vbase, kb);
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(sV + 64 * i), 16,
+                                                     (int)(voff + 32 * i), 0, 0, 0);
+    };
 
-    for (int kb = k_lo; kb < k_hi; kb += C::STEP) {
-        uint4 kr[U], vr[U];
-        bool ok[U];
+    const float c = a.scale * kLog2e;
+    const float thr = 8.f / c;
+    float m_ref = -INFINITY, nmc = 0.f, m_thr = -INFINITY, l_lane = 0.f;
+    f32x4 acc[DB];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int key = kb + u * C::NKG + kgrp;
-            ok[u] = key < k_hi;
-            kr[u] = ok[u] ? *(const uint4 *)(Kp + (int64_t)key * D) : make_uint4(0, 0, 0, 0);
-            vr[u] = ok[u] ? *(const uint4 *)(Vp + (int64_t)key * D) : make_uint4(0, 0, 0, 0);
-        }
-        float s[U][GH];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float k0 = bf16_lo(kr[u].x), k1 = bf16_hi(kr[u].x);
-            const float k2 = bf16_lo(kr[u].y), k3 = bf16_hi(kr[u].y);
-            const float k4 = bf16_lo(kr[u].z), k5 = bf16_hi(kr[u].z);
-            const float k6 = bf16_lo(kr[u].w), k7 = bf16_hi(kr[u].w);
-#pragma unroll
-            for (int h = 0; h < GH; ++h) {
-                float t = q[h][0] * k0;
-                t = __builtin_fmaf(q[h][1], k1, t);
-                t = __builtin_fmaf(q[h][2], k2, t);
-                t = __builtin_fmaf(q[h][3], k3, t);
-                t = __builtin_fmaf(q[h][4], k4, t);
-                t = __builtin_fmaf(q[h][5], k5, t);
-                t = __builtin_fmaf(q[h][6], k6, t);
-                t = __builtin_fmaf(q[h][7], k7, t);
-                s[u][h] = group_sum<C::LPK>(t);
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < GH; ++h) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                s[u][h] = ok[u] ? s[u][h] : -INFINITY;
-                mx = fmaxf(mx, s[u][h]);
-            }
-            const float m_new = fmaxf(m[h], mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m[h] - m_use);
-            l[h] *= alpha;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                acc[h][i] *= alpha;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float p = __builtin_amdgcn_exp2f(s[u][h] - m_use);
-                l[h] += p;
-                acc[h][0] = __builtin_fmaf(p, bf16_lo(vr[u].x), acc[h][0]);
-                acc[h][1] = __builtin_fmaf(p, bf16_hi(vr[u].x), acc[h][1]);
-                acc[h][2] = __builtin_fmaf(p, bf16_lo(vr[u].y), acc[h][2]);
-                acc[h][3] = __builtin_fmaf(p, bf16_hi(vr[u].y), acc[h][3]);
-                acc[h][4] = __builtin_fmaf(p, bf16_lo(vr[u].z), acc[h][4]);
-                acc[h][5] = __builtin_fmaf(p, bf16_hi(vr[u].z), acc[h][5]);
-                acc[h][6] = __builtin_fmaf(p, bf16_lo(vr[u].w), acc[h][6]);
-                acc[h][7] = __builtin_fmaf(p, bf16_hi(vr[u].w), acc[h][7]);
-            }
-            m[h] = m_new;
-        }
-    }
+    for (int i = 0; i < DB; ++i)
+        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // fold the key groups' states through LDS
-    if (dl == 0) {
+    if (wave < nb) {
+        load_k(k_lo + BK * wave);
+        dma_v(k_lo + BK * wave);
+    }
+    for (int n = wave; n < nb; n += NW) {
+        const int kb = k_lo + BK * n;
+        const bool more = n + NW < nb;
+        // S^T for the two 16-key halves: lane l holds keys 16 half + 4(l/16) + i
+        // for the query head in column l%16
+        f32x4 s[2];
 #pragma unroll
-        for (int h = 0; h < GH; ++h) {
-            s_m[kgrp][h] = m[h];
-            s_l[kgrp][h] = l[h];
+        for (int half = 0; half < 2; ++half) {
+            s[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, kf[half][0]), qf[0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int kk = 1; kk < KK; ++kk)
+                s[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, kf[half][kk]), qf[kk], s[half], 0, 0, 0);
         }
+        if (more)
+            load_k(kb + BK * NW);
+        // V block n has landed once only the next K loads may be outstanding
+        if (more)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * KK));  // vmcnt(2 KK)
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
+        bf16x8 vf[DB];
+#pragma unroll
+        for (int i = 0; i < DB; ++i) {
+            const char *base = (const char *)sV + 8 * lane + 1024 * i;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const_cast<char *>(base)));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const_cast<char *>(base + 512)));
+            vf[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+        if (more) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block is in registers
+            dma_v(kb + BK * NW);
+        }
+
+        // mask keys past the split, row maximum per query column
+        const int rel = k_hi - kb - 4 * r4;  // key 16 half + 4 r4 + i valid iff 16 half + i < rel
+        float mx = -INFINITY;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s[half][i] = (16 * half + i < rel) ? s[half][i] : -INFINITY;
+                mx = fmaxf(mx, s[half][i]);
+            }
+        {
+            auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+            auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+        }
+        if (__any(mx > m_thr)) {
+            const float m_new = fmaxf(m_ref, mx);
+            const float alpha = (m_new == m_ref) ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+            l_lane *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i)
+                acc[i] *= alpha;
+            m_ref = m_new;
+            nmc = (m_new == -INFINITY) ? 0.f : -(m_new * c);
+            m_thr = m_new + thr;
+        }
+        float p[2][4];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[half][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[half][i], c, nmc));
+                l_lane += p[half][i];
+            }
+        uint4 pw;
+        pw.x = pack_bf16x2(p[0][0], p[0][1]);
+        pw.y = pack_bf16x2(p[0][2], p[0][3]);
+        pw.z = pack_bf16x2(p[1][0], p[1][1]);
+        pw.w = pack_bf16x2(p[1][2], p[1][3]);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[i], pb, acc[i], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy may still target LDS
+
+    // this wave's state -> LDS: reference (log2 units), row sum over the four
+    // lane rows of each column, accumulator [column][dim]
+    {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
+        l_lane = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
+        l_lane = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+    }
+    float *const s_acc = (float *)sV;  // [16][D]
+    if (r4 == 0) {
+        s_mc[wave][l16] = (m_ref == -INFINITY) ? -INFINITY : m_ref * c;
+        s_l[wave][l16] = l_lane;
     }
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
-        *(float4 *)&s_acc[kgrp][h][8 * dl] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-        *(float4 *)&s_acc[kgrp][h][8 * dl + 4] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-    }
+    for (int i = 0; i < DB; ++i)
+        *(float4 *)(s_acc + l16 * D + 16 * i + 4 * r4) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
     __syncthreads();
 
+    // fold the waves' states (rescale to the largest reference, add) and
+    // write the split's partial; thread t covers column t / (D/4), dims
+    // 4 (t % (D/4)) .. +3 of it, for the chunk's GH columns
     const int64_t part0 = ((int64_t)b * a.Hq + h0) * a.splits + split;
-    for (int e = tid; e < GH * D; e += C::NT) {
-        const int h = e / D, dd = e % D;
+    for (int e = threadIdx.x; e < GH * (D / 4); e += 64 * NW) {
+        const int col = e / (D / 4), d4 = 4 * (e % (D / 4));
         float M = -INFINITY;
-        for (int kg = 0; kg < C::NKG; ++kg)
-            M = fmaxf(M, s_m[kg][h]);
-        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            M = fmaxf(M, s_mc[w][col]);
+        float L = 0.f;
+        float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
         if (M != -INFINITY) {
-            for (int kg = 0; kg < C::NKG; ++kg) {
-                const float mk = s_m[kg][h];
-                const float w = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
-                L = __builtin_fmaf(w, s_l[kg][h], L);
-                A = __builtin_fmaf(w, s_acc[kg][h][dd], A);
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float mw = s_mc[w][col];
+                const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+                L = __builtin_fmaf(f, s_l[w][col], L);
+                const float4 v = *(const float4 *)((const float *)sVall[w] + col * D + d4);
+                A.x = __builtin_fmaf(f, v.x, A.x);
+                A.y = __builtin_fmaf(f, v.y, A.y);
+                A.z = __builtin_fmaf(f, v.z, A.z);
+                A.w = __builtin_fmaf(f, v.w, A.w);
             }
         }
-        const int64_t p = part0 + (int64_t)h * a.splits;
-        a.part_acc[p * D + dd] = A;
-        if (dd == 0) {
+        const int64_t p = part0 + (int64_t)col * a.splits;
+        *(float4 *)(a.part_acc + p * D + d4) = A;
+        if (d4 == 0) {
             a.part_ml[2 * p] = M;
             a.part_ml[2 * p + 1] = L;
         }
     }
 }
 
-// One 64-lane wave per (b, query head); lane handles d/64 output dims.
+// One 64-lane wave per (b, query head); lane handles d/64 output dims. The
+// splits' partial states are read in parallel (one split per lane for the
+// references and sums; every lane's dims of up to 16 splits in one batch of
+// loads issued before any of them is needed), so the kernel costs about two
+// memory latencies rather than one per split.
+__device__ __forceinline__ float wave_max(float x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        x = fmaxf(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        x += __shfl_xor(x, off, 64);
+    return x;
+}
+
 template <int D>
 __global__ void __launch_bounds__(64)
 decode_combine_kernel(DecodeArgs a)
 {
     constexpr int PER = D / 64;
+    constexpr int CH = 16;  // splits per batch of loads
     const int lane = threadIdx.x;
     const int64_t bh = blockIdx.x;
     const int S = a.splits;
     const float *ml = a.part_ml + bh * S * 2;
-    const float *pa = a.part_acc + bh * S * D;
+    const float *pa = a.part_acc + bh * S * D + PER * lane;
 
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s)
-        M = fmaxf(M, ml[2 * s]);
-    float L = 0.f;
+    // first batch of accumulator loads, independent of the references
+    float v[CH][PER];
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            v[j][i] = j < S ? pa[(int64_t)j * D + i] : 0.f;
+
+    float mloc = -INFINITY;
+    for (int s = lane; s < S; s += 64)
+        mloc = fmaxf(mloc, ml[2 * s]);
+    const float M = wave_max(mloc);
+    float lloc = 0.f;
+    if (M != -INFINITY)
+        for (int s = lane; s < S; s += 64) {
+            const float ms = ml[2 * s];
+            lloc += (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * ml[2 * s + 1];
+        }
+    const float L = wave_sum(lloc);
+
     float o[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i)
         o[i] = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < S; ++s) {
-            const float ms = ml[2 * s];
-            const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-            L = __builtin_fmaf(w, ml[2 * s + 1], L);
+        for (int s0 = 0; s0 < S; s0 += CH) {
+            if (s0 > 0) {
 #pragma unroll
-            for (int i = 0; i < PER; ++i)
-                o[i] = __builtin_fmaf(w, pa[(int64_t)s * D + PER * lane + i], o[i]);
+                for (int j = 0; j < CH; ++j)
+#pragma unroll
+                    for (int i = 0; i < PER; ++i)
+                        v[j][i] = s0 + j < S ? pa[(int64_t)(s0 + j) * D + i] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                if (s0 + j < S) {
+                    const float ms = ml[2 * (s0 + j)];
+                    const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+#pragma unroll
+                    for (int i = 0; i < PER; ++i)
+                        o[i] = __builtin_fmaf(w, v[j][i], o[i]);
+                }
+            }
         }
     }
     const bool empty = !(L > 0.f);
@@ -262,29 +388,21 @@ decode_combine_kernel(DecodeArgs a)
         a.lse[bh] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
 }
 
-template <int D, int GH>
-hipError_t launch_split(const DecodeArgs &a, hipStream_t stream)
-{
-    const int G = a.Hq / a.Hkv;
-    const long long grid = (long long)a.B * a.Hkv * (G / GH) * a.splits;
-    if (grid > 0x7fffffffLL)
-        return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_split_kernel<D, GH, 4>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, a);
-    return hipGetLastError();
-}
-
 template <int D>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
 {
     const int G = a.Hq / a.Hkv;
     hipError_t e;
-    if (G % 4 == 0)
-        e = launch_split<D, 4>(a, stream);
-    else if (G % 2 == 0)
-        e = launch_split<D, 2>(a, stream);
-    else
-        e = launch_split<D, 1>(a, stream);
+    {
+        const int hchunks = (G + 15) / 16;
+        const long long grid = (long long)a.B * a.Hkv * hchunks * a.splits;
+        if (grid > 0x7fffffffLL)
+            return hipErrorInvalidConfiguration;
+        constexpr int NW = 4;
+        hipLaunchKernelGGL((decode_mfma_kernel<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
+                           stream, a, hchunks);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess)
         return e;
     const long long grid = (long long)a.B * a.Hq;

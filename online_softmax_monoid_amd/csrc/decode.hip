@@ -39,18 +39,46 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, p);
 }
 
+// kv length of stream b, clamped to [0, S_cap]
+__device__ __forceinline__ int clamped_len(const DecodeArgs &a, int b)
+{
+    const int len = a.lens[b];
+    return len < 0 ? 0 : (len > a.S_cap ? a.S_cap : len);
+}
+
+// Workgroups take streams longest first (ties by index), so the short
+// streams' splits come last and fill the gaps instead of a long stream's
+// splits running alone at the end. Up to 64 streams every wave ranks them
+// itself (lane i holds stream i's length); beyond that streams go in index
+// order.
+__device__ __forceinline__ int stream_by_rank(const DecodeArgs &a, int rank, int lane)
+{
+    if (a.B > 64)
+        return rank;
+    const int mine = lane < a.B ? clamped_len(a, lane) : -1;
+    int my_rank = 0;
+    for (int o = 0; o < a.B; ++o) {
+        const int lo = __builtin_amdgcn_readlane(mine, o);
+        my_rank += (lo > mine) || (lo == mine && o < lane);
+    }
+    const unsigned long long hit = __ballot(lane < a.B && my_rank == rank);
+    return hit ? (int)__builtin_ctzll(hit) : rank;  // exactly one lane matches
+}
+
 // ---- split kernel on MFMA ----------------------------------------------------
 // One workgroup of NW waves per (stream b, kv-head, chunk of up to 16 query
 // heads, split). The split's keys go in blocks of 32, block n to wave n % NW,
-// so no wave walks more than a quarter of a split (the long streams' splits
+// so no wave walks a whole long split alone (the long streams' splits
 // would otherwise leave a tail of lone waves). Per block:
-//   * K rows load straight into the A operands of v_mfma_f32_16x16x32_bf16
+//   * K and V rows go global -> LDS by buffer DMA in whole rows (reading
+//     the cache in 16-row x 64-byte fragment shapes directly runs at about
+//     70% of the contiguous read rate).
+//   * K fragments from LDS are the A operands of v_mfma_f32_16x16x32_bf16
 //     (lane l holds dims 8(l/16)..+7 of key l%16 of a 32-dim slice), and
 //     S^T = K Q^T puts the query heads in the 16 columns, so the dot
 //     products need no cross-lane sums; columns past the chunk's heads see
 //     zero queries and are never written out.
-//   * V rows go global -> LDS by buffer DMA, fragment-major: a transposing
-//     8-byte read of one 512-byte block gives lane l four consecutive keys of
+//   * Transposing 8-byte LDS reads of V give lane l four consecutive keys of
 //     dim l%16 (+16 per d-block), the A operand of O^T += V^T P^T.
 //   * The probabilities stay in registers as the B operand: lane l's eight
 //     keys are 4(l/16)+{0..3} of both 16-key halves, exactly the rows its
@@ -72,14 +100,17 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
     typedef __attribute__((address_space(3))) void lds_void;
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-    // per wave: one V block (32 keys x D bf16), reused at the end for the
-    // wave's accumulator (16 columns x D f32 -- the same 64 D bytes)
+    // per wave: one K and one V block (32 keys x D bf16 each); the V block is
+    // reused at the end for the wave's accumulator (16 columns x D f32 -- the
+    // same 64 D bytes)
+    __shared__ __attribute__((aligned(16))) uint4 sKall[NW][BK * D / 8];
     __shared__ __attribute__((aligned(16))) uint4 sVall[NW][BK * D / 8];
     __shared__ float s_mc[NW][16], s_l[NW][16];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, r4 = lane >> 4;
+    uint4 *const sK = sKall[wave];
     uint4 *const sV = sVall[wave];
 
     int id = blockIdx.x;
@@ -88,14 +119,13 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
     const int hc = id % hchunks;
     id /= hchunks;
     const int kvh = id % a.Hkv;
-    const int b = id / a.Hkv;
+    const int sr = id / a.Hkv;  // stream rank
+    const int b = stream_by_rank(a, sr, lane);
     const int G = a.Hq / a.Hkv;
     const int h0 = kvh * G + 16 * hc;
     const int GH = min(16, G - 16 * hc);  // query heads of this chunk
 
-    int len = a.lens[b];
-    len = len < 0 ? 0 : (len > a.S_cap ? a.S_cap : len);
-    len = __builtin_amdgcn_readfirstlane(len);
+    const int len = __builtin_amdgcn_readfirstlane(clamped_len(a, b));
     const int k_lo = (int)(((int64_t)split * len) / a.splits);
     const int k_hi = (int)(((int64_t)(split + 1) * len) / a.splits);
     const int nb = (k_hi - k_lo + BK - 1) / BK;
@@ -120,34 +150,52 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base + (int64_t)kb * D),
                                                  (short)0, keys * (D * 2), 0x00020000);
     };
-    // K: lane l loads dims 32kk + 8(l/16) .. +7 of key 16*half + l%16
-    const uint32_t koff0 = (uint32_t)(l16 * D + 8 * r4) * 2;
-    const uint32_t koff1 = koff0 + 16 * D * 2;
-    uint4 kf[2][KK];
-    auto load_k = [&](int kb) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t r = block_rsrc(kbase, kb);
+    // K and V blocks go global -> LDS by buffer DMA, each instruction four
+    // (head dim 128) whole key rows, so every read is a contiguous 1 KB. A
+    // row's 16-byte chunk c sits at slot c ^ (row % CPR) of the row, which
+    // keeps the fragment reads below free of (K) or low in (V) bank
+    // conflicts. Instruction i, lane l: row RPI i + l / CPR, slot l % CPR.
+    constexpr int CPR = D / 8;     // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;  // rows per DMA instruction
+    constexpr int NI = BK / RPI;   // DMA instructions per block
+    auto dma = [&](uint4 *buf, const uint16_t *base, int kb) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = block_rsrc(base, kb);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            kf[0][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(koff0 + 64 * kk), 0, 0));
-            kf[1][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(koff1 + 64 * kk), 0, 0));
+        for (int i = 0; i < NI; ++i) {
+            const int row = RPI * i + lane / CPR;
+            const int off = (row * CPR + ((lane % CPR) ^ (row % CPR))) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(buf + 64 * i), 16, off, 0, 0, 0);
         }
     };
-    // V DMA: instruction i fills LDS bytes [1024 i, 1024 i + 1024) = read
-    // blocks (d-block i, half 0) and (d-block i, half 1); lane l copies the
-    // 16 bytes V[16 hh + 4 rr + jj][16 i + 8 qh .. +7] with hh = l/32,
-    // t = l%32, rr = t/8, jj = (t/2)%4, qh = t%2
-    uint32_t voff;
-    {
-        const int hh = lane >> 5, t = lane & 31;
-        const int key = 16 * hh + 4 * (t >> 3) + ((t >> 1) & 3);
-        voff = (uint32_t)(key * D + 8 * (t & 1)) * 2;
-    }
-    auto dma_v = [&](int kb) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t r = block_rsrc(vbase, kb);
+    // K A fragments: lane l holds dims 32kk + 8(l/16) .. +7 of key 16 half + l%16
+    uint4 kf[2][KK];
+    auto read_k = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < DB; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(sV + 64 * i), 16,
-                                                     (int)(voff + 32 * i), 0, 0, 0);
+        for (int half = 0; half < 2; ++half) {
+            const int row = 16 * half + l16;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                kf[half][kk] = sK[row * CPR + ((4 * kk + r4) ^ (row % CPR))];
+        }
+    };
+    // V^T A fragments by transposing reads: for d-block db and half hh, lane
+    // L = 16 G + 4 j + q supplies the 8 bytes V[16 hh + 4 G + j][16 db + 4 q .. +3];
+    // lane l receives dim 16 db + l%16 of keys 16 hh + 4(l/16) + 0..3
+    bf16x8 vf[DB];
+    auto read_v = [&]() __attribute__((always_inline)) {
+        const int j = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            i16x4 h2[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int row = 16 * hh + 4 * r4 + j;
+                const int chunk = 2 * db + (q >> 1);
+                const char *p = (const char *)sV + row * (2 * D) + 16 * (chunk ^ (row % CPR)) + 8 * (q & 1);
+                h2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const_cast<char *>(p)));
+            }
+            vf[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
     };
 
     const float c = a.scale * kLog2e;
@@ -159,12 +207,21 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
         acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (wave < nb) {
-        load_k(k_lo + BK * wave);
-        dma_v(k_lo + BK * wave);
+        dma(sK, kbase, k_lo + BK * wave);
+        dma(sV, vbase, k_lo + BK * wave);
     }
     for (int n = wave; n < nb; n += NW) {
         const int kb = k_lo + BK * n;
-        const bool more = n + NW < nb;
+        // this block's copies have landed (nothing newer is in flight); take
+        // it into registers, then start the copies of this wave's next block
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        read_k();
+        read_v();
+        if (n + NW < nb) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block is in registers
+            dma(sK, kbase, kb + BK * NW);
+            dma(sV, vbase, kb + BK * NW);
+        }
         // S^T for the two 16-key halves: lane l holds keys 16 half + 4(l/16) + i
         // for the query head in column l%16
         f32x4 s[2];
@@ -176,25 +233,6 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
             for (int kk = 1; kk < KK; ++kk)
                 s[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8, kf[half][kk]), qf[kk], s[half], 0, 0, 0);
-        }
-        if (more)
-            load_k(kb + BK * NW);
-        // V block n has landed once only the next K loads may be outstanding
-        if (more)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * KK));  // vmcnt(2 KK)
-        else
-            __builtin_amdgcn_s_waitcnt(0x0F70);             // vmcnt(0)
-        bf16x8 vf[DB];
-#pragma unroll
-        for (int i = 0; i < DB; ++i) {
-            const char *base = (const char *)sV + 8 * lane + 1024 * i;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const_cast<char *>(base)));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const_cast<char *>(base + 512)));
-            vf[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-        if (more) {
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block is in registers
-            dma_v(kb + BK * NW);
         }
 
         // mask keys past the split, row maximum per query column
@@ -398,7 +436,10 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
         const long long grid = (long long)a.B * a.Hkv * hchunks * a.splits;
         if (grid > 0x7fffffffLL)
             return hipErrorInvalidConfiguration;
-        constexpr int NW = 4;
+#ifndef MIATTN_DECODE_NW
+#define MIATTN_DECODE_NW 2  // waves per split: LDS (16 KB per wave) allows 10 waves per CU
+#endif
+        constexpr int NW = MIATTN_DECODE_NW;
         hipLaunchKernelGGL((decode_mfma_kernel<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
                            stream, a, hchunks);
         e = hipGetLastError();

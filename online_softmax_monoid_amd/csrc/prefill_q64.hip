@@ -111,14 +111,16 @@ __device__ __forceinline__ void slot_end() { __builtin_amdgcn_sched_barrier(0); 
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
 
-template <bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
+template <bool CAUSAL, int NWV>
+__global__ void __launch_bounds__(64 * NWV, 1)
 fwd_q64_kernel(FwdArgs a, int n_qtiles)
 {
     constexpr int D = 128;
-    constexpr int QB = 2;            // 32-row query blocks per wave
-    constexpr int BN = 32;           // keys per tile
-    constexpr int BM = 4 * 32 * QB;  // query rows per workgroup
+    constexpr int QB = 2;              // 32-row query blocks per wave
+    constexpr int BN = 32;             // keys per tile
+    constexpr int BM = NWV * 32 * QB;  // query rows per workgroup
+    constexpr int DPW = 8 / NWV;       // copy instructions per wave per tile, each of K and V
+    static_assert(NWV * DPW == 8 && 3 * DPW < 16, "vmcnt field holds the in-flight copies");
     constexpr int TILE_CH = BN * D / 8;     // 16-byte chunks per tile (512)
 
     __shared__ __attribute__((aligned(16))) uint4 sK0[TILE_CH];
@@ -182,7 +184,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
 
     // ---- global -> LDS copies ---------------------------------------------------
     // A tile takes 8 DMA instructions (1 KB each) for K and 8 for V; wave w
-    // issues instructions 2w and 2w+1 of each. Every copy gets a buffer
+    // issues instructions DPW w .. DPW w + DPW - 1 of each. Every copy gets a buffer
     // resource covering just its tile, so keys at or past Sk read as zero.
     //
     // K layout: block kk (1 KB) holds lane L's A fragment for dims
@@ -191,10 +193,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     // L = 16G + 4jj + q, the four values V[16kc + 8hh + 4(G/2) + jj]
     // [32db + 16(G%2) + 4q .. +3]; a transposing 8-byte read of the block
     // gives lane L the values of dim 32db + L%32 at four consecutive keys.
-    uint32_t koff[2], voff[2];
+    uint32_t koff[DPW], voff[DPW];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int i = 2 * wave + h;
+    for (int h = 0; h < DPW; ++h) {
+        const int i = DPW * wave + h;
         koff[h] = (uint32_t)(l32 * D + 16 * i + 8 * g) * 2;
         const int db = i >> 1, kc = i & 1, tt = l32;
         const int G4 = tt >> 3, jj = (tt >> 1) & 3, qh = tt & 1;
@@ -211,15 +213,15 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     auto dma_k = [&](uint4 *buf, int tile) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase, tile);
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(buf + 64 * (2 * wave + h)), 16,
+        for (int h = 0; h < DPW; ++h)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(buf + 64 * (DPW * wave + h)), 16,
                                                      (int)koff[h], 0, 0, 0);
     };
     auto dma_v = [&](uint4 *buf, int tile) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, tile);
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(buf + 64 * (2 * wave + h)), 16,
+        for (int h = 0; h < DPW; ++h)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(buf + 64 * (DPW * wave + h)), 16,
                                                      (int)voff[h], 0, 0, 0);
     };
 
@@ -390,7 +392,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     // Tile m's K and V live in buffer m % 4. Step j: copies of K tile j+4 (into
     // tile j's K buffer, last read in step j-2) and V tile j+3 (into tile j-1's
     // V buffer, last read in step j-1); stage A; stage B; wait until the copies
-    // the next step reads (V tile j+1, K tile j+3) are complete -- the six
+    // the next step reads (V tile j+1, K tile j+3) are complete -- the 3 DPW
     // newer copy instructions of this wave may still fly -- and barrier.
     auto step = [&](auto PI, auto MASKc, int j, Sc &sc, Sc &sn, Pc &pc, Pc &pn)
         __attribute__((always_inline)) {
@@ -468,7 +470,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
                 slot_end();
             }
         }
-        __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * DPW));  // vmcnt(3 DPW)
         __builtin_amdgcn_s_barrier();
         slot_end();
     };
@@ -537,18 +539,23 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
 
 }  // namespace
 
+#ifndef MIATTN_Q64_WAVES
+#define MIATTN_Q64_WAVES 4
+#endif
+
 hipError_t launch_fwd_q64(const FwdArgs &a, bool causal, hipStream_t stream)
 {
-    constexpr int BM = 256;
+    constexpr int NWV = MIATTN_Q64_WAVES;  // waves per workgroup
+    constexpr int BM = NWV * 64;
     const int n_qtiles = (a.Sq + BM - 1) / BM;
     const long long n_tiles = (long long)a.B * a.Hq * n_qtiles;
     if (n_tiles > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     if (causal)
-        hipLaunchKernelGGL(fwd_q64_kernel<true>, dim3((unsigned)n_tiles), dim3(256), 0, stream, a,
+        hipLaunchKernelGGL((fwd_q64_kernel<true, NWV>), dim3((unsigned)n_tiles), dim3(64 * NWV), 0, stream, a,
                            n_qtiles);
     else
-        hipLaunchKernelGGL(fwd_q64_kernel<false>, dim3((unsigned)n_tiles), dim3(256), 0, stream,
+        hipLaunchKernelGGL((fwd_q64_kernel<false, NWV>), dim3((unsigned)n_tiles), dim3(64 * NWV), 0, stream,
                            a, n_qtiles);
     return hipGetLastError();
 }

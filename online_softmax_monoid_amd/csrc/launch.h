@@ -35,8 +35,9 @@ struct DecodeArgs {
 hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream);
 // head dimension 128 only: two alternating wave groups (prefill_pp.hip)
 hipError_t launch_fwd_pp(const FwdArgs &a, bool causal, hipStream_t stream);
-// head dimension 128 only: 64 query rows per wave (prefill_q64.hip), the default
-hipError_t launch_fwd_q64(const FwdArgs &a, bool causal, hipStream_t stream);
+// head dimensions 128 (64 query rows per wave) and 256 (32 rows per wave):
+// the software-pipelined kernel of prefill_q64.hip, the default for both
+hipError_t launch_fwd_q64(const FwdArgs &a, int d, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t stream);
 
 }  // namespace miattn

@@ -30,10 +30,10 @@
 // whose K and V then stay in its L2, and walks them heaviest causal tile
 // first; the query heads of one GQA group sharing a kv-head are adjacent.
 //
-// Head dimensions 64 and 256 use this kernel; head dimension 128 uses the
-// 64-rows-per-wave kernel of prefill_q64.hip (this one with
-// -DMIATTN_D128_SIMPLE, the two-group kernel of prefill_pp.hip with
-// -DMIATTN_D128_PINGPONG).
+// Head dimension 64 uses this kernel; head dimensions 128 and 256 use the
+// software-pipelined kernel of prefill_q64.hip (this one with
+// -DMIATTN_D128_SIMPLE / -DMIATTN_D256_SIMPLE; at 128 the two-group kernel of
+// prefill_pp.hip with -DMIATTN_D128_PINGPONG).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -461,11 +461,15 @@ hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
         return causal ? launch<128, MIATTN_FWD_D128, true>(a, stream)
                       : launch<128, MIATTN_FWD_D128, false>(a, stream);
 #else
-        return launch_fwd_q64(a, causal, stream);
+        return launch_fwd_q64(a, 128, causal, stream);
 #endif
     case 256:
+#if defined(MIATTN_D256_SIMPLE)
         return causal ? launch<256, MIATTN_FWD_D256, true>(a, stream)
                       : launch<256, MIATTN_FWD_D256, false>(a, stream);
+#else
+        return launch_fwd_q64(a, 256, causal, stream);
+#endif
     default:
         return hipErrorInvalidValue;
     }

@@ -1,5 +1,5 @@
-// prefill_q64.hip -- fused attention forward on gfx950, head dimension 128,
-// 64 query rows per wave, hand-placed instruction schedule.
+// prefill_q64.hip -- fused attention forward on gfx950, head dimensions 128
+// (64 query rows per wave) and 256 (32 rows per wave), software-pipelined.
 //
 // Same operation and online-softmax monoid as prefill.hip. The design answers
 // two gfx950 limits measured on the simpler kernel:
@@ -15,10 +15,11 @@
 //    runs, so the softmax of one tile is spread between the MFMAs of another.
 //
 // The register file then holds one wave per SIMD (four waves, 256 query rows
-// per workgroup); each wave runs a two-stage software pipeline per 32-key
-// tile j, and every stage is laid out slot by slot (one MFMA per slot, the
-// VALU and LDS work of the slot after it, a scheduling barrier between
-// slots):
+// per workgroup at head dimension 128; at 256 the accumulator alone takes 128
+// registers and a wave owns one 32-row block, which gives the same 16 QK + 16
+// PV MFMAs per tile); each wave runs a two-stage software pipeline per 32-key
+// tile j, laid out in groups of four MFMAs with the VALU and LDS work placed
+// between them:
 //
 //   stage A: S_{j+1} = K_{j+1} Q^T (16 MFMAs)       | exp/pack/row-sum of the
 //            second 16 keys of tile j; row max of S_{j+1} for query block 0;
@@ -111,17 +112,19 @@ __device__ __forceinline__ void slot_end() { __builtin_amdgcn_sched_barrier(0); 
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
 
-template <bool CAUSAL, int NWV>
+template <bool CAUSAL, int NWV, int D, int QB>
 __global__ void __launch_bounds__(64 * NWV, 1)
 fwd_q64_kernel(FwdArgs a, int n_qtiles)
 {
-    constexpr int D = 128;
-    constexpr int QB = 2;              // 32-row query blocks per wave
+    // D = 128 runs QB = 2 query blocks (64 rows) per wave, D = 256 one block
+    // (32 rows): either way a tile step is 16 QK and 16 PV MFMAs per wave
     constexpr int BN = 32;             // keys per tile
     constexpr int BM = NWV * 32 * QB;  // query rows per workgroup
-    constexpr int DPW = 8 / NWV;       // copy instructions per wave per tile, each of K and V
-    static_assert(NWV * DPW == 8 && 3 * DPW < 16, "vmcnt field holds the in-flight copies");
-    constexpr int TILE_CH = BN * D / 8;     // 16-byte chunks per tile (512)
+    constexpr int KKN = D / 16;        // 16-dim steps of QK = K fragments = copy instructions per tile
+    constexpr int DBN = D / 32;        // 32-dim blocks of the output
+    constexpr int DPW = KKN / NWV;     // copy instructions per wave per tile, each of K and V
+    static_assert(QB * KKN == 16 && NWV * DPW == KKN && 3 * DPW < 16, "tile step shape");
+    constexpr int TILE_CH = BN * D / 8;     // 16-byte chunks per tile
 
     __shared__ __attribute__((aligned(16))) uint4 sK0[TILE_CH];
     __shared__ __attribute__((aligned(16))) uint4 sK1[TILE_CH];
@@ -167,14 +170,14 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     const int nwb = (wave_end + BN - 1) / BN;  // tiles this wave computes
 
     // ---- Q fragments (B operands of S^T = K Q^T) ------------------------------
-    bf16x8 qf[QB][D / 16];
+    bf16x8 qf[QB][KKN];
     {
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0 * D, (uint32_t)Sq * D * 2);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const uint32_t off = (uint32_t)(q0 + 32 * qb + l32) * D * 2 + 16 * g;
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
+            for (int kk = 0; kk < KKN; ++kk) {
                 Frag8 f;
                 f.u = buf_load16(rq, off + 32 * kk);  // rows >= Sq read as 0
                 qf[qb][kk] = f.v;
@@ -183,8 +186,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     }
 
     // ---- global -> LDS copies ---------------------------------------------------
-    // A tile takes 8 DMA instructions (1 KB each) for K and 8 for V; wave w
-    // issues instructions DPW w .. DPW w + DPW - 1 of each. Every copy gets a buffer
+    // A tile takes D/16 DMA instructions (1 KB each) for K and as many for V;
+    // wave w issues instructions DPW w .. DPW w + DPW - 1 of each. Every copy gets a buffer
     // resource covering just its tile, so keys at or past Sk read as zero.
     //
     // K layout: block kk (1 KB) holds lane L's A fragment for dims
@@ -226,8 +229,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     };
 
     // ---- fragments from LDS -------------------------------------------------------
-    Frag8 kf[D / 16];  // A fragments of the K tile the next QK uses
-    bf16x8 vf[4][2];   // A fragments of V^T: [d-block][16-key chunk]
+    Frag8 kf[KKN];      // A fragments of the K tile the next QK uses
+    bf16x8 vf[DBN][2];  // A fragments of V^T: [d-block][16-key chunk]
     auto read_k = [&](const uint4 *buf, int kk) __attribute__((always_inline)) {
         kf[kk].u = buf[64 * kk + lane];
     };
@@ -367,13 +370,13 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     Sc sA, sB;      // scores of the even / odd tile in flight
     Pc pA, pB;      // probabilities of the even / odd tile
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+    for (int kk = 0; kk < KKN; ++kk)
         read_k(sK0, kk);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-        qk_mfma(sA, 0, kk);
-        qk_mfma(sA, 1, kk);
-    }
+    for (int kk = 0; kk < KKN; ++kk)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            qk_mfma(sA, qb, kk);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         row_max(sA, qb, 0, 0, true);
@@ -384,7 +387,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
         probs_quad(sA, pA, qb, 0, 1);
     }
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+    for (int kk = 0; kk < KKN; ++kk)
         read_k(sK1, kk);
     __syncthreads();  // every wave has read K tile 0 before K tile 4 replaces it
 
@@ -405,68 +408,90 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
         apply_alpha();
         slot_end();
 
-        // Stage A, four groups of four MFMAs (QK of tile j+1, query block 0
-        // then 1). Groups 0-1 read V_j; the groups compute chunk 1 of tile
-        // j's probabilities (block 0, then block 1) and, in groups 2-3, the
-        // row maximum of block 0 of tile j+1 (its MFMAs finished in group 1).
+        // Stage A, four groups of four MFMAs (QK of tile j+1; with two query
+        // blocks, block 0 then block 1). Groups 0-1 read V_j; the groups
+        // compute chunk 1 of tile j's probabilities and, with two query
+        // blocks, in groups 2-3 the row maximum of block 0 of tile j+1 (its
+        // MFMAs finished in group 1).
+        constexpr int NRV = 2 * DBN;  // read_v calls per tile (two reads each)
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int sl = 4 * grp + i;
-                qk_mfma(sn, sl >> 3, sl & 7);
+                qk_mfma(sn, sl / KKN, sl % KKN);
                 if (grp < 2)
-                    read_v(vb[P], 2 * grp + (i >> 1), i & 1);
+#pragma unroll
+                    for (int c = sl * NRV / 8; c < (sl + 1) * NRV / 8; ++c)
+                        read_v(vb[P], c >> 1, c & 1);
             }
-            probs_quad(sc, pc, grp >> 1, 1, grp & 1);
-            if (grp == 2)
-                row_max(sn, 0, 0, j + 1, MASK);
-            if (grp == 3) {
-                row_max(sn, 0, 1, j + 1, MASK);
-                row_max(sn, 0, 2, j + 1, MASK);
+            if (grp < 2 * QB)
+                probs_quad(sc, pc, grp >> 1, 1, grp & 1);
+            if constexpr (QB == 2) {
+                if (grp == 2)
+                    row_max(sn, 0, 0, j + 1, MASK);
+                if (grp == 3) {
+                    row_max(sn, 0, 1, j + 1, MASK);
+                    row_max(sn, 0, 2, j + 1, MASK);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 if (grp < 2)
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+                    __builtin_amdgcn_sched_group_barrier(0x100, NRV / 4, 0);  // LDS reads
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
             }
             slot_end();
         }
-        move_ref(0);
-        slot_end();
+        if constexpr (QB == 2) {
+            move_ref(0);
+            slot_end();
+        }
 
         // Stage B, four groups of four MFMAs (PV of tile j). Each group reads
-        // two K_{j+2} fragments; groups 0-1 compute chunk 0 of tile j+1 for
-        // block 0 and the row maximum of block 1, groups 2-3 chunk 0 for
-        // block 1 after its reference update.
+        // D/64 K_{j+2} fragments. With two query blocks, groups 0-1 compute
+        // chunk 0 of tile j+1 for block 0 and the row maximum of block 1,
+        // groups 2-3 chunk 0 for block 1 after its reference update; with one,
+        // group 0 takes the row maximum and groups 1-2 chunk 0.
+        constexpr int KPG = KKN / 4;  // K reads per group
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int sl = 4 * grp + i;
-                pv_mfma(pc, sl & 1, (sl >> 1) & 3, sl >> 3);
-                if (i < 2)
-                    read_k(kb[(P + 2) & 3], 2 * grp + i);
+                const int idx = sl & 7;
+                pv_mfma(pc, idx % QB, idx / QB, sl >> 3);
+                if (i < KPG)
+                    read_k(kb[(P + 2) & 3], KPG * grp + i);
             }
-            probs_quad(sn, pn, grp >> 1, 0, grp & 1);
-            if (grp == 0)
-                row_max(sn, 1, 0, j + 1, MASK);
-            if (grp == 1) {
-                row_max(sn, 1, 1, j + 1, MASK);
-                row_max(sn, 1, 2, j + 1, MASK);
+            if constexpr (QB == 2) {
+                probs_quad(sn, pn, grp >> 1, 0, grp & 1);
+                if (grp == 0)
+                    row_max(sn, 1, 0, j + 1, MASK);
+                if (grp == 1) {
+                    row_max(sn, 1, 1, j + 1, MASK);
+                    row_max(sn, 1, 2, j + 1, MASK);
+                }
+            } else {
+                if (grp == 0) {
+                    row_max(sn, 0, 0, j + 1, MASK);
+                    row_max(sn, 0, 1, j + 1, MASK);
+                    row_max(sn, 0, 2, j + 1, MASK);
+                }
+                if (grp == 1 || grp == 2)
+                    probs_quad(sn, pn, 0, 0, grp - 1);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                if (i < 2)
+                if (i < KPG)
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
             }
             slot_end();
-            if (grp == 1) {
-                move_ref(1);
+            if (grp == (QB == 2 ? 1 : 0)) {
+                move_ref(QB - 1);
                 slot_end();
             }
         }
@@ -537,27 +562,40 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     }
 }
 
-}  // namespace
-
 #ifndef MIATTN_Q64_WAVES
 #define MIATTN_Q64_WAVES 4
 #endif
 
-hipError_t launch_fwd_q64(const FwdArgs &a, bool causal, hipStream_t stream)
+template <int D, int QB>
+hipError_t launch_q64(const FwdArgs &a, bool causal, hipStream_t stream)
 {
     constexpr int NWV = MIATTN_Q64_WAVES;  // waves per workgroup
-    constexpr int BM = NWV * 64;
+    constexpr int BM = NWV * 32 * QB;
     const int n_qtiles = (a.Sq + BM - 1) / BM;
     const long long n_tiles = (long long)a.B * a.Hq * n_qtiles;
     if (n_tiles > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     if (causal)
-        hipLaunchKernelGGL((fwd_q64_kernel<true, NWV>), dim3((unsigned)n_tiles), dim3(64 * NWV), 0, stream, a,
-                           n_qtiles);
+        hipLaunchKernelGGL((fwd_q64_kernel<true, NWV, D, QB>), dim3((unsigned)n_tiles), dim3(64 * NWV),
+                           0, stream, a, n_qtiles);
     else
-        hipLaunchKernelGGL((fwd_q64_kernel<false, NWV>), dim3((unsigned)n_tiles), dim3(64 * NWV), 0, stream,
-                           a, n_qtiles);
+        hipLaunchKernelGGL((fwd_q64_kernel<false, NWV, D, QB>), dim3((unsigned)n_tiles), dim3(64 * NWV),
+                           0, stream, a, n_qtiles);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_q64(const FwdArgs &a, int d, bool causal, hipStream_t stream)
+{
+    switch (d) {
+    case 128:
+        return launch_q64<128, 2>(a, causal, stream);
+    case 256:
+        return launch_q64<256, 1>(a, causal, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace miattn

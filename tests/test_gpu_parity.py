@@ -199,7 +199,10 @@ def test_decode_workload_full():
 
 
 @pytest.mark.parametrize("d,Hq,Hkv,splits", [(128, 32, 8, 16), (64, 4, 4, 3), (256, 8, 1, 7),
-                                              (128, 6, 2, 1), (64, 3, 1, 40)])
+                                              (128, 6, 2, 1), (64, 3, 1, 40),
+                                              # query-head groups wider than the 16 MFMA
+                                              # columns: 20 = 16 + 4 and 34 = 16 + 16 + 2
+                                              (128, 40, 2, 5), (64, 34, 1, 4)])
 def test_decode_edge_lengths(d, Hq, Hkv, splits):
     lens = np.array([0, 1, 3, 15, 16, 17, 200, 511], dtype=np.int32)
     S_cap = 511
@@ -213,6 +216,23 @@ def test_decode_edge_lengths(d, Hq, Hkv, splits):
     _note(f"[gpu] decode d={d} Hq={Hq} Hkv={Hkv} splits={splits}: {m}")
     H.assert_parity(m, "decode edges")
     assert m["empty_rows"] == Hq  # the stream of length 0
+
+
+def test_decode_many_streams():
+    """More streams than one wave can rank by length (they then go in index
+    order), with lengths spread over [0, S_cap]."""
+    rng = np.random.Generator(np.random.PCG64(4242))
+    lens = rng.integers(0, 300, size=70, endpoint=True).astype(np.int32)
+    lens[[3, 40]] = 0
+    _, q, kc, vc = inputs.draw_decode_bits(4243, 70, 8, 2, 128, 0, 0, 300, lens=lens)
+    s = inputs.default_scale(128)
+    o, lse, guards = H.run_decode(q, kc, vc, lens, s, 6)
+    assert guards
+    o_ref, lse_ref = oracle.attn_decode(q, kc, vc, lens, s)
+    m = H.metrics(o, lse, o_ref, lse_ref)
+    _note(f"[gpu] decode 70 streams: {m}")
+    H.assert_parity(m, "decode many streams")
+    assert m["empty_rows"] == 2 * 8
 
 
 def test_decode_padding_is_never_read():

@@ -38,6 +38,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_b2_h32_s4096_d128_causal_
 KERNEL_SOURCES = ("online_softmax_monoid_amd/csrc/prefill.hip",
                   "online_softmax_monoid_amd/csrc/prefill_pp.hip",
                   "online_softmax_monoid_amd/csrc/prefill_q64.hip",
+                  "online_softmax_monoid_amd/csrc/tile_order.h",
                   "online_softmax_monoid_amd/csrc/launch.h")
 
 

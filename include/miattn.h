@@ -62,7 +62,8 @@ extern "C" {
 typedef enum {
     MIATTN_OK = 0,
     MIATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad scale */
-    MIATTN_ERR_UNSUPPORTED = 2, /* head dimension not in {64, 128, 256} */
+    MIATTN_ERR_UNSUPPORTED = 2, /* head dimension not in {64, 128, 256}, or a
+                                   prefill head slice of 2 GiB or more */
     MIATTN_ERR_HIP = 3          /* the HIP runtime reported a launch error */
 } miattn_status;
 
@@ -85,8 +86,10 @@ typedef enum {
  *
  * Sizes: B, Sq, Sk >= 0 (B == 0 or Sq == 0: nothing to do, pointers unused;
  * Sk == 0: every row is empty, k and v unused); Hq, Hkv >= 1 with
- * Hq % Hkv == 0; d in {64, 128, 256}. Offsets are 64-bit, so any size that
- * fits device memory is accepted.
+ * Hq % Hkv == 0; d in {64, 128, 256}. One head's slice of Q and of K / V
+ * must stay below 2 GiB (Sq * d * 2 and Sk * d * 2 < 2^31; Sq, Sk < 4M at
+ * d = 256): the kernels address within a head with 32-bit buffer offsets.
+ * Offsets across heads and batches are 64-bit.
  */
 MIATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
              int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,

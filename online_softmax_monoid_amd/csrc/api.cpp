@@ -81,6 +81,9 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
         return fail(MIATTN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d, Sq=%d, Sk=%d)", B, Sq, Sk);
     MIATTN_TRY(check_heads_dim(Hq, Hkv, d));
     MIATTN_TRY(check_scale(scale));
+    if ((int64_t)Sq * d * 2 >= ((int64_t)1 << 31) || (int64_t)Sk * d * 2 >= ((int64_t)1 << 31))
+        return fail(MIATTN_ERR_UNSUPPORTED,
+                    "one head's Q or K/V slice reaches 2 GiB (Sq=%d, Sk=%d, d=%d)", Sq, Sk, d);
     if (B == 0 || Sq == 0)
         return MIATTN_OK;
     MIATTN_TRY(check_ptr(q, "q", 16));

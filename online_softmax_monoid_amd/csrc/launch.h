@@ -33,8 +33,6 @@ struct DecodeArgs {
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream);
-// head dimension 128 only: two alternating wave groups (prefill_pp.hip)
-hipError_t launch_fwd_pp(const FwdArgs &a, bool causal, hipStream_t stream);
 // head dimensions 128 (64 query rows per wave) and 256 (32 rows per wave):
 // the software-pipelined kernel of prefill_q64.hip, the default for both
 hipError_t launch_fwd_q64(const FwdArgs &a, int d, bool causal, hipStream_t stream);

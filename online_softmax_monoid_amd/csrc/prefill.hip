@@ -32,8 +32,7 @@
 //
 // Head dimension 64 uses this kernel; head dimensions 128 and 256 use the
 // software-pipelined kernel of prefill_q64.hip (this one with
-// -DMIATTN_D128_SIMPLE / -DMIATTN_D256_SIMPLE; at 128 the two-group kernel of
-// prefill_pp.hip with -DMIATTN_D128_PINGPONG).
+// -DMIATTN_D128_SIMPLE / -DMIATTN_D256_SIMPLE).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -455,9 +454,7 @@ hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
         return causal ? launch<64, MIATTN_FWD_D64, true>(a, stream)
                       : launch<64, MIATTN_FWD_D64, false>(a, stream);
     case 128:
-#if defined(MIATTN_D128_PINGPONG)
-        return launch_fwd_pp(a, causal, stream);
-#elif defined(MIATTN_D128_SIMPLE)
+#if defined(MIATTN_D128_SIMPLE)
         return causal ? launch<128, MIATTN_FWD_D128, true>(a, stream)
                       : launch<128, MIATTN_FWD_D128, false>(a, stream);
 #else

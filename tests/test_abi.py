@@ -63,6 +63,8 @@ def _fwd(**kw):
     (dict(Sk=-1), M.MIATTN_ERR_INVALID_ARG, "sizes"),
     (dict(d=96), M.MIATTN_ERR_UNSUPPORTED, "head dimension"),
     (dict(d=32), M.MIATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(Sq=1 << 23, d=128), M.MIATTN_ERR_UNSUPPORTED, "2 GiB"),
+    (dict(Sk=1 << 22, d=256), M.MIATTN_ERR_UNSUPPORTED, "2 GiB"),
     (dict(scale=0.0), M.MIATTN_ERR_INVALID_ARG, "scale"),
     (dict(scale=-1.0), M.MIATTN_ERR_INVALID_ARG, "scale"),
     (dict(scale=float("inf")), M.MIATTN_ERR_INVALID_ARG, "scale"),

@@ -335,10 +335,11 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
 }
 
 // One 64-lane wave per (b, query head); lane handles d/64 output dims. The
-// splits' partial states are read in parallel (one split per lane for the
-// references and sums; every lane's dims of up to 16 splits in one batch of
-// loads issued before any of them is needed), so the kernel costs about two
-// memory latencies rather than one per split.
+// splits' partial states are read in one round of loads issued together (one
+// split per lane for the references and sums; every lane's dims of up to 16
+// splits), and each split's weight is computed once, in its lane, then
+// broadcast, so the kernel costs about one memory latency (more only past 16
+// or 64 splits).
 __device__ __forceinline__ float wave_max(float x)
 {
 #pragma unroll
@@ -360,31 +361,35 @@ __global__ void __launch_bounds__(64)
 decode_combine_kernel(DecodeArgs a)
 {
     constexpr int PER = D / 64;
-    constexpr int CH = 16;  // splits per batch of loads
+    constexpr int CH = 16;  // splits per batch of accumulator loads
     const int lane = threadIdx.x;
     const int64_t bh = blockIdx.x;
     const int S = a.splits;
     const float *ml = a.part_ml + bh * S * 2;
     const float *pa = a.part_acc + bh * S * D + PER * lane;
 
-    // first batch of accumulator loads, independent of the references
+    // one round of loads: the first CH splits' accumulator slices and, one
+    // split per lane, the references and sums
     float v[CH][PER];
 #pragma unroll
     for (int j = 0; j < CH; ++j)
 #pragma unroll
         for (int i = 0; i < PER; ++i)
             v[j][i] = j < S ? pa[(int64_t)j * D + i] : 0.f;
+    const float m0 = lane < S ? ml[2 * lane] : -INFINITY;
+    const float l0 = lane < S ? ml[2 * lane + 1] : 0.f;
 
-    float mloc = -INFINITY;
-    for (int s = lane; s < S; s += 64)
+    float mloc = m0;
+    for (int s = lane + 64; s < S; s += 64)
         mloc = fmaxf(mloc, ml[2 * s]);
     const float M = wave_max(mloc);
-    float lloc = 0.f;
-    if (M != -INFINITY)
-        for (int s = lane; s < S; s += 64) {
-            const float ms = ml[2 * s];
-            lloc += (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * ml[2 * s + 1];
-        }
+    // weight of split `lane` (splits past 64 are reloaded below)
+    const float w0 = (M == -INFINITY || m0 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
+    float lloc = w0 * l0;
+    for (int s = lane + 64; s < S; s += 64) {
+        const float ms = ml[2 * s];
+        lloc += (M == -INFINITY || ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * ml[2 * s + 1];
+    }
     const float L = wave_sum(lloc);
 
     float o[PER];
@@ -402,9 +407,15 @@ decode_combine_kernel(DecodeArgs a)
             }
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
-                if (s0 + j < S) {
-                    const float ms = ml[2 * (s0 + j)];
-                    const float w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+                const int s = s0 + j;
+                if (s < S) {
+                    float w;
+                    if (s < 64) {
+                        w = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(w0), s));
+                    } else {
+                        const float ms = ml[2 * s];
+                        w = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+                    }
 #pragma unroll
                     for (int i = 0; i < PER; ++i)
                         o[i] = __builtin_fmaf(w, v[j][i], o[i]);

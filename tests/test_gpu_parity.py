@@ -202,7 +202,9 @@ def test_decode_workload_full():
                                               (128, 6, 2, 1), (64, 3, 1, 40),
                                               # query-head groups wider than the 16 MFMA
                                               # columns: 20 = 16 + 4 and 34 = 16 + 16 + 2
-                                              (128, 40, 2, 5), (64, 34, 1, 4)])
+                                              (128, 40, 2, 5), (64, 34, 1, 4),
+                                              # more splits than a wave has lanes
+                                              (64, 4, 2, 100)])
 def test_decode_edge_lengths(d, Hq, Hkv, splits):
     lens = np.array([0, 1, 3, 15, 16, 17, 200, 511], dtype=np.int32)
     S_cap = 511

@@ -1,32 +1,33 @@
 // prefill_q64.hip -- fused attention forward on gfx950, head dimensions 128
-// (64 query rows per wave) and 256 (32 rows per wave), software-pipelined.
+// and 256, software-pipelined.
 //
 // Same operation and online-softmax monoid as prefill.hip. The design answers
 // two gfx950 limits measured on the simpler kernel:
 //
-//  * LDS read bandwidth (about 150-200 bytes/ns per CU): with 32 query rows
-//    per wave every 16-byte K or V fragment read from LDS feeds one
-//    32x32x16 MFMA, which needs more LDS bandwidth than the CU has at full
-//    MFMA rate. Here a wave owns two 32-row query blocks (64 rows) and every
-//    fragment feeds two MFMAs.
+//  * LDS read bandwidth (about 150-200 bytes/ns per CU): every 16-byte K or V
+//    fragment a wave reads from LDS feeds one 32x32x16 MFMA per 32-row query
+//    block the wave owns. The kernel is written for QB = 1 or 2 blocks per
+//    wave (32 or 64 query rows).
 //  * VALU issue: the softmax costs about four VALU instructions and one
 //    v_exp_f32 per score, roughly what the score's MFMA share takes on the
 //    matrix unit. A wave can issue independent VALU work while its own MFMA
 //    runs, so the softmax of one tile is spread between the MFMAs of another.
 //
-// The register file then holds one wave per SIMD (four waves, 256 query rows
-// per workgroup at head dimension 128; at 256 the accumulator alone takes 128
-// registers and a wave owns one 32-row block, which gives the same 16 QK + 16
-// PV MFMAs per tile); each wave runs a two-stage software pipeline per 32-key
-// tile j, laid out in groups of four MFMAs with the VALU and LDS work placed
-// between them:
+// Shapes in use: head dimension 128 runs eight waves of 32 query rows (two
+// waves per SIMD, 256 rows per workgroup), which measured a few per cent
+// faster than four waves of 64 rows: the second wave on the SIMD fills the
+// issue slots the first leaves idle while it waits on a dependent VALU chain.
+// Head dimension 256 runs four waves of 32 rows, one per SIMD: the f32
+// accumulator alone takes 128 registers. Each wave runs a two-stage software
+// pipeline per 32-key tile j, laid out in groups of four MFMAs with the VALU
+// and LDS work placed between them:
 //
-//   stage A: S_{j+1} = K_{j+1} Q^T (16 MFMAs)       | exp/pack/row-sum of the
+//   stage A: S_{j+1} = K_{j+1} Q^T                   | exp/pack/row-sum of the
 //            second 16 keys of tile j; row max of S_{j+1} for query block 0;
 //            transposing LDS reads of V_j
-//   stage B: O^T += V_j^T P_j (16 MFMAs)             | row max of S_{j+1} for
-//            query block 1; exp/pack/row-sum of the first 16 keys of tile
-//            j+1; LDS reads of K_{j+2}
+//   stage B: O^T += V_j^T P_j                         | row max of S_{j+1} for
+//            the last query block; exp/pack/row-sum of the first 16 keys of
+//            tile j+1; LDS reads of K_{j+2}
 //
 // K and V tiles of 32 keys go global -> LDS by range-checked buffer DMA (keys
 // past Sk arrive as zeros) into four-deep rings, one barrier per tile. Both
@@ -73,6 +74,11 @@ union Frag8 {
 // unlike fmaxf, needs no quieting of its operands first
 __device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+__device__ __forceinline__ float uniform_f(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
 __device__ __forceinline__ float halves_max(float x)
 {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -112,8 +118,8 @@ __device__ __forceinline__ void slot_end() { __builtin_amdgcn_sched_barrier(0); 
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
 
-template <bool CAUSAL, int NWV, int D, int QB>
-__global__ void __launch_bounds__(64 * NWV, 1)
+template <bool CAUSAL, int NWV, int D, int QB, int WPE>
+__global__ void __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_q64_kernel(FwdArgs a, int n_qtiles)
 {
     // D = 128 runs QB = 2 query blocks (64 rows) per wave, D = 256 one block
@@ -123,7 +129,9 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     constexpr int KKN = D / 16;        // 16-dim steps of QK = K fragments = copy instructions per tile
     constexpr int DBN = D / 32;        // 32-dim blocks of the output
     constexpr int DPW = KKN / NWV;     // copy instructions per wave per tile, each of K and V
-    static_assert(QB * KKN == 16 && NWV * DPW == KKN && 3 * DPW < 16, "tile step shape");
+    constexpr int NG = QB * KKN / 4;   // groups of four MFMAs per stage
+    constexpr int NPV = QB * DBN;      // PV MFMAs per 16-key chunk
+    static_assert((NG == 2 || NG == 4) && NWV * DPW == KKN && 3 * DPW < 16, "tile step shape");
     constexpr int TILE_CH = BN * D / 8;     // 16-byte chunks per tile
 
     __shared__ __attribute__((aligned(16))) uint4 sK0[TILE_CH];
@@ -246,8 +254,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
 
     // ---- monoid state per query block -------------------------------------------
     constexpr float kLazy = 8.f;
-    const float c = a.scale * kLog2e;
-    const float thr = kLazy / c;
+    // wave-uniform constants held in scalar registers (the VALU computes them,
+    // so without the readfirstlane each would occupy a vector register)
+    const float c = uniform_f(a.scale * kLog2e);
+    const float thr = uniform_f(kLazy / c);
     float m_ref[QB], nmc[QB], m_thr[QB], alpha_acc[QB], l_half[QB];  // nmc = -m_ref * c
     f32x16 acc[QB][D / 32];
 #pragma unroll
@@ -408,14 +418,14 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
         apply_alpha();
         slot_end();
 
-        // Stage A, four groups of four MFMAs (QK of tile j+1; with two query
+        // Stage A, NG groups of four MFMAs (QK of tile j+1; with two query
         // blocks, block 0 then block 1). Groups 0-1 read V_j; the groups
         // compute chunk 1 of tile j's probabilities and, with two query
         // blocks, in groups 2-3 the row maximum of block 0 of tile j+1 (its
         // MFMAs finished in group 1).
         constexpr int NRV = 2 * DBN;  // read_v calls per tile (two reads each)
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
+        for (int grp = 0; grp < NG; ++grp) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int sl = 4 * grp + i;
@@ -449,19 +459,19 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
             slot_end();
         }
 
-        // Stage B, four groups of four MFMAs (PV of tile j). Each group reads
+        // Stage B, NG groups of four MFMAs (PV of tile j). Each group reads
         // D/64 K_{j+2} fragments. With two query blocks, groups 0-1 compute
         // chunk 0 of tile j+1 for block 0 and the row maximum of block 1,
         // groups 2-3 chunk 0 for block 1 after its reference update; with one,
         // group 0 takes the row maximum and groups 1-2 chunk 0.
-        constexpr int KPG = KKN / 4;  // K reads per group
+        constexpr int KPG = KKN / NG;  // K reads per group
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
+        for (int grp = 0; grp < NG; ++grp) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int sl = 4 * grp + i;
-                const int idx = sl & 7;
-                pv_mfma(pc, idx % QB, idx / QB, sl >> 3);
+                const int idx = sl % NPV;
+                pv_mfma(pc, idx % QB, idx / QB, sl / NPV);
                 if (i < KPG)
                     read_k(kb[(P + 2) & 3], KPG * grp + i);
             }
@@ -479,7 +489,11 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
                     row_max(sn, 0, 1, j + 1, MASK);
                     row_max(sn, 0, 2, j + 1, MASK);
                 }
-                if (grp == 1 || grp == 2)
+                if (NG == 2 && grp == 1) {
+                    probs_quad(sn, pn, 0, 0, 0);
+                    probs_quad(sn, pn, 0, 0, 1);
+                }
+                if (NG == 4 && (grp == 1 || grp == 2))
                     probs_quad(sn, pn, 0, 0, grp - 1);
             }
 #pragma unroll
@@ -562,24 +576,32 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     }
 }
 
-#ifndef MIATTN_Q64_WAVES
-#define MIATTN_Q64_WAVES 4
+// Build switches for measuring other shapes: the number of waves per
+// workgroup at each head dimension, and 64 (QB=2, one wave per SIMD) or 32
+// (QB=1, two waves per SIMD) query rows per wave at head dimension 128.
+#ifndef MIATTN_Q64_D128_QB
+#define MIATTN_Q64_D128_QB 1
+#endif
+#ifndef MIATTN_Q64_D128_WAVES
+#define MIATTN_Q64_D128_WAVES 8
+#endif
+#ifndef MIATTN_Q64_D256_WAVES
+#define MIATTN_Q64_D256_WAVES 4
 #endif
 
-template <int D, int QB>
+template <int D, int QB, int NWV, int WPE>
 hipError_t launch_q64(const FwdArgs &a, bool causal, hipStream_t stream)
 {
-    constexpr int NWV = MIATTN_Q64_WAVES;  // waves per workgroup
     constexpr int BM = NWV * 32 * QB;
     const int n_qtiles = (a.Sq + BM - 1) / BM;
     const long long n_tiles = (long long)a.B * a.Hq * n_qtiles;
     if (n_tiles > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     if (causal)
-        hipLaunchKernelGGL((fwd_q64_kernel<true, NWV, D, QB>), dim3((unsigned)n_tiles), dim3(64 * NWV),
+        hipLaunchKernelGGL((fwd_q64_kernel<true, NWV, D, QB, WPE>), dim3((unsigned)n_tiles), dim3(64 * NWV),
                            0, stream, a, n_qtiles);
     else
-        hipLaunchKernelGGL((fwd_q64_kernel<false, NWV, D, QB>), dim3((unsigned)n_tiles), dim3(64 * NWV),
+        hipLaunchKernelGGL((fwd_q64_kernel<false, NWV, D, QB, WPE>), dim3((unsigned)n_tiles), dim3(64 * NWV),
                            0, stream, a, n_qtiles);
     return hipGetLastError();
 }
@@ -590,9 +612,13 @@ hipError_t launch_fwd_q64(const FwdArgs &a, int d, bool causal, hipStream_t stre
 {
     switch (d) {
     case 128:
-        return launch_q64<128, 2>(a, causal, stream);
+#if MIATTN_Q64_D128_QB == 1
+        return launch_q64<128, 1, MIATTN_Q64_D128_WAVES, 2 * MIATTN_Q64_D128_WAVES / 8>(a, causal, stream);
+#else
+        return launch_q64<128, 2, MIATTN_Q64_D128_WAVES, MIATTN_Q64_D128_WAVES / 4>(a, causal, stream);
+#endif
     case 256:
-        return launch_q64<256, 1>(a, causal, stream);
+        return launch_q64<256, 1, MIATTN_Q64_D256_WAVES, MIATTN_Q64_D256_WAVES / 4>(a, causal, stream);
     default:
         return hipErrorInvalidValue;
     }

@@ -33,9 +33,12 @@ struct DecodeArgs {
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream);
-// head dimensions 128 (64 query rows per wave) and 256 (32 rows per wave):
-// the software-pipelined kernel of prefill_q64.hip, the default for both
+// head dimensions 128 and 256: the software-pipelined kernel of
+// prefill_q64.hip, the default for both
 hipError_t launch_fwd_q64(const FwdArgs &a, int d, bool causal, hipStream_t stream);
+// head dimension 128: the two-wave ping-pong kernel of prefill_pingpong.hip
+// (built in, selected with -DMIATTN_D128_PINGPONG)
+hipError_t launch_fwd_pingpong(const FwdArgs &a, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t stream);
 
 }  // namespace miattn

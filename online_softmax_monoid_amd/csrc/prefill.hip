@@ -30,9 +30,10 @@
 // whose K and V then stay in its L2, and walks them heaviest causal tile
 // first; the query heads of one GQA group sharing a kv-head are adjacent.
 //
-// Head dimension 64 uses this kernel; head dimensions 128 and 256 use the
+// Head dimension 64 uses this kernel; head dimensions 128 and 256 the
 // software-pipelined kernel of prefill_q64.hip (this one with
-// -DMIATTN_D128_SIMPLE / -DMIATTN_D256_SIMPLE).
+// -DMIATTN_D128_SIMPLE / -DMIATTN_D256_SIMPLE; at 128 the two-wave ping-pong
+// kernel of prefill_pingpong.hip with -DMIATTN_D128_PINGPONG).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -457,6 +458,8 @@ hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
 #if defined(MIATTN_D128_SIMPLE)
         return causal ? launch<128, MIATTN_FWD_D128, true>(a, stream)
                       : launch<128, MIATTN_FWD_D128, false>(a, stream);
+#elif defined(MIATTN_D128_PINGPONG)
+        return launch_fwd_pingpong(a, causal, stream);
 #else
         return launch_fwd_q64(a, 128, causal, stream);
 #endif

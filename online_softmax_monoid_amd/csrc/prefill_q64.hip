@@ -30,7 +30,7 @@
 //            tile j+1; LDS reads of K_{j+2}
 //
 // K and V tiles of 32 keys go global -> LDS by range-checked buffer DMA (keys
-// past Sk arrive as zeros) into four-deep rings, one barrier per tile. Both
+// past the workgroup's last visible key arrive as zeros) into four-deep rings, one barrier per tile. Both
 // are stored fragment-major: each LDS read instruction of a wave reads one
 // contiguous 1 KB (K, ds_read_b128) or 512 B (V, ds_read_b64_tr_b16) block,
 // which is free of bank conflicts and needs no address arithmetic.
@@ -217,8 +217,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     }
     const uint16_t *const kbase = a.k + krow0 * D;
     const uint16_t *const vbase = a.v + krow0 * D;
+    // keys at or past kv_end (at most Sk; no row of the workgroup sees them)
+    // arrive as zeros, and the prefetches past the range cost no memory traffic
     auto tile_rsrc = [&](const uint16_t *base, int tile) __attribute__((always_inline)) {
-        const int keys = __builtin_amdgcn_readfirstlane(min(max(Sk - tile * BN, 0), BN));  // below Sk
+        const int keys = __builtin_amdgcn_readfirstlane(min(max(kv_end - tile * BN, 0), BN));
         return make_rsrc(base + (int64_t)tile * (BN * D), (uint32_t)keys * (D * 2));
     };
     auto dma_k = [&](uint4 *buf, int tile) __attribute__((always_inline)) {

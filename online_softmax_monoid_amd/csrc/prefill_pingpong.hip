@@ -11,32 +11,33 @@
 // Inside one wave that overlap is limited by the softmax's dependent chains.
 // Here the two waves sharing a SIMD split the roles instead:
 //
-//   MFMA phase (step j):  DMA issue for K_{j+4} and V_{j+3}; LDS reads of
-//                         the V_j fragments; S_{j+1} = K_{j+1} Q^T and
-//                         O^T += V_j^T P_j, 16 MFMAs back to back (five QK
-//                         first to cover the V reads, then PV and QK
-//                         alternating)
-//   VALU phase (step j):  LDS reads of the K_{j+2} fragments, then the
-//                         softmax of S_{j+1}: row maximum, lazy reference
-//                         update, exp2, bf16 pack, row sum -> P_{j+1}
+//   MFMA phase (step j):  copies of K_{j+4} and V_{j+3}; bf16 packing of tile
+//                         j's exponentials and their f32 row sum, placed
+//                         between PV of tile j (8 MFMAs) and QK of tile j+1
+//                         (8 MFMAs, the first four alternating with the last
+//                         four PV); every MFMA operand is in registers
+//   VALU phase (step j):  LDS reads of the V_{j+1} fragments; mask, row
+//                         maximum, lazy reference update and exp2 of S_{j+1}
+//                         (in place of the scores); LDS reads of the K_{j+2}
+//                         fragments
 //
 // Every phase ends at a workgroup barrier. Waves 0-3 start with their first
 // MFMA phase while waves 4-7 wait one barrier, so from then on one wave of
 // each SIMD runs MFMAs while the other runs its softmax, and they swap at
-// each barrier. The MFMA-phase wave raises its issue priority so that its
-// next MFMA goes out as soon as the matrix core frees up. Reading V in the
-// MFMA phase keeps its fragments out of the registers the softmax needs.
+// each barrier (a workgroup's waves are placed on the SIMDs round-robin, so
+// waves w and w+4 share one). The MFMA-phase wave raises its issue priority
+// so that its next MFMA goes out as soon as the matrix core frees up.
 //
 // K / V ring (four tiles each). With barrier slots numbered from the first
 // MFMA phase, waves 0-3 run MFMA(j) in slot 2j+2 and VALU(j) in slot 2j+3,
-// waves 4-7 one slot later. K tile t is read from LDS in VALU(t-2) (last in
-// slot 2t) and V tile t in MFMA(t) (last in slot 2t+3); a wave consumes what
-// it reads before its phase after next. A wave issues the copies of K_{j+4}
-// and V_{j+3} in its MFMA(j) (slot 2j+2 or 2j+3), after the last reads of
-// the tiles they replace (slots 2j+1 and 2j+1), and waits for them by the end
-// of slot 2j+6 (waves 0-3: end of MFMA(j+2), with the four newer copies still
-// in flight; waves 4-7: end of VALU(j+1), with the two newer ones in flight),
-// before any wave reads them (slots 2j+7 and 2j+8).
+// waves 4-7 one slot later. K tile t is read in VALU(t-2) and V tile t in
+// VALU(t-1), last in slots 2t and 2t+2, and a wave consumes what it reads in
+// its next phase. A wave issues the copies of K_{j+4} and V_{j+3} in its
+// MFMA(j) (slot 2j+2 or 2j+3), after the tiles they replace (K_j, V_{j-1})
+// were last read in slot 2j and consumed in slot 2j+1, and waits for them by
+// the end of slot 2j+6 (waves 0-3: end of MFMA(j+2), with the four newer
+// copies still in flight; waves 4-7: end of VALU(j+1), with the two newer
+// ones in flight), before any wave reads them in slot 2j+7.
 //
 // Causal masking: a wave walks the workgroup's tiles but skips the MFMAs
 // and the softmax of tiles it cannot see, which leaves the SIMD to its

@@ -150,9 +150,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 #ifndef MIATTN_PP_PRIO
 #define MIATTN_PP_PRIO 1
 #endif
-#ifndef MIATTN_PP_PAIRS
-#define MIATTN_PP_PAIRS 0
-#endif
 
 template <bool CAUSAL>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -417,11 +414,7 @@ fwd_pingpong_kernel(FwdArgs a, int n_qtiles)
     // see that tile (j = nwb-1): the tile then lies past the wave's last key,
     // so the mask hides all of it and its softmax is skipped anyway. A dead
     // step only issues the wave's share of the copies.
-#if MIATTN_PP_PAIRS
-    const int grp = wave & 1;   // waves 2i and 2i+1 share a SIMD
-#else
     const int grp = wave >> 2;  // waves w and w+4 share a SIMD
-#endif
     auto run = [&](auto GRP) __attribute__((always_inline)) {
         constexpr int GR = decltype(GRP)::value;
         auto end_mfma = [&]() __attribute__((always_inline)) {

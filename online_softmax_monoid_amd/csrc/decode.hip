@@ -152,18 +152,27 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
     };
     // K and V blocks go global -> LDS by buffer DMA, each instruction four
     // (head dim 128) whole key rows, so every read is a contiguous 1 KB. A
-    // row's 16-byte chunk c sits at slot c ^ (row % CPR) of the row, which
-    // keeps the fragment reads below free of (K) or low in (V) bank
-    // conflicts. Instruction i, lane l: row RPI i + l / CPR, slot l % CPR.
+    // row's 16-byte chunk c sits at slot c ^ swz(row) of the row, which keeps
+    // the fragment reads below free of (K) or low in (V) bank conflicts.
+    // Instruction i, lane l: row RPI i + l / CPR, slot (l % CPR) ^ swz(row).
     constexpr int CPR = D / 8;     // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;  // rows per DMA instruction
     constexpr int NI = BK / RPI;   // DMA instructions per block
+    // Row key of the swizzle. At head dimension 128 it is the row index
+    // (mod 16) rotated left by one bit: the 16 rows of a K read still get 16
+    // different keys, and the 32 lanes of a transposing V read (rows
+    // 4G + j, G in {0, 1} or {2, 3}, two chunks each) then reach 16 different
+    // slots instead of 8, which halves their bank conflicts.
+    auto swz = [](int row) __attribute__((always_inline)) {
+        const int m = row % CPR;
+        return D == 128 ? (((2 * m) & 15) | (m >> 3)) : m;
+    };
     auto dma = [&](uint4 *buf, const uint16_t *base, int kb) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t r = block_rsrc(base, kb);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int row = RPI * i + lane / CPR;
-            const int off = (row * CPR + ((lane % CPR) ^ (row % CPR))) * 16;
+            const int off = (row * CPR + ((lane % CPR) ^ swz(row))) * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(buf + 64 * i), 16, off, 0, 0, 0);
         }
     };
@@ -175,7 +184,7 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
             const int row = 16 * half + l16;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-                kf[half][kk] = sK[row * CPR + ((4 * kk + r4) ^ (row % CPR))];
+                kf[half][kk] = sK[row * CPR + ((4 * kk + r4) ^ swz(row))];
         }
     };
     // V^T A fragments by transposing reads: for d-block db and half hh, lane
@@ -191,7 +200,7 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
             for (int hh = 0; hh < 2; ++hh) {
                 const int row = 16 * hh + 4 * r4 + j;
                 const int chunk = 2 * db + (q >> 1);
-                const char *p = (const char *)sV + row * (2 * D) + 16 * (chunk ^ (row % CPR)) + 8 * (q & 1);
+                const char *p = (const char *)sV + row * (2 * D) + 16 * (chunk ^ swz(row)) + 8 * (q & 1);
                 h2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const_cast<char *>(p)));
             }
             vf[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));

@@ -261,6 +261,9 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     const float c = uniform_f(a.scale * kLog2e);
     const float thr = uniform_f(kLazy / c);
     float m_ref[QB], nmc[QB], m_thr[QB], alpha_acc[QB], l_half[QB];  // nmc = -m_ref * c
+    // One query block per wave: the row sum of the tile whose probabilities
+    // are being built, added to l_half once the tile passes its check
+    float tsum = 0.f;
     f32x16 acc[QB][D / 32];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -279,9 +282,13 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     using Sc = f32x16[QB];
     using Pc = Frag8[QB][2];  // [query block][16-key chunk]
     auto qk_mfma = [&](Sc &s, int qb, int kk) __attribute__((always_inline)) {
-        // Q fragments stay in AGPRs and are read there by the MFMA (else the
-        // allocator parks them in AGPRs and copies them back every tile)
-        asm volatile("" : "+a"(qf[qb][kk]));
+        // At one wave per SIMD (512 registers, more than the 256 VGPRs) Q
+        // stays in AGPRs and is read there by the MFMA, else the allocator
+        // parks it in AGPRs and copies it back every tile. At two waves per
+        // SIMD the whole working set fits in 256 VGPRs, and any AGPR use
+        // would split the budget into 128 + 128.
+        if constexpr (WPE == 1)
+            asm volatile("" : "+a"(qf[qb][kk]));
         if (kk == 0) {
             const f32x16 zero = {};
             s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk].v, qf[qb][kk], zero, 0, 0, 0);
@@ -309,10 +316,15 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
             e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * h + 4 * quad + i], c, nmc[qb]));
         p[qb][h].w[2 * quad] = pack_bf16x2(e[0], e[1]);
         p[qb][h].w[2 * quad + 1] = pack_bf16x2(e[2], e[3]);
-        l_half[qb] += (e[0] + e[1]) + (e[2] + e[3]);
+        if constexpr (QB == 1) {
+            tsum += (e[0] + e[1]) + (e[2] + e[3]);
+            pin(tsum);
+        } else {
+            l_half[qb] += (e[0] + e[1]) + (e[2] + e[3]);
+            pin(l_half[qb]);
+        }
         pin(p[qb][h].w[2 * quad]);
         pin(p[qb][h].w[2 * quad + 1]);
-        pin(l_half[qb]);
     };
     // row maximum in three parts (scores 0-7, scores 8-15, both halves of the
     // wave); a masked tile first selects hidden keys to -inf
@@ -367,6 +379,42 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
         }
     };
 
+    // hide the keys of tile j a row of query block qb cannot see (select to -inf)
+    auto mask_tile = [&](Sc &s, int qb, int j) __attribute__((always_inline)) {
+        const int my_q = q0 + 32 * qb + l32;
+        const int lim = j < nwb ? (CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1) : -1;
+        const int rel = lim - j * BN - 4 * g;  // key r visible iff offset(r) <= rel
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            s[qb][r] = (8 * (r >> 2) + (r & 3) <= rel) ? s[qb][r] : -INFINITY;
+    };
+    // One query block per wave: the lazy reference is checked by the tile's
+    // row sums instead of its row maximum. A lane's 16 probabilities are all
+    // at most 2^8 when their sum is, which is the bound the reference keeps;
+    // otherwise (or while some row has not seen a key) the tile takes this
+    // slow path: exact maximum, reference update, rescale, probabilities
+    // again. The scores are already masked.
+    bool ref_unset = true;  // some row of the wave still has m_ref = -inf
+    auto slow_tile = [&](Sc &s, Pc &p) __attribute__((always_inline)) {
+        row_max(s, 0, 0, 0, false);
+        row_max(s, 0, 1, 0, false);
+        row_max(s, 0, 2, 0, false);
+        move_ref(0);
+        apply_alpha();
+        tsum = 0.f;
+        probs_quad(s, p, 0, 0, 0);
+        probs_quad(s, p, 0, 0, 1);
+        probs_quad(s, p, 0, 1, 0);
+        probs_quad(s, p, 0, 1, 1);
+        ref_unset = __any(m_ref[0] == -INFINITY);
+    };
+    auto check_tile = [&](Sc &s, Pc &p) __attribute__((always_inline)) {
+        if (ref_unset || __any(tsum > 256.f))
+            slow_tile(s, p);
+        l_half[0] += tsum;
+        tsum = 0.f;
+    };
+
     // ---- prologue -------------------------------------------------------------------
     // Copies of K tiles 0-3 and V tiles 0-2, drained. Then S_0, its statistics
     // and the first chunk of P_0 without overlap, and K tile 1 into registers.
@@ -398,6 +446,9 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
         probs_quad(sA, pA, qb, 0, 0);
         probs_quad(sA, pA, qb, 0, 1);
     }
+    apply_alpha();  // the first reference moves consume their rescale here
+    if constexpr (QB == 1)
+        ref_unset = __any(m_ref[0] == -INFINITY);
 #pragma unroll
     for (int kk = 0; kk < KKN; ++kk)
         read_k(sK1, kk);
@@ -417,7 +468,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
         uint4 *const vb[4] = {sV0, sV1, sV2, sV3};
         dma_k(kb[P], j + 4);
         dma_v(vb[(P + 3) & 3], j + 3);
-        apply_alpha();
+        if constexpr (QB == 2)
+            apply_alpha();
         slot_end();
 
         // Stage A, NG groups of four MFMAs (QK of tile j+1; with two query
@@ -459,6 +511,9 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
         if constexpr (QB == 2) {
             move_ref(0);
             slot_end();
+        } else {
+            check_tile(sc, pc);  // tile j's probabilities are complete
+            slot_end();
         }
 
         // Stage B, NG groups of four MFMAs (PV of tile j). Each group reads
@@ -486,11 +541,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
                     row_max(sn, 1, 2, j + 1, MASK);
                 }
             } else {
-                if (grp == 0) {
-                    row_max(sn, 0, 0, j + 1, MASK);
-                    row_max(sn, 0, 1, j + 1, MASK);
-                    row_max(sn, 0, 2, j + 1, MASK);
-                }
+                if (MASK && grp == 0)
+                    mask_tile(sn, 0, j + 1);
                 if (NG == 2 && grp == 1) {
                     probs_quad(sn, pn, 0, 0, 0);
                     probs_quad(sn, pn, 0, 0, 1);
@@ -506,7 +558,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
             }
             slot_end();
-            if (grp == (QB == 2 ? 1 : 0)) {
+            if (QB == 2 && grp == 1) {
                 move_ref(QB - 1);
                 slot_end();
             }

@@ -35,9 +35,14 @@
 // contiguous 1 KB (K, ds_read_b128) or 512 B (V, ds_read_b64_tr_b16) block,
 // which is free of bank conflicts and needs no address arithmetic.
 //
-// The running maximum moves lazily (only when a tile's row maximum exceeds it
-// by more than 8 in log2 units), so probabilities stay below 2^8 and the
-// accumulator is rescaled only on the rare tiles that move it.
+// The running maximum moves lazily: probabilities stay at most 2^8 above the
+// reference and the accumulator is rescaled only on the rare tiles that move
+// it. With two query blocks per wave the reference moves when a tile's row
+// maximum exceeds it by more than 8 in log2 units. With one block the check
+// uses the tile's row sums, which the softmax computes anyway: a lane whose
+// 16 probabilities sum to at most 2^8 has none above 2^8, and only a tile
+// that fails (or a wave with a row that has seen no key yet) takes the exact
+// maximum and recomputes its probabilities.
 
 #include <hip/hip_runtime.h>
 #include <math.h>

@@ -259,3 +259,37 @@ def test_decode_lengths_clamped_on_device():
     o, lse, _ = H.run_decode(q, kc, vc, lens, s, 4)
     o_ref, lse_ref = oracle.attn_decode(q, kc, vc, np.array([0, 64], dtype=np.int32), s)
     H.assert_parity(H.metrics(o, lse, o_ref, lse_ref), "decode clamp")
+
+
+# Scores that make the running reference move late or far. Every query row is
+# the same +-1 vector u and key jstar is gamma * u, so row i's score for jstar
+# is gamma * sqrt(d) above the O(1) scores of the random keys: 33 (gamma = 2)
+# or 200 (gamma = 12) log2 units at d = 128. The first makes a tile's row sums
+# exceed the reference's bound when jstar arrives in the middle of the keys;
+# the second overflows them to inf. Sq > Sk with causal leaves the first rows
+# of the first waves without any visible key. All values are exact in bf16.
+REF_CASES = [
+    # (d, causal, Sq, Sk, jstar, gamma)
+    (128, True, 1000, 1000, 700, 2.0),
+    (128, False, 600, 1000, 700, 2.0),
+    (128, True, 1000, 1000, 5, 2.0),
+    (128, True, 1000, 1000, 700, 12.0),
+    (256, True, 700, 700, 450, 2.0),
+    (256, False, 300, 700, 450, 12.0),
+    (128, True, 300, 200, 150, 2.0),
+    (256, True, 300, 200, 150, 2.0),
+]
+
+
+@pytest.mark.parametrize("case", REF_CASES)
+def test_reference_moves_late_or_far(case):
+    d, causal, Sq, Sk, jstar, gamma = case
+    seed = 2000 + REF_CASES.index(case)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    u = np.where(rng.random(d) < 0.5, -1.0, 1.0).astype(np.float32)
+    q = inputs.bf16_bits(np.broadcast_to(u, (1, 2, Sq, d)).copy())
+    kf = rng.standard_normal(size=(1, 1, Sk, d), dtype=np.float32) * np.float32(0.5)
+    kf[0, 0, jstar, :] = np.float32(gamma) * u
+    k = inputs.bf16_bits(kf)
+    v = _rand_bits(seed + 1, (1, 1, Sk, d))
+    _check_full(q, k, v, causal, inputs.default_scale(d), f"reference {case}")

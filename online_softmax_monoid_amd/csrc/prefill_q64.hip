@@ -592,18 +592,37 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
         step(IntC<2>{}, IntC<0>{}, j + 2, sA, sB, pA, pB);
         step(IntC<3>{}, IntC<0>{}, j + 3, sB, sA, pB, pA);
     }
+    // Masked steps. From tile nwb on the wave sees no key of the tiles it
+    // would touch (PV of tile j, QK of tile j+1): it only issues its share of
+    // the copies and keeps the barrier, leaving its SIMD to the other wave.
+    // (Step nwb-1 still runs: its PV is live, and the tile nwb it scores is
+    // all masked and never checked.)
+    auto mstep = [&](auto PI, int j, Sc &sc, Sc &sn, Pc &pc, Pc &pn) __attribute__((always_inline)) {
+        constexpr int P = decltype(PI)::value;
+        if (j < nwb) {
+            step(PI, IntC<1>{}, j, sc, sn, pc, pn);
+        } else {
+            uint4 *const kb[4] = {sK0, sK1, sK2, sK3};
+            uint4 *const vb[4] = {sV0, sV1, sV2, sV3};
+            dma_k(kb[P], j + 4);
+            dma_v(vb[(P + 3) & 3], j + 3);
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * DPW));  // vmcnt(3 DPW)
+            __builtin_amdgcn_s_barrier();
+            slot_end();
+        }
+    };
     for (; j + 3 < nblk; j += 4) {
-        step(IntC<0>{}, IntC<1>{}, j, sA, sB, pA, pB);
-        step(IntC<1>{}, IntC<1>{}, j + 1, sB, sA, pB, pA);
-        step(IntC<2>{}, IntC<1>{}, j + 2, sA, sB, pA, pB);
-        step(IntC<3>{}, IntC<1>{}, j + 3, sB, sA, pB, pA);
+        mstep(IntC<0>{}, j, sA, sB, pA, pB);
+        mstep(IntC<1>{}, j + 1, sB, sA, pB, pA);
+        mstep(IntC<2>{}, j + 2, sA, sB, pA, pB);
+        mstep(IntC<3>{}, j + 3, sB, sA, pB, pA);
     }
     if (j < nblk)
-        step(IntC<0>{}, IntC<1>{}, j, sA, sB, pA, pB);
+        mstep(IntC<0>{}, j, sA, sB, pA, pB);
     if (j + 1 < nblk)
-        step(IntC<1>{}, IntC<1>{}, j + 1, sB, sA, pB, pA);
+        mstep(IntC<1>{}, j + 1, sB, sA, pB, pA);
     if (j + 2 < nblk)
-        step(IntC<2>{}, IntC<1>{}, j + 2, sA, sB, pA, pB);
+        mstep(IntC<2>{}, j + 2, sA, sB, pA, pB);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy may still target LDS
     apply_alpha();
 

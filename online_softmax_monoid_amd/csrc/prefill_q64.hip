@@ -666,6 +666,9 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
 #ifndef MIATTN_Q64_D256_WAVES
 #define MIATTN_Q64_D256_WAVES 4
 #endif
+#ifndef MIATTN_Q64_D128_WPE  // waves per SIMD the d = 128 kernel is compiled for
+#define MIATTN_Q64_D128_WPE (2 * MIATTN_Q64_D128_WAVES / 8)
+#endif
 
 template <int D, int QB, int NWV, int WPE>
 hipError_t launch_q64(const FwdArgs &a, bool causal, hipStream_t stream)
@@ -691,7 +694,7 @@ hipError_t launch_fwd_q64(const FwdArgs &a, int d, bool causal, hipStream_t stre
     switch (d) {
     case 128:
 #if MIATTN_Q64_D128_QB == 1
-        return launch_q64<128, 1, MIATTN_Q64_D128_WAVES, 2 * MIATTN_Q64_D128_WAVES / 8>(a, causal, stream);
+        return launch_q64<128, 1, MIATTN_Q64_D128_WAVES, MIATTN_Q64_D128_WPE>(a, causal, stream);
 #else
         return launch_q64<128, 2, MIATTN_Q64_D128_WAVES, MIATTN_Q64_D128_WAVES / 4>(a, causal, stream);
 #endif

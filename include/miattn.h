@@ -17,7 +17,8 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers into caller-owned memory; the
  *     library allocates nothing and keeps no state between calls, apart from
- *     a thread-local copy of the last error message.
+ *     a thread-local copy of the last error message and a per-device cache
+ *     of how many prefill workgroups fit on the device at once.
  *   - Tensors are dense, row-major, contiguous. bf16 tensors are raw IEEE
  *     bfloat16 bit patterns (uint16); q, k, v, o and the workspace must be
  *     16-byte aligned, lse and kv_lens 4-byte aligned.

@@ -134,8 +134,10 @@ __device__ __forceinline__ u32x4 make_desc(const void *base, uint32_t bytes)
 // copies is explicit in the kernel.
 __device__ __forceinline__ void copy_to_lds(u32x4 desc, uint32_t voffset, uint32_t lds_base)
 {
-    // M0 holds the LDS address; one wait state between writing M0 and the copy
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    // M0 holds the LDS address. The compiler's hazard check does not look
+    // inside the assembly: five wait states cover a descriptor word written by
+    // a VALU instruction (v_readfirstlane) and M0 (which needs one).
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
                  : "v"(voffset), "s"(desc), "{m0}"(lds_base)
                  : "memory");

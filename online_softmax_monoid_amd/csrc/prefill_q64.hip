@@ -30,10 +30,15 @@
 //            tile j+1; LDS reads of K_{j+2}
 //
 // K and V tiles of 32 keys go global -> LDS by range-checked buffer DMA (keys
-// past the workgroup's last visible key arrive as zeros) into four-deep rings, one barrier per tile. Both
-// are stored fragment-major: each LDS read instruction of a wave reads one
-// contiguous 1 KB (K, ds_read_b128) or 512 B (V, ds_read_b64_tr_b16) block,
-// which is free of bank conflicts and needs no address arithmetic.
+// past the item's last visible key arrive as zeros) into four-deep rings, one
+// barrier per tile. Both are stored fragment-major: each LDS read instruction
+// of a wave reads one contiguous 1 KB (K, ds_read_b128) or 512 B (V,
+// ds_read_b64_tr_b16) block, which is free of bank conflicts.
+//
+// The grid is persistent: one workgroup per resident slot walks a fixed list
+// of work items (query tile of one query head). The copy stream does not stop
+// at an item's end: the last steps of an item already copy the next item's
+// first K and V tiles, so the next item starts without waiting for HBM.
 //
 // The running maximum moves lazily: probabilities stay at most 2^8 above the
 // reference and the accumulator is rescaled only on the rare tiles that move
@@ -47,6 +52,9 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <algorithm>
+#include <atomic>
 
 #include "launch.h"
 #include "tile_order.h"
@@ -117,36 +125,87 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 
 __device__ __forceinline__ void slot_end() { __builtin_amdgcn_sched_barrier(0); }
 
+// Workgroup barrier that no memory access of the source crosses: the copies
+// into LDS are invisible to the compiler, so it must not move an LDS read
+// above the barrier that publishes the copied data.
+__device__ __forceinline__ void barrier()
+{
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Keep a value's computation inside its slot: an input pinned here cannot be
 // consumed earlier, an output pinned here cannot be computed later (the
 // compiler would otherwise sink work towards its uses across slots).
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor (raw, 32-bit offsets, range-checked against `bytes`)
+__device__ __forceinline__ u32x4 make_desc(const void *base, uint32_t bytes)
+{
+    const uint64_t addr = (uint64_t)(uintptr_t)base;
+    u32x4 d;
+    d.x = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    d.y = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32) & 0xffffu);
+    d.z = __builtin_amdgcn_readfirstlane(bytes);
+    d.w = 0x00020000u;
+    return d;
+}
+
+// 16 bytes per lane from global memory (byte voffset, range-checked: bytes
+// out of range read as zero) straight into LDS at lds_base + 16 * lane.
+// Written as inline assembly so that the compiler neither drains these copies
+// before LDS reads it cannot prove disjoint nor counts them: every wait on
+// them is explicit in the kernel. M0 holds the LDS address. The compiler's
+// hazard check does not look inside the assembly, so it carries its own wait
+// states: five, the most any of its inputs needs (a descriptor word written
+// by a VALU instruction such as v_readfirstlane and read by a vector memory
+// instruction; M0 written and read by an LDS copy needs one). No instruction
+// offset: it would move the LDS address as well.
+__device__ __forceinline__ void copy_to_lds(u32x4 desc, uint32_t voffset, uint32_t lds_base)
+{
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voffset), "s"(desc), "{m0}"(lds_base)
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+
+// One work item: the BM query rows of one (batch, query head) and the keys
+// they see (same tile order as prefill.hip)
+struct Item {
+    int64_t qrow0, krow0;  // first row of the query head / kv-head
+    int q_wg, kv_end, nblk;
+};
+
 template <bool CAUSAL, int NWV, int D, int QB, int WPE>
 __global__ void __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-fwd_q64_kernel(FwdArgs a, int n_qtiles)
+fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 {
-    // D = 128 runs QB = 2 query blocks (64 rows) per wave, D = 256 one block
-    // (32 rows): either way a tile step is 16 QK and 16 PV MFMAs per wave
+    // D = 128 runs QB = 1 (32 rows, two waves per SIMD) or 2 (64 rows, one
+    // wave per SIMD) query blocks per wave, D = 256 one block
     constexpr int BN = 32;             // keys per tile
-    constexpr int BM = NWV * 32 * QB;  // query rows per workgroup
+    constexpr int BM = NWV * 32 * QB;  // query rows per work item
     constexpr int KKN = D / 16;        // 16-dim steps of QK = K fragments = copy instructions per tile
     constexpr int DBN = D / 32;        // 32-dim blocks of the output
     constexpr int DPW = KKN / NWV;     // copy instructions per wave per tile, each of K and V
     constexpr int NG = QB * KKN / 4;   // groups of four MFMAs per stage
     constexpr int NPV = QB * DBN;      // PV MFMAs per 16-key chunk
     static_assert((NG == 2 || NG == 4) && NWV * DPW == KKN && 3 * DPW < 16, "tile step shape");
-    constexpr int TILE_CH = BN * D / 8;     // 16-byte chunks per tile
+    constexpr int TILE_CH = BN * D / 8;  // 16-byte chunks per tile
 
-    __shared__ __attribute__((aligned(16))) uint4 sK0[TILE_CH];
-    __shared__ __attribute__((aligned(16))) uint4 sK1[TILE_CH];
-    __shared__ __attribute__((aligned(16))) uint4 sK2[TILE_CH];
-    __shared__ __attribute__((aligned(16))) uint4 sK3[TILE_CH];
-    __shared__ __attribute__((aligned(16))) uint4 sV0[TILE_CH];
-    __shared__ __attribute__((aligned(16))) uint4 sV1[TILE_CH];
-    __shared__ __attribute__((aligned(16))) uint4 sV2[TILE_CH];
-    __shared__ __attribute__((aligned(16))) uint4 sV3[TILE_CH];
+    __shared__ __attribute__((aligned(16))) uint4 sK_[4 * TILE_CH];  // K ring, 4 tiles
+    __shared__ __attribute__((aligned(16))) uint4 sV_[4 * TILE_CH];  // V ring
+    uint4 *const sK = sK_;  // the lambdas below may not name __shared__ variables
+    uint4 *const sV = sV_;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -154,54 +213,41 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     const int l32 = lane & 31;
     const int g = lane >> 5;
 
-    // ---- work decomposition (same order as prefill.hip) ---------------------
-    const int G = a.Hq / a.Hkv;
-    const TileOrder to = tile_order((int)blockIdx.x, a.B * a.Hkv, G, n_qtiles, CAUSAL);
-    const int unit = to.unit, gq = to.gq, qtile = to.qtile;
-    const int b = unit / a.Hkv;
-    const int kvh = unit - b * a.Hkv;
-    const int hq = kvh * G + gq;
-
     const int Sq = a.Sq, Sk = a.Sk;
     const int diag = Sk - Sq;
-    const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
-    const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
+    const int G = a.Hq / a.Hkv;
 
-    const int q_wg = qtile * BM;
-    const int q_wg_last = min(q_wg + BM, Sq) - 1;
-    const int q0 = q_wg + wave * 32 * QB;  // first row of this wave
-    const bool wave_live = q0 < Sq;
-
-    int kv_end = Sk;
-    int wave_end = wave_live ? Sk : 0;
-    if (CAUSAL) {
-        kv_end = min(Sk, max(0, q_wg_last + diag + 1));
-        if (wave_live)
-            wave_end = min(Sk, max(0, min(q0 + 32 * QB - 1, Sq - 1) + diag + 1));
-    }
-    const int nblk = (kv_end + BN - 1) / BN;   // tiles the workgroup walks
-    const int nwb = (wave_end + BN - 1) / BN;  // tiles this wave computes
-
-    // ---- Q fragments (B operands of S^T = K Q^T) ------------------------------
-    bf16x8 qf[QB][KKN];
-    {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0 * D, (uint32_t)Sq * D * 2);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const uint32_t off = (uint32_t)(q0 + 32 * qb + l32) * D * 2 + 16 * g;
-#pragma unroll
-            for (int kk = 0; kk < KKN; ++kk) {
-                Frag8 f;
-                f.u = buf_load16(rq, off + 32 * kk);  // rows >= Sq read as 0
-                qf[qb][kk] = f.v;
-            }
-        }
-    }
+    // ---- schedule --------------------------------------------------------------------
+    // Workgroup w runs on XCD w % 8 and takes, round after round, items
+    // xcd + 8 li: li = r GX + s in even rounds, r GX + GX-1-s in odd ones (s =
+    // w / 8, GX = workgroups per XCD). The items of an XCD are the ones the
+    // tile order puts there, and the alternating direction pairs heavy
+    // causal tiles with light ones.
+    const int xcd = (int)blockIdx.x & 7, wslot = (int)blockIdx.x >> 3, GX = (int)gridDim.x >> 3;
+    auto item_id = [&](int r) __attribute__((always_inline)) {
+        const int li = r * GX + ((r & 1) ? GX - 1 - wslot : wslot);
+        return xcd + 8 * li;
+    };
+    auto describe = [&](int id) __attribute__((always_inline)) {
+        const TileOrder to = tile_order(id, a.B * a.Hkv, G, n_qtiles, CAUSAL);
+        const int b = to.unit / a.Hkv;
+        const int kvh = to.unit - b * a.Hkv;
+        const int hq = kvh * G + to.gq;
+        Item it;
+        it.qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
+        it.krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
+        it.q_wg = to.qtile * BM;
+        const int q_wg_last = min(it.q_wg + BM, Sq) - 1;
+        it.kv_end = CAUSAL ? min(Sk, max(0, q_wg_last + diag + 1)) : Sk;
+        it.nblk = (it.kv_end + BN - 1) / BN;
+        return it;
+    };
 
     // ---- global -> LDS copies ---------------------------------------------------
-    // A tile takes D/16 DMA instructions (1 KB each) for K and as many for V;
-    // wave w issues instructions DPW w .. DPW w + DPW - 1 of each. Every copy gets a buffer
-    // resource covering just its tile, so keys at or past Sk read as zero.
+    // A tile takes D/16 copy instructions (1 KB each) for K and as many for V;
+    // wave w issues instructions DPW w .. DPW w + DPW - 1 of each. Every copy's
+    // descriptor covers just its tile up to the item's last visible key, so
+    // keys past it read as zero and copies past the range move no data.
     //
     // K layout: block kk (1 KB) holds lane L's A fragment for dims
     // 16kk + 8(L/32) .. +7 of key L%32, at byte 16L.
@@ -220,43 +266,51 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
         const int dim = 32 * db + 16 * (G4 & 1) + 8 * qh;
         voff[h] = (uint32_t)(key * D + dim) * 2;
     }
-    const uint16_t *const kbase = a.k + krow0 * D;
-    const uint16_t *const vbase = a.v + krow0 * D;
-    // keys at or past kv_end (at most Sk; no row of the workgroup sees them)
-    // arrive as zeros, and the prefetches past the range cost no memory traffic
-    auto tile_rsrc = [&](const uint16_t *base, int tile) __attribute__((always_inline)) {
-        const int keys = __builtin_amdgcn_readfirstlane(min(max(kv_end - tile * BN, 0), BN));
-        return make_rsrc(base + (int64_t)tile * (BN * D), (uint32_t)keys * (D * 2));
-    };
-    auto dma_k = [&](uint4 *buf, int tile) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase, tile);
+    // LDS byte addresses (M0 values) of this wave's share of ring slot 0
+    constexpr uint32_t TILE_B = TILE_CH * 16;
+    const uint32_t m0k = lds_addr(sK) + 1024 * DPW * wave;
+    const uint32_t m0v = lds_addr(sV) + 1024 * DPW * wave;
+    // copy of the BN keys from src on, of which `keys` exist (none if keys <=
+    // 0), into ring slot s. The descriptor ends at the last key that exists:
+    // keys past it read as zero, and a copy of no key moves no data.
+    auto dma_k = [&](int s, const uint16_t *src, int keys) __attribute__((always_inline)) {
+        const u32x4 d = make_desc(src, (uint32_t)max(keys, 0) * (D * 2));
+        const uint32_t m0 = m0k + (uint32_t)(s & 3) * TILE_B;
 #pragma unroll
         for (int h = 0; h < DPW; ++h)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(buf + 64 * (DPW * wave + h)), 16,
-                                                     (int)koff[h], 0, 0, 0);
+            copy_to_lds(d, koff[h], m0 + 1024 * h);
     };
-    auto dma_v = [&](uint4 *buf, int tile) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, tile);
+    auto dma_v = [&](int s, const uint16_t *src, int keys) __attribute__((always_inline)) {
+        const u32x4 d = make_desc(src, (uint32_t)max(keys, 0) * (D * 2));
+        const uint32_t m0 = m0v + (uint32_t)(s & 3) * TILE_B;
 #pragma unroll
         for (int h = 0; h < DPW; ++h)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(buf + 64 * (DPW * wave + h)), 16,
-                                                     (int)voff[h], 0, 0, 0);
+            copy_to_lds(d, voff[h], m0 + 1024 * h);
     };
-
     // ---- fragments from LDS -------------------------------------------------------
     Frag8 kf[KKN];      // A fragments of the K tile the next QK uses
     bf16x8 vf[DBN][2];  // A fragments of V^T: [d-block][16-key chunk]
-    auto read_k = [&](const uint4 *buf, int kk) __attribute__((always_inline)) {
-        kf[kk].u = buf[64 * kk + lane];
+    // Reads take a lane's LDS byte address in the slot (K: slot + 16 lane, V:
+    // slot + 8 lane), computed once per step ahead of everything else so that
+    // the reads can start with the step's first MFMA.
+    auto read_k = [&](uint32_t addr, int kk) __attribute__((always_inline)) {
+        typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+        kf[kk].u = __builtin_bit_cast(uint4, *(lds_u32x4 *)(uintptr_t)(addr + 1024 * kk));
     };
-    auto read_v = [&](const uint4 *buf, int db, int kc) __attribute__((always_inline)) {
-        const char *base = (const char *)buf + 8 * lane;
+    auto read_v = [&](uint32_t addr, int db, int kc) __attribute__((always_inline)) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)(const_cast<char *>(base + ((2 * db + kc) * 2 + 0) * 512)));
+            (lds_i16x4 *)(uintptr_t)(addr + ((2 * db + kc) * 2 + 0) * 512));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)(const_cast<char *>(base + ((2 * db + kc) * 2 + 1) * 512)));
+            (lds_i16x4 *)(uintptr_t)(addr + ((2 * db + kc) * 2 + 1) * 512));
         const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         vf[db][kc] = __builtin_bit_cast(bf16x8, both);
+    };
+    const uint32_t lds_k = lds_addr(sK), lds_v = lds_addr(sV);
+    auto kread_addr = [&](int s) __attribute__((always_inline)) {
+        return lds_k + (uint32_t)(s & 3) * TILE_B + 16 * lane;
+    };
+    auto vread_addr = [&](int s) __attribute__((always_inline)) {
+        return lds_v + (uint32_t)(s & 3) * TILE_B + 8 * lane;
     };
 
     // ---- monoid state per query block -------------------------------------------
@@ -269,20 +323,55 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     // One query block per wave: the row sum of the tile whose probabilities
     // are being built, added to l_half once the tile passes its check
     float tsum = 0.f;
+    bool ref_unset = true;  // some row of the wave still has m_ref = -inf
     f32x16 acc[QB][D / 32];
+    auto reset_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m_ref[qb] = -INFINITY;
-        nmc[qb] = 0.f;
-        m_thr[qb] = -INFINITY;
-        alpha_acc[qb] = 1.f;
-        l_half[qb] = 0.f;
+        for (int qb = 0; qb < QB; ++qb) {
+            m_ref[qb] = -INFINITY;
+            nmc[qb] = 0.f;
+            m_thr[qb] = -INFINITY;
+            alpha_acc[qb] = 1.f;
+            l_half[qb] = 0.f;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                acc[qb][db][r] = 0.f;
-    }
+                for (int r = 0; r < 16; ++r)
+                    acc[qb][db][r] = 0.f;
+        }
+        tsum = 0.f;
+        ref_unset = true;
+    };
+
+    // ---- the current and the next item (the lambdas below read these) ---------------
+    int ph = 0;                      // ring slot of the current item's tile 0
+    int nblk = 0, nwb = 0, q0 = 0, kv_end = 0;
+    int64_t qrow0 = 0, krow0 = 0;
+    bool has_next = false;
+    int kv_end_n = 0, q_wg_n = 0;  // kv_end_n = 0 without a next item
+    int64_t qrow0_n = 0;
+    // The copy stream: the next K / V copy's source and the keys that exist
+    // from it on, and the next item's tile 0
+    const uint16_t *kp = a.k, *vp = a.v, *kn = a.k, *vn = a.v;
+    int krem = 0, vrem = 0;
+
+    // ---- Q fragments (B operands of S^T = K Q^T) ------------------------------
+    bf16x8 qf[QB][KKN];
+    // Q rows of an item (query head rows from qrow0_, the wave's first row q0w)
+    // straight from global memory into the fragments; rows >= Sq read as 0
+    auto load_q = [&](int64_t qrow0_, int q0w) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0_ * D, (uint32_t)Sq * D * 2);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const uint32_t off = (uint32_t)(q0w + 32 * qb + l32) * D * 2 + 16 * g;
+#pragma unroll
+            for (int kk = 0; kk < KKN; ++kk) {
+                Frag8 f;
+                f.u = buf_load16(rq, off + 32 * kk);
+                qf[qb][kk] = f.v;
+            }
+        }
+    };
 
     using Sc = f32x16[QB];
     using Pc = Frag8[QB][2];  // [query block][16-key chunk]
@@ -308,7 +397,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
 
     // Softmax work, in pieces placed between the MFMAs. Scores of a query
     // block: s[qb][r], key 8(r/4) + 4g + r%4 of the tile; chunk h = keys
-    // 16h .. 16h+15 = r in [8h, 8h+8). Every piece pins     // its outputs at the end of its group of MFMAs (else the compiler sinks
+    // 16h .. 16h+15 = r in [8h, 8h+8). Every piece pins
+    // its outputs at the end of its group of MFMAs (else the compiler sinks
     // them towards their uses); inside the group its independent chains
     // overlap one another.
     //
@@ -399,7 +489,6 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
     // otherwise (or while some row has not seen a key) the tile takes this
     // slow path: exact maximum, reference update, rescale, probabilities
     // again. The scores are already masked.
-    bool ref_unset = true;  // some row of the wave still has m_ref = -inf
     auto slow_tile = [&](Sc &s, Pc &p) __attribute__((always_inline)) {
         row_max(s, 0, 0, 0, false);
         row_max(s, 0, 1, 0, false);
@@ -420,59 +509,99 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
         tsum = 0.f;
     };
 
-    // ---- prologue -------------------------------------------------------------------
-    // Copies of K tiles 0-3 and V tiles 0-2, drained. Then S_0, its statistics
-    // and the first chunk of P_0 without overlap, and K tile 1 into registers.
-    dma_k(sK0, 0);
-    dma_k(sK1, 1);
-    dma_k(sK2, 2);
-    dma_k(sK3, 3);
-    dma_v(sV0, 0);
-    dma_v(sV1, 1);
-    dma_v(sV2, 2);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the copies
-    __syncthreads();
-    Sc sA, sB;      // scores of the even / odd tile in flight
-    Pc pA, pB;      // probabilities of the even / odd tile
+    // ---- prologue of an item ------------------------------------------------------
+    // The first K tiles (0-3) and V tiles (0-2) are normally copied during the
+    // previous item's last steps; the first item, and one that follows an item
+    // of fewer than four tiles, copies what is missing here and drains. Then
+    // S_0, its statistics and the first chunk of P_0 without overlap, and K
+    // tile 1 into registers.
+    Sc sA, sB;  // scores of the even / odd tile in flight
+    Pc pA, pB;  // probabilities of the even / odd tile
+    // Head dimension 256 loads the next item's Q rows into registers during
+    // the current item's epilogue, 128 loads them here (each the faster of the
+    // two as measured).
+    constexpr bool QPREF = (D == 256);
+    auto prologue = [&](int kmiss, int vmiss) __attribute__((always_inline)) {
+        if constexpr (!QPREF)
+            load_q(qrow0, q0);
+        if (!QPREF || kmiss > 0 || vmiss > 0) {
+            for (int t = 0; t < kmiss; ++t)
+                dma_k(ph + t, a.k + (krow0 + t * BN) * D, kv_end - t * BN);
+            for (int t = 0; t < vmiss; ++t)
+                dma_v(ph + t, a.v + (krow0 + t * BN) * D, kv_end - t * BN);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies (and Q)
+        }
+        barrier();
 #pragma unroll
-    for (int kk = 0; kk < KKN; ++kk)
-        read_k(sK0, kk);
+        for (int kk = 0; kk < KKN; ++kk)
+            read_k(kread_addr(ph), kk);
 #pragma unroll
-    for (int kk = 0; kk < KKN; ++kk)
+        for (int kk = 0; kk < KKN; ++kk)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-            qk_mfma(sA, qb, kk);
+            for (int qb = 0; qb < QB; ++qb)
+                qk_mfma(sA, qb, kk);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        row_max(sA, qb, 0, 0, true);
-        row_max(sA, qb, 1, 0, true);
-        row_max(sA, qb, 2, 0, true);
-        move_ref(qb);
-        probs_quad(sA, pA, qb, 0, 0);
-        probs_quad(sA, pA, qb, 0, 1);
-    }
-    apply_alpha();  // the first reference moves consume their rescale here
-    if constexpr (QB == 1)
-        ref_unset = __any(m_ref[0] == -INFINITY);
+        for (int qb = 0; qb < QB; ++qb) {
+            row_max(sA, qb, 0, 0, true);
+            row_max(sA, qb, 1, 0, true);
+            row_max(sA, qb, 2, 0, true);
+            move_ref(qb);
+            probs_quad(sA, pA, qb, 0, 0);
+            probs_quad(sA, pA, qb, 0, 1);
+        }
+        apply_alpha();  // the first reference moves consume their rescale here
+        if constexpr (QB == 1)
+            ref_unset = __any(m_ref[0] == -INFINITY);
 #pragma unroll
-    for (int kk = 0; kk < KKN; ++kk)
-        read_k(sK1, kk);
-    __syncthreads();  // every wave has read K tile 0 before K tile 4 replaces it
+        for (int kk = 0; kk < KKN; ++kk)
+            read_k(kread_addr(ph + 1), kk);
+        // every wave has read K tile 0 before step 0 copies K tile 4 into its slot
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        barrier();
+    };
+
+    // Copies of step j of an item: K of stream position j+4 and V of j+3, which
+    // are the item's own tiles, the next item's first tiles (K 0-3, V 0-2), or
+    // nothing.
+    auto step_copies = [&](int j) __attribute__((always_inline)) {
+        dma_k(ph + j, kp, krem);
+        dma_v(ph + j + 3, vp, vrem);
+        // after the item's last tile, the next item's first ones
+        if (j + 5 == nblk) {
+            kp = kn;
+            krem = kv_end_n;
+        } else {
+            kp += BN * D;
+            krem -= BN;
+        }
+        if (j + 4 == nblk) {
+            vp = vn;
+            vrem = kv_end_n;
+        } else {
+            vp += BN * D;
+            vrem -= BN;
+        }
+    };
+    // wait until the copies the next step reads (V tile j+1, K tile j+3) are
+    // complete -- the 3 DPW newer copy instructions of this wave may still
+    // fly -- and barrier
+    auto step_end = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * DPW));  // vmcnt(3 DPW)
+        barrier();
+    };
 
     // ---- one tile step ------------------------------------------------------------------
-    // Tile m's K and V live in buffer m % 4. Step j: copies of K tile j+4 (into
-    // tile j's K buffer, last read in step j-2) and V tile j+3 (into tile j-1's
-    // V buffer, last read in step j-1); stage A; stage B; wait until the copies
-    // the next step reads (V tile j+1, K tile j+3) are complete -- the 3 DPW
-    // newer copy instructions of this wave may still fly -- and barrier.
-    auto step = [&](auto PI, auto MASKc, int j, Sc &sc, Sc &sn, Pc &pc, Pc &pn)
-        __attribute__((always_inline)) {
-        constexpr int P = decltype(PI)::value;  // j % 4
+    // Tile t of the copy stream lives in ring slot t % 4; the current item's
+    // tile j is stream position ph + j. Step j: copies of stream positions
+    // j+4 (K, into tile j's slot, last read in step j-2) and j+3 (V, into tile
+    // j-1's slot, last read in step j-1); stage A; stage B; wait; barrier.
+    auto step = [&](auto MASKc, int j, Sc &sc, Sc &sn, Pc &pc, Pc &pn) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(MASKc)::value;
-        uint4 *const kb[4] = {sK0, sK1, sK2, sK3};
-        uint4 *const vb[4] = {sV0, sV1, sV2, sV3};
-        dma_k(kb[P], j + 4);
-        dma_v(vb[(P + 3) & 3], j + 3);
+        uint32_t kread = kread_addr(ph + j + 2);  // K tile j+2
+        uint32_t vread = vread_addr(ph + j);      // V tile j
+        pin(kread);
+        pin(vread);
+        step_copies(j);
         if constexpr (QB == 2)
             apply_alpha();
         slot_end();
@@ -492,7 +621,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
                 if (grp < 2)
 #pragma unroll
                     for (int c = sl * NRV / 8; c < (sl + 1) * NRV / 8; ++c)
-                        read_v(vb[P], c >> 1, c & 1);
+                        read_v(vread, c >> 1, c & 1);
             }
             if (grp < 2 * QB)
                 probs_quad(sc, pc, grp >> 1, 1, grp & 1);
@@ -535,7 +664,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
                 const int idx = sl % NPV;
                 pv_mfma(pc, idx % QB, idx / QB, sl / NPV);
                 if (i < KPG)
-                    read_k(kb[(P + 2) & 3], KPG * grp + i);
+                    read_k(kread, KPG * grp + i);
             }
             if constexpr (QB == 2) {
                 probs_quad(sn, pn, grp >> 1, 0, grp & 1);
@@ -568,90 +697,143 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
                 slot_end();
             }
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * DPW));  // vmcnt(3 DPW)
-        __builtin_amdgcn_s_barrier();
-        slot_end();
+        step_end();
     };
 
-    // Leading steps of this wave that need no mask (a multiple of 4): tile j+1
-    // fully visible to every row of the wave and within its range.
-    int n_fast;
-    {
-        int first_masked = Sk / BN;  // ragged key tail
-        if (CAUSAL)
-            first_masked = min(first_masked, max(0, (q0 + diag + 1) / BN));
-        n_fast = min(nwb, first_masked) - 1;
-        n_fast = max(0, n_fast) & ~3;
-        n_fast = __builtin_amdgcn_readfirstlane(n_fast);
-    }
-
-    int j = 0;
-    for (; j < n_fast; j += 4) {
-        step(IntC<0>{}, IntC<0>{}, j, sA, sB, pA, pB);
-        step(IntC<1>{}, IntC<0>{}, j + 1, sB, sA, pB, pA);
-        step(IntC<2>{}, IntC<0>{}, j + 2, sA, sB, pA, pB);
-        step(IntC<3>{}, IntC<0>{}, j + 3, sB, sA, pB, pA);
-    }
     // Masked steps. From tile nwb on the wave sees no key of the tiles it
     // would touch (PV of tile j, QK of tile j+1): it only issues its share of
     // the copies and keeps the barrier, leaving its SIMD to the other wave.
     // (Step nwb-1 still runs: its PV is live, and the tile nwb it scores is
     // all masked and never checked.)
-    auto mstep = [&](auto PI, int j, Sc &sc, Sc &sn, Pc &pc, Pc &pn) __attribute__((always_inline)) {
-        constexpr int P = decltype(PI)::value;
+    auto mstep = [&](int j, Sc &sc, Sc &sn, Pc &pc, Pc &pn) __attribute__((always_inline)) {
         if (j < nwb) {
-            step(PI, IntC<1>{}, j, sc, sn, pc, pn);
+            step(IntC<1>{}, j, sc, sn, pc, pn);
         } else {
-            uint4 *const kb[4] = {sK0, sK1, sK2, sK3};
-            uint4 *const vb[4] = {sV0, sV1, sV2, sV3};
-            dma_k(kb[P], j + 4);
-            dma_v(vb[(P + 3) & 3], j + 3);
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * DPW));  // vmcnt(3 DPW)
-            __builtin_amdgcn_s_barrier();
-            slot_end();
+            step_copies(j);
+            step_end();
         }
     };
-    for (; j + 3 < nblk; j += 4) {
-        mstep(IntC<0>{}, j, sA, sB, pA, pB);
-        mstep(IntC<1>{}, j + 1, sB, sA, pB, pA);
-        mstep(IntC<2>{}, j + 2, sA, sB, pA, pB);
-        mstep(IntC<3>{}, j + 3, sB, sA, pB, pA);
-    }
-    if (j < nblk)
-        mstep(IntC<0>{}, j, sA, sB, pA, pB);
-    if (j + 1 < nblk)
-        mstep(IntC<1>{}, j + 1, sB, sA, pB, pA);
-    if (j + 2 < nblk)
-        mstep(IntC<2>{}, j + 2, sA, sB, pA, pB);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy may still target LDS
-    apply_alpha();
 
-    // ---- epilogue ------------------------------------------------------------------
+    // ---- epilogue of an item ------------------------------------------------------
+    auto epilogue = [&]() __attribute__((always_inline)) {
+        apply_alpha();
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int my_q = q0 + 32 * qb + l32;
-        const float l_tot = halves_sum(l_half[qb]);
-        if (my_q < Sq) {
-            const bool empty = !(l_tot > 0.f);
-            const float inv = empty ? 0.f : 1.f / l_tot;
-            uint16_t *orow = a.o + (qrow0 + my_q) * D + 4 * g;
+        for (int qb = 0; qb < QB; ++qb) {
+            const int my_q = q0 + 32 * qb + l32;
+            const float l_tot = halves_sum(l_half[qb]);
+            if (my_q < Sq) {
+                const bool empty = !(l_tot > 0.f);
+                const float inv = empty ? 0.f : 1.f / l_tot;
+                uint16_t *orow = a.o + (qrow0 + my_q) * D + 4 * g;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+                for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int rho = 0; rho < 4; ++rho) {
-                    uint2 w;
-                    if (empty) {
-                        w = make_uint2(0, 0);
-                    } else {
-                        w.x = pack_bf16x2(acc[qb][db][4 * rho] * inv, acc[qb][db][4 * rho + 1] * inv);
-                        w.y = pack_bf16x2(acc[qb][db][4 * rho + 2] * inv, acc[qb][db][4 * rho + 3] * inv);
+                    for (int rho = 0; rho < 4; ++rho) {
+                        uint2 w;
+                        if (empty) {
+                            w = make_uint2(0, 0);
+                        } else {
+                            w.x = pack_bf16x2(acc[qb][db][4 * rho] * inv, acc[qb][db][4 * rho + 1] * inv);
+                            w.y = pack_bf16x2(acc[qb][db][4 * rho + 2] * inv, acc[qb][db][4 * rho + 3] * inv);
+                        }
+                        *(uint2 *)(orow + 32 * db + 8 * rho) = w;
                     }
-                    *(uint2 *)(orow + 32 * db + 8 * rho) = w;
-                }
-            if (g == 0)
-                a.lse[qrow0 + my_q] = empty ? -INFINITY : m_ref[qb] * a.scale + logf(l_tot);
+                if (g == 0)
+                    a.lse[qrow0 + my_q] = empty ? -INFINITY : m_ref[qb] * a.scale + logf(l_tot);
+            }
         }
+    };
+
+    // ---- the items of this workgroup ----------------------------------------------
+    int kmiss = 4, vmiss = 3;  // first tiles of the current item not yet copied
+    int id = item_id(0);
+    Item nx = describe(id < n_items ? id : 0);
+    if constexpr (QPREF)
+        load_q(nx.qrow0, nx.q_wg + wave * 32 * QB);
+    for (int r = 0; id < n_items; ++r) {
+        const Item cur = nx;
+        const int id_n = item_id(r + 1);
+        has_next = id_n < n_items;
+        kv_end_n = 0;
+        if (has_next) {
+            nx = describe(id_n);
+            qrow0_n = nx.qrow0;
+            kv_end_n = nx.kv_end;
+            q_wg_n = nx.q_wg;
+            kn = a.k + nx.krow0 * D;
+            vn = a.v + nx.krow0 * D;
+        }
+        qrow0 = cur.qrow0;
+        krow0 = cur.krow0;
+        kv_end = cur.kv_end;
+        nblk = cur.nblk;
+        q0 = cur.q_wg + wave * 32 * QB;  // first row of this wave
+        const bool wave_live = q0 < Sq;
+        int wave_end = wave_live ? Sk : 0;
+        if (CAUSAL && wave_live)
+            wave_end = min(Sk, max(0, min(q0 + 32 * QB - 1, Sq - 1) + diag + 1));
+        nwb = (wave_end + BN - 1) / BN;  // tiles this wave computes
+        // the copy stream of step 0: K tile 4 and V tile 3, of this item or
+        // (when it is shorter) of the next
+        if (nblk > 4) {
+            kp = a.k + (krow0 + 4 * BN) * D;
+            krem = kv_end - 4 * BN;
+        } else {
+            kp = kn + (4 - nblk) * BN * D;
+            krem = kv_end_n - (4 - nblk) * BN;
+        }
+        if (nblk > 3) {
+            vp = a.v + (krow0 + 3 * BN) * D;
+            vrem = kv_end - 3 * BN;
+        } else {
+            vp = vn + (3 - nblk) * BN * D;
+            vrem = kv_end_n - (3 - nblk) * BN;
+        }
+
+        reset_state();
+        prologue(kmiss, vmiss);
+
+        // Leading steps of this wave that need no mask (an even number): tile
+        // j+1 fully visible to every row of the wave and within its range.
+        int n_fast;
+        {
+            int first_masked = Sk / BN;  // ragged key tail
+            if (CAUSAL)
+                first_masked = min(first_masked, max(0, (q0 + diag + 1) / BN));
+            n_fast = min(nwb, first_masked) - 1;
+            n_fast = max(0, n_fast) & ~1;
+            n_fast = __builtin_amdgcn_readfirstlane(n_fast);
+        }
+        int j = 0;
+        if constexpr (D == 256) {  // four steps per iteration (measured faster at 256, not at 128)
+            for (; j + 3 < n_fast; j += 4) {
+                step(IntC<0>{}, j, sA, sB, pA, pB);
+                step(IntC<0>{}, j + 1, sB, sA, pB, pA);
+                step(IntC<0>{}, j + 2, sA, sB, pA, pB);
+                step(IntC<0>{}, j + 3, sB, sA, pB, pA);
+            }
+        }
+        for (; j < n_fast; j += 2) {
+            step(IntC<0>{}, j, sA, sB, pA, pB);
+            step(IntC<0>{}, j + 1, sB, sA, pB, pA);
+        }
+        for (; j + 1 < nblk; j += 2) {
+            mstep(j, sA, sB, pA, pB);
+            mstep(j + 1, sB, sA, pB, pA);
+        }
+        if (j < nblk)
+            mstep(j, sA, sB, pA, pB);
+        // the last QK has used Q: the next item's rows load during the epilogue
+        if (QPREF && has_next)
+            load_q(qrow0_n, q_wg_n + wave * 32 * QB);
+        epilogue();
+
+        kmiss = max(0, 4 - nblk);
+        vmiss = max(0, 3 - nblk);
+        ph = (ph + nblk) & 3;
+        id = id_n;
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy may still target LDS
 }
 
 // Build switches for measuring other shapes: the number of waves per
@@ -670,21 +852,60 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles)
 #define MIATTN_Q64_D128_WPE (2 * MIATTN_Q64_D128_WAVES / 8)
 #endif
 
+// Workgroups resident on the current device at once for a kernel: compute
+// units times the kernel's occupancy, cached per device and kernel.
+template <typename K>
+int resident_workgroups(K kernel, int threads)
+{
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    if (dev >= 0 && dev < kMaxDev) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0)
+            return v;
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+        return 0;
+    const int v = cus * per_cu;
+    if (v > 0 && dev >= 0 && dev < kMaxDev)
+        cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// One workgroup per resident slot (a multiple of 8, so that each XCD holds the
+// same number), each walking its share of the n_items work items.
+template <bool CAUSAL, int D, int QB, int NWV, int WPE>
+hipError_t launch_q64_t(const FwdArgs &a, int n_qtiles, int n_items, hipStream_t stream)
+{
+    const auto kernel = fwd_q64_kernel<CAUSAL, NWV, D, QB, WPE>;
+    const int resident = resident_workgroups(kernel, 64 * NWV);
+    if (resident < 8)
+        return hipErrorInvalidConfiguration;
+    const long long want = ((long long)n_items + 7) / 8 * 8;
+    const int grid = (int)std::min<long long>(want, resident / 8 * 8);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * NWV), 0, stream, a, n_qtiles, n_items);
+    return hipGetLastError();
+}
+
 template <int D, int QB, int NWV, int WPE>
 hipError_t launch_q64(const FwdArgs &a, bool causal, hipStream_t stream)
 {
     constexpr int BM = NWV * 32 * QB;
     const int n_qtiles = (a.Sq + BM - 1) / BM;
-    const long long n_tiles = (long long)a.B * a.Hq * n_qtiles;
-    if (n_tiles > 0x7fffffffLL)
+    const long long n_items = (long long)a.B * a.Hq * n_qtiles;
+    // item ids, and 8 GX per round past the last one, stay within int
+    if (n_items > 0x7fff0000LL)
         return hipErrorInvalidConfiguration;
+    if (n_items == 0)
+        return hipSuccess;
     if (causal)
-        hipLaunchKernelGGL((fwd_q64_kernel<true, NWV, D, QB, WPE>), dim3((unsigned)n_tiles), dim3(64 * NWV),
-                           0, stream, a, n_qtiles);
-    else
-        hipLaunchKernelGGL((fwd_q64_kernel<false, NWV, D, QB, WPE>), dim3((unsigned)n_tiles), dim3(64 * NWV),
-                           0, stream, a, n_qtiles);
-    return hipGetLastError();
+        return launch_q64_t<true, D, QB, NWV, WPE>(a, n_qtiles, (int)n_items, stream);
+    return launch_q64_t<false, D, QB, NWV, WPE>(a, n_qtiles, (int)n_items, stream);
 }
 
 }  // namespace

@@ -59,6 +59,11 @@
 #include "launch.h"
 #include "tile_order.h"
 
+// Build switch: K/V ring depth (tiles, a power of two) at head dimension 128
+#ifndef MIATTN_Q64_D128_RING
+#define MIATTN_Q64_D128_RING 4
+#endif
+
 namespace miattn {
 namespace {
 
@@ -124,6 +129,10 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 }
 
 __device__ __forceinline__ void slot_end() { __builtin_amdgcn_sched_barrier(0); }
+
+// s_waitcnt immediate that waits for vmcnt <= n only (6-bit count: bits 3:0
+// and 15:14; expcnt and lgkmcnt fields at their maximum)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // Workgroup barrier that no memory access of the source crosses: the copies
 // into LDS are invisible to the compiler, so it must not move an LDS read
@@ -199,11 +208,17 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     constexpr int DPW = KKN / NWV;     // copy instructions per wave per tile, each of K and V
     constexpr int NG = QB * KKN / 4;   // groups of four MFMAs per stage
     constexpr int NPV = QB * DBN;      // PV MFMAs per 16-key chunk
-    static_assert((NG == 2 || NG == 4) && NWV * DPW == KKN && 3 * DPW < 16, "tile step shape");
+    // K and V rings of RING tiles: K tile j+RING and V tile j+RING-1 are copied
+    // in step j (eight tiles of 8 KB each at head dimension 128, four of 16 KB
+    // at 256, within the 160 KB of LDS)
+    constexpr int RING = D == 128 ? MIATTN_Q64_D128_RING : 4;
+    constexpr int INFLIGHT = DPW + 2 * DPW * (RING - 3);  // copies newer than K tile j+3 at step j's end
+    static_assert((RING & (RING - 1)) == 0 && RING >= 4, "ring of 2^n >= 4 tiles");
+    static_assert((NG == 2 || NG == 4) && NWV * DPW == KKN && INFLIGHT < 64, "tile step shape");
     constexpr int TILE_CH = BN * D / 8;  // 16-byte chunks per tile
 
-    __shared__ __attribute__((aligned(16))) uint4 sK_[4 * TILE_CH];  // K ring, 4 tiles
-    __shared__ __attribute__((aligned(16))) uint4 sV_[4 * TILE_CH];  // V ring
+    __shared__ __attribute__((aligned(16))) uint4 sK_[RING * TILE_CH];  // K ring
+    __shared__ __attribute__((aligned(16))) uint4 sV_[RING * TILE_CH];  // V ring
     uint4 *const sK = sK_;  // the lambdas below may not name __shared__ variables
     uint4 *const sV = sV_;
 
@@ -275,14 +290,14 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // keys past it read as zero, and a copy of no key moves no data.
     auto dma_k = [&](int s, const uint16_t *src, int keys) __attribute__((always_inline)) {
         const u32x4 d = make_desc(src, (uint32_t)max(keys, 0) * (D * 2));
-        const uint32_t m0 = m0k + (uint32_t)(s & 3) * TILE_B;
+        const uint32_t m0 = m0k + (uint32_t)(s & (RING - 1)) * TILE_B;
 #pragma unroll
         for (int h = 0; h < DPW; ++h)
             copy_to_lds(d, koff[h], m0 + 1024 * h);
     };
     auto dma_v = [&](int s, const uint16_t *src, int keys) __attribute__((always_inline)) {
         const u32x4 d = make_desc(src, (uint32_t)max(keys, 0) * (D * 2));
-        const uint32_t m0 = m0v + (uint32_t)(s & 3) * TILE_B;
+        const uint32_t m0 = m0v + (uint32_t)(s & (RING - 1)) * TILE_B;
 #pragma unroll
         for (int h = 0; h < DPW; ++h)
             copy_to_lds(d, voff[h], m0 + 1024 * h);
@@ -307,10 +322,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     };
     const uint32_t lds_k = lds_addr(sK), lds_v = lds_addr(sV);
     auto kread_addr = [&](int s) __attribute__((always_inline)) {
-        return lds_k + (uint32_t)(s & 3) * TILE_B + 16 * lane;
+        return lds_k + (uint32_t)(s & (RING - 1)) * TILE_B + 16 * lane;
     };
     auto vread_addr = [&](int s) __attribute__((always_inline)) {
-        return lds_v + (uint32_t)(s & 3) * TILE_B + 8 * lane;
+        return lds_v + (uint32_t)(s & (RING - 1)) * TILE_B + 8 * lane;
     };
 
     // ---- monoid state per query block -------------------------------------------
@@ -510,11 +525,11 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     };
 
     // ---- prologue of an item ------------------------------------------------------
-    // The first K tiles (0-3) and V tiles (0-2) are normally copied during the
-    // previous item's last steps; the first item, and one that follows an item
-    // of fewer than four tiles, copies what is missing here and drains. Then
-    // S_0, its statistics and the first chunk of P_0 without overlap, and K
-    // tile 1 into registers.
+    // The first K tiles (0 .. RING-1) and V tiles (0 .. RING-2) are normally
+    // copied during the previous item's last steps; the first item, and one
+    // that follows an item of fewer than RING tiles, copies what is missing
+    // here and drains. Then S_0, its statistics and the first chunk of P_0
+    // without overlap, and K tile 1 into registers.
     Sc sA, sB;  // scores of the even / odd tile in flight
     Pc pA, pB;  // probabilities of the even / odd tile
     // Head dimension 256 loads the next item's Q rows into registers during
@@ -555,26 +570,26 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 #pragma unroll
         for (int kk = 0; kk < KKN; ++kk)
             read_k(kread_addr(ph + 1), kk);
-        // every wave has read K tile 0 before step 0 copies K tile 4 into its slot
+        // every wave has read K tile 0 before step 0 copies K tile RING into its slot
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         barrier();
     };
 
-    // Copies of step j of an item: K of stream position j+4 and V of j+3, which
-    // are the item's own tiles, the next item's first tiles (K 0-3, V 0-2), or
-    // nothing.
+    // Copies of step j of an item: K of stream position j+RING and V of
+    // j+RING-1, which are the item's own tiles, the next item's first tiles (K
+    // 0 .. RING-1, V 0 .. RING-2), or nothing.
     auto step_copies = [&](int j) __attribute__((always_inline)) {
         dma_k(ph + j, kp, krem);
-        dma_v(ph + j + 3, vp, vrem);
+        dma_v(ph + j + RING - 1, vp, vrem);
         // after the item's last tile, the next item's first ones
-        if (j + 5 == nblk) {
+        if (j + RING + 1 == nblk) {
             kp = kn;
             krem = kv_end_n;
         } else {
             kp += BN * D;
             krem -= BN;
         }
-        if (j + 4 == nblk) {
+        if (j + RING == nblk) {
             vp = vn;
             vrem = kv_end_n;
         } else {
@@ -583,10 +598,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         }
     };
     // wait until the copies the next step reads (V tile j+1, K tile j+3) are
-    // complete -- the 3 DPW newer copy instructions of this wave may still
+    // complete -- the INFLIGHT newer copy instructions of this wave may still
     // fly -- and barrier
     auto step_end = [&]() __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * DPW));  // vmcnt(3 DPW)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(INFLIGHT));
         barrier();
     };
 
@@ -745,7 +760,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     };
 
     // ---- the items of this workgroup ----------------------------------------------
-    int kmiss = 4, vmiss = 3;  // first tiles of the current item not yet copied
+    int kmiss = RING, vmiss = RING - 1;  // first tiles of the current item not yet copied
     int id = item_id(0);
     Item nx = describe(id < n_items ? id : 0);
     if constexpr (QPREF)
@@ -773,21 +788,21 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         if (CAUSAL && wave_live)
             wave_end = min(Sk, max(0, min(q0 + 32 * QB - 1, Sq - 1) + diag + 1));
         nwb = (wave_end + BN - 1) / BN;  // tiles this wave computes
-        // the copy stream of step 0: K tile 4 and V tile 3, of this item or
+        // the copy stream of step 0: K tile RING and V tile RING-1, of this item or
         // (when it is shorter) of the next
-        if (nblk > 4) {
-            kp = a.k + (krow0 + 4 * BN) * D;
-            krem = kv_end - 4 * BN;
+        if (nblk > RING) {
+            kp = a.k + (krow0 + RING * BN) * D;
+            krem = kv_end - RING * BN;
         } else {
-            kp = kn + (4 - nblk) * BN * D;
-            krem = kv_end_n - (4 - nblk) * BN;
+            kp = kn + (RING - nblk) * BN * D;
+            krem = kv_end_n - (RING - nblk) * BN;
         }
-        if (nblk > 3) {
-            vp = a.v + (krow0 + 3 * BN) * D;
-            vrem = kv_end - 3 * BN;
+        if (nblk > RING - 1) {
+            vp = a.v + (krow0 + (RING - 1) * BN) * D;
+            vrem = kv_end - (RING - 1) * BN;
         } else {
-            vp = vn + (3 - nblk) * BN * D;
-            vrem = kv_end_n - (3 - nblk) * BN;
+            vp = vn + (RING - 1 - nblk) * BN * D;
+            vrem = kv_end_n - (RING - 1 - nblk) * BN;
         }
 
         reset_state();
@@ -828,9 +843,9 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
             load_q(qrow0_n, q_wg_n + wave * 32 * QB);
         epilogue();
 
-        kmiss = max(0, 4 - nblk);
-        vmiss = max(0, 3 - nblk);
-        ph = (ph + nblk) & 3;
+        kmiss = max(0, RING - nblk);
+        vmiss = max(0, RING - 1 - nblk);
+        ph = (ph + nblk) & (RING - 1);
         id = id_n;
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy may still target LDS

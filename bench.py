@@ -39,6 +39,8 @@ KERNEL_SOURCES = ("online_softmax_monoid_amd/csrc/prefill.hip",
                   "online_softmax_monoid_amd/csrc/prefill_q64.hip",
                   "online_softmax_monoid_amd/csrc/prefill_pingpong.hip",
                   "online_softmax_monoid_amd/csrc/tile_order.h",
+                  "online_softmax_monoid_amd/csrc/lds_copy.h",
+                  "online_softmax_monoid_amd/csrc/resident.h",
                   "online_softmax_monoid_amd/csrc/launch.h")
 
 

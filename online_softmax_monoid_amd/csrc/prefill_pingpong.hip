@@ -48,6 +48,7 @@
 #include <stdint.h>
 
 #include "launch.h"
+#include "lds_copy.h"
 #include "tile_order.h"
 
 namespace miattn {
@@ -113,41 +114,6 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 }
 
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor (raw, 32-bit offsets, range-checked against `bytes`)
-__device__ __forceinline__ u32x4 make_desc(const void *base, uint32_t bytes)
-{
-    const uint64_t a = (uint64_t)(uintptr_t)base;
-    u32x4 d;
-    d.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    d.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
-    d.z = __builtin_amdgcn_readfirstlane(bytes);
-    d.w = 0x00020000u;
-    return d;
-}
-
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16 *
-// lane (out-of-range bytes read as zero). Written as inline assembly so that
-// the compiler does not make later LDS reads wait for it: every wait on these
-// copies is explicit in the kernel.
-__device__ __forceinline__ void copy_to_lds(u32x4 desc, uint32_t voffset, uint32_t lds_base)
-{
-    // M0 holds the LDS address. The compiler's hazard check does not look
-    // inside the assembly: five wait states cover a descriptor word written by
-    // a VALU instruction (v_readfirstlane) and M0 (which needs one).
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voffset), "s"(desc), "{m0}"(lds_base)
-                 : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
-}
 
 #ifndef MIATTN_PP_PRIO
 #define MIATTN_PP_PRIO 1

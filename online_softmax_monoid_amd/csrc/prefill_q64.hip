@@ -54,9 +54,10 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <atomic>
 
 #include "launch.h"
+#include "lds_copy.h"
+#include "resident.h"
 #include "tile_order.h"
 
 // Build switch: K/V ring depth (tiles, a power of two) at head dimension 128
@@ -130,9 +131,6 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 
 __device__ __forceinline__ void slot_end() { __builtin_amdgcn_sched_barrier(0); }
 
-// s_waitcnt immediate that waits for vmcnt <= n only (6-bit count: bits 3:0
-// and 15:14; expcnt and lgkmcnt fields at their maximum)
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 // Workgroup barrier that no memory access of the source crosses: the copies
 // into LDS are invisible to the compiler, so it must not move an LDS read
@@ -149,44 +147,6 @@ __device__ __forceinline__ void barrier()
 // compiler would otherwise sink work towards its uses across slots).
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor (raw, 32-bit offsets, range-checked against `bytes`)
-__device__ __forceinline__ u32x4 make_desc(const void *base, uint32_t bytes)
-{
-    const uint64_t addr = (uint64_t)(uintptr_t)base;
-    u32x4 d;
-    d.x = __builtin_amdgcn_readfirstlane((uint32_t)addr);
-    d.y = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32) & 0xffffu);
-    d.z = __builtin_amdgcn_readfirstlane(bytes);
-    d.w = 0x00020000u;
-    return d;
-}
-
-// 16 bytes per lane from global memory (byte voffset, range-checked: bytes
-// out of range read as zero) straight into LDS at lds_base + 16 * lane.
-// Written as inline assembly so that the compiler neither drains these copies
-// before LDS reads it cannot prove disjoint nor counts them: every wait on
-// them is explicit in the kernel. M0 holds the LDS address. The compiler's
-// hazard check does not look inside the assembly, so it carries its own wait
-// states: five, the most any of its inputs needs (a descriptor word written
-// by a VALU instruction such as v_readfirstlane and read by a vector memory
-// instruction; M0 written and read by an LDS copy needs one). No instruction
-// offset: it would move the LDS address as well.
-__device__ __forceinline__ void copy_to_lds(u32x4 desc, uint32_t voffset, uint32_t lds_base)
-{
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voffset), "s"(desc), "{m0}"(lds_base)
-                 : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
-}
 
 // One work item: the BM query rows of one (batch, query head) and the keys
 // they see (same tile order as prefill.hip)
@@ -866,31 +826,6 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 #ifndef MIATTN_Q64_D128_WPE  // waves per SIMD the d = 128 kernel is compiled for
 #define MIATTN_Q64_D128_WPE (2 * MIATTN_Q64_D128_WAVES / 8)
 #endif
-
-// Workgroups resident on the current device at once for a kernel: compute
-// units times the kernel's occupancy, cached per device and kernel.
-template <typename K>
-int resident_workgroups(K kernel, int threads)
-{
-    constexpr int kMaxDev = 64;
-    static std::atomic<int> cache[kMaxDev];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return 0;
-    if (dev >= 0 && dev < kMaxDev) {
-        const int v = cache[dev].load(std::memory_order_relaxed);
-        if (v > 0)
-            return v;
-    }
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
-        return 0;
-    const int v = cus * per_cu;
-    if (v > 0 && dev >= 0 && dev < kMaxDev)
-        cache[dev].store(v, std::memory_order_relaxed);
-    return v;
-}
 
 // One workgroup per resident slot (a multiple of 8, so that each XCD holds the
 // same number), each walking its share of the n_items work items.

@@ -114,6 +114,52 @@ def test_ragged_and_edge_shapes(case):
     _check_full(q, k, v, causal, inputs.default_scale(d), f"ragged {case}")
 
 
+# Several work items per persistent workgroup (more items than the device
+# holds workgroups), where the copy stream runs from one item into the next:
+# items shorter than the four-tile ring (some first tiles copied in the
+# previous item, the rest in the item's own prologue), items that see no key
+# at all (Sq > Sk causal: the first query tile), GQA groups, and a number of
+# (batch, kv-head) units that is not a multiple of the 8 XCDs (the other tile
+# order). The last two are checked on sampled rows. Values are drawn with
+# standard deviation 0.5, as in the Llama-class workload: a row that sees only
+# one or two keys has |O| up to the largest |v|, and where that passes 4 the
+# bf16 rounding of O alone (half an ulp, 2^-6) exceeds the 1e-2 bound.
+PERSIST = [
+    # B, Hq, Hkv, Sq, Sk, d, causal, rows sampled per head (0: all)
+    (8, 64, 8, 256, 64, 128, False, 0),     # 512 items of 2 tiles
+    (8, 64, 8, 256, 100, 128, True, 0),     # 4 tiles, leading rows empty
+    (4, 64, 4, 512, 40, 128, True, 0),      # items of 0 and 2 tiles, alternating
+    (8, 32, 4, 256, 64, 256, False, 0),     # head dimension 256: 512 items of 2 tiles
+    (8, 32, 8, 256, 40, 256, True, 0),      # 256: items of 0 and 2 tiles
+    (2, 48, 16, 1536, 1536, 128, True, 96),  # GQA 3, items of 8 .. 48 tiles
+    (3, 30, 3, 2048, 2048, 128, True, 64),  # 9 units: not a multiple of 8
+]
+
+
+@pytest.mark.parametrize("case", PERSIST)
+def test_persistent_item_walk(case):
+    B, Hq, Hkv, Sq, Sk, d, causal, per_head = case
+    seed = 3000 + PERSIST.index(case)
+    q = _rand_bits(seed, (B, Hq, Sq, d), 0.5)
+    k = _rand_bits(seed + 1, (B, Hkv, Sk, d), 0.5)
+    v = _rand_bits(seed + 2, (B, Hkv, Sk, d), 0.5)
+    scale = inputs.default_scale(d)
+    if per_head == 0:
+        _check_full(q, k, v, causal, scale, f"persistent {case}")
+        return
+    _note(f"[gpu] persistent {case}: running the HIP path")
+    o, lse, guards = H.run_fwd(q, k, v, causal, scale)
+    assert guards
+    rng = np.random.Generator(np.random.PCG64(seed + 3))
+    rows = np.sort(np.concatenate([h * Sq + rng.choice(Sq, per_head, replace=False)
+                                   for h in range(B * Hq)]))
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal, scale, rows=rows)
+    m = H.metrics(o.reshape(-1, d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref)
+    _note(f"[gpu] persistent {case}: {m}")
+    H.assert_parity(m, f"persistent {case}")
+    assert not np.any(o == H.NAN_BF16) and not np.any(np.isnan(lse))
+
+
 def test_gqa_is_bitwise_repeated_mha():
     q = _rand_bits(21, (1, 8, 150, 128))
     k = _rand_bits(22, (1, 2, 150, 128))

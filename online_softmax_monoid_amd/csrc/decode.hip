@@ -100,12 +100,15 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
     typedef __attribute__((address_space(3))) void lds_void;
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-    // per wave: one K and one V block (32 keys x D bf16 each); the V block is
-    // reused at the end for the wave's accumulator (16 columns x D f32 -- the
-    // same 64 D bytes)
+    // per wave: one K and one V block (32 keys x D bf16 each); at the end the
+    // V block holds the wave's accumulator (16 columns x D f32 -- the same
+    // 64 D bytes) and the K block its 16 references and row sums. Nothing
+    // else, so that a workgroup takes exactly 32 D bytes per wave of LDS and
+    // five two-wave workgroups fit on a CU at head dimension 128.
     __shared__ __attribute__((aligned(16))) uint4 sKall[NW][BK * D / 8];
     __shared__ __attribute__((aligned(16))) uint4 sVall[NW][BK * D / 8];
-    __shared__ float s_mc[NW][16], s_l[NW][16];
+    auto s_mc = [&](int w_) __attribute__((always_inline)) { return (float *)&sKall[w_][0]; };
+    auto s_l = [&](int w_) __attribute__((always_inline)) { return (float *)&sKall[w_][0] + 16; };
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -301,8 +304,8 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
     }
     float *const s_acc = (float *)sV;  // [16][D]
     if (r4 == 0) {
-        s_mc[wave][l16] = (m_ref == -INFINITY) ? -INFINITY : m_ref * c;
-        s_l[wave][l16] = l_lane;
+        s_mc(wave)[l16] = (m_ref == -INFINITY) ? -INFINITY : m_ref * c;
+        s_l(wave)[l16] = l_lane;
     }
 #pragma unroll
     for (int i = 0; i < DB; ++i)
@@ -318,15 +321,15 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w)
-            M = fmaxf(M, s_mc[w][col]);
+            M = fmaxf(M, s_mc(w)[col]);
         float L = 0.f;
         float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
         if (M != -INFINITY) {
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                const float mw = s_mc[w][col];
+                const float mw = s_mc(w)[col];
                 const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-                L = __builtin_fmaf(f, s_l[w][col], L);
+                L = __builtin_fmaf(f, s_l(w)[col], L);
                 const float4 v = *(const float4 *)((const float *)sVall[w] + col * D + d4);
                 A.x = __builtin_fmaf(f, v.x, A.x);
                 A.y = __builtin_fmaf(f, v.y, A.y);

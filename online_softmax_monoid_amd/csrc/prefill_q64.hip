@@ -203,8 +203,24 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         const int li = r * GX + ((r & 1) ? GX - 1 - wslot : wslot);
         return xcd + 8 * li;
     };
+    // Fewer (batch, kv-head) units than XCDs, dividing them (e.g. two): each
+    // unit gets 8 / units XCDs, each XCD an equal share of the unit's query
+    // heads, heaviest query tile first. The workgroups of an XCD then read one
+    // unit's K and V, in step, instead of every unit's.
+    const int n_units = a.B * a.Hkv;
+    const int xpu = n_units < 8 && 8 % n_units == 0 ? 8 / n_units : 0;  // XCDs per unit
+    const bool by_xcd = xpu > 0 && G % xpu == 0;
     auto describe = [&](int id) __attribute__((always_inline)) {
-        const TileOrder to = tile_order(id, a.B * a.Hkv, G, n_qtiles, CAUSAL);
+        TileOrder to;
+        if (by_xcd) {
+            const int gsub = G / xpu, x = id & 7, pos = id >> 3;
+            const int rank = pos / gsub;
+            to.unit = x / xpu;
+            to.gq = (x % xpu) * gsub + (pos - rank * gsub);
+            to.qtile = CAUSAL ? n_qtiles - 1 - rank : rank;
+        } else {
+            to = tile_order(id, n_units, G, n_qtiles, CAUSAL);
+        }
         const int b = to.unit / a.Hkv;
         const int kvh = to.unit - b * a.Hkv;
         const int hq = kvh * G + to.gq;

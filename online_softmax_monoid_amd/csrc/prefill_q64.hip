@@ -30,8 +30,8 @@
 //            tile j+1; LDS reads of K_{j+2}
 //
 // K and V tiles of 32 keys go global -> LDS by range-checked buffer DMA (keys
-// past the item's last visible key arrive as zeros) into four-deep rings, one
-// barrier per tile. Both are stored fragment-major: each LDS read instruction
+// past the item's last visible key arrive as zeros) into rings of RING tiles
+// (four by default), one barrier per tile. Both are stored fragment-major: each LDS read instruction
 // of a wave reads one contiguous 1 KB (K, ds_read_b128) or 512 B (V,
 // ds_read_b64_tr_b16) block, which is free of bank conflicts.
 //
@@ -582,10 +582,11 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     };
 
     // ---- one tile step ------------------------------------------------------------------
-    // Tile t of the copy stream lives in ring slot t % 4; the current item's
-    // tile j is stream position ph + j. Step j: copies of stream positions
-    // j+4 (K, into tile j's slot, last read in step j-2) and j+3 (V, into tile
-    // j-1's slot, last read in step j-1); stage A; stage B; wait; barrier.
+    // Tile t of the copy stream lives in ring slot t % RING; the current
+    // item's tile j is stream position ph + j. Step j: copies of stream
+    // positions j+RING (K, into tile j's slot, last read in step j-2) and
+    // j+RING-1 (V, into tile j-1's slot, last read in step j-1); stage A;
+    // stage B; wait; barrier.
     auto step = [&](auto MASKc, int j, Sc &sc, Sc &sn, Pc &pc, Pc &pn) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(MASKc)::value;
         uint32_t kread = kread_addr(ph + j + 2);  // K tile j+2
@@ -706,32 +707,39 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     };
 
     // ---- epilogue of an item ------------------------------------------------------
+    // O = acc / l in bf16 and LSE. Lanes l and l+32 hold the same row, dims
+    // 4(l/32) .. +3 of every 8: they swap half of their packed values so that
+    // each stores 16 contiguous bytes (half the store instructions).
     auto epilogue = [&]() __attribute__((always_inline)) {
         apply_alpha();
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int my_q = q0 + 32 * qb + l32;
             const float l_tot = halves_sum(l_half[qb]);
-            if (my_q < Sq) {
-                const bool empty = !(l_tot > 0.f);
-                const float inv = empty ? 0.f : 1.f / l_tot;
-                uint16_t *orow = a.o + (qrow0 + my_q) * D + 4 * g;
+            const bool empty = !(l_tot > 0.f);
+            const float inv = empty ? 0.f : __builtin_amdgcn_rcpf(l_tot);
+            uint16_t *orow = a.o + (qrow0 + min(my_q, Sq - 1)) * D + 8 * g;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                    for (int rho = 0; rho < 4; ++rho) {
-                        uint2 w;
-                        if (empty) {
-                            w = make_uint2(0, 0);
-                        } else {
-                            w.x = pack_bf16x2(acc[qb][db][4 * rho] * inv, acc[qb][db][4 * rho + 1] * inv);
-                            w.y = pack_bf16x2(acc[qb][db][4 * rho + 2] * inv, acc[qb][db][4 * rho + 3] * inv);
-                        }
-                        *(uint2 *)(orow + 32 * db + 8 * rho) = w;
-                    }
-                if (g == 0)
-                    a.lse[qrow0 + my_q] = empty ? -INFINITY : m_ref[qb] * a.scale + logf(l_tot);
-            }
+                for (int pr = 0; pr < 2; ++pr) {
+                    const f32x16 &x = acc[qb][db];
+                    const int r0 = 8 * pr, r1 = 8 * pr + 4;  // rho 2pr and 2pr+1
+                    const uint32_t a0 = empty ? 0u : pack_bf16x2(x[r0] * inv, x[r0 + 1] * inv);
+                    const uint32_t a1 = empty ? 0u : pack_bf16x2(x[r0 + 2] * inv, x[r0 + 3] * inv);
+                    const uint32_t b0 = empty ? 0u : pack_bf16x2(x[r1] * inv, x[r1 + 1] * inv);
+                    const uint32_t b1 = empty ? 0u : pack_bf16x2(x[r1 + 2] * inv, x[r1 + 3] * inv);
+                    // lane g = 0 keeps rho 2pr and receives the partner's; g = 1 keeps 2pr+1
+                    const uint32_t s0 = g == 0 ? b0 : a0, s1 = g == 0 ? b1 : a1;
+                    const auto t0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
+                    const auto t1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
+                    const uint32_t p0 = g == 0 ? t0[1] : t0[0], p1 = g == 0 ? t1[1] : t1[0];
+                    const uint4 w = g == 0 ? make_uint4(a0, a1, p0, p1) : make_uint4(p0, p1, b0, b1);
+                    if (my_q < Sq)
+                        *(uint4 *)(orow + 32 * db + 16 * pr) = w;
+                }
+            if (g == 0 && my_q < Sq)
+                a.lse[qrow0 + my_q] = empty ? -INFINITY : m_ref[qb] * a.scale + logf(l_tot);
         }
     };
 

@@ -302,14 +302,18 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
         auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_lane), __float_as_uint(l_lane), false, false);
         l_lane = __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
     }
-    float *const s_acc = (float *)sV;  // [16][D]
+    // [16][D], the 16-byte chunk c of column col at chunk c ^ col: the 16
+    // lanes of a write (one column each, same chunk) then reach 16 different
+    // bank groups instead of one
+    float *const s_acc = (float *)sV;
     if (r4 == 0) {
         s_mc(wave)[l16] = (m_ref == -INFINITY) ? -INFINITY : m_ref * c;
         s_l(wave)[l16] = l_lane;
     }
 #pragma unroll
     for (int i = 0; i < DB; ++i)
-        *(float4 *)(s_acc + l16 * D + 16 * i + 4 * r4) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+        *(float4 *)(s_acc + l16 * D + 4 * ((4 * i + r4) ^ l16)) =
+            make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
     __syncthreads();
 
     // fold the waves' states (rescale to the largest reference, add) and
@@ -330,7 +334,7 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
                 const float mw = s_mc(w)[col];
                 const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
                 L = __builtin_fmaf(f, s_l(w)[col], L);
-                const float4 v = *(const float4 *)((const float *)sVall[w] + col * D + d4);
+                const float4 v = *(const float4 *)((const float *)sVall[w] + col * D + 4 * ((d4 / 4) ^ col));
                 A.x = __builtin_fmaf(f, v.x, A.x);
                 A.y = __builtin_fmaf(f, v.y, A.y);
                 A.z = __builtin_fmaf(f, v.z, A.z);

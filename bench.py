@@ -132,6 +132,49 @@ class Decode:
                                stream)
 
 
+class DecodePaged:
+    """The decode workload with its cache in pages of ``page`` keys, pool
+    pages in a seeded random order; two pool copies used alternately, as for
+    Decode. The page size is fixed at construction: the pools are sized for
+    it."""
+
+    PAGE = 16  # page size the bench reports
+
+    def __init__(self, w, torch, page=PAGE):
+        import numpy as np
+        from online_softmax_monoid_amd import inputs, miattn
+        self.w = w
+        lens, q, kc, vc = inputs.decode_inputs(w)
+        P = self.page = int(page)
+        table, self.num_pages = inputs.paged_layout(w.seed + 7, lens, P, w.S_cap // P,
+                                                    spare_pages=64)
+        kp = dev_bits(inputs.scatter_to_pages(kc, table, self.num_pages, P))
+        vp = dev_bits(inputs.scatter_to_pages(vc, table, self.num_pages, P))
+        del kc, vc
+        self.pools = [(kp, vp), (kp.clone(), vp.clone())]
+        self.max_pages = table.shape[1]
+        assert kp.numel() == self.num_pages * w.Hkv * P * w.d
+        self.table = torch.from_numpy(table).to("cuda")
+        self.q = dev_bits(q)
+        self.lens = torch.from_numpy(lens.astype(np.int32)).to("cuda")
+        self.o = torch.empty(w.B * w.Hq * w.d, dtype=torch.int16, device="cuda")
+        self.lse = torch.empty(w.B * w.Hq, dtype=torch.float32, device="cuda")
+        self.ws_bytes = miattn.attn_fwd_decode_workspace_size(w.B, w.Hq, w.d, w.num_splits)
+        self.ws = torch.empty(self.ws_bytes // 4, dtype=torch.float32, device="cuda")
+        self.i = 0
+        self.bytes = (2 * int(lens.sum()) * w.Hkv * w.d * 2 + 2 * w.B * w.Hq * w.d * 2
+                      + 4 * w.B * w.Hq)
+
+    def __call__(self, stream):
+        from online_softmax_monoid_amd import miattn
+        w = self.w
+        kp, vp = self.pools[self.i & 1]
+        self.i += 1
+        miattn.attn_fwd_decode_paged(self.q, kp, vp, self.table, self.lens, self.o, self.lse,
+                                     w.B, w.Hq, w.Hkv, self.num_pages, self.page, self.max_pages,
+                                     w.d, w.num_splits, w.scale, self.ws, self.ws_bytes, stream)
+
+
 def time_launches(fn, stream, torch, n):
     """Per-launch durations (ms) from HIP events recorded on the launch stream."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -271,6 +314,16 @@ def main():
     del lng
     torch.cuda.empty_cache()
 
+    log("bench: paged decode (16-key pages)")
+    dp = DecodePaged(inputs.WORKLOADS[DECODE_WID], torch)
+    time_launches(dp, stream, torch, args.warmup)
+    pms = time_launches(dp, stream, torch, args.steps)
+    p_avg = sum(pms) / len(pms)
+    p_gbs = dp.bytes / (p_avg * 1e-3) / 1e9
+    log(f"bench: paged decode {p_avg:.4f} ms ({p_gbs:.0f} GB/s)")
+    del dp
+    torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (f64 oracle on a row sample)")
@@ -316,6 +369,9 @@ def main():
         "long_context_gqa_d256": {"value": round(l_tflops, 2), "unit": "TFLOP/s",
                                   "ms": round(l_avg, 3),
                                   "frac": round(l_tflops / PEAK_BF16_TFLOPS, 4)},
+        "decode_paged": {"value": round(p_gbs, 1), "unit": "GB/s", "ms": round(p_avg, 4),
+                         "frac": round(p_gbs / PEAK_HBM_GBS, 4), "bound": "hbm",
+                         "page_size": DecodePaged.PAGE},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -138,6 +138,44 @@ MIATTN_API int attn_fwd_decode(const void *q, const void *k_cache, const void *v
                     void *workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
+/*
+ * Decode forward over a paged KV cache: attn_fwd_decode with each stream's
+ * cache rows read through a block table. A paged cache is the paper's gather
+ * view (§2.1 "Views": one source coordinate of a read comes from an index
+ * tensor; the paged KV cache of vLLM is its example), so the operation is
+ * attn_fwd_decode on the gathered cache
+ *
+ *   K[b, g, r, :] = k_pages[block_table[b, r / page_size], g, r % page_size, :]
+ *
+ * (V likewise) for r < kv_lens[b]. The keys, splits and results are those of
+ * attn_fwd_decode on that cache, bit for bit.
+ *
+ *   k_pages, v_pages  bf16  [num_pages, Hkv, page_size, d]  page pool
+ *   block_table       int32 [B, max_pages_per_seq]  DEVICE; entry p of stream
+ *                     b is the pool page holding its keys
+ *                     [p * page_size, (p + 1) * page_size). Only the entries
+ *                     that cover keys < kv_lens[b] are used; entries outside
+ *                     [0, num_pages) are clamped into it on the device, so a
+ *                     bad entry gives wrong values but never a read outside
+ *                     the pool.
+ *   kv_lens           int32 [B] DEVICE, clamped on the device to
+ *                     [0, max_pages_per_seq * page_size]
+ *   q, o, lse, num_splits, scale, workspace: as for attn_fwd_decode (the
+ *                     workspace size is attn_fwd_decode_workspace_size's)
+ *
+ * Sizes: B >= 0 (0: nothing to do); num_pages >= 1 unless
+ * max_pages_per_seq == 0 (then every stream is empty and the pools and table
+ * are unused); page_size a power of two in [16, 2^20];
+ * max_pages_per_seq * page_size < 2^31; Hq, Hkv, d as for attn_fwd_decode.
+ * Two calls sharing one workspace must be ordered.
+ */
+MIATTN_API int attn_fwd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                          const int *block_table, const int *kv_lens, void *o,
+                          float *lse, int B, int Hq, int Hkv, int num_pages,
+                          int page_size, int max_pages_per_seq, int d,
+                          int num_splits, float scale, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* Message for the last non-OK status returned on the calling thread. */
 MIATTN_API const char *miattn_last_error(void);
 

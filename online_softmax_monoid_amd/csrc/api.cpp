@@ -161,8 +161,75 @@ int attn_fwd_decode(const void *q, const void *k_cache, const void *v_cache, con
     return hip_status(miattn::launch_decode(a, d, stream), "attn_fwd_decode launch");
 }
 
+int attn_fwd_decode_paged(const void *q, const void *k_pages, const void *v_pages,
+                          const int *block_table, const int *kv_lens, void *o, float *lse,
+                          int B, int Hq, int Hkv, int num_pages, int page_size,
+                          int max_pages_per_seq, int d, int num_splits, float scale,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (B < 0 || num_pages < 0 || max_pages_per_seq < 0)
+        return fail(MIATTN_ERR_INVALID_ARG,
+                    "sizes must be >= 0 (B=%d, num_pages=%d, max_pages_per_seq=%d)", B, num_pages,
+                    max_pages_per_seq);
+    if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "page_size must be a power of two in [16, 2^20] (got %d)",
+                    page_size);
+    if ((int64_t)max_pages_per_seq * page_size >= ((int64_t)1 << 31))
+        return fail(MIATTN_ERR_INVALID_ARG,
+                    "max_pages_per_seq * page_size must stay below 2^31 (%d * %d)",
+                    max_pages_per_seq, page_size);
+    MIATTN_TRY(check_heads_dim(Hq, Hkv, d));
+    MIATTN_TRY(check_scale(scale));
+    if (num_splits < 1)
+        return fail(MIATTN_ERR_INVALID_ARG, "num_splits must be >= 1 (got %d)", num_splits);
+    if (B == 0)
+        return MIATTN_OK;
+    if (max_pages_per_seq > 0 && num_pages == 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "num_pages must be >= 1 when max_pages_per_seq > 0");
+    MIATTN_TRY(check_ptr(q, "q", 16));
+    MIATTN_TRY(check_ptr(o, "o", 16));
+    MIATTN_TRY(check_ptr(lse, "lse", 4));
+    MIATTN_TRY(check_ptr(kv_lens, "kv_lens", 4));
+    if (max_pages_per_seq > 0) {
+        MIATTN_TRY(check_ptr(k_pages, "k_pages", 16));
+        MIATTN_TRY(check_ptr(v_pages, "v_pages", 16));
+        MIATTN_TRY(check_ptr(block_table, "block_table", 4));
+    }
+    MIATTN_TRY(check_ptr(workspace, "workspace", 16));
+    const size_t need = attn_fwd_decode_workspace_size(B, Hq, d, num_splits);
+    if (workspace_bytes < need)
+        return fail(MIATTN_ERR_INVALID_ARG, "workspace too small: %zu bytes, need %zu",
+                    workspace_bytes, need);
+    int shift = 0;
+    while ((1 << shift) < page_size)
+        ++shift;
+    miattn::DecodeArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k_pages);
+    a.v = static_cast<const uint16_t *>(v_pages);
+    a.lens = kv_lens;
+    a.o = static_cast<uint16_t *>(o);
+    a.lse = lse;
+    a.part_acc = static_cast<float *>(workspace);
+    a.part_ml = a.part_acc + (size_t)B * Hq * num_splits * d;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.S_cap = max_pages_per_seq * page_size;
+    a.splits = num_splits;
+    a.scale = scale;
+    if (max_pages_per_seq > 0) {
+        a.table = block_table;
+        a.max_pages = max_pages_per_seq;
+        a.num_pages = num_pages;
+        a.page_shift = shift;
+    }
+    // without pages every stream is empty: the contiguous path with S_cap = 0
+    return hip_status(miattn::launch_decode(a, d, stream), "attn_fwd_decode_paged launch");
+}
+
 const char *miattn_last_error(void) { return g_last_error.c_str(); }
 
-int miattn_version(void) { return 100; }
+int miattn_version(void) { return 200; }
 
 }  // extern "C"

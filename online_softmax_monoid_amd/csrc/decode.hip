@@ -15,6 +15,13 @@
 // Splitting is valid because the combine is associative (§2.5 "Schedules":
 // split on any associative monoid).
 //
+// Paged caches (the paper's gather view: a paged KV cache is an ordinary read
+// whose source row comes from an index tensor, §2.1 "Views"): key row r of
+// stream b and kv-head g is row r % P of page table[b][r / P] of a pool
+// [num_pages, Hkv, P, d]. Only the address of each copied row changes; the
+// kernels are otherwise the same, so a paged cache gives bit for bit the
+// result of the contiguous cache holding the same rows.
+//
 // Partial maxima are kept in log2 units (scores times scale*log2(e)), so every
 // exponential is one v_exp_f32.
 
@@ -87,7 +94,7 @@ __device__ __forceinline__ int stream_by_rank(const DecodeArgs &a, int rank, int
 // reference maximum moves lazily (only past a margin of 8 in log2 units), as
 // in the prefill kernels. At the end the NW waves' states are folded through
 // LDS with the monoid combine and written as the split's partial state.
-template <int D, int NW>
+template <int D, int NW, bool PAGED>
 __global__ void __launch_bounds__(64 * NW)
 decode_mfma_kernel(DecodeArgs a, int hchunks)
 {
@@ -179,6 +186,50 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(buf + 64 * i), 16, off, 0, 0, 0);
         }
     };
+    // Paged: the element offset in the pool of each lane's 16 bytes of block
+    // kb (the same for K and V). Its 32 rows lie in at most three pages (page
+    // size >= 16), whose table entries are read once per block (clamped to the
+    // table row and to the pool, so that no entry can send a copy outside
+    // it). Rows past the split repeat its last row instead of reading zeros:
+    // their scores are masked and their probabilities are exactly 0.
+    auto paged_offsets = [&](int kb, int64_t (&off)[NI]) __attribute__((always_inline)) {
+        const int sh = a.page_shift;
+        const int lp0 = kb >> sh;
+        const int *trow = a.table + (int64_t)b * a.max_pages;
+        int pg[3];
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const int e = trow[min(lp0 + t, a.max_pages - 1)];
+            pg[t] = min(max(e, 0), a.num_pages - 1);
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int rb = RPI * i + lane / CPR;  // row in the block
+            const int r = min(kb + rb, k_hi - 1);
+            const int t = (r >> sh) - lp0;
+            const int p = t == 0 ? pg[0] : (t == 1 ? pg[1] : pg[2]);
+            off[i] = ((((int64_t)p * a.Hkv + kvh) << sh) + (r & ((1 << sh) - 1))) * D +
+                     8 * ((lane % CPR) ^ swz(rb));
+        }
+    };
+    auto dma_paged = [&](uint4 *buf, const uint16_t *pool, const int64_t (&off)[NI])
+                         __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            __builtin_amdgcn_global_load_lds((const void *)(pool + off[i]), (lds_void *)(buf + 64 * i),
+                                             16, 0, 0);
+    };
+    auto copy_block = [&](int kb) __attribute__((always_inline)) {
+        if constexpr (PAGED) {
+            int64_t off[NI];
+            paged_offsets(kb, off);
+            dma_paged(sK, a.k, off);
+            dma_paged(sV, a.v, off);
+        } else {
+            dma(sK, kbase, kb);
+            dma(sV, vbase, kb);
+        }
+    };
     // K A fragments: lane l holds dims 32kk + 8(l/16) .. +7 of key 16 half + l%16
     uint4 kf[2][KK];
     auto read_k = [&]() __attribute__((always_inline)) {
@@ -218,10 +269,8 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
     for (int i = 0; i < DB; ++i)
         acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (wave < nb) {
-        dma(sK, kbase, k_lo + BK * wave);
-        dma(sV, vbase, k_lo + BK * wave);
-    }
+    if (wave < nb)
+        copy_block(k_lo + BK * wave);
     for (int n = wave; n < nb; n += NW) {
         const int kb = k_lo + BK * n;
         // this block's copies have landed (nothing newer is in flight); take
@@ -231,8 +280,7 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
         read_v();
         if (n + NW < nb) {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block is in registers
-            dma(sK, kbase, kb + BK * NW);
-            dma(sV, vbase, kb + BK * NW);
+            copy_block(kb + BK * NW);
         }
         // S^T for the two 16-key halves: lane l holds keys 16 half + 4(l/16) + i
         // for the query head in column l%16
@@ -453,7 +501,7 @@ decode_combine_kernel(DecodeArgs a)
         a.lse[bh] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
 {
     const int G = a.Hq / a.Hkv;
@@ -467,7 +515,7 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
 #define MIATTN_DECODE_NW 2  // waves per split: LDS (16 KB per wave) allows 10 waves per CU
 #endif
         constexpr int NW = MIATTN_DECODE_NW;
-        hipLaunchKernelGGL((decode_mfma_kernel<D, NW>), dim3((unsigned)grid), dim3(64 * NW), 0,
+        hipLaunchKernelGGL((decode_mfma_kernel<D, NW, PAGED>), dim3((unsigned)grid), dim3(64 * NW), 0,
                            stream, a, hchunks);
         e = hipGetLastError();
     }
@@ -484,13 +532,14 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
 
 hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t stream)
 {
+    const bool paged = a.table != nullptr;
     switch (d) {
     case 64:
-        return launch_d<64>(a, stream);
+        return paged ? launch_d<64, true>(a, stream) : launch_d<64, false>(a, stream);
     case 128:
-        return launch_d<128>(a, stream);
+        return paged ? launch_d<128, true>(a, stream) : launch_d<128, false>(a, stream);
     case 256:
-        return launch_d<256>(a, stream);
+        return paged ? launch_d<256, true>(a, stream) : launch_d<256, false>(a, stream);
     default:
         return hipErrorInvalidValue;
     }

@@ -29,6 +29,11 @@ struct DecodeArgs {
     float *part_ml;   // [B, Hq, splits, 2]  (m in log2 units, l)
     int B, Hq, Hkv, S_cap, splits;
     float scale;
+    // paged caches only (table == nullptr: contiguous [B, Hkv, S_cap, d]):
+    // k, v are pools [num_pages, Hkv, page_size, d], table is [B, max_pages],
+    // page_size = 1 << page_shift, S_cap = max_pages * page_size
+    const int *table = nullptr;
+    int max_pages = 0, num_pages = 0, page_shift = 0;
 };
 
 // Each returns hipSuccess or the launch error.

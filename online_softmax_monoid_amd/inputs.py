@@ -208,3 +208,45 @@ def draw_decode_bits(seed: int, B: int, Hq: int, Hkv: int, d: int, len_lo: int,
 def decode_inputs(w: Decode, pad_bits: int = 0):
     return draw_decode_bits(w.seed, w.B, w.Hq, w.Hkv, w.d, w.len_lo, w.len_hi,
                             w.S_cap, w.std, pad_bits=pad_bits)
+
+
+def paged_layout(seed: int, lens: np.ndarray, page_size: int, max_pages: int,
+                 spare_pages: int = 0):
+    """A random page assignment for a paged cache: block table [B, max_pages]
+    int32 and the pool size.
+
+    Stream b's logical pages 0 .. ceil(lens[b] / page_size) - 1 get distinct
+    pool pages in a seeded random order; ``spare_pages`` more pool pages
+    belong to no stream. Table entries past a stream's last page hold -1
+    (never used). No attention arithmetic happens here: this only decides
+    where rows are stored.
+    """
+    lens = np.asarray(lens, dtype=np.int64)
+    used = (lens + page_size - 1) // page_size
+    assert (used <= max_pages).all()
+    num_pages = int(used.sum()) + int(spare_pages)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = np.full((len(lens), max_pages), -1, dtype=np.int32)
+    pos = 0
+    for b, n in enumerate(used):
+        table[b, :n] = perm[pos:pos + n]
+        pos += int(n)
+    return table, num_pages
+
+
+def scatter_to_pages(cache_bits: np.ndarray, table: np.ndarray, num_pages: int,
+                     page_size: int, fill_bits: int = 0) -> np.ndarray:
+    """Store a contiguous cache [B, Hkv, S_cap, d] in a page pool
+    [num_pages, Hkv, page_size, d] by the block table (entries < 0 skipped);
+    pool rows no table entry reaches hold ``fill_bits``."""
+    B, Hkv, S_cap, d = cache_bits.shape
+    pool = np.full((num_pages, Hkv, page_size, d), fill_bits, dtype=np.uint16)
+    for b in range(B):
+        for p, page in enumerate(table[b]):
+            if page < 0:
+                continue
+            lo = p * page_size
+            n = max(0, min(page_size, S_cap - lo))
+            pool[page, :, :n, :] = cache_bits[b, :, lo:lo + n, :]
+    return pool

@@ -22,7 +22,7 @@ MIATTN_ERR_UNSUPPORTED = 2
 MIATTN_ERR_HIP = 3
 
 EXPORTS = ("attn_fwd", "attn_fwd_decode_workspace_size", "attn_fwd_decode",
-           "miattn_last_error", "miattn_version")
+           "attn_fwd_decode_paged", "miattn_last_error", "miattn_version")
 
 
 class MiattnError(RuntimeError):
@@ -52,6 +52,9 @@ def load(path: str = LIB_PATH):
     L.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp,
                                   ctypes.c_size_t, vp]
     L.attn_fwd_decode.restype = i
+    L.attn_fwd_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f,
+                                        vp, ctypes.c_size_t, vp]
+    L.attn_fwd_decode_paged.restype = i
     L.miattn_last_error.argtypes = []
     L.miattn_last_error.restype = ctypes.c_char_p
     L.miattn_version.argtypes = []
@@ -98,6 +101,17 @@ def attn_fwd_decode(q, k_cache, v_cache, kv_lens, o, lse, B, Hq, Hkv, S_cap, d, 
                                   _addr(o), _addr(lse), int(B), int(Hq), int(Hkv), int(S_cap),
                                   int(d), int(num_splits), float(scale), _addr(workspace),
                                   int(workspace_bytes), _stream(stream)))
+
+
+def attn_fwd_decode_paged(q, k_pages, v_pages, block_table, kv_lens, o, lse, B, Hq, Hkv,
+                          num_pages, page_size, max_pages_per_seq, d, num_splits, scale,
+                          workspace, workspace_bytes, stream=None):
+    _check(load().attn_fwd_decode_paged(_addr(q), _addr(k_pages), _addr(v_pages),
+                                        _addr(block_table), _addr(kv_lens), _addr(o), _addr(lse),
+                                        int(B), int(Hq), int(Hkv), int(num_pages), int(page_size),
+                                        int(max_pages_per_seq), int(d), int(num_splits),
+                                        float(scale), _addr(workspace), int(workspace_bytes),
+                                        _stream(stream)))
 
 
 def miattn_last_error() -> str:

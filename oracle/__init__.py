@@ -139,6 +139,38 @@ def attn_decode(q_bits, kc_bits, vc_bits, lens, scale: float, nthreads: int = 0)
     return o[:B * Hq].reshape(B, Hq, d), lse[:B * Hq].reshape(B, Hq)
 
 
+def gather_pages(pool_bits, block_table, lens, page_size: int):
+    """The gather view of a paged cache (tang paper, §2.1 "Views": a read whose
+    source coordinate comes from an index tensor; paged KV caches are its
+    example). pool [num_pages, Hkv, P, d], block_table [B, max_pages] ->
+    the contiguous cache [B, Hkv, max_pages * P, d] with
+
+        K[b, g, r, :] = pool[block_table[b, r // P], g, r % P, :]
+
+    for r < lens[b] and zero bits elsewhere. Entries outside [0, num_pages)
+    are clamped into it, as the C interface defines for bad entries."""
+    pool = _u16(pool_bits)
+    table = np.asarray(block_table, dtype=np.int64)
+    num_pages, Hkv, P, d = pool.shape
+    assert P == page_size
+    B, max_pages = table.shape
+    out = np.zeros((B, Hkv, max_pages * P, d), dtype=np.uint16)
+    for b in range(B):
+        for r in range(int(lens[b])):
+            page = min(max(int(table[b, r // P]), 0), num_pages - 1)
+            out[b, :, r, :] = pool[page, :, r % P, :]
+    return out
+
+
+def attn_decode_paged(q_bits, k_pool_bits, v_pool_bits, block_table, lens, page_size: int,
+                      scale: float, nthreads: int = 0):
+    """Decode attention over a paged cache: the two-pass f64 decode of the
+    gathered cache."""
+    kc = gather_pages(k_pool_bits, block_table, lens, page_size)
+    vc = gather_pages(v_pool_bits, block_table, lens, page_size)
+    return attn_decode(q_bits, kc, vc, lens, scale, nthreads)
+
+
 def attn_probs(q_bits, k_bits, causal: bool, scale: float, row: int):
     """Probability row p[Sk] of flat query row ``row`` (masked keys are 0)."""
     q = _u16(q_bits)

@@ -77,6 +77,28 @@ def run_decode(q, kc, vc, lens, scale, splits, ws_fill=float("nan")):
     return ob[:n * d].reshape(B, Hq, d), lh[:n].reshape(B, Hq), guards
 
 
+def run_decode_paged(q, k_pool, v_pool, table, lens, page_size, scale, splits,
+                     ws_fill=float("nan")):
+    torch = torch_mod()
+    B, Hq, d = q.shape
+    num_pages, Hkv, P, _ = k_pool.shape
+    assert P == page_size and v_pool.shape == k_pool.shape
+    qd, kd, vd = dev_bits(q), dev_bits(k_pool), dev_bits(v_pool)
+    td = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).to("cuda")
+    ld = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).to("cuda")
+    n = B * Hq
+    o, lse = nan_out(n * d, n)
+    nbytes = miattn.attn_fwd_decode_workspace_size(B, Hq, d, splits)
+    ws = torch.full((max(nbytes // 4, 4),), ws_fill, dtype=torch.float32, device="cuda")
+    miattn.attn_fwd_decode_paged(qd, kd, vd, td, ld, o, lse, B, Hq, Hkv, num_pages, page_size,
+                                 table.shape[1], d, splits, scale, ws, nbytes)
+    torch.cuda.synchronize()
+    ob = host_bits(o)
+    lh = lse.cpu().numpy()
+    guards = bool(np.all(ob[n * d:] == NAN_BF16) and np.all(np.isnan(lh[n:])))
+    return ob[:n * d].reshape(B, Hq, d), lh[:n].reshape(B, Hq), guards
+
+
 def metrics(o_bits, lse, o_ref, lse_ref):
     """Error metrics of GPU outputs against f64 references (same shapes)."""
     og = inputs.bf16_to_f32(o_bits).astype(np.float64)

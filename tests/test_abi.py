@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_workspace_size():
-    assert M.miattn_version() == 100
+    assert M.miattn_version() == 200
     assert M.attn_fwd_decode_workspace_size(32, 32, 128, 16) == 32 * 32 * 16 * 130 * 4
     assert M.attn_fwd_decode_workspace_size(0, 32, 128, 16) == 0
     assert M.attn_fwd_decode_workspace_size(1, 0, 128, 16) == 0
@@ -119,6 +119,51 @@ def test_attn_fwd_decode_rejects(kw, status, needle):
 
 def test_decode_empty_batch_is_a_no_op():
     assert _dec(B=0, q=0, k=0, v=0, lens=0, o=0, lse=0, ws=0, wsb=0) == M.MIATTN_OK
+
+
+def _paged(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, lens=FAKE, o=FAKE, lse=FAKE, B=2, Hq=4,
+                Hkv=2, num_pages=8, page_size=16, max_pages=4, d=128, ns=4, scale=0.1, ws=FAKE,
+                wsb=None, stream=0)
+    args.update(kw)
+    if args["wsb"] is None:
+        args["wsb"] = M.attn_fwd_decode_workspace_size(args["B"], args["Hq"], args["d"],
+                                                       max(args["ns"], 1))
+    return M.load().attn_fwd_decode_paged(
+        args["q"], args["k"], args["v"], args["table"], args["lens"], args["o"], args["lse"],
+        args["B"], args["Hq"], args["Hkv"], args["num_pages"], args["page_size"],
+        args["max_pages"], args["d"], args["ns"], args["scale"], args["ws"], args["wsb"],
+        args["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=0), M.MIATTN_ERR_INVALID_ARG, "q is NULL"),
+    (dict(table=0), M.MIATTN_ERR_INVALID_ARG, "block_table is NULL"),
+    (dict(table=FAKE + 2), M.MIATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(k=0), M.MIATTN_ERR_INVALID_ARG, "k_pages is NULL"),
+    (dict(v=FAKE + 8), M.MIATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(lens=0), M.MIATTN_ERR_INVALID_ARG, "kv_lens is NULL"),
+    (dict(ws=0), M.MIATTN_ERR_INVALID_ARG, "workspace is NULL"),
+    (dict(wsb=100), M.MIATTN_ERR_INVALID_ARG, "workspace too small"),
+    (dict(page_size=8), M.MIATTN_ERR_INVALID_ARG, "page_size"),
+    (dict(page_size=48), M.MIATTN_ERR_INVALID_ARG, "page_size"),
+    (dict(page_size=1 << 21), M.MIATTN_ERR_INVALID_ARG, "page_size"),
+    (dict(max_pages=1 << 20, page_size=1 << 11), M.MIATTN_ERR_INVALID_ARG, "2^31"),
+    (dict(num_pages=0), M.MIATTN_ERR_INVALID_ARG, "num_pages"),
+    (dict(num_pages=-1), M.MIATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(max_pages=-1), M.MIATTN_ERR_INVALID_ARG, "sizes"),
+    (dict(ns=0), M.MIATTN_ERR_INVALID_ARG, "num_splits"),
+    (dict(Hq=5), M.MIATTN_ERR_INVALID_ARG, "multiple"),
+    (dict(d=80), M.MIATTN_ERR_UNSUPPORTED, "head dimension"),
+    (dict(scale=float("inf")), M.MIATTN_ERR_INVALID_ARG, "scale"),
+])
+def test_attn_fwd_decode_paged_rejects(kw, status, needle):
+    assert _paged(**kw) == status
+    assert needle in M.miattn_last_error()
+
+
+def test_decode_paged_empty_batch_is_a_no_op():
+    assert _paged(B=0, q=0, k=0, v=0, table=0, lens=0, o=0, lse=0, ws=0, wsb=0) == M.MIATTN_OK
 
 
 def test_product_path_does_not_import_the_oracle():

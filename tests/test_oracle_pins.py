@@ -384,6 +384,58 @@ def test_decode_ignores_padding_bits():
     assert np.array_equal(o0, on) and np.array_equal(l0, ln)
 
 
+# ------------------------------------------------------------ paged decode --
+def test_paged_gather_inverts_the_page_scatter():
+    """The oracle's gather view undoes the input module's scatter for any page
+    permutation (a swapped r // P and r % P, or a wrong page stride, fails)."""
+    lens = np.array([0, 1, 16, 17, 40, 64], dtype=np.int32)
+    _, q, kc, vc = inputs.draw_decode_bits(2024, 6, 4, 2, 8, 0, 0, 64, lens=lens)
+    for P in (4, 16, 64):
+        table, npg = inputs.paged_layout(7 + P, lens, P, 64 // P, spare_pages=3)
+        pool = inputs.scatter_to_pages(kc, table, npg, P, fill_bits=int(inputs.BF16_NAN))
+        back = oracle.gather_pages(pool, table, lens, P)
+        for b, n in enumerate(lens):
+            assert np.array_equal(back[b, :, :n], kc[b, :, :n])
+            assert not back[b, :, n:].any()
+
+
+def test_paged_decode_brute_force_tiny():
+    """Decode over a page pool read key by key through the block table, with
+    textbook softmax in pure Python, against the oracle's gathered decode (the
+    scale is exact in f32, as the C oracle takes it)."""
+    rng = np.random.Generator(np.random.PCG64(99))
+    B, Hq, Hkv, d, P, max_pages, npg = 4, 4, 2, 4, 4, 3, 9
+    lens = [0, 3, 9, 4]
+    q = _rand_bits(rng, (B, Hq, d), 0.5)
+    kp = _rand_bits(rng, (npg, Hkv, P, d), 0.5)
+    vp = _rand_bits(rng, (npg, Hkv, P, d))
+    table = np.array([[-1, -1, -1], [5, -1, -1], [2, 8, 0], [7, -1, -1]], dtype=np.int32)
+    o, lse = oracle.attn_decode_paged(q, kp, vp, table, np.array(lens, np.int32), P, 0.375)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            rows = [(int(table[b][r // P]), r % P) for r in range(lens[b])]
+            kk = [[[[int(x) for x in kp[pg, g, i]] for pg, i in rows]]]
+            vv = [[[[int(x) for x in vp[pg, g, i]] for pg, i in rows]]]
+            qq = [[[[int(x) for x in q[b, h]]]]]
+            if not rows:
+                assert np.all(o[b, h] == 0) and np.isneginf(lse[b, h])
+                continue
+            ob, lb = brute.attention(qq, kk, vv, False, 0.375)
+            _close(o[b, h], ob[0][0][0], rtol=1e-12, atol=1e-14)
+            _close(lse[b, h], lb[0][0][0], rtol=1e-12)
+
+
+def test_paged_gather_clamps_bad_entries():
+    """Entries outside [0, num_pages) read the nearest pool page, as the C
+    interface defines."""
+    pool = np.arange(3 * 1 * 16 * 2, dtype=np.uint16).reshape(3, 1, 16, 2)
+    table = np.array([[-4, 7]], dtype=np.int32)
+    g = oracle.gather_pages(pool, table, np.array([32], np.int32), 16)
+    assert np.array_equal(g[0, 0, :16], pool[0, 0]) and np.array_equal(g[0, 0, 16:], pool[2, 0])
+
+
 # ------------------------------------------------------------- shared bits --
 def test_bf16_rounding_matches_torch():
     import torch

@@ -132,6 +132,40 @@ class Decode:
                                stream)
 
 
+class PrefillWindow:
+    """Causal prefill with a sliding window of W keys before each row's own
+    (attn_fwd_window), on seeded N(0, 1) draws."""
+
+    def __init__(self, torch, seed, B, Hq, Hkv, S, d, W):
+        from online_softmax_monoid_amd import inputs
+        self.shape = (B, Hq, Hkv, S, d, W)
+        q, k, v = inputs.draw_prefill_bits(seed, B, Hq, Hkv, S, S, d)
+        self.q, self.k, self.v = dev_bits(q), dev_bits(k), dev_bits(v)
+        n = B * Hq * S
+        self.o = torch.empty(n * d, dtype=torch.int16, device="cuda")
+        self.lse = torch.empty(n, dtype=torch.float32, device="cuda")
+        # visible (query, key) pairs per head: row i sees min(i, W) + 1 keys
+        pairs = W * (W + 1) // 2 + (S - W) * (W + 1) if S > W else S * (S + 1) // 2
+        self.flops = 4.0 * d * pairs * B * Hq
+        # Q, K, V read once, O and LSE written once
+        self.bytes = 2 * d * 2 * (B * Hq * S + B * Hkv * S) + 4 * B * Hq * S
+        self.scale = inputs.default_scale(d)
+
+    def __call__(self, stream):
+        from online_softmax_monoid_amd import miattn
+        B, Hq, Hkv, S, d, W = self.shape
+        miattn.attn_fwd_window(self.q, self.k, self.v, self.o, self.lse, B, Hq, Hkv, S, S, d,
+                               True, W, self.scale, stream)
+
+
+# Sliding-window workloads: the window row of the pages' variant table (window
+# 128, forward, n = 8k, d = 64; batch and heads not stated there, 4 x 16 here)
+# and a long window at d = 128 with GQA.
+WINDOW_LEGS = (("window_d64_w128", dict(seed=7100, B=4, Hq=16, Hkv=16, S=8192, d=64, W=128)),
+               ("window_d128_w4096", dict(seed=7200, B=1, Hq=32, Hkv=8, S=16384, d=128,
+                                          W=4096)))
+
+
 class DecodePaged:
     """The decode workload with its cache in pages of ``page`` keys, pool
     pages in a seeded random order; two pool copies used alternately, as for
@@ -314,6 +348,22 @@ def main():
     del lng
     torch.cuda.empty_cache()
 
+    windows = {}
+    for name, cfg in WINDOW_LEGS:
+        wl = PrefillWindow(torch, **cfg)
+        time_launches(wl, stream, torch, 3)
+        wms = time_launches(wl, stream, torch, 10)
+        w_avg = sum(wms) / len(wms)
+        w_tf = wl.flops / (w_avg * 1e-3) / 1e12
+        w_gbs = wl.bytes / (w_avg * 1e-3) / 1e9
+        log(f"bench: {name} {w_avg:.4f} ms ({w_tf:.1f} TFLOP/s, {w_gbs:.0f} GB/s)")
+        windows[name] = {"value": round(w_tf, 2), "unit": "TFLOP/s", "ms": round(w_avg, 4),
+                         "frac": round(w_tf / PEAK_BF16_TFLOPS, 4), "GB/s": round(w_gbs, 1),
+                         "hbm_frac": round(w_gbs / PEAK_HBM_GBS, 4),
+                         "shape": {k: v for k, v in cfg.items() if k != "seed"}}
+        del wl
+        torch.cuda.empty_cache()
+
     log("bench: paged decode (16-key pages)")
     dp = DecodePaged(inputs.WORKLOADS[DECODE_WID], torch)
     time_launches(dp, stream, torch, args.warmup)
@@ -369,6 +419,7 @@ def main():
         "long_context_gqa_d256": {"value": round(l_tflops, 2), "unit": "TFLOP/s",
                                   "ms": round(l_avg, 3),
                                   "frac": round(l_tflops / PEAK_BF16_TFLOPS, 4)},
+        **windows,
         "decode_paged": {"value": round(p_gbs, 1), "unit": "GB/s", "ms": round(p_avg, 4),
                          "frac": round(p_gbs / PEAK_HBM_GBS, 4), "bound": "hbm",
                          "page_size": DecodePaged.PAGE},

@@ -97,6 +97,24 @@ MIATTN_API int attn_fwd(const void *q, const void *k, const void *v, void *o, fl
              float scale, hipStream_t stream);
 
 /*
+ * Prefill forward with a sliding window: attn_fwd with the further mask
+ *
+ *   key j is visible to query i only if  j >= i + (Sk - Sq) - window_left
+ *
+ * (window_left >= 0; with causal != 0 a row then sees its own aligned key and
+ * the window_left keys before it). Every other argument, size limit and error
+ * is attn_fwd's. The window only changes the mask, so the reduction is the
+ * same online-softmax monoid (the tang paper, §2.3 "Rewrites": a change of
+ * the score or the mask leaves the monoid alone); key tiles that the window
+ * hides from every row of a query tile are skipped, not computed under the
+ * mask (the cost §7.3 of the paper measures when they are not). A row that
+ * sees no key gets O = +0 and LSE = -inf.
+ */
+MIATTN_API int attn_fwd_window(const void *q, const void *k, const void *v, void *o,
+                    float *lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                    int causal, int window_left, float scale, hipStream_t stream);
+
+/*
  * Bytes of workspace attn_fwd_decode needs: B * Hq * num_splits * (d + 2) * 4
  * (one f32 partial state (m, l, acc[d]) per stream, head and split).
  * Returns 0 for invalid arguments.

@@ -74,8 +74,9 @@ int hip_status(hipError_t e, const char *what)
 
 extern "C" {
 
-int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq,
-             int Hkv, int Sq, int Sk, int d, int causal, float scale, hipStream_t stream)
+static int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                    int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window, float scale,
+                    hipStream_t stream, const char *what)
 {
     if (B < 0 || Sq < 0 || Sk < 0)
         return fail(MIATTN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d, Sq=%d, Sk=%d)", B, Sq, Sk);
@@ -105,7 +106,25 @@ int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, i
     a.Sq = Sq;
     a.Sk = Sk;
     a.scale = scale;
-    return hip_status(miattn::launch_fwd(a, d, causal != 0, stream), "attn_fwd launch");
+    a.window = window;
+    return hip_status(miattn::launch_fwd(a, d, causal != 0, stream), what);
+}
+
+int attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq,
+             int Hkv, int Sq, int Sk, int d, int causal, float scale, hipStream_t stream)
+{
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, -1, scale, stream,
+                    "attn_fwd launch");
+}
+
+int attn_fwd_window(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                    int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+                    float scale, hipStream_t stream)
+{
+    if (window_left < 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "window_left must be >= 0 (got %d)", window_left);
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, window_left, scale, stream,
+                    "attn_fwd_window launch");
 }
 
 size_t attn_fwd_decode_workspace_size(int B, int Hq, int d, int num_splits)
@@ -230,6 +249,6 @@ int attn_fwd_decode_paged(const void *q, const void *k_pages, const void *v_page
 
 const char *miattn_last_error(void) { return g_last_error.c_str(); }
 
-int miattn_version(void) { return 200; }
+int miattn_version(void) { return 300; }
 
 }  // extern "C"

@@ -16,6 +16,9 @@ struct FwdArgs {
     float *lse;
     int B, Hq, Hkv, Sq, Sk;
     float scale;
+    // sliding window: key j is visible to query i only if
+    // j >= i + (Sk - Sq) - window; window < 0: no lower bound
+    int window = -1;
 };
 
 struct DecodeArgs {

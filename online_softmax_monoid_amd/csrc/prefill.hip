@@ -139,10 +139,6 @@ fwd_kernel(FwdArgs a, int n_qtiles)
     const int Sq = a.Sq, Sk = a.Sk;
     const int diag = Sk - Sq;  // key j is visible to query i iff j <= i + diag
     const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
-    const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
-    const uint16_t *__restrict__ Kp = a.k + krow0 * D;
-    const uint16_t *__restrict__ Vp = a.v + krow0 * D;
-
     const int q_wg = qtile * C::BM;
     const int q_wg_last = min(q_wg + C::BM, Sq) - 1;
     const int q0 = q_wg + wave * 32;
@@ -156,7 +152,15 @@ fwd_kernel(FwdArgs a, int n_qtiles)
         if (wave_live)
             wave_end = min(Sk, max(0, min(q0 + 31, Sq - 1) + diag + 1));
     }
-    const int nblk = (kv_end + BN - 1) / BN;
+    // Sliding window: the workgroup's keys start at the tile holding its first
+    // row's first visible key; tiles below it are hidden from every row and
+    // are never loaded. Tile indices below count from there (key kofs).
+    const bool windowed = a.window >= 0;
+    const int kofs = windowed ? min(kv_end, max(0, q_wg + diag - a.window)) / BN * BN : 0;
+    const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk + kofs;
+    const uint16_t *__restrict__ Kp = a.k + krow0 * D;
+    const uint16_t *__restrict__ Vp = a.v + krow0 * D;
+    const int nblk = (kv_end - kofs + BN - 1) / BN;
 
     // ---- Q fragment: B operand of S^T = K Q^T (a1) ------------------------
     bf16x8 qf[D / 16];
@@ -180,8 +184,8 @@ fwd_kernel(FwdArgs a, int n_qtiles)
     uint4 vreg[C::VPT][4];
 
     // keys at or beyond Sk read as 0 (buffer range check)
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kp, (uint32_t)Sk * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vp, (uint32_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kp, (uint32_t)(Sk - kofs) * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vp, (uint32_t)(Sk - kofs) * D * 2);
     auto load_k = [&](int blk) {
         const uint32_t base = (uint32_t)blk * BN * D * 2;
 #pragma unroll
@@ -277,16 +281,18 @@ fwd_kernel(FwdArgs a, int n_qtiles)
 
     // mask (a3), monoid update (a4) and value contraction (a5) of tile blk
     auto softmax_pv = [&](int blk, f32x16 (&s)[BN / 32]) {
-        const int j0 = blk * BN;
-        const bool full = (j0 + BN <= Sk) && (!CAUSAL || j0 + BN - 1 <= q0 + diag);
+        const int j0 = kofs + blk * BN;  // first key of the tile
+        const bool full = (j0 + BN <= Sk) && (!CAUSAL || j0 + BN - 1 <= q0 + diag) &&
+                          (!windowed || j0 >= q0 + 31 + diag - a.window);
         if (!full) {
             const int lim = CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1;
+            const int low = windowed ? my_q + diag - a.window : 0;  // first visible key
 #pragma unroll
             for (int bb = 0; bb < BN / 32; ++bb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = j0 + 32 * bb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    s[bb][r] = (key <= lim) ? s[bb][r] : -INFINITY;
+                    s[bb][r] = (key <= lim && key >= low) ? s[bb][r] : -INFINITY;
                 }
         }
         float mx = -INFINITY;
@@ -298,7 +304,11 @@ fwd_kernel(FwdArgs a, int n_qtiles)
         mx = halves_max(mx);
         if (__any(mx > m_ref + thr)) {  // rare after the first tile
             const float m_new = fmaxf(m_ref, mx);
-            const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * c);  // 0 if m_ref = -inf
+            // 0 when the row sees its first key; 1 when its maximum does not
+            // move, also for a row that has seen no key yet (-inf - -inf is
+            // NaN) while another row of the wave moves
+            const float alpha =
+                (m_new == m_ref) ? 1.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
             l_half *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
@@ -341,7 +351,7 @@ fwd_kernel(FwdArgs a, int n_qtiles)
 
     // Blocks this wave computes (the workgroup iterates over nblk for the
     // barriers; fully masked tiles of a wave are skipped).
-    const int nwb = (wave_end + BN - 1) / BN;
+    const int nwb = (max(0, wave_end - kofs) + BN - 1) / BN;
 
     // ---- prologue: K tiles 0 and 1, V tile 0; scores of tile 0 -------------
     // Staged on every path (an empty key range reads zeros), then all global
@@ -459,6 +469,8 @@ hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
         return causal ? launch<128, MIATTN_FWD_D128, true>(a, stream)
                       : launch<128, MIATTN_FWD_D128, false>(a, stream);
 #elif defined(MIATTN_D128_PINGPONG)
+        if (a.window >= 0)  // the ping-pong kernel has no window
+            return launch_fwd_q64(a, 128, causal, stream);
         return launch_fwd_pingpong(a, causal, stream);
 #else
         return launch_fwd_q64(a, 128, causal, stream);

@@ -151,11 +151,12 @@ __device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
 // One work item: the BM query rows of one (batch, query head) and the keys
 // they see (same tile order as prefill.hip)
 struct Item {
-    int64_t qrow0, krow0;  // first row of the query head / kv-head
+    int64_t qrow0, krow0;  // first row of the query head / the item's first key row
     int q_wg, kv_end, nblk;
+    int kofs;  // key of the item's tile 0 (nonzero only with a sliding window)
 };
 
-template <bool CAUSAL, int NWV, int D, int QB, int WPE>
+template <bool CAUSAL, int NWV, int D, int QB, int WPE, bool WIN>
 __global__ void __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 {
@@ -190,6 +191,9 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 
     const int Sq = a.Sq, Sk = a.Sk;
     const int diag = Sk - Sq;
+    // WIN: sliding window (a separate instantiation, so that the kernel
+    // without one carries none of its work); query i sees keys from i + wlo on
+    const int wlo = WIN ? diag - a.window : 0;
     const int G = a.Hq / a.Hkv;
 
     // ---- schedule --------------------------------------------------------------------
@@ -226,10 +230,16 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         const int hq = kvh * G + to.gq;
         Item it;
         it.qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
-        it.krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
         it.q_wg = to.qtile * BM;
         const int q_wg_last = min(it.q_wg + BM, Sq) - 1;
-        it.kv_end = CAUSAL ? min(Sk, max(0, q_wg_last + diag + 1)) : Sk;
+        const int kv_end = CAUSAL ? min(Sk, max(0, q_wg_last + diag + 1)) : Sk;
+        // With a sliding window the item's keys start at the tile holding its
+        // first row's first visible key; tiles below it are hidden from every
+        // row and never copied. Tile indices and key counts of the item count
+        // from that tile's first key.
+        it.kofs = WIN ? min(kv_end, max(0, it.q_wg + diag - a.window)) / BN * BN : 0;
+        it.krow0 = ((int64_t)b * a.Hkv + kvh) * Sk + it.kofs;
+        it.kv_end = kv_end - it.kofs;
         it.nblk = (it.kv_end + BN - 1) / BN;
         return it;
     };
@@ -336,7 +346,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 
     // ---- the current and the next item (the lambdas below read these) ---------------
     int ph = 0;                      // ring slot of the current item's tile 0
-    int nblk = 0, nwb = 0, q0 = 0, kv_end = 0;
+    int nblk = 0, nwb = 0, q0 = 0, kv_end = 0, kofs = 0;
     int64_t qrow0 = 0, krow0 = 0;
     bool has_next = false;
     int kv_end_n = 0, q_wg_n = 0;  // kv_end_n = 0 without a next item
@@ -412,18 +422,29 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         pin(p[qb][h].w[2 * quad]);
         pin(p[qb][h].w[2 * quad + 1]);
     };
+    // The keys of tile j that row q0 + 32 qb + l32 sees: score r (key
+    // 8(r/4) + 4g + r%4 of the tile) is visible iff rlo <= 8(r/4) + r%4 <= rel.
+    // Past the wave's last tile it sees none.
+    auto visible_offsets = [&](int qb, int j, int &rel, int &rlo) __attribute__((always_inline)) {
+        const int my_q = q0 + 32 * qb + l32;
+        const int lim = j < nwb ? (CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1) - kofs : -1;
+        const int base = j * BN + 4 * g;
+        rel = lim - base;
+        rlo = WIN ? my_q + wlo - kofs - base : -BN;
+    };
     // row maximum in three parts (scores 0-7, scores 8-15, both halves of the
     // wave); a masked tile first selects hidden keys to -inf
     float mxa[QB], mxb[QB];
     auto row_max = [&](Sc &s, int qb, int part, int j, bool masked) __attribute__((always_inline)) {
         if (part < 2) {
             if (masked) {
-                const int my_q = q0 + 32 * qb + l32;
-                const int lim = j < nwb ? (CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1) : -1;
-                const int rel = lim - j * BN - 4 * g;  // key r visible iff offset(r) <= rel
+                int rel, rlo;
+                visible_offsets(qb, j, rel, rlo);
 #pragma unroll
-                for (int r = 8 * part; r < 8 * part + 8; ++r)
-                    s[qb][r] = (8 * (r >> 2) + (r & 3) <= rel) ? s[qb][r] : -INFINITY;
+                for (int r = 8 * part; r < 8 * part + 8; ++r) {
+                    const int o = 8 * (r >> 2) + (r & 3);
+                    s[qb][r] = (o <= rel && (!WIN || o >= rlo)) ? s[qb][r] : -INFINITY;
+                }
             }
             const int r0 = 8 * part;
             float m = fmax_ieee(fmax_ieee(s[qb][r0], s[qb][r0 + 1]), s[qb][r0 + 2]);
@@ -467,12 +488,13 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 
     // hide the keys of tile j a row of query block qb cannot see (select to -inf)
     auto mask_tile = [&](Sc &s, int qb, int j) __attribute__((always_inline)) {
-        const int my_q = q0 + 32 * qb + l32;
-        const int lim = j < nwb ? (CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1) : -1;
-        const int rel = lim - j * BN - 4 * g;  // key r visible iff offset(r) <= rel
+        int rel, rlo;
+        visible_offsets(qb, j, rel, rlo);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            s[qb][r] = (8 * (r >> 2) + (r & 3) <= rel) ? s[qb][r] : -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+            const int o = 8 * (r >> 2) + (r & 3);
+            s[qb][r] = (o <= rel && (!WIN || o >= rlo)) ? s[qb][r] : -INFINITY;
+        }
     };
     // One query block per wave: the lazy reference is checked by the tile's
     // row sums instead of its row maximum. A lane's 16 probabilities are all
@@ -766,12 +788,13 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         krow0 = cur.krow0;
         kv_end = cur.kv_end;
         nblk = cur.nblk;
+        kofs = WIN ? cur.kofs : 0;
         q0 = cur.q_wg + wave * 32 * QB;  // first row of this wave
         const bool wave_live = q0 < Sq;
         int wave_end = wave_live ? Sk : 0;
         if (CAUSAL && wave_live)
             wave_end = min(Sk, max(0, min(q0 + 32 * QB - 1, Sq - 1) + diag + 1));
-        nwb = (wave_end + BN - 1) / BN;  // tiles this wave computes
+        nwb = (max(0, wave_end - kofs) + BN - 1) / BN;  // tiles this wave computes
         // the copy stream of step 0: K tile RING and V tile RING-1, of this item or
         // (when it is shorter) of the next
         if (nblk > RING) {
@@ -794,16 +817,28 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 
         // Leading steps of this wave that need no mask (an even number): tile
         // j+1 fully visible to every row of the wave and within its range.
-        int n_fast;
+        int n_fast, n_lead = 0;
         {
-            int first_masked = Sk / BN;  // ragged key tail
+            int first_masked = (Sk - kofs) / BN;  // ragged key tail
             if (CAUSAL)
-                first_masked = min(first_masked, max(0, (q0 + diag + 1) / BN));
+                first_masked = min(first_masked, max(0, q0 + diag + 1 - kofs) / BN);
             n_fast = min(nwb, first_masked) - 1;
             n_fast = max(0, n_fast) & ~1;
             n_fast = __builtin_amdgcn_readfirstlane(n_fast);
+            if constexpr (WIN) {
+                // leading steps whose tile j+1 starts below the window of the
+                // wave's last row (an even number, at most n_fast)
+                const int qmax = min(q0 + 32 * QB - 1, Sq - 1);
+                const int first_full = (max(0, qmax + wlo - kofs) + BN - 1) / BN;
+                n_lead = min(n_fast, (max(0, first_full - 1) + 1) & ~1);
+                n_lead = __builtin_amdgcn_readfirstlane(n_lead);
+            }
         }
         int j = 0;
+        for (; j < n_lead; j += 2) {  // sliding window: masked leading steps
+            mstep(j, sA, sB, pA, pB);
+            mstep(j + 1, sB, sA, pB, pA);
+        }
         if constexpr (D == 256) {  // four steps per iteration (measured faster at 256, not at 128)
             for (; j + 3 < n_fast; j += 4) {
                 step(IntC<0>{}, j, sA, sB, pA, pB);
@@ -853,10 +888,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 
 // One workgroup per resident slot (a multiple of 8, so that each XCD holds the
 // same number), each walking its share of the n_items work items.
-template <bool CAUSAL, int D, int QB, int NWV, int WPE>
+template <bool CAUSAL, int D, int QB, int NWV, int WPE, bool WIN>
 hipError_t launch_q64_t(const FwdArgs &a, int n_qtiles, int n_items, hipStream_t stream)
 {
-    const auto kernel = fwd_q64_kernel<CAUSAL, NWV, D, QB, WPE>;
+    const auto kernel = fwd_q64_kernel<CAUSAL, NWV, D, QB, WPE, WIN>;
     const int resident = resident_workgroups(kernel, 64 * NWV);
     if (resident < 8)
         return hipErrorInvalidConfiguration;
@@ -877,9 +912,12 @@ hipError_t launch_q64(const FwdArgs &a, bool causal, hipStream_t stream)
         return hipErrorInvalidConfiguration;
     if (n_items == 0)
         return hipSuccess;
-    if (causal)
-        return launch_q64_t<true, D, QB, NWV, WPE>(a, n_qtiles, (int)n_items, stream);
-    return launch_q64_t<false, D, QB, NWV, WPE>(a, n_qtiles, (int)n_items, stream);
+    const int n = (int)n_items;
+    if (a.window >= 0)
+        return causal ? launch_q64_t<true, D, QB, NWV, WPE, true>(a, n_qtiles, n, stream)
+                      : launch_q64_t<false, D, QB, NWV, WPE, true>(a, n_qtiles, n, stream);
+    return causal ? launch_q64_t<true, D, QB, NWV, WPE, false>(a, n_qtiles, n, stream)
+                  : launch_q64_t<false, D, QB, NWV, WPE, false>(a, n_qtiles, n, stream);
 }
 
 }  // namespace

@@ -21,7 +21,7 @@ MIATTN_ERR_INVALID_ARG = 1
 MIATTN_ERR_UNSUPPORTED = 2
 MIATTN_ERR_HIP = 3
 
-EXPORTS = ("attn_fwd", "attn_fwd_decode_workspace_size", "attn_fwd_decode",
+EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_fwd_decode_workspace_size", "attn_fwd_decode",
            "attn_fwd_decode_paged", "miattn_last_error", "miattn_version")
 
 
@@ -47,6 +47,8 @@ def load(path: str = LIB_PATH):
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     L.attn_fwd.restype = i
+    L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_window.restype = i
     L.attn_fwd_decode_workspace_size.argtypes = [i, i, i, i]
     L.attn_fwd_decode_workspace_size.restype = ctypes.c_size_t
     L.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp,
@@ -89,6 +91,14 @@ def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, scale, stream=None)
     _check(load().attn_fwd(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), int(B),
                            int(Hq), int(Hkv), int(Sq), int(Sk), int(d), int(bool(causal)),
                            float(scale), _stream(stream)))
+
+
+def attn_fwd_window(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, window_left, scale,
+                    stream=None):
+    _check(load().attn_fwd_window(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), int(B),
+                                  int(Hq), int(Hkv), int(Sq), int(Sk), int(d),
+                                  int(bool(causal)), int(window_left), float(scale),
+                                  _stream(stream)))
 
 
 def attn_fwd_decode_workspace_size(B, Hq, d, num_splits) -> int:

@@ -54,6 +54,10 @@ def lib():
                                       c_int, c_int, c_int, ctypes.c_float, i64p,
                                       ctypes.c_int64, f64p, f64p, c_int]
         L.oracle_attn_fwd.restype = c_int
+        L.oracle_attn_fwd_window.argtypes = [u16p, u16p, u16p, c_int, c_int, c_int, c_int,
+                                             c_int, c_int, c_int, c_int, ctypes.c_float, i64p,
+                                             ctypes.c_int64, f64p, f64p, c_int]
+        L.oracle_attn_fwd_window.restype = c_int
         L.oracle_attn_decode.argtypes = [u16p, u16p, u16p, i32p, c_int, c_int, c_int,
                                          c_int, c_int, ctypes.c_float, f64p, f64p,
                                          c_int]
@@ -82,13 +86,14 @@ def max_threads() -> int:
 
 
 def attn_fwd(q_bits, k_bits, v_bits, causal: bool, scale: float, rows=None,
-             nthreads: int = 0):
+             nthreads: int = 0, window: int = -1):
     """Two-pass f64 attention on bf16 bit arrays.
 
     q_bits: [B,Hq,Sq,d], k_bits / v_bits: [B,Hkv,Sk,d] (uint16).
-    rows: optional flat row ids ((b*Hq + h)*Sq + i). Returns (o, lse) as f64:
-    o has shape [B,Hq,Sq,d] and lse [B,Hq,Sq] when rows is None, else
-    [len(rows), d] and [len(rows)].
+    rows: optional flat row ids ((b*Hq + h)*Sq + i). window >= 0 hides keys
+    j < i + Sk - Sq - window from row i (sliding window); < 0: none.
+    Returns (o, lse) as f64: o has shape [B,Hq,Sq,d] and lse [B,Hq,Sq] when
+    rows is None, else [len(rows), d] and [len(rows)].
     """
     q = _u16(q_bits)
     k = _u16(k_bits)
@@ -105,11 +110,11 @@ def attn_fwd(q_bits, k_bits, v_bits, causal: bool, scale: float, rows=None,
         rows_p = _ptr(rows, ctypes.c_int64)
     o = np.empty((max(n, 1), d), dtype=np.float64)
     lse = np.empty(max(n, 1), dtype=np.float64)
-    rc = lib().oracle_attn_fwd(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
-                               _ptr(v, ctypes.c_uint16), B, Hq, Hkv, Sq, Sk, d,
-                               int(bool(causal)), float(scale), rows_p, n,
-                               _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
-                               int(nthreads))
+    rc = lib().oracle_attn_fwd_window(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                      _ptr(v, ctypes.c_uint16), B, Hq, Hkv, Sq, Sk, d,
+                                      int(bool(causal)), int(window), float(scale), rows_p, n,
+                                      _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
+                                      int(nthreads))
     if rc != 0:
         raise ValueError("oracle_attn_fwd rejected its arguments")
     o, lse = o[:n], lse[:n]

@@ -14,7 +14,8 @@
  *   for every batch b, query head h and query row i
  *     g    = h / (Hq / Hkv)                      grouped-query head map (§2.1
  *                                                "Views": heads as two dims)
- *     J_i  = { j in [0, Sk) : !causal || j <= i + Sk - Sq }
+ *     J_i  = { j in [0, Sk) : (!causal || j <= i + Sk - Sq)
+ *                              && (window < 0 || j >= i + Sk - Sq - window) }
  *     s_j  = scale * sum_t Q[b,h,i,t] * K[b,g,j,t]          (pass 1)
  *     m    = max_{j in J_i} s_j
  *     l    = sum_{j in J_i} exp(s_j - m)                     (pass 2)
@@ -34,6 +35,10 @@
  * Inputs are the bf16 bit patterns the GPU reads; each is widened exactly
  * (bits << 16 gives the float32 pattern, then float -> double). The scale is
  * the float32 value handed to the GPU, widened to double.
+ *
+ * The window term is the sliding-window variant (no window: window < 0). A
+ * change of the mask leaves the monoid alone (§2.3 "Rewrites"), so the
+ * definition is the same two passes over a smaller key set.
  *
  * Decode (one query row per stream and head, keys [0, len_b) of a cache of
  * capacity S_cap) is the same definition with J = [0, len_b).
@@ -104,7 +109,7 @@ static void attend_row(const uint16_t *qrow, const uint16_t *k,
     *lse = m + log(l);
 }
 
-/* Number of keys visible to query row i: the prefix J_i = [0, n). */
+/* End of the keys visible to query row i: J_i ends at n (exclusive). */
 static int64_t visible_keys(int64_t i, int64_t Sq, int64_t Sk, int causal)
 {
     if (!causal)
@@ -122,16 +127,26 @@ static int bad_shape(int B, int Hq, int Hkv, int d)
     return B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0;
 }
 
+/* Start of the keys visible to query row i under a window (0 without). */
+static int64_t first_visible_key(int64_t i, int64_t Sq, int64_t Sk, int window)
+{
+    if (window < 0)
+        return 0;
+    int64_t lo = i + (Sk - Sq) - window;  /* keys j >= i + Sk - Sq - window */
+    return lo < 0 ? 0 : lo;
+}
+
 /*
  * Prefill oracle. q: [B,Hq,Sq,d], k and v: [B,Hkv,Sk,d] bf16 bits.
  * rows: flat row ids r = (b*Hq + h)*Sq + i to evaluate, or NULL for all
- * B*Hq*Sq rows in order. Writes o[nrows*d] and lse[nrows] (row order of
- * `rows`). Returns 0, or -1 on a bad argument.
+ * B*Hq*Sq rows in order. window: the sliding window (< 0: none). Writes
+ * o[nrows*d] and lse[nrows] (row order of `rows`). Returns 0, or -1 on a bad
+ * argument.
  */
-int oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                    int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
-                    float scale, const int64_t *rows, int64_t nrows,
-                    double *o, double *lse, int nthreads)
+int oracle_attn_fwd_window(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
+                           int window, float scale, const int64_t *rows, int64_t nrows,
+                           double *o, double *lse, int nthreads)
 {
     if (bad_shape(B, Hq, Hkv, d) || Sq < 0 || Sk < 0)
         return -1;
@@ -171,13 +186,25 @@ int oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                 const uint16_t *qrow = q + r * (int64_t)d;
                 const uint16_t *kh = k + (b * Hkv + g) * (int64_t)Sk * d;
                 const uint16_t *vh = v + (b * Hkv + g) * (int64_t)Sk * d;
-                attend_row(qrow, kh, vh, visible_keys(i, Sq, Sk, causal), d, sc,
+                const int64_t lo = first_visible_key(i, Sq, Sk, window);
+                const int64_t hi = visible_keys(i, Sq, Sk, causal);
+                attend_row(qrow, kh + lo * d, vh + lo * d, hi - lo, d, sc,
                            s, o + n * (int64_t)d, lse + n);
             }
             free(s);
         }
     }
     return err ? -1 : 0;
+}
+
+/* Prefill oracle without a window. */
+int oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
+                    float scale, const int64_t *rows, int64_t nrows,
+                    double *o, double *lse, int nthreads)
+{
+    return oracle_attn_fwd_window(q, k, v, B, Hq, Hkv, Sq, Sk, d, causal, -1, scale,
+                                  rows, nrows, o, lse, nthreads);
 }
 
 /*

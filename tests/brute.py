@@ -19,13 +19,15 @@ def bf16_value(bits: int) -> float:
     return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
 
 
-def _visible(i, j, Sq, Sk, causal):
+def _visible(i, j, Sq, Sk, causal, window=-1):
     # bottom-right aligned causal mask: key j is visible to query i iff
-    # j - i <= Sk - Sq
-    return (not causal) or (j - i <= Sk - Sq)
+    # j - i <= Sk - Sq; a sliding window further needs j - i >= Sk - Sq - window
+    if causal and j - i > Sk - Sq:
+        return False
+    return window < 0 or j - i >= Sk - Sq - window
 
 
-def attention(q, k, v, causal, scale):
+def attention(q, k, v, causal, scale, window=-1):
     """q: nested lists [B][Hq][Sq][d] of bf16 bits; k, v: [B][Hkv][Sk][d].
 
     Returns (o, lse) as nested lists of Python floats.
@@ -39,7 +41,7 @@ def attention(q, k, v, causal, scale):
         for h in range(Hq):
             kvh = h // group
             for i in range(Sq):
-                keys = [j for j in range(Sk) if _visible(i, j, Sq, Sk, causal)]
+                keys = [j for j in range(Sk) if _visible(i, j, Sq, Sk, causal, window)]
                 if not keys:
                     o[b][h][i] = [0.0] * d
                     lse[b][h][i] = -math.inf

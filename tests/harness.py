@@ -42,15 +42,20 @@ def host_bits(t) -> np.ndarray:
     return t.cpu().numpy().view(np.uint16)
 
 
-def run_fwd(q, k, v, causal, scale, stream=None):
-    """Run attn_fwd on bit arrays; returns (o_bits [B,Hq,Sq,d], lse f32, guards_ok)."""
+def run_fwd(q, k, v, causal, scale, stream=None, window=-1):
+    """Run attn_fwd (attn_fwd_window when window >= 0) on bit arrays; returns
+    (o_bits [B,Hq,Sq,d], lse f32, guards_ok)."""
     torch = torch_mod()
     B, Hq, Sq, d = q.shape
     _, Hkv, Sk, _ = k.shape
     qd, kd, vd = dev_bits(q), dev_bits(k), dev_bits(v)
     n = B * Hq * Sq
     o, lse = nan_out(n * d, n)
-    miattn.attn_fwd(qd, kd, vd, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, scale, stream)
+    if window >= 0:
+        miattn.attn_fwd_window(qd, kd, vd, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, window, scale,
+                               stream)
+    else:
+        miattn.attn_fwd(qd, kd, vd, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, scale, stream)
     torch.cuda.synchronize()
     ob = host_bits(o)
     lh = lse.cpu().numpy()

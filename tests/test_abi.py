@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_workspace_size():
-    assert M.miattn_version() == 200
+    assert M.miattn_version() == 300
     assert M.attn_fwd_decode_workspace_size(32, 32, 128, 16) == 32 * 32 * 16 * 130 * 4
     assert M.attn_fwd_decode_workspace_size(0, 32, 128, 16) == 0
     assert M.attn_fwd_decode_workspace_size(1, 0, 128, 16) == 0
@@ -84,6 +84,18 @@ def test_binding_raises_with_message():
     with pytest.raises(M.MiattnError) as e:
         M.attn_fwd(0, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 8, 8, 64, False, 0.125, stream=0)
     assert e.value.status == M.MIATTN_ERR_INVALID_ARG and "q is NULL" in e.value.message
+
+
+def test_attn_fwd_window_rejects_a_negative_window():
+    L = M.load()
+    assert L.attn_fwd_window(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 8, 8, 64, 1, -3, 0.125,
+                             0) == M.MIATTN_ERR_INVALID_ARG
+    assert "window_left" in M.miattn_last_error()
+    # the other checks are attn_fwd's
+    assert L.attn_fwd_window(0, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 8, 8, 64, 1, 4, 0.125,
+                             0) == M.MIATTN_ERR_INVALID_ARG
+    assert "q is NULL" in M.miattn_last_error()
+    assert L.attn_fwd_window(0, 0, 0, 0, 0, 0, 2, 2, 8, 8, 64, 1, 4, 0.125, 0) == M.MIATTN_OK
 
 
 def _dec(**kw):

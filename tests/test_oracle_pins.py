@@ -78,6 +78,63 @@ def test_brute_force_tiny(case):
                 assert np.all(o[:, :, i] == 0) and np.all(np.isneginf(lse[:, :, i]))
 
 
+# --------------------------------------------------------- sliding window --
+WINDOW_CASES = [
+    # B, Hq, Hkv, Sq, Sk, d, causal, window
+    (1, 2, 1, 6, 6, 4, True, 0),
+    (1, 2, 2, 5, 9, 3, True, 2),     # Sq < Sk
+    (2, 1, 1, 7, 4, 2, True, 1),     # Sq > Sk: the first rows see no key
+    (1, 2, 1, 5, 8, 4, False, 3),    # window without the causal bound
+    (1, 2, 1, 9, 3, 2, False, 0),    # rows whose window starts past the last key
+    (1, 1, 1, 6, 6, 2, True, 100),   # window wider than every row's prefix
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES)
+def test_window_brute_force_tiny(case):
+    B, Hq, Hkv, Sq, Sk, d, causal, window = case
+    rng = np.random.Generator(np.random.PCG64(hash(case) % (2 ** 32)))
+    q = _rand_bits(rng, (B, Hq, Sq, d))
+    k = _rand_bits(rng, (B, Hkv, Sk, d))
+    v = _rand_bits(rng, (B, Hkv, Sk, d))
+    o, lse = oracle.attn_fwd(q, k, v, causal, 0.5, window=window)
+    bo, blse = brute.attention(q.tolist(), k.tolist(), v.tolist(), causal, 0.5, window=window)
+    _close(o, np.array(bo, dtype=np.float64).reshape(o.shape))
+    _close(lse, np.array(blse, dtype=np.float64))
+    for i in range(Sq):  # a row with no key in its window: (+0, -inf) exactly
+        lo = i + Sk - Sq - window
+        hi = min(Sk - 1, i + Sk - Sq) if causal else Sk - 1
+        if max(lo, 0) > hi:
+            assert np.all(o[:, :, i] == 0) and np.all(np.isneginf(lse[:, :, i]))
+
+
+def test_window_zero_keeps_the_aligned_key():
+    """Causal with window 0: row i sees key i + Sk - Sq alone, so O is that
+    key's value row and LSE its scaled score (closed form)."""
+    rng = np.random.Generator(np.random.PCG64(17))
+    B, H, Sq, Sk, d = 2, 3, 9, 12, 8
+    q = _rand_bits(rng, (B, H, Sq, d))
+    k = _rand_bits(rng, (B, H, Sk, d))
+    v = _rand_bits(rng, (B, H, Sk, d))
+    o, lse = oracle.attn_fwd(q, k, v, True, 0.25, window=0)
+    qf, kf, vf = (inputs.bf16_to_f32(x).astype(np.float64) for x in (q, k, v))
+    for i in range(Sq):
+        j = i + Sk - Sq
+        assert np.array_equal(o[:, :, i], vf[:, :, j])
+        _close(lse[:, :, i], 0.25 * np.einsum("bhd,bhd->bh", qf[:, :, i], kf[:, :, j]))
+
+
+def test_wide_window_equals_no_window():
+    rng = np.random.Generator(np.random.PCG64(18))
+    q = _rand_bits(rng, (1, 2, 40, 16))
+    k = _rand_bits(rng, (1, 2, 50, 16))
+    v = _rand_bits(rng, (1, 2, 50, 16))
+    for causal in (False, True):
+        o0, l0 = oracle.attn_fwd(q, k, v, causal, 0.25)
+        o1, l1 = oracle.attn_fwd(q, k, v, causal, 0.25, window=90)
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
 # --------------------------------------------------------------------- T2 --
 @pytest.mark.parametrize("causal", [False, True])
 def test_zero_keys_give_uniform_weights(causal):

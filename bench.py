@@ -166,6 +166,40 @@ WINDOW_LEGS = (("window_d64_w128", dict(seed=7100, B=4, Hq=16, Hkv=16, S=8192, d
                                           W=4096)))
 
 
+class PrefillScoreMod:
+    """Non-causal prefill with a score modifier (attn_fwd_ext): a soft cap, or
+    ALiBi with the geometric slopes 2^(-8 (h + 1) / Hq)."""
+
+    def __init__(self, torch, seed, B, H, S, d, softcap=0.0, alibi=False):
+        import numpy as np
+        from online_softmax_monoid_amd import inputs
+        self.shape = (B, H, S, d)
+        q, k, v = inputs.draw_prefill_bits(seed, B, H, H, S, S, d)
+        self.q, self.k, self.v = dev_bits(q), dev_bits(k), dev_bits(v)
+        n = B * H * S
+        self.o = torch.empty(n * d, dtype=torch.int16, device="cuda")
+        self.lse = torch.empty(n, dtype=torch.float32, device="cuda")
+        self.softcap = softcap
+        self.alibi = None
+        if alibi:
+            sl = (2.0 ** (-8.0 * (np.arange(H) + 1) / H)).astype(np.float32)
+            self.alibi = torch.from_numpy(sl).to("cuda")
+        self.flops = 4.0 * d * S * S * B * H
+        self.scale = inputs.default_scale(d)
+
+    def __call__(self, stream):
+        from online_softmax_monoid_amd import miattn
+        B, H, S, d = self.shape
+        miattn.attn_fwd_ext(self.q, self.k, self.v, self.o, self.lse, B, H, H, S, S, d, False,
+                            -1, self.softcap, self.alibi, self.scale, stream)
+
+
+# The score-variant rows of the pages' table (forward, n = 2k, d = 64; batch
+# and heads not stated there, 4 x 16 here); cap 30
+SCOREMOD_LEGS = (("softcap_d64_n2k", dict(seed=6200, B=4, H=16, S=2048, d=64, softcap=30.0)),
+                 ("alibi_d64_n2k", dict(seed=6300, B=4, H=16, S=2048, d=64, alibi=True)))
+
+
 class DecodePaged:
     """The decode workload with its cache in pages of ``page`` keys, pool
     pages in a seeded random order; two pool copies used alternately, as for
@@ -362,6 +396,19 @@ def main():
                          "hbm_frac": round(w_gbs / PEAK_HBM_GBS, 4),
                          "shape": {k: v for k, v in cfg.items() if k != "seed"}}
         del wl
+        torch.cuda.empty_cache()
+
+    for name, cfg in SCOREMOD_LEGS:
+        sm = PrefillScoreMod(torch, **cfg)
+        time_launches(sm, stream, torch, 3)
+        sms = time_launches(sm, stream, torch, 10)
+        s_avg = sum(sms) / len(sms)
+        s_tf = sm.flops / (s_avg * 1e-3) / 1e12
+        log(f"bench: {name} {s_avg:.4f} ms ({s_tf:.1f} TFLOP/s)")
+        windows[name] = {"value": round(s_tf, 2), "unit": "TFLOP/s", "ms": round(s_avg, 4),
+                         "frac": round(s_tf / PEAK_BF16_TFLOPS, 4),
+                         "shape": {k: v for k, v in cfg.items() if k != "seed"}}
+        del sm
         torch.cuda.empty_cache()
 
     log("bench: paged decode (16-key pages)")

@@ -115,6 +115,27 @@ MIATTN_API int attn_fwd_window(const void *q, const void *k, const void *v, void
                     int causal, int window_left, float scale, hipStream_t stream);
 
 /*
+ * Prefill forward with the score and mask variants: attn_fwd with
+ *
+ *   window_left   >= 0: the sliding window of attn_fwd_window; < 0: none
+ *   softcap       > 0: every scaled score s becomes softcap * tanh(s / softcap)
+ *                 (the soft cap of the paper's variant table, §7.3); 0: none
+ *   alibi_slopes  DEVICE float [Hq] or NULL: the scaled score of query i and
+ *                 key j of query head h gets - alibi_slopes[h] * |i + Sk - Sq - j|
+ *                 added (ALiBi, §7.3); the slopes are not inspected on the host
+ *
+ * applied in that order: the modifier to the scaled score, then the mask.
+ * LSE is the log-sum-exp of the modified scores. Only the score changes, so
+ * the reduction is the same online-softmax monoid (§2.3 "Rewrites").
+ * softcap must be finite and >= 0; softcap > 0 together with alibi_slopes is
+ * MIATTN_ERR_UNSUPPORTED. Every other argument, limit and error is attn_fwd's.
+ */
+MIATTN_API int attn_fwd_ext(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
+                 int window_left, float softcap, const float *alibi_slopes,
+                 float scale, hipStream_t stream);
+
+/*
  * Bytes of workspace attn_fwd_decode needs: B * Hq * num_splits * (d + 2) * 4
  * (one f32 partial state (m, l, acc[d]) per stream, head and split).
  * Returns 0 for invalid arguments.

@@ -76,7 +76,8 @@ extern "C" {
 
 static int fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B,
                     int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window, float scale,
-                    hipStream_t stream, const char *what)
+                    hipStream_t stream, const char *what, float softcap = 0.f,
+                    const float *alibi = nullptr)
 {
     if (B < 0 || Sq < 0 || Sk < 0)
         return fail(MIATTN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d, Sq=%d, Sk=%d)", B, Sq, Sk);
@@ -107,6 +108,8 @@ static int fwd_impl(const void *q, const void *k, const void *v, void *o, float 
     a.Sk = Sk;
     a.scale = scale;
     a.window = window;
+    a.softcap = softcap;
+    a.alibi = alibi;
     return hip_status(miattn::launch_fwd(a, d, causal != 0, stream), what);
 }
 
@@ -125,6 +128,21 @@ int attn_fwd_window(const void *q, const void *k, const void *v, void *o, float 
         return fail(MIATTN_ERR_INVALID_ARG, "window_left must be >= 0 (got %d)", window_left);
     return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, window_left, scale, stream,
                     "attn_fwd_window launch");
+}
+
+int attn_fwd_ext(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq,
+                 int Hkv, int Sq, int Sk, int d, int causal, int window_left, float softcap,
+                 const float *alibi_slopes, float scale, hipStream_t stream)
+{
+    if (!(softcap >= 0.f) || !isfinite(softcap))
+        return fail(MIATTN_ERR_INVALID_ARG, "softcap must be finite and >= 0 (got %g)",
+                    (double)softcap);
+    if (softcap > 0.f && alibi_slopes != nullptr)
+        return fail(MIATTN_ERR_UNSUPPORTED, "softcap and alibi_slopes together are not supported");
+    if (alibi_slopes != nullptr && !aligned(alibi_slopes, 4))
+        return fail(MIATTN_ERR_INVALID_ARG, "alibi_slopes is not 4-byte aligned");
+    return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, window_left < 0 ? -1 : window_left,
+                    scale, stream, "attn_fwd_ext launch", softcap, alibi_slopes);
 }
 
 size_t attn_fwd_decode_workspace_size(int B, int Hq, int d, int num_splits)
@@ -249,6 +267,6 @@ int attn_fwd_decode_paged(const void *q, const void *k_pages, const void *v_page
 
 const char *miattn_last_error(void) { return g_last_error.c_str(); }
 
-int miattn_version(void) { return 300; }
+int miattn_version(void) { return 400; }
 
 }  // extern "C"

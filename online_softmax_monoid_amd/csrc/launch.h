@@ -19,6 +19,11 @@ struct FwdArgs {
     // sliding window: key j is visible to query i only if
     // j >= i + (Sk - Sq) - window; window < 0: no lower bound
     int window = -1;
+    // score modifiers (at most one): soft cap s <- softcap * tanh(s / softcap)
+    // of the scaled score (softcap > 0), or ALiBi s <- s - slope_h * |i + Sk - Sq - j|
+    // with alibi[h] the slope of query head h (alibi != nullptr)
+    float softcap = 0.f;
+    const float *alibi = nullptr;
 };
 
 struct DecodeArgs {

@@ -114,7 +114,10 @@ struct Cfg {
     static_assert((BN * KCH) % NT == 0, "K tile must split evenly over threads");
 };
 
-template <int D, int BN, int NW, bool PIPE, bool CAUSAL>
+// Score modifiers: none, soft cap, ALiBi
+enum { kModNone = 0, kModSoftcap = 1, kModAlibi = 2 };
+
+template <int D, int BN, int NW, bool PIPE, bool CAUSAL, int MOD>
 __global__ void __launch_bounds__(NW * 64)
 fwd_kernel(FwdArgs a, int n_qtiles)
 {
@@ -280,8 +283,32 @@ fwd_kernel(FwdArgs a, int n_qtiles)
             acc[db][r] = 0.f;
 
     // mask (a3), monoid update (a4) and value contraction (a5) of tile blk
+    // Score modifiers on the raw scores (q.k before the scale), applied before
+    // the mask: the soft cap keeps (cap / scale) tanh(s scale / cap), with
+    // tanh(x) = 1 - 2 / (exp(2x) + 1); ALiBi subtracts (slope / scale) times
+    // the distance |i + Sk - Sq - key|.
+    const float sc_in = MOD == kModSoftcap ? 2.f * a.scale / a.softcap * kLog2e : 0.f;
+    const float sc_out = MOD == kModSoftcap ? a.softcap / a.scale : 0.f;
+    const float slope = MOD == kModAlibi ? a.alibi[hq] / a.scale : 0.f;
     auto softmax_pv = [&](int blk, f32x16 (&s)[BN / 32]) {
         const int j0 = kofs + blk * BN;  // first key of the tile
+        if constexpr (MOD == kModSoftcap) {
+#pragma unroll
+            for (int bb = 0; bb < BN / 32; ++bb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float e = __builtin_amdgcn_exp2f(s[bb][r] * sc_in);
+                    s[bb][r] = sc_out * __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f);
+                }
+        } else if constexpr (MOD == kModAlibi) {
+#pragma unroll
+            for (int bb = 0; bb < BN / 32; ++bb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = j0 + 32 * bb + 8 * (r >> 2) + 4 * g + (r & 3);
+                    s[bb][r] = __builtin_fmaf(-slope, (float)abs(my_q + diag - key), s[bb][r]);
+                }
+        }
         const bool full = (j0 + BN <= Sk) && (!CAUSAL || j0 + BN - 1 <= q0 + diag) &&
                           (!windowed || j0 >= q0 + 31 + diag - a.window);
         if (!full) {
@@ -431,17 +458,27 @@ fwd_kernel(FwdArgs a, int n_qtiles)
     }
 }
 
-template <int D, int BN, int NW, bool PIPE, bool CAUSAL>
-hipError_t launch(const FwdArgs &a, hipStream_t stream)
+template <int D, int BN, int NW, bool PIPE, bool CAUSAL, int MOD>
+hipError_t launch_mod(const FwdArgs &a, hipStream_t stream)
 {
     constexpr int BM = NW * 32;
     const int n_qtiles = (a.Sq + BM - 1) / BM;
     const long long n_tiles = (long long)a.B * a.Hq * n_qtiles;
     if (n_tiles > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_kernel<D, BN, NW, PIPE, CAUSAL>), dim3((unsigned)n_tiles), dim3(NW * 64),
+    hipLaunchKernelGGL((fwd_kernel<D, BN, NW, PIPE, CAUSAL, MOD>), dim3((unsigned)n_tiles), dim3(NW * 64),
                        0, stream, a, n_qtiles);
     return hipGetLastError();
+}
+
+template <int D, int BN, int NW, bool PIPE, bool CAUSAL>
+hipError_t launch(const FwdArgs &a, hipStream_t stream)
+{
+    if (a.softcap > 0.f)
+        return launch_mod<D, BN, NW, PIPE, CAUSAL, kModSoftcap>(a, stream);
+    if (a.alibi != nullptr)
+        return launch_mod<D, BN, NW, PIPE, CAUSAL, kModAlibi>(a, stream);
+    return launch_mod<D, BN, NW, PIPE, CAUSAL, kModNone>(a, stream);
 }
 
 }  // namespace
@@ -469,7 +506,7 @@ hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
         return causal ? launch<128, MIATTN_FWD_D128, true>(a, stream)
                       : launch<128, MIATTN_FWD_D128, false>(a, stream);
 #elif defined(MIATTN_D128_PINGPONG)
-        if (a.window >= 0)  // the ping-pong kernel has no window
+        if (a.window >= 0 || a.softcap > 0.f || a.alibi != nullptr)  // not in the ping-pong kernel
             return launch_fwd_q64(a, 128, causal, stream);
         return launch_fwd_pingpong(a, causal, stream);
 #else

@@ -154,9 +154,13 @@ struct Item {
     int64_t qrow0, krow0;  // first row of the query head / the item's first key row
     int q_wg, kv_end, nblk;
     int kofs;  // key of the item's tile 0 (nonzero only with a sliding window)
+    float slope;  // ALiBi slope of the query head over the scale (raw score units)
 };
 
-template <bool CAUSAL, int NWV, int D, int QB, int WPE, bool WIN>
+// Score modifiers: none, soft cap, ALiBi
+enum { kModNone = 0, kModSoftcap = 1, kModAlibi = 2 };
+
+template <bool CAUSAL, int NWV, int D, int QB, int WPE, bool WIN, int MOD>
 __global__ void __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 {
@@ -230,6 +234,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         const int hq = kvh * G + to.gq;
         Item it;
         it.qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
+        it.slope = MOD == kModAlibi ? a.alibi[hq] / a.scale : 0.f;
         it.q_wg = to.qtile * BM;
         const int q_wg_last = min(it.q_wg + BM, Sq) - 1;
         const int kv_end = CAUSAL ? min(Sk, max(0, q_wg_last + diag + 1)) : Sk;
@@ -347,6 +352,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // ---- the current and the next item (the lambdas below read these) ---------------
     int ph = 0;                      // ring slot of the current item's tile 0
     int nblk = 0, nwb = 0, q0 = 0, kv_end = 0, kofs = 0;
+    float slope = 0.f;
     int64_t qrow0 = 0, krow0 = 0;
     bool has_next = false;
     int kv_end_n = 0, q_wg_n = 0;  // kv_end_n = 0 without a next item
@@ -421,6 +427,29 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         }
         pin(p[qb][h].w[2 * quad]);
         pin(p[qb][h].w[2 * quad + 1]);
+    };
+    // Score modifiers on the raw scores of tile j (the kernel's scores are
+    // q.k before the scale): the soft cap keeps (cap / scale) tanh(s scale /
+    // cap), tanh(x) = 1 - 2 / (exp(2x) + 1); ALiBi subtracts (slope / scale)
+    // times the distance |i + Sk - Sq - key|. Applied before the mask.
+    static_assert(MOD == kModNone || QB == 1, "score modifiers need one query block per wave");
+    const float sc_in = MOD == kModSoftcap ? 2.f * a.scale / a.softcap * kLog2e : 0.f;
+    const float sc_out = MOD == kModSoftcap ? a.softcap / a.scale : 0.f;
+    auto modify_tile = [&](Sc &s, int j) __attribute__((always_inline)) {
+        if constexpr (MOD == kModSoftcap) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = __builtin_amdgcn_exp2f(s[0][r] * sc_in);
+                s[0][r] = sc_out * __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f);
+            }
+        } else if constexpr (MOD == kModAlibi) {
+            const int d0 = q0 + l32 + diag - kofs - j * BN - 4 * g;  // distance to key offset 0
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int dist = d0 - (8 * (r >> 2) + (r & 3));
+                s[0][r] = __builtin_fmaf(-slope, (float)abs(dist), s[0][r]);
+            }
+        }
     };
     // The keys of tile j that row q0 + 32 qb + l32 sees: score r (key
     // 8(r/4) + 4g + r%4 of the tile) is visible iff rlo <= 8(r/4) + r%4 <= rel.
@@ -553,6 +582,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
                 qk_mfma(sA, qb, kk);
+        modify_tile(sA, 0);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             row_max(sA, qb, 0, 0, true);
@@ -689,6 +719,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
                     row_max(sn, 1, 2, j + 1, MASK);
                 }
             } else {
+                if (MOD != kModNone && grp == 0)
+                    modify_tile(sn, j + 1);
                 if (MASK && grp == 0)
                     mask_tile(sn, 0, j + 1);
                 if (NG == 2 && grp == 1) {
@@ -789,6 +821,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         kv_end = cur.kv_end;
         nblk = cur.nblk;
         kofs = WIN ? cur.kofs : 0;
+        slope = cur.slope;
         q0 = cur.q_wg + wave * 32 * QB;  // first row of this wave
         const bool wave_live = q0 < Sq;
         int wave_end = wave_live ? Sk : 0;
@@ -888,10 +921,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 
 // One workgroup per resident slot (a multiple of 8, so that each XCD holds the
 // same number), each walking its share of the n_items work items.
-template <bool CAUSAL, int D, int QB, int NWV, int WPE, bool WIN>
+template <bool CAUSAL, int D, int QB, int NWV, int WPE, bool WIN, int MOD>
 hipError_t launch_q64_t(const FwdArgs &a, int n_qtiles, int n_items, hipStream_t stream)
 {
-    const auto kernel = fwd_q64_kernel<CAUSAL, NWV, D, QB, WPE, WIN>;
+    const auto kernel = fwd_q64_kernel<CAUSAL, NWV, D, QB, WPE, WIN, MOD>;
     const int resident = resident_workgroups(kernel, 64 * NWV);
     if (resident < 8)
         return hipErrorInvalidConfiguration;
@@ -899,6 +932,16 @@ hipError_t launch_q64_t(const FwdArgs &a, int n_qtiles, int n_items, hipStream_t
     const int grid = (int)std::min<long long>(want, resident / 8 * 8);
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(64 * NWV), 0, stream, a, n_qtiles, n_items);
     return hipGetLastError();
+}
+
+template <int D, int QB, int NWV, int WPE, int MOD>
+hipError_t dispatch_win(const FwdArgs &a, bool causal, int n_qtiles, int n, hipStream_t stream)
+{
+    if (a.window >= 0)
+        return causal ? launch_q64_t<true, D, QB, NWV, WPE, true, MOD>(a, n_qtiles, n, stream)
+                      : launch_q64_t<false, D, QB, NWV, WPE, true, MOD>(a, n_qtiles, n, stream);
+    return causal ? launch_q64_t<true, D, QB, NWV, WPE, false, MOD>(a, n_qtiles, n, stream)
+                  : launch_q64_t<false, D, QB, NWV, WPE, false, MOD>(a, n_qtiles, n, stream);
 }
 
 template <int D, int QB, int NWV, int WPE>
@@ -913,11 +956,16 @@ hipError_t launch_q64(const FwdArgs &a, bool causal, hipStream_t stream)
     if (n_items == 0)
         return hipSuccess;
     const int n = (int)n_items;
-    if (a.window >= 0)
-        return causal ? launch_q64_t<true, D, QB, NWV, WPE, true>(a, n_qtiles, n, stream)
-                      : launch_q64_t<false, D, QB, NWV, WPE, true>(a, n_qtiles, n, stream);
-    return causal ? launch_q64_t<true, D, QB, NWV, WPE, false>(a, n_qtiles, n, stream)
-                  : launch_q64_t<false, D, QB, NWV, WPE, false>(a, n_qtiles, n, stream);
+    if constexpr (QB == 1) {
+        if (a.softcap > 0.f)
+            return dispatch_win<D, QB, NWV, WPE, kModSoftcap>(a, causal, n_qtiles, n, stream);
+        if (a.alibi != nullptr)
+            return dispatch_win<D, QB, NWV, WPE, kModAlibi>(a, causal, n_qtiles, n, stream);
+    } else {
+        if (a.softcap > 0.f || a.alibi != nullptr)
+            return hipErrorNotSupported;
+    }
+    return dispatch_win<D, QB, NWV, WPE, kModNone>(a, causal, n_qtiles, n, stream);
 }
 
 }  // namespace

@@ -21,7 +21,8 @@ MIATTN_ERR_INVALID_ARG = 1
 MIATTN_ERR_UNSUPPORTED = 2
 MIATTN_ERR_HIP = 3
 
-EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_fwd_decode_workspace_size", "attn_fwd_decode",
+EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_fwd_ext", "attn_fwd_decode_workspace_size",
+           "attn_fwd_decode",
            "attn_fwd_decode_paged", "miattn_last_error", "miattn_version")
 
 
@@ -49,6 +50,8 @@ def load(path: str = LIB_PATH):
     L.attn_fwd.restype = i
     L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
     L.attn_fwd_window.restype = i
+    L.attn_fwd_ext.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, f, vp]
+    L.attn_fwd_ext.restype = i
     L.attn_fwd_decode_workspace_size.argtypes = [i, i, i, i]
     L.attn_fwd_decode_workspace_size.restype = ctypes.c_size_t
     L.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp,
@@ -99,6 +102,14 @@ def attn_fwd_window(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, window_left,
                                   int(Hq), int(Hkv), int(Sq), int(Sk), int(d),
                                   int(bool(causal)), int(window_left), float(scale),
                                   _stream(stream)))
+
+
+def attn_fwd_ext(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, window_left, softcap,
+                 alibi_slopes, scale, stream=None):
+    _check(load().attn_fwd_ext(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), int(B),
+                               int(Hq), int(Hkv), int(Sq), int(Sk), int(d), int(bool(causal)),
+                               int(window_left), float(softcap), _addr(alibi_slopes),
+                               float(scale), _stream(stream)))
 
 
 def attn_fwd_decode_workspace_size(B, Hq, d, num_splits) -> int:

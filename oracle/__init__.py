@@ -58,6 +58,12 @@ def lib():
                                              c_int, c_int, c_int, c_int, ctypes.c_float, i64p,
                                              ctypes.c_int64, f64p, f64p, c_int]
         L.oracle_attn_fwd_window.restype = c_int
+        f32p = ctypes.POINTER(ctypes.c_float)
+        L.oracle_attn_fwd_ext.argtypes = [u16p, u16p, u16p, c_int, c_int, c_int, c_int,
+                                          c_int, c_int, c_int, c_int, ctypes.c_float, f32p,
+                                          ctypes.c_float, i64p, ctypes.c_int64, f64p, f64p,
+                                          c_int]
+        L.oracle_attn_fwd_ext.restype = c_int
         L.oracle_attn_decode.argtypes = [u16p, u16p, u16p, i32p, c_int, c_int, c_int,
                                          c_int, c_int, ctypes.c_float, f64p, f64p,
                                          c_int]
@@ -86,12 +92,14 @@ def max_threads() -> int:
 
 
 def attn_fwd(q_bits, k_bits, v_bits, causal: bool, scale: float, rows=None,
-             nthreads: int = 0, window: int = -1):
+             nthreads: int = 0, window: int = -1, softcap: float = 0.0, alibi=None):
     """Two-pass f64 attention on bf16 bit arrays.
 
     q_bits: [B,Hq,Sq,d], k_bits / v_bits: [B,Hkv,Sk,d] (uint16).
     rows: optional flat row ids ((b*Hq + h)*Sq + i). window >= 0 hides keys
     j < i + Sk - Sq - window from row i (sliding window); < 0: none.
+    softcap > 0 caps each scaled score s to softcap * tanh(s / softcap);
+    alibi (float32 [Hq]) subtracts alibi[h] * |i + Sk - Sq - j| from it.
     Returns (o, lse) as f64: o has shape [B,Hq,Sq,d] and lse [B,Hq,Sq] when
     rows is None, else [len(rows), d] and [len(rows)].
     """
@@ -110,11 +118,15 @@ def attn_fwd(q_bits, k_bits, v_bits, causal: bool, scale: float, rows=None,
         rows_p = _ptr(rows, ctypes.c_int64)
     o = np.empty((max(n, 1), d), dtype=np.float64)
     lse = np.empty(max(n, 1), dtype=np.float64)
-    rc = lib().oracle_attn_fwd_window(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
-                                      _ptr(v, ctypes.c_uint16), B, Hq, Hkv, Sq, Sk, d,
-                                      int(bool(causal)), int(window), float(scale), rows_p, n,
-                                      _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
-                                      int(nthreads))
+    if alibi is not None:
+        alibi = np.ascontiguousarray(alibi, dtype=np.float32)
+        assert alibi.shape == (Hq,)
+    al_p = _ptr(alibi, ctypes.c_float) if alibi is not None else None
+    rc = lib().oracle_attn_fwd_ext(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                   _ptr(v, ctypes.c_uint16), B, Hq, Hkv, Sq, Sk, d,
+                                   int(bool(causal)), int(window), float(softcap), al_p,
+                                   float(scale), rows_p, n, _ptr(o, ctypes.c_double),
+                                   _ptr(lse, ctypes.c_double), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_attn_fwd rejected its arguments")
     o, lse = o[:n], lse[:n]

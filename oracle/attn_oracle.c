@@ -17,6 +17,8 @@
  *     J_i  = { j in [0, Sk) : (!causal || j <= i + Sk - Sq)
  *                              && (window < 0 || j >= i + Sk - Sq - window) }
  *     s_j  = scale * sum_t Q[b,h,i,t] * K[b,g,j,t]          (pass 1)
+ *     s_j <- softcap * tanh(s_j / softcap)          (soft cap, softcap > 0)
+ *     s_j <- s_j - slope_h * |i + Sk - Sq - j|      (ALiBi, slopes given)
  *     m    = max_{j in J_i} s_j
  *     l    = sum_{j in J_i} exp(s_j - m)                     (pass 2)
  *     O    = sum_{j in J_i} exp(s_j - m) * V[b,g,j,:] / l
@@ -36,9 +38,11 @@
  * (bits << 16 gives the float32 pattern, then float -> double). The scale is
  * the float32 value handed to the GPU, widened to double.
  *
- * The window term is the sliding-window variant (no window: window < 0). A
- * change of the mask leaves the monoid alone (§2.3 "Rewrites"), so the
- * definition is the same two passes over a smaller key set.
+ * The window term is the sliding-window variant (no window: window < 0), the
+ * two score lines the soft-cap and ALiBi variants (§7.3's variant table). A
+ * change of the score or the mask leaves the monoid alone (§2.3 "Rewrites"),
+ * so the definition is the same two passes over modified scores or a smaller
+ * key set.
  *
  * Decode (one query row per stream and head, keys [0, len_b) of a cache of
  * capacity S_cap) is the same definition with J = [0, len_b).
@@ -63,6 +67,15 @@ static double widen_bf16(uint16_t bits)
     return (double)f;
 }
 
+/* Score modifiers of one row: none when softcap == 0 and slope == 0. */
+typedef struct {
+    double softcap;  /* > 0: soft cap */
+    double slope;    /* ALiBi slope of the row's query head */
+    int64_t dist0;   /* i + Sk - Sq - (key index of the first key passed) */
+} score_mod;
+
+static const score_mod no_mod = {0.0, 0.0, 0};
+
 /*
  * Two-pass softmax attention of one query row over keys 0..nkeys-1 of one
  * (b, kv-head) slice. k and v point at that slice's first key row; rows are
@@ -71,7 +84,7 @@ static double widen_bf16(uint16_t bits)
  */
 static void attend_row(const uint16_t *qrow, const uint16_t *k,
                        const uint16_t *v, int64_t nkeys, int d, double scale,
-                       double *s, double *o, double *lse)
+                       score_mod mod, double *s, double *o, double *lse)
 {
     int t;
     int64_t j;
@@ -91,6 +104,10 @@ static void attend_row(const uint16_t *qrow, const uint16_t *k,
         for (t = 0; t < d; ++t)
             dot += widen_bf16(qrow[t]) * widen_bf16(krow[t]);
         s[j] = scale * dot;
+        if (mod.softcap > 0.0)
+            s[j] = mod.softcap * tanh(s[j] / mod.softcap);
+        if (mod.slope != 0.0)
+            s[j] -= mod.slope * (double)llabs(mod.dist0 - j);
         if (s[j] > m)
             m = s[j];
     }
@@ -143,12 +160,13 @@ static int64_t first_visible_key(int64_t i, int64_t Sq, int64_t Sk, int window)
  * o[nrows*d] and lse[nrows] (row order of `rows`). Returns 0, or -1 on a bad
  * argument.
  */
-int oracle_attn_fwd_window(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                           int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
-                           int window, float scale, const int64_t *rows, int64_t nrows,
-                           double *o, double *lse, int nthreads)
+int oracle_attn_fwd_ext(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
+                        int window, float softcap, const float *alibi, float scale,
+                        const int64_t *rows, int64_t nrows, double *o, double *lse,
+                        int nthreads)
 {
-    if (bad_shape(B, Hq, Hkv, d) || Sq < 0 || Sk < 0)
+    if (bad_shape(B, Hq, Hkv, d) || Sq < 0 || Sk < 0 || !(softcap >= 0.f))
         return -1;
     const int64_t total = (int64_t)B * Hq * Sq;
     if (rows == NULL)
@@ -188,13 +206,27 @@ int oracle_attn_fwd_window(const uint16_t *q, const uint16_t *k, const uint16_t 
                 const uint16_t *vh = v + (b * Hkv + g) * (int64_t)Sk * d;
                 const int64_t lo = first_visible_key(i, Sq, Sk, window);
                 const int64_t hi = visible_keys(i, Sq, Sk, causal);
-                attend_row(qrow, kh + lo * d, vh + lo * d, hi - lo, d, sc,
+                score_mod mod = no_mod;
+                mod.softcap = (double)softcap;
+                mod.slope = alibi ? (double)alibi[h] : 0.0;
+                mod.dist0 = i + (Sk - Sq) - lo;
+                attend_row(qrow, kh + lo * d, vh + lo * d, hi - lo, d, sc, mod,
                            s, o + n * (int64_t)d, lse + n);
             }
             free(s);
         }
     }
     return err ? -1 : 0;
+}
+
+/* Prefill oracle with a window and no score modifier. */
+int oracle_attn_fwd_window(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
+                           int window, float scale, const int64_t *rows, int64_t nrows,
+                           double *o, double *lse, int nthreads)
+{
+    return oracle_attn_fwd_ext(q, k, v, B, Hq, Hkv, Sq, Sk, d, causal, window, 0.f, NULL,
+                               scale, rows, nrows, o, lse, nthreads);
 }
 
 /* Prefill oracle without a window. */
@@ -245,7 +277,7 @@ int oracle_attn_decode(const uint16_t *q, const uint16_t *kc,
                 int64_t g = h / G;
                 const uint16_t *kh = kc + (b * Hkv + g) * (int64_t)S_cap * d;
                 const uint16_t *vh = vc + (b * Hkv + g) * (int64_t)S_cap * d;
-                attend_row(q + n * (int64_t)d, kh, vh, lens[b], d, sc, s,
+                attend_row(q + n * (int64_t)d, kh, vh, lens[b], d, sc, no_mod, s,
                            o + n * (int64_t)d, lse + n);
             }
             free(s);

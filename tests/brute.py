@@ -27,7 +27,7 @@ def _visible(i, j, Sq, Sk, causal, window=-1):
     return window < 0 or j - i >= Sk - Sq - window
 
 
-def attention(q, k, v, causal, scale, window=-1):
+def attention(q, k, v, causal, scale, window=-1, softcap=0.0, alibi=None):
     """q: nested lists [B][Hq][Sq][d] of bf16 bits; k, v: [B][Hkv][Sk][d].
 
     Returns (o, lse) as nested lists of Python floats.
@@ -50,7 +50,12 @@ def attention(q, k, v, causal, scale, window=-1):
                 for j in keys:
                     dot = math.fsum(bf16_value(q[b][h][i][t]) * bf16_value(k[b][kvh][j][t])
                                     for t in range(d))
-                    e[j] = math.exp(scale * dot)
+                    sj = scale * dot
+                    if softcap > 0:
+                        sj = softcap * math.tanh(sj / softcap)
+                    if alibi is not None:
+                        sj -= alibi[h] * abs(i + Sk - Sq - j)
+                    e[j] = math.exp(sj)
                 z = math.fsum(e.values())
                 o[b][h][i] = [math.fsum(e[j] * bf16_value(v[b][kvh][j][t]) for j in keys) / z
                               for t in range(d)]

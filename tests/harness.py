@@ -63,6 +63,27 @@ def run_fwd(q, k, v, causal, scale, stream=None, window=-1):
     return ob[:n * d].reshape(B, Hq, Sq, d), lh[:n].reshape(B, Hq, Sq), guards
 
 
+def run_fwd_ext(q, k, v, causal, scale, window=-1, softcap=0.0, alibi=None):
+    """Run attn_fwd_ext on bit arrays (alibi: float32 slopes [Hq] or None);
+    returns (o_bits [B,Hq,Sq,d], lse f32, guards_ok)."""
+    torch = torch_mod()
+    B, Hq, Sq, d = q.shape
+    _, Hkv, Sk, _ = k.shape
+    qd, kd, vd = dev_bits(q), dev_bits(k), dev_bits(v)
+    ad = None
+    if alibi is not None:
+        ad = torch.from_numpy(np.ascontiguousarray(alibi, dtype=np.float32)).to("cuda")
+    n = B * Hq * Sq
+    o, lse = nan_out(n * d, n)
+    miattn.attn_fwd_ext(qd, kd, vd, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, window, softcap, ad,
+                        scale)
+    torch.cuda.synchronize()
+    ob = host_bits(o)
+    lh = lse.cpu().numpy()
+    guards = bool(np.all(ob[n * d:] == NAN_BF16) and np.all(np.isnan(lh[n:])))
+    return ob[:n * d].reshape(B, Hq, Sq, d), lh[:n].reshape(B, Hq, Sq), guards
+
+
 def run_decode(q, kc, vc, lens, scale, splits, ws_fill=float("nan")):
     torch = torch_mod()
     B, Hq, d = q.shape

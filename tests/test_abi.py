@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_workspace_size():
-    assert M.miattn_version() == 300
+    assert M.miattn_version() == 400
     assert M.attn_fwd_decode_workspace_size(32, 32, 128, 16) == 32 * 32 * 16 * 130 * 4
     assert M.attn_fwd_decode_workspace_size(0, 32, 128, 16) == 0
     assert M.attn_fwd_decode_workspace_size(1, 0, 128, 16) == 0
@@ -96,6 +96,20 @@ def test_attn_fwd_window_rejects_a_negative_window():
                              0) == M.MIATTN_ERR_INVALID_ARG
     assert "q is NULL" in M.miattn_last_error()
     assert L.attn_fwd_window(0, 0, 0, 0, 0, 0, 2, 2, 8, 8, 64, 1, 4, 0.125, 0) == M.MIATTN_OK
+
+
+@pytest.mark.parametrize("softcap,alibi,status,needle", [
+    (-1.0, 0, M.MIATTN_ERR_INVALID_ARG, "softcap"),
+    (float("nan"), 0, M.MIATTN_ERR_INVALID_ARG, "softcap"),
+    (float("inf"), 0, M.MIATTN_ERR_INVALID_ARG, "softcap"),
+    (5.0, FAKE, M.MIATTN_ERR_UNSUPPORTED, "together"),
+    (0.0, FAKE + 2, M.MIATTN_ERR_INVALID_ARG, "alibi_slopes"),
+])
+def test_attn_fwd_ext_rejects(softcap, alibi, status, needle):
+    L = M.load()
+    assert L.attn_fwd_ext(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 8, 8, 64, 1, -1, softcap,
+                          alibi, 0.125, 0) == status
+    assert needle in M.miattn_last_error()
 
 
 def _dec(**kw):

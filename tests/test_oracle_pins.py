@@ -135,6 +135,69 @@ def test_wide_window_equals_no_window():
         assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
 
 
+# ------------------------------------------------------- score modifiers --
+MOD_CASES = [
+    # B, Hq, Hkv, Sq, Sk, d, causal, window, softcap, alibi slopes (or None)
+    (1, 2, 1, 6, 6, 4, True, -1, 0.75, None),   # caps exact in f32, as the C oracle takes them
+    (1, 2, 2, 5, 9, 3, False, -1, 3.0, None),
+    (2, 1, 1, 7, 4, 2, True, 2, 1.5, None),
+    (1, 2, 1, 6, 6, 4, True, -1, 0.0, (0.5, 0.125)),
+    (1, 2, 2, 5, 9, 3, False, -1, 0.0, (0.25, 1.0)),
+    (1, 2, 1, 8, 8, 4, True, 3, 0.0, (0.75, 0.0)),
+]
+
+
+@pytest.mark.parametrize("case", MOD_CASES)
+def test_score_modifiers_brute_force_tiny(case):
+    B, Hq, Hkv, Sq, Sk, d, causal, window, softcap, alibi = case
+    rng = np.random.Generator(np.random.PCG64(hash(case) % (2 ** 32)))
+    q = _rand_bits(rng, (B, Hq, Sq, d))
+    k = _rand_bits(rng, (B, Hkv, Sk, d))
+    v = _rand_bits(rng, (B, Hkv, Sk, d))
+    al = None if alibi is None else np.array(alibi, dtype=np.float32)
+    o, lse = oracle.attn_fwd(q, k, v, causal, 0.5, window=window, softcap=softcap, alibi=al)
+    bo, blse = brute.attention(q.tolist(), k.tolist(), v.tolist(), causal, 0.5, window=window,
+                               softcap=softcap, alibi=None if al is None else al.tolist())
+    _close(o, np.array(bo, dtype=np.float64).reshape(o.shape))
+    _close(lse, np.array(blse, dtype=np.float64))
+
+
+def test_alibi_steep_slope_keeps_the_aligned_key():
+    """A slope of 200 per key leaves the aligned key (distance 0) alone, with
+    or without the causal bound: O is its value row, LSE its scaled score."""
+    rng = np.random.Generator(np.random.PCG64(21))
+    B, H, Sq, Sk, d = 1, 2, 7, 10, 8
+    q = _rand_bits(rng, (B, H, Sq, d), 0.25)
+    k = _rand_bits(rng, (B, H, Sk, d), 0.25)
+    v = _rand_bits(rng, (B, H, Sk, d))
+    qf, kf, vf = (inputs.bf16_to_f32(x).astype(np.float64) for x in (q, k, v))
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd(q, k, v, causal, 0.5, alibi=np.full(H, 200.0, np.float32))
+        for i in range(Sq):
+            j = i + Sk - Sq
+            _close(o[:, :, i], vf[:, :, j], rtol=1e-12, atol=1e-12)
+            _close(lse[:, :, i], 0.5 * np.einsum("bhd,bhd->bh", qf[:, :, i], kf[:, :, j]),
+                   rtol=1e-12)
+
+
+def test_softcap_limits():
+    """A cap far above the scores changes nothing to 1e-9; a cap near zero
+    flattens them: O is the mean of V over the row's keys, LSE ln(n)."""
+    rng = np.random.Generator(np.random.PCG64(22))
+    q = _rand_bits(rng, (1, 2, 12, 8))
+    k = _rand_bits(rng, (1, 2, 12, 8))
+    v = _rand_bits(rng, (1, 2, 12, 8))
+    vf = inputs.bf16_to_f32(v).astype(np.float64)
+    o0, l0 = oracle.attn_fwd(q, k, v, True, 0.5)
+    o1, l1 = oracle.attn_fwd(q, k, v, True, 0.5, softcap=1e6)
+    _close(o1, o0, rtol=1e-9, atol=1e-12)
+    _close(l1, l0, rtol=1e-9)
+    o2, l2 = oracle.attn_fwd(q, k, v, True, 0.5, softcap=1e-7)
+    for i in range(12):
+        _close(o2[:, :, i], vf[:, :, :i + 1].mean(axis=2), rtol=1e-5, atol=1e-6)
+        _close(l2[:, :, i], np.full((1, 2), math.log(i + 1)), rtol=1e-5, atol=1e-6)
+
+
 # --------------------------------------------------------------------- T2 --
 @pytest.mark.parametrize("causal", [False, True])
 def test_zero_keys_give_uniform_weights(causal):

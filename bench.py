@@ -200,6 +200,40 @@ SCOREMOD_LEGS = (("softcap_d64_n2k", dict(seed=6200, B=4, H=16, S=2048, d=64, so
                  ("alibi_d64_n2k", dict(seed=6300, B=4, H=16, S=2048, d=64, alibi=True)))
 
 
+class PrefillVarlen:
+    """Chunked prefill of a packed batch (attn_fwd_varlen): 16 sequences of
+    U[512, 4096] new queries, each against a cached prefix of U[0, 2048] keys
+    plus itself, causal (bottom-right), Hq 32, Hkv 8, d 128."""
+
+    def __init__(self, torch, seed=7300, n_seq=16, Hq=32, Hkv=8, d=128):
+        import numpy as np
+        from online_softmax_monoid_amd import inputs
+        rng = np.random.Generator(np.random.PCG64(seed))
+        lq = rng.integers(512, 4096, size=n_seq, endpoint=True)
+        lk = lq + rng.integers(0, 2048, size=n_seq, endpoint=True)
+        self.cu_q = torch.tensor(np.concatenate([[0], np.cumsum(lq)]), dtype=torch.int32,
+                                 device="cuda")
+        self.cu_k = torch.tensor(np.concatenate([[0], np.cumsum(lk)]), dtype=torch.int32,
+                                 device="cuda")
+        self.dims = (n_seq, int(lq.sum()), int(lk.sum()), int(lq.max()), int(lk.max()), Hq, Hkv, d)
+        q, k, v = inputs.draw_prefill_bits(seed + 1, 1, Hq, Hkv, int(lq.sum()), int(lk.sum()), d)
+        self.q, self.k, self.v = dev_bits(q), dev_bits(k), dev_bits(v)
+        self.o = torch.empty(Hq * int(lq.sum()) * d, dtype=torch.int16, device="cuda")
+        self.lse = torch.empty(Hq * int(lq.sum()), dtype=torch.float32, device="cuda")
+        # causal pairs: row i of a sequence sees i + (Sk - Sq) + 1 keys
+        pairs = sum(int(a) * (int(b) - int(a)) + int(a) * (int(a) + 1) // 2 for a, b in zip(lq, lk))
+        self.flops = 4.0 * d * Hq * pairs
+        self.scale = inputs.default_scale(d)
+        self.shape = {"sequences": n_seq, "total_q": int(lq.sum()), "total_k": int(lk.sum()),
+                      "Hq": Hq, "Hkv": Hkv, "d": d, "causal": True}
+
+    def __call__(self, stream):
+        from online_softmax_monoid_amd import miattn
+        n, tq, tk, mq, mk, Hq, Hkv, d = self.dims
+        miattn.attn_fwd_varlen(self.q, self.k, self.v, self.o, self.lse, self.cu_q, self.cu_k, n,
+                               tq, tk, mq, mk, Hq, Hkv, d, True, self.scale, stream)
+
+
 class DecodePaged:
     """The decode workload with its cache in pages of ``page`` keys, pool
     pages in a seeded random order; two pool copies used alternately, as for
@@ -410,6 +444,19 @@ def main():
                          "shape": {k: v for k, v in cfg.items() if k != "seed"}}
         del sm
         torch.cuda.empty_cache()
+
+    vl = PrefillVarlen(torch)
+    time_launches(vl, stream, torch, 3)
+    vms = time_launches(vl, stream, torch, 10)
+    v_avg = sum(vms) / len(vms)
+    v_tf = vl.flops / (v_avg * 1e-3) / 1e12
+    log(f"bench: varlen_chunked_d128 {v_avg:.4f} ms ({v_tf:.1f} TFLOP/s)")
+    windows["varlen_chunked_d128"] = {"value": round(v_tf, 2), "unit": "TFLOP/s",
+                                      "ms": round(v_avg, 4),
+                                      "frac": round(v_tf / PEAK_BF16_TFLOPS, 4),
+                                      "shape": vl.shape}
+    del vl
+    torch.cuda.empty_cache()
 
     log("bench: paged decode (16-key pages)")
     dp = DecodePaged(inputs.WORKLOADS[DECODE_WID], torch)

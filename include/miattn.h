@@ -136,6 +136,39 @@ MIATTN_API int attn_fwd_ext(const void *q, const void *k, const void *v, void *o
                  float scale, hipStream_t stream);
 
 /*
+ * Prefill forward over a packed batch of sequences of different lengths
+ * (chunked prefill of several streams at once): attn_fwd applied to each
+ * sequence b on its own, with
+ *
+ *   q, o  bf16 [Hq,  total_q, d]   rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *                                  of each head are sequence b's queries
+ *   k, v  bf16 [Hkv, total_k, d]   rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1
+ *                                  are its keys
+ *   lse   f32  [Hq,  total_q]
+ *   cu_seqlens_q, cu_seqlens_k   int32 [B + 1] DEVICE arrays, non-decreasing,
+ *                                  starting at 0 and ending at total_q /
+ *                                  total_k. They are not inspected on the
+ *                                  host; on the device each sequence's range
+ *                                  is clamped into [0, total) and to
+ *                                  max_seqlen_q / max_seqlen_k rows, so bad
+ *                                  offsets give wrong values but no access
+ *                                  outside the tensors.
+ *
+ * Each sequence has its own Sq = its query count and Sk = its key count,
+ * with attn_fwd's bottom-right causal alignment (a chunk of new queries
+ * against its cached prefix plus itself when Sk > Sq). max_seqlen_q must be
+ * at least the longest query count (it sizes the launch). Head dimensions
+ * 128 and 256 (64: MIATTN_ERR_UNSUPPORTED); total_q * d * 2 and
+ * total_k * d * 2 below 2^31. B == 0, total_q == 0 or max_seqlen_q == 0:
+ * nothing to do.
+ */
+MIATTN_API int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o,
+                    float *lse, const int *cu_seqlens_q, const int *cu_seqlens_k,
+                    int B, int total_q, int total_k, int max_seqlen_q,
+                    int max_seqlen_k, int Hq, int Hkv, int d, int causal,
+                    float scale, hipStream_t stream);
+
+/*
  * Bytes of workspace attn_fwd_decode needs: B * Hq * num_splits * (d + 2) * 4
  * (one f32 partial state (m, l, acc[d]) per stream, head and split).
  * Returns 0 for invalid arguments.

@@ -265,8 +265,55 @@ int attn_fwd_decode_paged(const void *q, const void *k_pages, const void *v_page
     return hip_status(miattn::launch_decode(a, d, stream), "attn_fwd_decode_paged launch");
 }
 
+int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                    const int *cu_seqlens_q, const int *cu_seqlens_k, int B, int total_q,
+                    int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int d,
+                    int causal, float scale, hipStream_t stream)
+{
+    if (B < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+        return fail(MIATTN_ERR_INVALID_ARG,
+                    "sizes must be >= 0 (B=%d, total_q=%d, total_k=%d, max_seqlen_q=%d, "
+                    "max_seqlen_k=%d)", B, total_q, total_k, max_seqlen_q, max_seqlen_k);
+    MIATTN_TRY(check_heads_dim(Hq, Hkv, d));
+    if (d == 64)
+        return fail(MIATTN_ERR_UNSUPPORTED, "packed variable-length batches need d = 128 or 256");
+    MIATTN_TRY(check_scale(scale));
+    if ((int64_t)total_q * d * 2 >= ((int64_t)1 << 31) || (int64_t)total_k * d * 2 >= ((int64_t)1 << 31))
+        return fail(MIATTN_ERR_UNSUPPORTED,
+                    "one head's packed Q or K/V reaches 2 GiB (total_q=%d, total_k=%d, d=%d)",
+                    total_q, total_k, d);
+    if (B == 0 || total_q == 0 || max_seqlen_q == 0)
+        return MIATTN_OK;
+    MIATTN_TRY(check_ptr(q, "q", 16));
+    MIATTN_TRY(check_ptr(o, "o", 16));
+    MIATTN_TRY(check_ptr(lse, "lse", 4));
+    MIATTN_TRY(check_ptr(cu_seqlens_q, "cu_seqlens_q", 4));
+    MIATTN_TRY(check_ptr(cu_seqlens_k, "cu_seqlens_k", 4));
+    if (total_k > 0) {
+        MIATTN_TRY(check_ptr(k, "k", 16));
+        MIATTN_TRY(check_ptr(v, "v", 16));
+    }
+    miattn::FwdArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.o = static_cast<uint16_t *>(o);
+    a.lse = lse;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Sq = max_seqlen_q;
+    a.Sk = max_seqlen_k;
+    a.scale = scale;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.total_q = total_q;
+    a.total_k = total_k;
+    return hip_status(miattn::launch_fwd(a, d, causal != 0, stream), "attn_fwd_varlen launch");
+}
+
 const char *miattn_last_error(void) { return g_last_error.c_str(); }
 
-int miattn_version(void) { return 400; }
+int miattn_version(void) { return 500; }
 
 }  // extern "C"

@@ -24,6 +24,13 @@ struct FwdArgs {
     // with alibi[h] the slope of query head h (alibi != nullptr)
     float softcap = 0.f;
     const float *alibi = nullptr;
+    // packed variable-length batch (cu_q != nullptr): q, o [Hq, total_q, d],
+    // k, v [Hkv, total_k, d], lse [Hq, total_q]; sequence b's rows are
+    // [cu_q[b], cu_q[b+1]) and keys [cu_k[b], cu_k[b+1]); Sq, Sk hold the
+    // longest lengths
+    const int *cu_q = nullptr;
+    const int *cu_k = nullptr;
+    int total_q = 0, total_k = 0;
 };
 
 struct DecodeArgs {

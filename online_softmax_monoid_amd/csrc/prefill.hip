@@ -497,6 +497,8 @@ hipError_t launch(const FwdArgs &a, hipStream_t stream)
 
 hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
 {
+    if (a.cu_q != nullptr)  // packed variable-length batches: the persistent kernel only
+        return d == 64 ? hipErrorNotSupported : launch_fwd_q64(a, d, causal, stream);
     switch (d) {
     case 64:
         return causal ? launch<64, MIATTN_FWD_D64, true>(a, stream)

@@ -155,12 +155,14 @@ struct Item {
     int q_wg, kv_end, nblk;
     int kofs;  // key of the item's tile 0 (nonzero only with a sliding window)
     float slope;  // ALiBi slope of the query head over the scale (raw score units)
+    int sq, sk;   // query rows and keys of the item's sequence
+    bool live;    // the item has query rows (a packed batch has items past its sequences' ends)
 };
 
 // Score modifiers: none, soft cap, ALiBi
 enum { kModNone = 0, kModSoftcap = 1, kModAlibi = 2 };
 
-template <bool CAUSAL, int NWV, int D, int QB, int WPE, bool WIN, int MOD>
+template <bool CAUSAL, int NWV, int D, int QB, int WPE, bool WIN, int MOD, bool VARLEN>
 __global__ void __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 {
@@ -193,11 +195,13 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     const int l32 = lane & 31;
     const int g = lane >> 5;
 
-    const int Sq = a.Sq, Sk = a.Sk;
-    const int diag = Sk - Sq;
+    // query rows and keys of the current item's sequence (all items share them
+    // unless the batch is packed with variable lengths)
+    int Sq = a.Sq, Sk = a.Sk;
+    int diag = Sk - Sq;
     // WIN: sliding window (a separate instantiation, so that the kernel
     // without one carries none of its work); query i sees keys from i + wlo on
-    const int wlo = WIN ? diag - a.window : 0;
+    int wlo = WIN ? diag - a.window : 0;
     const int G = a.Hq / a.Hkv;
 
     // ---- schedule --------------------------------------------------------------------
@@ -233,17 +237,36 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         const int kvh = to.unit - b * a.Hkv;
         const int hq = kvh * G + to.gq;
         Item it;
-        it.qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
+        int64_t kbase;
+        if constexpr (VARLEN) {
+            // sequence b of a packed batch; offsets clamped into the tensors
+            // (at most the longest length), so no access leaves them
+            const int q_lo = min(max(a.cu_q[b], 0), a.total_q);
+            const int q_hi = min(max(a.cu_q[b + 1], q_lo), a.total_q);
+            const int k_lo = min(max(a.cu_k[b], 0), a.total_k);
+            const int k_hi = min(max(a.cu_k[b + 1], k_lo), a.total_k);
+            it.sq = min(q_hi - q_lo, a.Sq);
+            it.sk = min(k_hi - k_lo, a.Sk);
+            it.qrow0 = (int64_t)hq * a.total_q + q_lo;
+            kbase = (int64_t)kvh * a.total_k + k_lo;
+        } else {
+            it.sq = a.Sq;
+            it.sk = a.Sk;
+            it.qrow0 = ((int64_t)b * a.Hq + hq) * a.Sq;
+            kbase = ((int64_t)b * a.Hkv + kvh) * a.Sk;
+        }
+        const int dg = it.sk - it.sq;
         it.slope = MOD == kModAlibi ? a.alibi[hq] / a.scale : 0.f;
         it.q_wg = to.qtile * BM;
-        const int q_wg_last = min(it.q_wg + BM, Sq) - 1;
-        const int kv_end = CAUSAL ? min(Sk, max(0, q_wg_last + diag + 1)) : Sk;
+        it.live = it.q_wg < it.sq;
+        const int q_wg_last = min(it.q_wg + BM, it.sq) - 1;
+        const int kv_end = CAUSAL ? min(it.sk, max(0, q_wg_last + dg + 1)) : it.sk;
         // With a sliding window the item's keys start at the tile holding its
         // first row's first visible key; tiles below it are hidden from every
         // row and never copied. Tile indices and key counts of the item count
         // from that tile's first key.
-        it.kofs = WIN ? min(kv_end, max(0, it.q_wg + diag - a.window)) / BN * BN : 0;
-        it.krow0 = ((int64_t)b * a.Hkv + kvh) * Sk + it.kofs;
+        it.kofs = WIN ? min(kv_end, max(0, it.q_wg + dg - a.window)) / BN * BN : 0;
+        it.krow0 = kbase + it.kofs;
         it.kv_end = kv_end - it.kofs;
         it.nblk = (it.kv_end + BN - 1) / BN;
         return it;
@@ -366,8 +389,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     bf16x8 qf[QB][KKN];
     // Q rows of an item (query head rows from qrow0_, the wave's first row q0w)
     // straight from global memory into the fragments; rows >= Sq read as 0
-    auto load_q = [&](int64_t qrow0_, int q0w) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0_ * D, (uint32_t)Sq * D * 2);
+    auto load_q = [&](int64_t qrow0_, int q0w, int sq_) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0_ * D, (uint32_t)sq_ * D * 2);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const uint32_t off = (uint32_t)(q0w + 32 * qb + l32) * D * 2 + 16 * g;
@@ -565,7 +588,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     constexpr bool QPREF = (D == 256);
     auto prologue = [&](int kmiss, int vmiss) __attribute__((always_inline)) {
         if constexpr (!QPREF)
-            load_q(qrow0, q0);
+            load_q(qrow0, q0, Sq);
         if (!QPREF || kmiss > 0 || vmiss > 0) {
             for (int t = 0; t < kmiss; ++t)
                 dma_k(ph + t, a.k + (krow0 + t * BN) * D, kv_end - t * BN);
@@ -799,22 +822,47 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 
     // ---- the items of this workgroup ----------------------------------------------
     int kmiss = RING, vmiss = RING - 1;  // first tiles of the current item not yet copied
-    int id = item_id(0);
-    Item nx = describe(id < n_items ? id : 0);
+    // the walk's next item from round r on (a packed batch skips items past
+    // its sequences' ends)
+    auto next_item = [&](int &r, Item &it) __attribute__((always_inline)) {
+        int id_ = item_id(r);
+        if (id_ < n_items)
+            it = describe(id_);
+        if constexpr (VARLEN) {
+            while (id_ < n_items && !it.live) {
+                id_ = item_id(++r);
+                if (id_ < n_items)
+                    it = describe(id_);
+            }
+        }
+        return id_;
+    };
+    int r = 0;
+    Item nx = describe(0);
+    int id = next_item(r, nx);
     if constexpr (QPREF)
-        load_q(nx.qrow0, nx.q_wg + wave * 32 * QB);
-    for (int r = 0; id < n_items; ++r) {
+        load_q(nx.qrow0, nx.q_wg + wave * 32 * QB, nx.sq);
+    int sq_n = 0;
+    while (id < n_items) {
         const Item cur = nx;
-        const int id_n = item_id(r + 1);
+        int r_n = r + 1;
+        const int id_n = next_item(r_n, nx);
         has_next = id_n < n_items;
         kv_end_n = 0;
         if (has_next) {
-            nx = describe(id_n);
+            sq_n = nx.sq;
             qrow0_n = nx.qrow0;
             kv_end_n = nx.kv_end;
             q_wg_n = nx.q_wg;
             kn = a.k + nx.krow0 * D;
             vn = a.v + nx.krow0 * D;
+        }
+        if constexpr (VARLEN) {
+            Sq = cur.sq;
+            Sk = cur.sk;
+            diag = Sk - Sq;
+            if constexpr (WIN)
+                wlo = diag - a.window;
         }
         qrow0 = cur.qrow0;
         krow0 = cur.krow0;
@@ -892,13 +940,14 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
             mstep(j, sA, sB, pA, pB);
         // the last QK has used Q: the next item's rows load during the epilogue
         if (QPREF && has_next)
-            load_q(qrow0_n, q_wg_n + wave * 32 * QB);
+            load_q(qrow0_n, q_wg_n + wave * 32 * QB, sq_n);
         epilogue();
 
         kmiss = max(0, RING - nblk);
         vmiss = max(0, RING - 1 - nblk);
         ph = (ph + nblk) & (RING - 1);
         id = id_n;
+        r = r_n;
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy may still target LDS
 }
@@ -921,10 +970,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 
 // One workgroup per resident slot (a multiple of 8, so that each XCD holds the
 // same number), each walking its share of the n_items work items.
-template <bool CAUSAL, int D, int QB, int NWV, int WPE, bool WIN, int MOD>
+template <bool CAUSAL, int D, int QB, int NWV, int WPE, bool WIN, int MOD, bool VARLEN = false>
 hipError_t launch_q64_t(const FwdArgs &a, int n_qtiles, int n_items, hipStream_t stream)
 {
-    const auto kernel = fwd_q64_kernel<CAUSAL, NWV, D, QB, WPE, WIN, MOD>;
+    const auto kernel = fwd_q64_kernel<CAUSAL, NWV, D, QB, WPE, WIN, MOD, VARLEN>;
     const int resident = resident_workgroups(kernel, 64 * NWV);
     if (resident < 8)
         return hipErrorInvalidConfiguration;
@@ -956,6 +1005,12 @@ hipError_t launch_q64(const FwdArgs &a, bool causal, hipStream_t stream)
     if (n_items == 0)
         return hipSuccess;
     const int n = (int)n_items;
+    if (a.cu_q != nullptr) {  // packed variable-length batch: no window or modifier
+        if (a.window >= 0 || a.softcap > 0.f || a.alibi != nullptr)
+            return hipErrorNotSupported;
+        return causal ? launch_q64_t<true, D, QB, NWV, WPE, false, kModNone, true>(a, n_qtiles, n, stream)
+                      : launch_q64_t<false, D, QB, NWV, WPE, false, kModNone, true>(a, n_qtiles, n, stream);
+    }
     if constexpr (QB == 1) {
         if (a.softcap > 0.f)
             return dispatch_win<D, QB, NWV, WPE, kModSoftcap>(a, causal, n_qtiles, n, stream);

@@ -156,6 +156,30 @@ def attn_decode(q_bits, kc_bits, vc_bits, lens, scale: float, nthreads: int = 0)
     return o[:B * Hq].reshape(B, Hq, d), lse[:B * Hq].reshape(B, Hq)
 
 
+def attn_fwd_varlen(q_bits, k_bits, v_bits, cu_q, cu_k, causal: bool, scale: float,
+                    nthreads: int = 0):
+    """A packed batch of sequences: q [Hq, total_q, d], k / v [Hkv, total_k, d];
+    sequence b is rows cu_q[b] .. cu_q[b+1]-1 against keys cu_k[b] .. cu_k[b+1]-1,
+    each the plain attention of attn_fwd on its own. Returns o [Hq, total_q, d]
+    and lse [Hq, total_q] (f64)."""
+    q = _u16(q_bits)
+    k = _u16(k_bits)
+    v = _u16(v_bits)
+    Hq, total_q, d = q.shape
+    Hkv, total_k, _ = k.shape
+    o = np.zeros((Hq, total_q, d), dtype=np.float64)
+    lse = np.full((Hq, total_q), -np.inf, dtype=np.float64)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if q1 == q0:
+            continue
+        ob, lb = attn_fwd(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1], causal,
+                          scale, nthreads=nthreads)
+        o[:, q0:q1] = ob[0]
+        lse[:, q0:q1] = lb[0]
+    return o, lse
+
+
 def gather_pages(pool_bits, block_table, lens, page_size: int):
     """The gather view of a paged cache (tang paper, §2.1 "Views": a read whose
     source coordinate comes from an index tensor; paged KV caches are its

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_workspace_size():
-    assert M.miattn_version() == 400
+    assert M.miattn_version() == 500
     assert M.attn_fwd_decode_workspace_size(32, 32, 128, 16) == 32 * 32 * 16 * 130 * 4
     assert M.attn_fwd_decode_workspace_size(0, 32, 128, 16) == 0
     assert M.attn_fwd_decode_workspace_size(1, 0, 128, 16) == 0
@@ -110,6 +110,25 @@ def test_attn_fwd_ext_rejects(softcap, alibi, status, needle):
     assert L.attn_fwd_ext(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 8, 8, 64, 1, -1, softcap,
                           alibi, 0.125, 0) == status
     assert needle in M.miattn_last_error()
+
+
+def test_attn_fwd_varlen_rejects():
+    L = M.load()
+    args = lambda **kw: [kw.get(n, dv) for n, dv in (
+        ("q", FAKE), ("k", FAKE), ("v", FAKE), ("o", FAKE), ("lse", FAKE), ("cq", FAKE),
+        ("ck", FAKE), ("B", 2), ("tq", 100), ("tk", 120), ("mq", 60), ("mk", 70), ("Hq", 4),
+        ("Hkv", 2), ("d", 128), ("causal", 1), ("scale", 0.1), ("stream", 0))]
+    for kw, status, needle in [
+            (dict(d=64), M.MIATTN_ERR_UNSUPPORTED, "d = 128 or 256"),
+            (dict(cq=0), M.MIATTN_ERR_INVALID_ARG, "cu_seqlens_q is NULL"),
+            (dict(ck=FAKE + 2), M.MIATTN_ERR_INVALID_ARG, "aligned"),
+            (dict(tq=-1), M.MIATTN_ERR_INVALID_ARG, "sizes"),
+            (dict(mk=-3), M.MIATTN_ERR_INVALID_ARG, "sizes"),
+            (dict(Hq=3), M.MIATTN_ERR_INVALID_ARG, "multiple"),
+            (dict(tq=1 << 23), M.MIATTN_ERR_UNSUPPORTED, "2 GiB")]:
+        assert L.attn_fwd_varlen(*args(**kw)) == status, kw
+        assert needle in M.miattn_last_error()
+    assert L.attn_fwd_varlen(*args(q=0, k=0, v=0, o=0, lse=0, cq=0, ck=0, B=0)) == M.MIATTN_OK
 
 
 def _dec(**kw):

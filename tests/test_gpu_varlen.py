@@ -1,0 +1,136 @@
+"""GPU: packed variable-length batches (attn_fwd_varlen) against the f64 oracle.
+
+Sequences of 0 to 1000 query rows and as many or more keys (a chunk of new
+queries against its cached prefix), causal and not, head dimensions 128 and
+256, GQA; max_seqlen_q above the longest sequence (the launch's items past a
+sequence's end are skipped); more work items than resident workgroups. A
+batch of equal lengths must match attn_fwd on the same data bit for bit.
+Tolerances as for attn_fwd.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from online_softmax_monoid_amd import inputs
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _bits(seed, shape, std=0.5):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return inputs.bf16_bits(rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std))
+
+
+def _run(q, k, v, cu_q, cu_k, max_q, max_k, causal, scale):
+    torch = H.torch_mod()
+    Hq, total_q, d = q.shape
+    Hkv, total_k, _ = k.shape
+    n = Hq * total_q
+    o, lse = H.nan_out(n * d, n)
+    cq = torch.tensor(cu_q, dtype=torch.int32, device="cuda")
+    ck = torch.tensor(cu_k, dtype=torch.int32, device="cuda")
+    H.miattn.attn_fwd_varlen(H.dev_bits(q), H.dev_bits(k), H.dev_bits(v), o, lse, cq, ck,
+                             len(cu_q) - 1, total_q, total_k, max_q, max_k, Hq, Hkv, d, causal,
+                             scale)
+    torch.cuda.synchronize()
+    ob = H.host_bits(o)
+    lh = lse.cpu().numpy()
+    guards = bool(np.all(ob[n * d:] == H.NAN_BF16) and np.all(np.isnan(lh[n:])))
+    return ob[:n * d].reshape(Hq, total_q, d), lh[:n].reshape(Hq, total_q), guards
+
+
+VARLEN = [
+    # seed, query lengths, extra cached keys per sequence, Hq, Hkv, d, causal
+    (1, [0, 1, 31, 32, 33, 257, 700], [0, 0, 0, 5, 100, 0, 64], 4, 2, 128, True),
+    (2, [0, 1, 31, 32, 33, 257, 700], [0, 3, 0, 0, 0, 9, 0], 4, 2, 128, False),
+    (3, [5, 300, 129, 1000], [0, 200, 0, 17], 4, 1, 256, True),
+    (4, [64, 65, 190], [1, 0, 300], 2, 2, 256, False),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN)
+def test_varlen_parity(case):
+    seed, lq, extra, Hq, Hkv, d, causal = case
+    lk = [a + b for a, b in zip(lq, extra)]
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q = _bits(seed * 10, (Hq, int(cu_q[-1]), d))
+    k = _bits(seed * 10 + 1, (Hkv, int(cu_k[-1]), d))
+    v = _bits(seed * 10 + 2, (Hkv, int(cu_k[-1]), d))
+    scale = inputs.default_scale(d)
+    label = f"varlen {case}"
+    _note(f"[gpu] {label}: running the HIP path")
+    o, lse, guards = _run(q, k, v, cu_q, cu_k, max(lq) + 100, max(lk) + 100, causal, scale)
+    assert guards, f"{label}: write outside the logical outputs"
+    o_ref, lse_ref = oracle.attn_fwd_varlen(q, k, v, cu_q, cu_k, causal, scale)
+    m = H.metrics(o, lse, o_ref, lse_ref)
+    _note(f"[gpu] {label}: {m}")
+    H.assert_parity(m, label)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_varlen_equal_lengths_match_attn_fwd(d):
+    B, Hq, Hkv, S = 3, 4, 2, 300
+    q = _bits(40 + d, (B, Hq, S, d))
+    k = _bits(41 + d, (B, Hkv, S, d))
+    v = _bits(42 + d, (B, Hkv, S, d))
+    pack = lambda x: np.ascontiguousarray(x.transpose(1, 0, 2, 3).reshape(x.shape[1], -1, d))
+    cu = (np.arange(B + 1) * S).astype(np.int32)
+    scale = inputs.default_scale(d)
+    for causal in (False, True):
+        o0, l0, _ = H.run_fwd(q, k, v, causal, scale)
+        o1, l1, guards = _run(pack(q), pack(k), pack(v), cu, cu, S, S, causal, scale)
+        assert guards
+        assert np.array_equal(o1, o0.transpose(1, 0, 2, 3).reshape(Hq, B * S, d))
+        assert np.array_equal(l1.view(np.uint32),
+                              l0.transpose(1, 0, 2).reshape(Hq, B * S).view(np.uint32))
+
+
+def test_varlen_many_sequences_sampled():
+    """40 sequences, lengths U[0, 1200], GQA 4: more items than resident
+    workgroups; every sequence's rows checked on a sample."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    lq = rng.integers(0, 1200, size=40, endpoint=True)
+    lk = lq + rng.integers(0, 300, size=40, endpoint=True)
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    Hq, Hkv, d = 16, 4, 128
+    q = _bits(78, (Hq, int(cu_q[-1]), d))
+    k = _bits(79, (Hkv, int(cu_k[-1]), d))
+    v = _bits(80, (Hkv, int(cu_k[-1]), d))
+    scale = inputs.default_scale(d)
+    _note("[gpu] varlen 40 sequences: running the HIP path")
+    o, lse, guards = _run(q, k, v, cu_q, cu_k, int(lq.max()), int(lk.max()), True, scale)
+    assert guards
+    # two sampled rows per (head, sequence) plus its first and last
+    picks = []
+    for b in range(40):
+        if lq[b] == 0:
+            continue
+        rows = {0, int(lq[b]) - 1, *rng.integers(0, lq[b], size=2).tolist()}
+        picks += [(b, r) for r in sorted(rows)]
+    o_ref = np.zeros((Hq, len(picks), d))
+    l_ref = np.zeros((Hq, len(picks)))
+    o_got = np.zeros((Hq, len(picks), d), dtype=np.uint16)
+    l_got = np.zeros((Hq, len(picks)), dtype=np.float32)
+    for n, (b, r) in enumerate(picks):
+        q0, k0, k1 = int(cu_q[b]), int(cu_k[b]), int(cu_k[b + 1])
+        # the row's own attention: Sq = lq[b], Sk = lk[b], row r of the sequence
+        rows = np.arange(Hq) * int(lq[b]) + r
+        ob, lb = oracle.attn_fwd(q[None, :, q0:q0 + int(lq[b])], k[None, :, k0:k1],
+                                 v[None, :, k0:k1], True, scale, rows=rows)
+        o_ref[:, n], l_ref[:, n] = ob, lb
+        o_got[:, n], l_got[:, n] = o[:, q0 + r], lse[:, q0 + r]
+    m = H.metrics(o_got, l_got, o_ref, l_ref)
+    _note(f"[gpu] varlen 40 sequences: {m}")
+    H.assert_parity(m, "varlen 40 sequences")

@@ -135,6 +135,51 @@ def test_wide_window_equals_no_window():
         assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
 
 
+# ------------------------------------------------------------- varlen --
+def test_varlen_equal_lengths_equal_the_batch():
+    """A batch of equal-length sequences packed head-major ([H, B*S, d]) gives
+    the batched result row for row (a wrong slice or transpose fails)."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    B, Hq, Hkv, Sq, Sk, d = 3, 4, 2, 9, 13, 8
+    q = _rand_bits(rng, (B, Hq, Sq, d))
+    k = _rand_bits(rng, (B, Hkv, Sk, d))
+    v = _rand_bits(rng, (B, Hkv, Sk, d))
+    pack = lambda x: np.ascontiguousarray(x.transpose(1, 0, 2, 3).reshape(x.shape[1], -1, d))
+    cu_q, cu_k = np.arange(B + 1) * Sq, np.arange(B + 1) * Sk
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd(q, k, v, causal, 0.25)
+        ov, lv = oracle.attn_fwd_varlen(pack(q), pack(k), pack(v), cu_q, cu_k, causal, 0.25)
+        assert np.array_equal(ov, o.transpose(1, 0, 2, 3).reshape(Hq, B * Sq, d))
+        assert np.array_equal(lv, lse.transpose(1, 0, 2).reshape(Hq, B * Sq))
+
+
+def test_varlen_brute_force_tiny():
+    """Ragged sequences (one with no rows, one with no keys), each against
+    brute force on the rows and keys read out of the packed arrays by index."""
+    rng = np.random.Generator(np.random.PCG64(32))
+    Hq, Hkv, d = 2, 1, 4
+    cu_q = [0, 3, 3, 8, 10]
+    cu_k = [0, 5, 7, 12, 12]
+    q = _rand_bits(rng, (Hq, cu_q[-1], d))
+    k = _rand_bits(rng, (Hkv, cu_k[-1], d))
+    v = _rand_bits(rng, (Hkv, cu_k[-1], d))
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_varlen(q, k, v, cu_q, cu_k, causal, 0.5)
+        for b in range(4):
+            rows = range(cu_q[b], cu_q[b + 1])
+            keys = range(cu_k[b], cu_k[b + 1])
+            if not rows:
+                continue
+            qq = [[[[int(x) for x in q[h, i]] for i in rows] for h in range(Hq)]]
+            kk = [[[[int(x) for x in k[g, j]] for j in keys] for g in range(Hkv)]]
+            vv = [[[[int(x) for x in v[g, j]] for j in keys] for g in range(Hkv)]]
+            bo, bl = brute.attention(qq, kk, vv, causal, 0.5)
+            for h in range(Hq):
+                for n, i in enumerate(rows):
+                    _close(o[h, i], bo[0][h][n])
+                    _close(lse[h, i], bl[0][h][n])
+
+
 # ------------------------------------------------------- score modifiers --
 MOD_CASES = [
     # B, Hq, Hkv, Sq, Sk, d, causal, window, softcap, alibi slopes (or None)

@@ -234,6 +234,32 @@ class PrefillVarlen:
                                tq, tk, mq, mk, Hq, Hkv, d, True, self.scale, stream)
 
 
+class Backward:
+    """attn_bwd on the prefill workload (B2 H32 S4096 d128 causal), fed by the
+    GPU forward's O and LSE and a seeded N(0, 1) upstream gradient.
+    Algorithmic flops: five products of the forward's size (S, dP, dV, dK,
+    dQ), 2.5 times the forward's."""
+
+    def __init__(self, pre, torch):
+        from online_softmax_monoid_amd import inputs
+        w = pre.w
+        self.pre = pre
+        pre(torch.cuda.current_stream())
+        (do,) = inputs.draw_prefill_bits(w.seed + 11, w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d)[:1]
+        self.do = dev_bits(do)
+        nq, nk = w.B * w.Hq * w.Sq * w.d, w.B * w.Hkv * w.Sk * w.d
+        self.dq = torch.empty(nq, dtype=torch.int16, device="cuda")
+        self.dk = torch.empty(nk, dtype=torch.int16, device="cuda")
+        self.dv = torch.empty(nk, dtype=torch.int16, device="cuda")
+        self.flops = 2.5 * pre.flops
+
+    def __call__(self, stream):
+        from online_softmax_monoid_amd import miattn
+        p, w = self.pre, self.pre.w
+        miattn.attn_bwd(p.q, p.k, p.v, p.o, p.lse, self.do, self.dq, self.dk, self.dv, w.B, w.Hq,
+                        w.Hkv, w.Sq, w.Sk, w.d, p.causal, w.scale, stream)
+
+
 class DecodePaged:
     """The decode workload with its cache in pages of ``page`` keys, pool
     pages in a seeded random order; two pool copies used alternately, as for
@@ -402,7 +428,13 @@ def main():
     dec_gbs = dec.bytes / (dec_avg * 1e-3) / 1e9
     log(f"bench: prefill {pre_avg:.4f} ms ({tflops:.1f} TFLOP/s), decode {dec_avg:.4f} ms "
         f"({dec_gbs:.0f} GB/s)")
-    del pre
+    bwd = Backward(pre, torch)
+    time_launches(bwd, stream, torch, 2)
+    bms = time_launches(bwd, stream, torch, 5)
+    b_avg = sum(bms) / len(bms)
+    b_tf = bwd.flops / (b_avg * 1e-3) / 1e12
+    log(f"bench: backward d128 {b_avg:.4f} ms ({b_tf:.1f} TFLOP/s)")
+    del bwd, pre
     torch.cuda.empty_cache()
 
     log("bench: long-context GQA workload")
@@ -510,6 +542,9 @@ def main():
         "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "ms": round(dec_avg, 4),
                    "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "bound": "hbm",
                    "algorithmic_bytes": dec.bytes},
+        "backward_d128": {"value": round(b_tf, 2), "unit": "TFLOP/s", "ms": round(b_avg, 4),
+                          "frac": round(b_tf / PEAK_BF16_TFLOPS, 4),
+                          "flops": "2.5 x the forward's (S, dP, dV, dK, dQ)"},
         "long_context_gqa_d256": {"value": round(l_tflops, 2), "unit": "TFLOP/s",
                                   "ms": round(l_avg, 3),
                                   "frac": round(l_tflops / PEAK_BF16_TFLOPS, 4)},

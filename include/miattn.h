@@ -169,6 +169,28 @@ MIATTN_API int attn_fwd_varlen(const void *q, const void *k, const void *v, void
                     float scale, hipStream_t stream);
 
 /*
+ * Prefill backward: the gradients of attn_fwd's O with respect to Q, K and V,
+ * given the forward's O and LSE and the upstream gradient dout (the flash
+ * backward: P is recomputed from LSE, and the softmax gradient uses
+ * D_i = dout_i . O_i; the tang paper, §3 "Gradients are comprehensions").
+ *
+ *   q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, scale: as for attn_fwd
+ *              (o and lse are attn_fwd's outputs for these inputs)
+ *   dout  bf16 [B, Hq,  Sq, d]   upstream gradient
+ *   dq    bf16 [B, Hq,  Sq, d]   written
+ *   dk    bf16 [B, Hkv, Sk, d]   written (summed over the Hq/Hkv query heads
+ *   dv    bf16 [B, Hkv, Sk, d]   written  that read each kv-head)
+ *
+ * f32 accumulation, bf16 results. Head dimensions 64 and 128 (256:
+ * MIATTN_ERR_UNSUPPORTED). Keys no query sees get zero gradients; rows with
+ * no visible key (LSE = -inf) contribute nothing.
+ */
+MIATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void *o,
+             const float *lse, const void *dout, void *dq, void *dk, void *dv,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
+             float scale, hipStream_t stream);
+
+/*
  * Bytes of workspace attn_fwd_decode needs: B * Hq * num_splits * (d + 2) * 4
  * (one f32 partial state (m, l, acc[d]) per stream, head and split).
  * Returns 0 for invalid arguments.

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmiattn.so")
-SOURCES = ["api.cpp", "prefill.hip", "prefill_q64.hip", "prefill_pingpong.hip", "decode.hip"]
+SOURCES = ["api.cpp", "prefill.hip", "prefill_q64.hip", "prefill_pingpong.hip", "decode.hip",
+           "backward.hip"]
 ARCH = "gfx950"
 
 

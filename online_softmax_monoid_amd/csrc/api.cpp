@@ -312,8 +312,55 @@ int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float 
     return hip_status(miattn::launch_fwd(a, d, causal != 0, stream), "attn_fwd_varlen launch");
 }
 
+int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             const void *dout, void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Sq,
+             int Sk, int d, int causal, float scale, hipStream_t stream)
+{
+    if (B < 0 || Sq < 0 || Sk < 0)
+        return fail(MIATTN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d, Sq=%d, Sk=%d)", B, Sq, Sk);
+    MIATTN_TRY(check_heads_dim(Hq, Hkv, d));
+    if (d == 256)
+        return fail(MIATTN_ERR_UNSUPPORTED, "the backward supports d = 64 and 128");
+    MIATTN_TRY(check_scale(scale));
+    if ((int64_t)Sq * d * 2 >= ((int64_t)1 << 31) || (int64_t)Sk * d * 2 >= ((int64_t)1 << 31))
+        return fail(MIATTN_ERR_UNSUPPORTED,
+                    "one head's Q or K/V slice reaches 2 GiB (Sq=%d, Sk=%d, d=%d)", Sq, Sk, d);
+    if (B == 0 || (Sq == 0 && Sk == 0))
+        return MIATTN_OK;
+    if (Sq > 0) {
+        MIATTN_TRY(check_ptr(q, "q", 16));
+        MIATTN_TRY(check_ptr(o, "o", 16));
+        MIATTN_TRY(check_ptr(dout, "dout", 16));
+        MIATTN_TRY(check_ptr(lse, "lse", 4));
+        MIATTN_TRY(check_ptr(dq, "dq", 16));
+    }
+    if (Sk > 0) {
+        MIATTN_TRY(check_ptr(k, "k", 16));
+        MIATTN_TRY(check_ptr(v, "v", 16));
+        MIATTN_TRY(check_ptr(dk, "dk", 16));
+        MIATTN_TRY(check_ptr(dv, "dv", 16));
+    }
+    miattn::BwdArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.o = static_cast<const uint16_t *>(o);
+    a.dout = static_cast<const uint16_t *>(dout);
+    a.lse = lse;
+    a.dq = static_cast<uint16_t *>(dq);
+    a.dk = static_cast<uint16_t *>(dk);
+    a.dv = static_cast<uint16_t *>(dv);
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Sq = Sq;
+    a.Sk = Sk;
+    a.scale = scale;
+    return hip_status(miattn::launch_bwd(a, d, causal != 0, stream), "attn_bwd launch");
+}
+
 const char *miattn_last_error(void) { return g_last_error.c_str(); }
 
-int miattn_version(void) { return 500; }
+int miattn_version(void) { return 600; }
 
 }  // extern "C"

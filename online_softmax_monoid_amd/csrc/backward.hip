@@ -1,0 +1,375 @@
+// backward.hip -- attention backward on gfx950: gradients dQ, dK, dV of the
+// prefill forward from the saved log-sum-exp (the flash backward; the tang
+// paper derives it as a comprehension, §3 "Gradients are comprehensions"):
+//
+//   P_ij  = exp(scale q_i.k_j - LSE_i)   (0 where the forward masks)
+//   D_i   = dO_i . O_i
+//   dS_ij = P_ij (dO_i.v_j - D_i)
+//   dV_j  = sum_i P_ij dO_i      dK_j = scale sum_i dS_ij q_i
+//   dQ_i  = scale sum_j dS_ij k_j
+//
+// Two kernels, no atomics: one wave per 32-key tile accumulates dK and dV over
+// the query heads of its kv-head and their query tiles; one wave per 32-row
+// query tile accumulates dQ over the key tiles. Every product is a
+// v_mfma_f32_32x32x16_bf16 with f32 accumulation. As in the forward, a score
+// accumulator holds, in lane l, one column (l % 32) and the 16 rows
+// 8(r/4) + 4(l/32) + r%4 of its registers r; its registers packed to bf16
+// are then directly the A operand of the next product over those rows, with
+// the other operand read in the same permuted row order. Only the operands
+// that need a transpose (Q and dO for dK/dV, K for dQ) pass through LDS.
+// Fragments are read from global memory by buffer loads, so rows past the
+// ends read as zeros.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace miattn {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+union Frag8 {
+    bf16x8 v;
+    uint4 u;
+    uint32_t w[4];
+    uint16_t h[8];
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+    bf16x2 p;
+    p[0] = (__bf16)lo;
+    p[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) { return (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// 16 bytes of row `row`, dims 16 kk + 8 g .. +7 (a fragment of the 32 x 16
+// A operand, or of the 16 x 32 B operand read by rows)
+template <int D>
+__device__ __forceinline__ bf16x8 frag(__amdgpu_buffer_rsrc_t r, int row, int kk, int g)
+{
+    Frag8 f;
+    f.u = buf_load16(r, (uint32_t)(row * D + 16 * kk + 8 * g) * 2);
+    return f.v;
+}
+
+// registers 8c .. 8c+7 of an accumulator as the bf16 A operand over rows
+// 16c + 4g + 0..3 and 16c + 8 + 4g + 0..3
+__device__ __forceinline__ bf16x8 pack_chunk(const f32x16 &x, int c)
+{
+    Frag8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        f.w[i] = pack_bf16x2(x[8 * c + 2 * i], x[8 * c + 2 * i + 1]);
+    return f.v;
+}
+
+// B operand over the same permuted rows from a transposed LDS tile t[dim][row]
+// (row stride TS): lane l gives dim n, rows 16c + 4g .. +3 and 16c + 8 + 4g .. +3
+template <int TS>
+__device__ __forceinline__ bf16x8 read_t(const uint16_t *t, int n, int c, int g)
+{
+    Frag8 f;
+    const uint2 a = *(const uint2 *)(t + n * TS + 16 * c + 4 * g);
+    const uint2 b = *(const uint2 *)(t + n * TS + 16 * c + 8 + 4 * g);
+    f.w[0] = a.x;
+    f.w[1] = a.y;
+    f.w[2] = b.x;
+    f.w[3] = b.y;
+    return f.v;
+}
+
+// the 8 values of a row fragment written transposed: t[16kk + 8g + e][row]
+template <int TS>
+__device__ __forceinline__ void write_t(uint16_t *t, bf16x8 v, int row, int kk, int g)
+{
+    Frag8 f;
+    f.v = v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        t[(16 * kk + 8 * g + e) * TS + row] = f.h[e];
+}
+
+constexpr int TS = 36;  // transposed tiles: 32 rows + 4 of padding (bank spread)
+
+// ---- dK, dV: one wave per (b, kv-head, 32-key tile) ----------------------------
+// S = Q K^T and dP = dO V^T put the key in the lane (column) and 16 query rows
+// in the registers; P and dS packed by registers are the A operands of
+// dV += P^T dO and dK += dS^T Q over those rows, with dO and Q read
+// transposed from LDS.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdArgs a, int n_ktiles)
+{
+    constexpr int KK = D / 16, DB = D / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t sQT[D * TS];
+    __shared__ __attribute__((aligned(16))) uint16_t sDT[D * TS];
+    __shared__ float sL[32], sDv[32];
+
+    const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
+    int id = blockIdx.x;
+    const int kt = id % n_ktiles;
+    id /= n_ktiles;
+    const int kvh = id % a.Hkv;
+    const int b = id / a.Hkv;
+    const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq, G = a.Hq / a.Hkv;
+    const int j0 = 32 * kt;
+    const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
+    const float c = a.scale * kLog2e;
+
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + krow0 * D, (uint32_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + krow0 * D, (uint32_t)Sk * D * 2);
+    bf16x8 kf[KK], vf[KK];  // B operands: key j0 + l32, dims 16kk + 8g
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        kf[kk] = frag<D>(rk, j0 + l32, kk, g);
+        vf[kk] = frag<D>(rv, j0 + l32, kk, g);
+    }
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            dk[db][r] = dv[db][r] = 0.f;
+
+    // query tiles that see any key of this tile: rows i with j0 <= i + diag
+    const int i_first = CAUSAL ? max(0, j0 - diag) : 0;
+    const int qt0 = i_first / 32, nqt = (Sq + 31) / 32;
+    const int my_key = j0 + l32;
+    for (int h = 0; h < G; ++h) {
+        const int hq = kvh * G + h;
+        const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0 * D, (uint32_t)Sq * D * 2);
+        const __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout + qrow0 * D, (uint32_t)Sq * D * 2);
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o + qrow0 * D, (uint32_t)Sq * D * 2);
+        for (int qt = qt0; qt < nqt; ++qt) {
+            const int i0 = 32 * qt;
+            bf16x8 qa[KK], da[KK];  // A operands: row i0 + l32, dims 16kk + 8g
+            float dot = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                qa[kk] = frag<D>(rq, i0 + l32, kk, g);
+                da[kk] = frag<D>(rdo, i0 + l32, kk, g);
+                const bf16x8 of = frag<D>(ro, i0 + l32, kk, g);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    dot += (float)da[kk][e] * (float)of[e];
+            }
+            dot += __shfl_xor(dot, 32, 64);  // D_i over both halves of the dims
+            __syncthreads();  // the previous tile's LDS reads are done
+            if (g == 0) {
+                const int i = i0 + l32;
+                sDv[l32] = dot;
+                sL[l32] = i < Sq ? a.lse[qrow0 + i] : -INFINITY;
+            }
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                write_t<TS>(sQT, qa[kk], l32, kk, g);
+                write_t<TS>(sDT, da[kk], l32, kk, g);
+            }
+            __syncthreads();
+
+            f32x16 s, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                s[r] = dp[r] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[kk], vf[kk], dp, 0, 0, 0);
+            }
+            // lane: key my_key; register r: row i0 + 8(r/4) + 4g + r%4
+            f32x16 p, ds;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ri = 8 * (r >> 2) + 4 * g + (r & 3);
+                const int i = i0 + ri;
+                const float L = sL[ri];
+                const bool vis = my_key < Sk && i < Sq && L > -INFINITY &&
+                                 (!CAUSAL || my_key <= i + diag);
+                p[r] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -L * kLog2e)) : 0.f;
+                ds[r] = p[r] * (dp[r] - sDv[ri]);
+            }
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+                const bf16x8 pa = pack_chunk(p, ch), sa = pack_chunk(ds, ch);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        pa, read_t<TS>(sDT, 32 * db + l32, ch, g), dv[db], 0, 0, 0);
+                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        sa, read_t<TS>(sQT, 32 * db + l32, ch, g), dk[db], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // lane: dim 32 db + l32; register r: key j0 + 8(r/4) + 4g + r%4
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (j < Sk) {
+                a.dk[(krow0 + j) * D + 32 * db + l32] = to_bf16(dk[db][r] * a.scale);
+                a.dv[(krow0 + j) * D + 32 * db + l32] = to_bf16(dv[db][r]);
+            }
+        }
+}
+
+// ---- dQ: one wave per (b, query head, 32-row query tile) -------------------------
+// S^T = K Q^T and dP^T = V dO^T put the query row in the lane and 16 keys in
+// the registers; dS packed by registers is the A operand of dQ += dS K over
+// those keys, with K read transposed from LDS.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(64) bwd_dq_kernel(BwdArgs a, int n_qtiles)
+{
+    constexpr int KK = D / 16, DB = D / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t sKT[D * TS];
+
+    const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
+    int id = blockIdx.x;
+    const int qt = id % n_qtiles;
+    id /= n_qtiles;
+    const int hq = id % a.Hq;
+    const int b = id / a.Hq;
+    const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq, G = a.Hq / a.Hkv;
+    const int kvh = hq / G;
+    const int i0 = 32 * qt, my_q = i0 + l32;
+    const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
+    const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
+    const float c = a.scale * kLog2e;
+
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0 * D, (uint32_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout + qrow0 * D, (uint32_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o + qrow0 * D, (uint32_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + krow0 * D, (uint32_t)Sk * D * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + krow0 * D, (uint32_t)Sk * D * 2);
+    bf16x8 qf[KK], df[KK];  // B operands: row my_q, dims 16kk + 8g
+    float dot = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        qf[kk] = frag<D>(rq, my_q, kk, g);
+        df[kk] = frag<D>(rdo, my_q, kk, g);
+        const bf16x8 of = frag<D>(ro, my_q, kk, g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            dot += (float)df[kk][e] * (float)of[e];
+    }
+    const float Di = dot + __shfl_xor(dot, 32, 64);
+    const float L = my_q < Sq ? a.lse[qrow0 + my_q] : -INFINITY;
+    const bool row_live = L > -INFINITY;
+
+    f32x16 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            dq[db][r] = 0.f;
+
+    const int kv_end = CAUSAL ? min(Sk, max(0, min(i0 + 31, Sq - 1) + diag + 1)) : Sk;
+    const int nkt = (kv_end + 31) / 32;
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int j0 = 32 * kt;
+        bf16x8 ka[KK], va[KK];  // A operands: key j0 + l32, dims 16kk + 8g
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            ka[kk] = frag<D>(rk, j0 + l32, kk, g);
+            va[kk] = frag<D>(rv, j0 + l32, kk, g);
+        }
+        __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            write_t<TS>(sKT, ka[kk], l32, kk, g);
+        __syncthreads();
+
+        f32x16 s, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            s[r] = dp[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk], df[kk], dp, 0, 0, 0);
+        }
+        // lane: row my_q; register r: key j0 + 8(r/4) + 4g + r%4
+        f32x16 ds;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool vis = row_live && j < Sk && (!CAUSAL || j <= my_q + diag);
+            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -L * kLog2e)) : 0.f;
+            ds[r] = p * (dp[r] - Di);
+        }
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+            const bf16x8 sa = pack_chunk(ds, ch);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    sa, read_t<TS>(sKT, 32 * db + l32, ch, g), dq[db], 0, 0, 0);
+        }
+    }
+    // lane: dim 32 db + l32; register r: row i0 + 8(r/4) + 4g + r%4
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (i < Sq)
+                a.dq[(qrow0 + i) * D + 32 * db + l32] = to_bf16(dq[db][r] * a.scale);
+        }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
+{
+    const int n_ktiles = (a.Sk + 31) / 32, n_qtiles = (a.Sq + 31) / 32;
+    const long long g1 = (long long)a.B * a.Hkv * n_ktiles, g2 = (long long)a.B * a.Hq * n_qtiles;
+    if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL)
+        return hipErrorInvalidConfiguration;
+    if (g1 > 0) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g1), dim3(64), 0, stream, a,
+                           n_ktiles);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    if (g2 > 0)
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)g2), dim3(64), 0, stream, a,
+                           n_qtiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, hipStream_t stream)
+{
+    switch (d) {
+    case 64:
+        return causal ? launch_bwd_t<64, true>(a, stream) : launch_bwd_t<64, false>(a, stream);
+    case 128:
+        return causal ? launch_bwd_t<128, true>(a, stream) : launch_bwd_t<128, false>(a, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace miattn

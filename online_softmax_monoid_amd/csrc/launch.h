@@ -51,6 +51,14 @@ struct DecodeArgs {
     int max_pages = 0, num_pages = 0, page_shift = 0;
 };
 
+struct BwdArgs {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float *lse;
+    uint16_t *dq, *dk, *dv;
+    int B, Hq, Hkv, Sq, Sk;
+    float scale;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream);
 // head dimensions 128 and 256: the software-pipelined kernel of
@@ -60,5 +68,7 @@ hipError_t launch_fwd_q64(const FwdArgs &a, int d, bool causal, hipStream_t stre
 // (built in, selected with -DMIATTN_D128_PINGPONG)
 hipError_t launch_fwd_pingpong(const FwdArgs &a, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t stream);
+// head dimensions 64 and 128: the backward kernels of backward.hip
+hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, hipStream_t stream);
 
 }  // namespace miattn

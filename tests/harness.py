@@ -84,6 +84,40 @@ def run_fwd_ext(q, k, v, causal, scale, window=-1, softcap=0.0, alibi=None):
     return ob[:n * d].reshape(B, Hq, Sq, d), lh[:n].reshape(B, Hq, Sq), guards
 
 
+def run_bwd(q, k, v, o_bits, lse, do, causal, scale):
+    """Run attn_bwd on bit arrays (o_bits bf16, lse f32 as the forward wrote
+    them); returns (dq, dk, dv) bits and guards_ok."""
+    torch = torch_mod()
+    B, Hq, Sq, d = q.shape
+    _, Hkv, Sk, _ = k.shape
+    nq, nk = B * Hq * Sq * d, B * Hkv * Sk * d
+    dq, _ = nan_out(nq, 1)
+    dk, _ = nan_out(nk, 1)
+    dv, _ = nan_out(nk, 1)
+    ld = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32).reshape(-1)).to("cuda")
+    miattn.attn_bwd(dev_bits(q), dev_bits(k), dev_bits(v), dev_bits(o_bits), ld, dev_bits(do),
+                    dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, causal, scale)
+    torch.cuda.synchronize()
+    out = []
+    guards = True
+    for t, n, shape in ((dq, nq, q.shape), (dk, nk, k.shape), (dv, nk, k.shape)):
+        b = host_bits(t)
+        guards &= bool(np.all(b[n:] == NAN_BF16))
+        out.append(b[:n].reshape(shape))
+    return out[0], out[1], out[2], guards
+
+
+def grad_metrics(bits, ref):
+    """rel-RMS and max-abs (relative to max |ref|) of bf16 gradient bits
+    against the f64 reference."""
+    g = inputs.bf16_to_f32(bits).astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    return {"finite": bool(np.all(np.isfinite(g))),
+            "rel_rms": float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)),
+            "max_abs_rel": float(np.abs(g - ref).max() / scale) if g.size else 0.0}
+
+
 def run_decode(q, kc, vc, lens, scale, splits, ws_fill=float("nan")):
     torch = torch_mod()
     B, Hq, d = q.shape

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_workspace_size():
-    assert M.miattn_version() == 500
+    assert M.miattn_version() == 600
     assert M.attn_fwd_decode_workspace_size(32, 32, 128, 16) == 32 * 32 * 16 * 130 * 4
     assert M.attn_fwd_decode_workspace_size(0, 32, 128, 16) == 0
     assert M.attn_fwd_decode_workspace_size(1, 0, 128, 16) == 0

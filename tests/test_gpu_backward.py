@@ -1,0 +1,91 @@
+"""GPU: the attention backward (attn_bwd) against the f64 backward oracle.
+
+O and LSE, the backward's inputs from the forward, come from the oracle
+(O rounded to bf16, LSE to f32) so that the backward is checked on its own;
+one case feeds it the GPU forward's outputs instead. The expected gradients
+are the oracle's f64 dQ, dK, dV from Q, K, V and dO alone.
+
+Tolerance, per gradient tensor: relative RMS error <= 2e-2 and max-abs error
+<= 5e-2 of the tensor's largest magnitude. The kernel rounds P and dS to
+bf16 for the MFMAs (2^-9 relative each), reads O in bf16 for D = dO.O, and
+rounds the results to bf16: each a 2^-9 relative error, and dS = P (dP - D)
+cancels where dP is close to D, so the relative error per element is larger
+than per tensor; the RMS bound allows for the sum of these four roundings
+with margin, the max bound for the cancellation.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import backward as bw
+from online_softmax_monoid_amd import inputs
+from tests import harness as H
+
+pytestmark = pytest.mark.gpu
+REL_RMS, MAX_REL = 2e-2, 5e-2
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _bits(seed, shape, std=1.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return inputs.bf16_bits(rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std))
+
+
+def _check(q, k, v, do, causal, scale, label, o_bits=None, lse=None):
+    if o_bits is None:
+        o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal, scale)
+        o_bits = inputs.bf16_bits(o_ref.astype(np.float32))
+        lse = lse_ref.astype(np.float32)
+    _note(f"[gpu] {label}: running the HIP backward")
+    dq, dk, dv, guards = H.run_bwd(q, k, v, o_bits, lse, do, causal, scale)
+    assert guards, f"{label}: write outside the gradients"
+    rq, rk, rv = bw.attn_bwd(q, k, v, do, causal, scale)
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        m = H.grad_metrics(got, ref)
+        _note(f"[gpu] {label} {name}: {m}")
+        assert m["finite"], f"{label} {name}: non-finite"
+        assert m["rel_rms"] <= REL_RMS, f"{label} {name}: {m}"
+        assert m["max_abs_rel"] <= MAX_REL, f"{label} {name}: {m}"
+
+
+BWD = [
+    # B, Hq, Hkv, Sq, Sk, d, causal
+    (1, 2, 2, 64, 64, 64, True),
+    (1, 2, 2, 77, 129, 64, False),
+    (2, 4, 2, 300, 300, 128, True),
+    (1, 4, 1, 129, 300, 128, True),    # Sq < Sk
+    (1, 2, 2, 200, 77, 128, True),     # Sq > Sk: leading rows see no key
+    (1, 4, 4, 190, 190, 128, False),
+    (2, 6, 3, 257, 257, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", BWD)
+def test_backward_parity(case):
+    B, Hq, Hkv, Sq, Sk, d, causal = case
+    seed = 8000 + 10 * BWD.index(case)
+    q = _bits(seed, (B, Hq, Sq, d), 0.5)
+    k = _bits(seed + 1, (B, Hkv, Sk, d), 0.5)
+    v = _bits(seed + 2, (B, Hkv, Sk, d))
+    do = _bits(seed + 3, (B, Hq, Sq, d))
+    _check(q, k, v, do, causal, inputs.default_scale(d), f"bwd {case}")
+
+
+def test_backward_after_the_gpu_forward():
+    """The whole step on the GPU: attn_fwd's O and LSE feed attn_bwd."""
+    B, Hq, Hkv, S, d = 1, 8, 2, 512, 128
+    q = _bits(8100, (B, Hq, S, d), 0.5)
+    k = _bits(8101, (B, Hkv, S, d), 0.5)
+    v = _bits(8102, (B, Hkv, S, d))
+    do = _bits(8103, (B, Hq, S, d))
+    scale = inputs.default_scale(d)
+    o_bits, lse, _ = H.run_fwd(q, k, v, True, scale)
+    _check(q, k, v, do, True, scale, "bwd after gpu fwd", o_bits=o_bits, lse=lse)

@@ -16,7 +16,8 @@
 // 8(r/4) + 4(l/32) + r%4 of its registers r; its registers packed to bf16
 // are then directly the A operand of the next product over those rows, with
 // the other operand read in the same permuted row order. Only the operands
-// that need a transpose (Q and dO for dK/dV, K for dQ) pass through LDS.
+// that need a transpose (Q and dO for dK/dV, K for dQ) pass through LDS, in
+// the forward's V layout and by transposing reads.
 // Fragments are read from global memory by buffer loads, so rows past the
 // ends read as zeros.
 
@@ -83,33 +84,39 @@ __device__ __forceinline__ bf16x8 pack_chunk(const f32x16 &x, int c)
     return f.v;
 }
 
-// B operand over the same permuted rows from a transposed LDS tile t[dim][row]
-// (row stride TS): lane l gives dim n, rows 16c + 4g .. +3 and 16c + 8 + 4g .. +3
-template <int TS>
-__device__ __forceinline__ bf16x8 read_t(const uint16_t *t, int n, int c, int g)
-{
-    Frag8 f;
-    const uint2 a = *(const uint2 *)(t + n * TS + 16 * c + 4 * g);
-    const uint2 b = *(const uint2 *)(t + n * TS + 16 * c + 8 + 4 * g);
-    f.w[0] = a.x;
-    f.w[1] = a.y;
-    f.w[2] = b.x;
-    f.w[3] = b.y;
-    return f.v;
-}
-
-// the 8 values of a row fragment written transposed: t[16kk + 8g + e][row]
-template <int TS>
-__device__ __forceinline__ void write_t(uint16_t *t, bf16x8 v, int row, int kk, int g)
+// A 32-row tile in LDS for transposing reads, the forward's V layout: 512-byte
+// blocks b = (2 db + c) 2 + hh, and in block b at byte 8L, for
+// L = 16 G + 4 jj + q, the four values of row 16c + 8hh + 4(G/2) + jj at dims
+// 32 db + 16 (G%2) + 4q .. +3. (D * 64 bytes per tile.)
+//
+// A lane holding row `row`, dims 16kk + 8g .. +7, writes them as two 8-byte
+// groups.
+__device__ __forceinline__ void write_blk(uint16_t *t, bf16x8 v, int row, int kk, int g)
 {
     Frag8 f;
     f.v = v;
+    const int c = row >> 4, hh = (row >> 3) & 1, G2 = (row >> 2) & 1, jj = row & 3;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-        t[(16 * kk + 8 * g + e) * TS + row] = f.h[e];
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const int dim = 16 * kk + 8 * g + 4 * h2;
+        const int db = dim >> 5, dp = dim & 31;
+        const int L = 16 * (2 * G2 + (dp >> 4)) + 4 * jj + ((dp & 15) >> 2);
+        *(uint2 *)((char *)t + ((2 * db + c) * 2 + hh) * 512 + 8 * L) =
+            make_uint2(f.w[2 * h2], f.w[2 * h2 + 1]);
+    }
 }
 
-constexpr int TS = 36;  // transposed tiles: 32 rows + 4 of padding (bank spread)
+// B operand over the permuted rows of pack_chunk: a transposing 8-byte read of
+// each block gives lane l dim 32 db + l%32 at rows 16c + 8hh + 4(l/32) .. +3
+__device__ __forceinline__ bf16x8 read_tr(const uint16_t *t, int db, int c, int lane)
+{
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const char *p = (const char *)t + ((2 * db + c) * 2) * 512 + 8 * lane;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const_cast<char *>(p)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const_cast<char *>(p + 512)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 // ---- dK, dV: one wave per (b, kv-head, 32-key tile) ----------------------------
 // S = Q K^T and dP = dO V^T put the key in the lane (column) and 16 query rows
@@ -120,8 +127,8 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdArgs a, int n_ktiles)
 {
     constexpr int KK = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t sQT[D * TS];
-    __shared__ __attribute__((aligned(16))) uint16_t sDT[D * TS];
+    __shared__ __attribute__((aligned(16))) uint16_t sQT[D * 32];
+    __shared__ __attribute__((aligned(16))) uint16_t sDT[D * 32];
     __shared__ float sL[32], sDv[32];
 
     const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
@@ -150,74 +157,84 @@ __global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdArgs a, int n_ktiles)
         for (int r = 0; r < 16; ++r)
             dk[db][r] = dv[db][r] = 0.f;
 
-    // query tiles that see any key of this tile: rows i with j0 <= i + diag
+    // query tiles that see any key of this tile: rows i with j0 <= i + diag,
+    // walked as one sequence over the group's query heads; the next tile's
+    // fragments load while the current one computes
     const int i_first = CAUSAL ? max(0, j0 - diag) : 0;
     const int qt0 = i_first / 32, nqt = (Sq + 31) / 32;
+    const int per_head = max(0, nqt - qt0), n_steps = G * per_head;
     const int my_key = j0 + l32;
-    for (int h = 0; h < G; ++h) {
-        const int hq = kvh * G + h;
+    bf16x8 qa[KK], da[KK], of[KK];  // A operands (row i0 + l32, dims 16kk + 8g) and O
+    auto load_step = [&](int t) __attribute__((always_inline)) {
+        const int hq = kvh * G + t / per_head, i0 = 32 * (qt0 + t % per_head);
         const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0 * D, (uint32_t)Sq * D * 2);
         const __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout + qrow0 * D, (uint32_t)Sq * D * 2);
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o + qrow0 * D, (uint32_t)Sq * D * 2);
-        for (int qt = qt0; qt < nqt; ++qt) {
-            const int i0 = 32 * qt;
-            bf16x8 qa[KK], da[KK];  // A operands: row i0 + l32, dims 16kk + 8g
-            float dot = 0.f;
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                qa[kk] = frag<D>(rq, i0 + l32, kk, g);
-                da[kk] = frag<D>(rdo, i0 + l32, kk, g);
-                const bf16x8 of = frag<D>(ro, i0 + l32, kk, g);
+        for (int kk = 0; kk < KK; ++kk) {
+            qa[kk] = frag<D>(rq, i0 + l32, kk, g);
+            da[kk] = frag<D>(rdo, i0 + l32, kk, g);
+            of[kk] = frag<D>(ro, i0 + l32, kk, g);
+        }
+    };
+    if (n_steps > 0)
+        load_step(0);
+    for (int t = 0; t < n_steps; ++t) {
+        const int hq = kvh * G + t / per_head, i0 = 32 * (qt0 + t % per_head);
+        const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
+        float dot = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    dot += (float)da[kk][e] * (float)of[e];
-            }
-            dot += __shfl_xor(dot, 32, 64);  // D_i over both halves of the dims
-            __syncthreads();  // the previous tile's LDS reads are done
-            if (g == 0) {
-                const int i = i0 + l32;
-                sDv[l32] = dot;
-                sL[l32] = i < Sq ? a.lse[qrow0 + i] : -INFINITY;
-            }
+        for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                write_t<TS>(sQT, qa[kk], l32, kk, g);
-                write_t<TS>(sDT, da[kk], l32, kk, g);
-            }
-            __syncthreads();
+            for (int e = 0; e < 8; ++e)
+                dot += (float)da[kk][e] * (float)of[kk][e];
+        dot += __shfl_xor(dot, 32, 64);  // D_i over both halves of the dims
+        __syncthreads();  // the previous tile's LDS reads are done
+        if (g == 0) {
+            const int i = i0 + l32;
+            sDv[l32] = dot;
+            sL[l32] = i < Sq ? a.lse[qrow0 + i] : -INFINITY;
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            write_blk(sQT, qa[kk], l32, kk, g);
+            write_blk(sDT, da[kk], l32, kk, g);
+        }
+        __syncthreads();
 
-            f32x16 s, dp;
+        f32x16 s, dp;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                s[r] = dp[r] = 0.f;
+        for (int r = 0; r < 16; ++r)
+            s[r] = dp[r] = 0.f;
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[kk], vf[kk], dp, 0, 0, 0);
-            }
-            // lane: key my_key; register r: row i0 + 8(r/4) + 4g + r%4
-            f32x16 p, ds;
+        for (int kk = 0; kk < KK; ++kk) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[kk], vf[kk], dp, 0, 0, 0);
+        }
+        if (t + 1 < n_steps)
+            load_step(t + 1);  // in flight during the rest of this step
+        // lane: key my_key; register r: row i0 + 8(r/4) + 4g + r%4
+        f32x16 p, ds;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ri = 8 * (r >> 2) + 4 * g + (r & 3);
-                const int i = i0 + ri;
-                const float L = sL[ri];
-                const bool vis = my_key < Sk && i < Sq && L > -INFINITY &&
-                                 (!CAUSAL || my_key <= i + diag);
-                p[r] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -L * kLog2e)) : 0.f;
-                ds[r] = p[r] * (dp[r] - sDv[ri]);
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int ri = 8 * (r >> 2) + 4 * g + (r & 3);
+            const int i = i0 + ri;
+            const float L = sL[ri];
+            const bool vis = my_key < Sk && i < Sq && L > -INFINITY &&
+                             (!CAUSAL || my_key <= i + diag);
+            p[r] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -L * kLog2e)) : 0.f;
+            ds[r] = p[r] * (dp[r] - sDv[ri]);
+        }
 #pragma unroll
-            for (int ch = 0; ch < 2; ++ch) {
-                const bf16x8 pa = pack_chunk(p, ch), sa = pack_chunk(ds, ch);
+        for (int ch = 0; ch < 2; ++ch) {
+            const bf16x8 pa = pack_chunk(p, ch), sa = pack_chunk(ds, ch);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        pa, read_t<TS>(sDT, 32 * db + l32, ch, g), dv[db], 0, 0, 0);
-                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        sa, read_t<TS>(sQT, 32 * db + l32, ch, g), dk[db], 0, 0, 0);
-                }
+            for (int db = 0; db < DB; ++db) {
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, read_tr(sDT, db, ch, lane),
+                                                                 dv[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, read_tr(sQT, db, ch, lane),
+                                                                 dk[db], 0, 0, 0);
             }
         }
     }
@@ -242,7 +259,7 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdArgs a, int n_qtiles)
 {
     constexpr int KK = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t sKT[D * TS];
+    __shared__ __attribute__((aligned(16))) uint16_t sKT[D * 32];
 
     const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
     int id = blockIdx.x;
@@ -297,7 +314,7 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdArgs a, int n_qtiles)
         __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-            write_t<TS>(sKT, ka[kk], l32, kk, g);
+            write_blk(sKT, ka[kk], l32, kk, g);
         __syncthreads();
 
         f32x16 s, dp;
@@ -323,8 +340,8 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdArgs a, int n_qtiles)
             const bf16x8 sa = pack_chunk(ds, ch);
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    sa, read_t<TS>(sKT, 32 * db + l32, ch, g), dq[db], 0, 0, 0);
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, read_tr(sKT, db, ch, lane),
+                                                                 dq[db], 0, 0, 0);
         }
     }
     // lane: dim 32 db + l32; register r: row i0 + 8(r/4) + 4g + r%4

@@ -31,7 +31,8 @@
 //
 // K and V tiles of 32 keys go global -> LDS by range-checked buffer DMA (keys
 // past the item's last visible key arrive as zeros) into rings of RING tiles
-// (four by default), one barrier per tile. Both are stored fragment-major: each LDS read instruction
+// (four by default), one barrier per tile. Both are stored fragment-major:
+// each LDS read instruction
 // of a wave reads one contiguous 1 KB (K, ds_read_b128) or 512 B (V,
 // ds_read_b64_tr_b16) block, which is free of bank conflicts.
 //
@@ -39,6 +40,13 @@
 // of work items (query tile of one query head). The copy stream does not stop
 // at an item's end: the last steps of an item already copy the next item's
 // first K and V tiles, so the next item starts without waiting for HBM.
+//
+// Variants, each a template argument so that the plain kernel carries none of
+// their work: a sliding window (WIN: items start at the first tile any of
+// their rows sees, tiles below are never copied), a score modifier (MOD: soft
+// cap or ALiBi, applied to a tile's scores right after its QK MFMAs), and
+// packed variable-length batches (VARLEN: each item takes its sequence's
+// lengths, and the walk skips items past a sequence's end).
 //
 // The running maximum moves lazily: probabilities stay at most 2^8 above the
 // reference and the accumulator is rescaled only on the rare tiles that move

@@ -230,9 +230,58 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     const int n_units = a.B * a.Hkv;
     const int xpu = n_units < 8 && 8 % n_units == 0 ? 8 / n_units : 0;  // XCDs per unit
     const bool by_xcd = xpu > 0 && G % xpu == 0;
+    // A packed batch of at most 64 sequences walks a compacted list instead:
+    // every wave holds sequence b's ranges in lane b, ranks the sequences by
+    // query tiles then keys (longest first), and numbers the live items rank
+    // by rank (rank r: each sequence's r-th heaviest query tile), the
+    // sequences of a rank in that order and their query heads together. No
+    // item of the list is past a sequence's end, and the heavy tiles come
+    // first.
+    const bool compact = VARLEN && a.B <= 64;
+    int v_qlo = 0, v_sq = 0, v_klo = 0, v_sk = 0, v_nq = 0, v_pos = 0;  // lane b: sequence b
+    int n_live = n_items;
+    if constexpr (VARLEN) {
+        if (compact) {
+            if (lane < a.B) {
+                v_qlo = min(max(a.cu_q[lane], 0), a.total_q);
+                const int q_hi = min(max(a.cu_q[lane + 1], v_qlo), a.total_q);
+                v_klo = min(max(a.cu_k[lane], 0), a.total_k);
+                const int k_hi = min(max(a.cu_k[lane + 1], v_klo), a.total_k);
+                v_sq = min(q_hi - v_qlo, a.Sq);
+                v_sk = min(k_hi - v_klo, a.Sk);
+                v_nq = (v_sq + BM - 1) / BM;
+            }
+            int pos = 0, live = 0;
+            for (int o = 0; o < a.B; ++o) {
+                const int nqo = __builtin_amdgcn_readlane(v_nq, o);
+                const int sko = __builtin_amdgcn_readlane(v_sk, o);
+                pos += (nqo > v_nq) || (nqo == v_nq && (sko > v_sk || (sko == v_sk && o < lane)));
+                live += nqo;
+            }
+            v_pos = pos;
+            n_live = min(n_items, live * a.Hq);
+        }
+    }
+    int rank_r = 0, rank_c0 = 0;  // the walk's current rank and its first list index
+    auto rank_size = [&](int r) __attribute__((always_inline)) {
+        return a.Hq * (int)__builtin_popcountll(__ballot(lane < a.B && v_nq > r));
+    };
     auto describe = [&](int id) __attribute__((always_inline)) {
         TileOrder to;
-        if (by_xcd) {
+        int b_c = 0;
+        if (compact) {
+            // ids only grow along a workgroup's walk
+            for (int n = rank_size(rank_r); id >= rank_c0 + n; n = rank_size(rank_r)) {
+                rank_c0 += n;
+                ++rank_r;
+            }
+            const int idx = id - rank_c0, k = idx / a.Hq, hq_c = idx - k * a.Hq;
+            const unsigned long long hit = __ballot(lane < a.B && v_pos == k);
+            b_c = hit ? (int)__builtin_ctzll(hit) : 0;  // exactly one lane matches
+            to.unit = b_c * a.Hkv + hq_c / G;
+            to.gq = hq_c % G;
+            to.qtile = __builtin_amdgcn_readlane(v_nq, b_c) - 1 - rank_r;
+        } else if (by_xcd) {
             const int gsub = G / xpu, x = id & 7, pos = id >> 3;
             const int rank = pos / gsub;
             to.unit = x / xpu;
@@ -246,7 +295,12 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         const int hq = kvh * G + to.gq;
         Item it;
         int64_t kbase;
-        if constexpr (VARLEN) {
+        if (compact) {
+            it.sq = __builtin_amdgcn_readlane(v_sq, b_c);
+            it.sk = __builtin_amdgcn_readlane(v_sk, b_c);
+            it.qrow0 = (int64_t)hq * a.total_q + __builtin_amdgcn_readlane(v_qlo, b_c);
+            kbase = (int64_t)kvh * a.total_k + __builtin_amdgcn_readlane(v_klo, b_c);
+        } else if constexpr (VARLEN) {
             // sequence b of a packed batch; offsets clamped into the tensors
             // (at most the longest length), so no access leaves them
             const int q_lo = min(max(a.cu_q[b], 0), a.total_q);
@@ -834,28 +888,28 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // its sequences' ends)
     auto next_item = [&](int &r, Item &it) __attribute__((always_inline)) {
         int id_ = item_id(r);
-        if (id_ < n_items)
+        if (id_ < n_live)
             it = describe(id_);
         if constexpr (VARLEN) {
-            while (id_ < n_items && !it.live) {
+            while (id_ < n_live && !it.live) {
                 id_ = item_id(++r);
-                if (id_ < n_items)
+                if (id_ < n_live)
                     it = describe(id_);
             }
         }
         return id_;
     };
     int r = 0;
-    Item nx = describe(0);
+    Item nx{};
     int id = next_item(r, nx);
     if constexpr (QPREF)
         load_q(nx.qrow0, nx.q_wg + wave * 32 * QB, nx.sq);
     int sq_n = 0;
-    while (id < n_items) {
+    while (id < n_live) {
         const Item cur = nx;
         int r_n = r + 1;
         const int id_n = next_item(r_n, nx);
-        has_next = id_n < n_items;
+        has_next = id_n < n_live;
         kv_end_n = 0;
         if (has_next) {
             sq_n = nx.sq;

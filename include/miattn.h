@@ -1,6 +1,8 @@
 /*
- * miattn.h -- C ABI of libmiattn, the fused softmax-attention forward for
- * AMD Instinct MI355X (gfx950).
+ * miattn.h -- C ABI of libmiattn, fused softmax attention for AMD Instinct
+ * MI355X (gfx950): prefill forward (with window, score-modifier and packed
+ * variants), split-KV decode over contiguous or paged caches, and the
+ * prefill backward.
  *
  * The operation is O = softmax(scale * Q K^T + mask) V together with the
  * per-row log-sum-exp, computed as one tiled reduction under the

@@ -134,3 +134,26 @@ def test_varlen_many_sequences_sampled():
     m = H.metrics(o_got, l_got, o_ref, l_ref)
     _note(f"[gpu] varlen 40 sequences: {m}")
     H.assert_parity(m, "varlen 40 sequences")
+
+
+def test_varlen_more_than_64_sequences():
+    """70 sequences (past what a wave ranks in its lanes): the walk over the
+    plain item space that skips items past each sequence's end."""
+    rng = np.random.Generator(np.random.PCG64(90))
+    lq = rng.integers(0, 300, size=70, endpoint=True)
+    lk = lq + rng.integers(0, 100, size=70, endpoint=True)
+    lq[[5, 33]] = 0
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    Hq, Hkv, d = 4, 2, 128
+    q = _bits(91, (Hq, int(cu_q[-1]), d))
+    k = _bits(92, (Hkv, int(cu_k[-1]), d))
+    v = _bits(93, (Hkv, int(cu_k[-1]), d))
+    scale = inputs.default_scale(d)
+    _note("[gpu] varlen 70 sequences: running the HIP path")
+    o, lse, guards = _run(q, k, v, cu_q, cu_k, int(lq.max()), int(lk.max()), True, scale)
+    assert guards
+    o_ref, lse_ref = oracle.attn_fwd_varlen(q, k, v, cu_q, cu_k, True, scale)
+    m = H.metrics(o, lse, o_ref, lse_ref)
+    _note(f"[gpu] varlen 70 sequences: {m}")
+    H.assert_parity(m, "varlen 70 sequences")

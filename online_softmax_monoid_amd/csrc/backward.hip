@@ -303,14 +303,18 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdArgs a, int n_qtiles)
 
     const int kv_end = CAUSAL ? min(Sk, max(0, min(i0 + 31, Sq - 1) + diag + 1)) : Sk;
     const int nkt = (kv_end + 31) / 32;
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int j0 = 32 * kt;
-        bf16x8 ka[KK], va[KK];  // A operands: key j0 + l32, dims 16kk + 8g
+    bf16x8 ka[KK], va[KK];  // A operands: key j0 + l32, dims 16kk + 8g (loaded a tile ahead)
+    auto load_tile = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            ka[kk] = frag<D>(rk, j0 + l32, kk, g);
-            va[kk] = frag<D>(rv, j0 + l32, kk, g);
+            ka[kk] = frag<D>(rk, 32 * kt + l32, kk, g);
+            va[kk] = frag<D>(rv, 32 * kt + l32, kk, g);
         }
+    };
+    if (nkt > 0)
+        load_tile(0);
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int j0 = 32 * kt;
         __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
@@ -326,6 +330,8 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdArgs a, int n_qtiles)
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk], df[kk], dp, 0, 0, 0);
         }
+        if (kt + 1 < nkt)
+            load_tile(kt + 1);  // in flight during the rest of this tile
         // lane: row my_q; register r: key j0 + 8(r/4) + 4g + r%4
         f32x16 ds;
 #pragma unroll

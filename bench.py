@@ -251,13 +251,16 @@ class Backward:
         self.dq = torch.empty(nq, dtype=torch.int16, device="cuda")
         self.dk = torch.empty(nk, dtype=torch.int16, device="cuda")
         self.dv = torch.empty(nk, dtype=torch.int16, device="cuda")
+        from online_softmax_monoid_amd import miattn
+        self.ws_bytes = miattn.attn_bwd_workspace_size(w.B, w.Hq, w.Sq)
+        self.ws = torch.empty(self.ws_bytes // 4, dtype=torch.float32, device="cuda")
         self.flops = 2.5 * pre.flops
 
     def __call__(self, stream):
         from online_softmax_monoid_amd import miattn
         p, w = self.pre, self.pre.w
         miattn.attn_bwd(p.q, p.k, p.v, p.o, p.lse, self.do, self.dq, self.dk, self.dv, w.B, w.Hq,
-                        w.Hkv, w.Sq, w.Sk, w.d, p.causal, w.scale, stream)
+                        w.Hkv, w.Sq, w.Sk, w.d, p.causal, w.scale, self.ws, self.ws_bytes, stream)
 
 
 class DecodePaged:

@@ -182,6 +182,9 @@ MIATTN_API int attn_fwd_varlen(const void *q, const void *k, const void *v, void
  *   dq    bf16 [B, Hq,  Sq, d]   written
  *   dk    bf16 [B, Hkv, Sk, d]   written (summed over the Hq/Hkv query heads
  *   dv    bf16 [B, Hkv, Sk, d]   written  that read each kv-head)
+ *   workspace  device scratch of at least attn_bwd_workspace_size(B, Hq, Sq)
+ *              bytes (f32 D_i per row, computed first); contents on entry do
+ *              not matter. Two calls sharing one workspace must be ordered.
  *
  * f32 accumulation, bf16 results. Head dimensions 64 and 128 (256:
  * MIATTN_ERR_UNSUPPORTED). Keys no query sees get zero gradients; rows with
@@ -190,7 +193,11 @@ MIATTN_API int attn_fwd_varlen(const void *q, const void *k, const void *v, void
 MIATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void *o,
              const float *lse, const void *dout, void *dq, void *dk, void *dv,
              int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
-             float scale, hipStream_t stream);
+             float scale, void *workspace, size_t workspace_bytes,
+             hipStream_t stream);
+
+/* Bytes of workspace attn_bwd needs: B * Hq * Sq * 4. 0 for invalid sizes. */
+MIATTN_API size_t attn_bwd_workspace_size(int B, int Hq, int Sq);
 
 /*
  * Bytes of workspace attn_fwd_decode needs: B * Hq * num_splits * (d + 2) * 4

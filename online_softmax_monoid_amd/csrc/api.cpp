@@ -312,9 +312,17 @@ int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float 
     return hip_status(miattn::launch_fwd(a, d, causal != 0, stream), "attn_fwd_varlen launch");
 }
 
+size_t attn_bwd_workspace_size(int B, int Hq, int Sq)
+{
+    if (B < 0 || Hq < 1 || Sq < 0)
+        return 0;
+    return (size_t)B * (size_t)Hq * (size_t)Sq * sizeof(float);
+}
+
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
              const void *dout, void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Sq,
-             int Sk, int d, int causal, float scale, hipStream_t stream)
+             int Sk, int d, int causal, float scale, void *workspace, size_t workspace_bytes,
+             hipStream_t stream)
 {
     if (B < 0 || Sq < 0 || Sk < 0)
         return fail(MIATTN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d, Sq=%d, Sk=%d)", B, Sq, Sk);
@@ -333,6 +341,11 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
         MIATTN_TRY(check_ptr(dout, "dout", 16));
         MIATTN_TRY(check_ptr(lse, "lse", 4));
         MIATTN_TRY(check_ptr(dq, "dq", 16));
+        MIATTN_TRY(check_ptr(workspace, "workspace", 4));
+        const size_t need = attn_bwd_workspace_size(B, Hq, Sq);
+        if (workspace_bytes < need)
+            return fail(MIATTN_ERR_INVALID_ARG, "workspace too small: %zu bytes, need %zu",
+                        workspace_bytes, need);
     }
     if (Sk > 0) {
         MIATTN_TRY(check_ptr(k, "k", 16));
@@ -350,6 +363,7 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
     a.dq = static_cast<uint16_t *>(dq);
     a.dk = static_cast<uint16_t *>(dk);
     a.dv = static_cast<uint16_t *>(dv);
+    a.dsum = static_cast<float *>(workspace);
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -361,6 +375,6 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
 
 const char *miattn_last_error(void) { return g_last_error.c_str(); }
 
-int miattn_version(void) { return 600; }
+int miattn_version(void) { return 700; }
 
 }  // extern "C"

@@ -8,7 +8,8 @@
 //   dV_j  = sum_i P_ij dO_i      dK_j = scale sum_i dS_ij q_i
 //   dQ_i  = scale sum_j dS_ij k_j
 //
-// Two kernels, no atomics: one wave per 32-key tile accumulates dK and dV over
+// D_i is computed once per row into the caller's workspace by a first small
+// kernel. Then two kernels, no atomics: one wave per 32-key tile accumulates dK and dV over
 // the query heads of its kv-head and their query tiles; one wave per 32-row
 // query tile accumulates dQ over the key tiles. Every product is a
 // v_mfma_f32_32x32x16_bf16 with f32 accumulation. As in the forward, a score
@@ -164,18 +165,16 @@ __global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdArgs a, int n_ktiles)
     const int qt0 = i_first / 32, nqt = (Sq + 31) / 32;
     const int per_head = max(0, nqt - qt0), n_steps = G * per_head;
     const int my_key = j0 + l32;
-    bf16x8 qa[KK], da[KK], of[KK];  // A operands (row i0 + l32, dims 16kk + 8g) and O
+    bf16x8 qa[KK], da[KK];  // A operands: row i0 + l32, dims 16kk + 8g
     auto load_step = [&](int t) __attribute__((always_inline)) {
         const int hq = kvh * G + t / per_head, i0 = 32 * (qt0 + t % per_head);
         const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0 * D, (uint32_t)Sq * D * 2);
         const __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout + qrow0 * D, (uint32_t)Sq * D * 2);
-        const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o + qrow0 * D, (uint32_t)Sq * D * 2);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             qa[kk] = frag<D>(rq, i0 + l32, kk, g);
             da[kk] = frag<D>(rdo, i0 + l32, kk, g);
-            of[kk] = frag<D>(ro, i0 + l32, kk, g);
         }
     };
     if (n_steps > 0)
@@ -183,17 +182,10 @@ __global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdArgs a, int n_ktiles)
     for (int t = 0; t < n_steps; ++t) {
         const int hq = kvh * G + t / per_head, i0 = 32 * (qt0 + t % per_head);
         const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
-        float dot = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                dot += (float)da[kk][e] * (float)of[kk][e];
-        dot += __shfl_xor(dot, 32, 64);  // D_i over both halves of the dims
         __syncthreads();  // the previous tile's LDS reads are done
         if (g == 0) {
             const int i = i0 + l32;
-            sDv[l32] = dot;
+            sDv[l32] = i < Sq ? a.dsum[qrow0 + i] : 0.f;
             sL[l32] = i < Sq ? a.lse[qrow0 + i] : -INFINITY;
         }
 #pragma unroll
@@ -276,21 +268,15 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdArgs a, int n_qtiles)
 
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0 * D, (uint32_t)Sq * D * 2);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout + qrow0 * D, (uint32_t)Sq * D * 2);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o + qrow0 * D, (uint32_t)Sq * D * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + krow0 * D, (uint32_t)Sk * D * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + krow0 * D, (uint32_t)Sk * D * 2);
     bf16x8 qf[KK], df[KK];  // B operands: row my_q, dims 16kk + 8g
-    float dot = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
         qf[kk] = frag<D>(rq, my_q, kk, g);
         df[kk] = frag<D>(rdo, my_q, kk, g);
-        const bf16x8 of = frag<D>(ro, my_q, kk, g);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            dot += (float)df[kk][e] * (float)of[e];
     }
-    const float Di = dot + __shfl_xor(dot, 32, 64);
+    const float Di = my_q < Sq ? a.dsum[qrow0 + my_q] : 0.f;
     const float L = my_q < Sq ? a.lse[qrow0 + my_q] : -INFINITY;
     const bool row_live = L > -INFINITY;
 
@@ -361,6 +347,32 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdArgs a, int n_qtiles)
         }
 }
 
+// ---- D_i = dO_i . O_i for every row, once (the workspace) -----------------------
+// one wave per 32 rows of a (b, query head): lane l32 + 32 g takes dims
+// 16kk + 8g .. +7 of row l32
+template <int D>
+__global__ void __launch_bounds__(64) bwd_dsum_kernel(BwdArgs a, int n_qtiles)
+{
+    constexpr int KK = D / 16;
+    const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
+    const int qt = blockIdx.x % n_qtiles, bh = blockIdx.x / n_qtiles;
+    const int Sq = a.Sq, i = 32 * qt + l32;
+    const int64_t qrow0 = (int64_t)bh * Sq;
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout + qrow0 * D, (uint32_t)Sq * D * 2);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o + qrow0 * D, (uint32_t)Sq * D * 2);
+    float dot = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        const bf16x8 d = frag<D>(rdo, i, kk, g), o = frag<D>(ro, i, kk, g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            dot += (float)d[e] * (float)o[e];
+    }
+    dot += __shfl_xor(dot, 32, 64);
+    if (g == 0 && i < Sq)
+        a.dsum[qrow0 + i] = dot;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
 {
@@ -368,6 +380,12 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
     const long long g1 = (long long)a.B * a.Hkv * n_ktiles, g2 = (long long)a.B * a.Hq * n_qtiles;
     if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
+    if (g2 > 0) {
+        hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)g2), dim3(64), 0, stream, a, n_qtiles);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     if (g1 > 0) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g1), dim3(64), 0, stream, a,
                            n_ktiles);

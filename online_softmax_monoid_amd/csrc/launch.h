@@ -55,6 +55,7 @@ struct BwdArgs {
     const uint16_t *q, *k, *v, *o, *dout;
     const float *lse;
     uint16_t *dq, *dk, *dv;
+    float *dsum;  // workspace: D_i = dO_i . O_i, f32 [B, Hq, Sq]
     int B, Hq, Hkv, Sq, Sk;
     float scale;
 };

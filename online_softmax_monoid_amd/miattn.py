@@ -22,6 +22,7 @@ MIATTN_ERR_UNSUPPORTED = 2
 MIATTN_ERR_HIP = 3
 
 EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_fwd_ext", "attn_fwd_varlen", "attn_bwd",
+           "attn_bwd_workspace_size",
            "attn_fwd_decode_workspace_size",
            "attn_fwd_decode",
            "attn_fwd_decode_paged", "miattn_last_error", "miattn_version")
@@ -55,8 +56,11 @@ def load(path: str = LIB_PATH):
     L.attn_fwd_ext.restype = i
     L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, vp]
     L.attn_fwd_varlen.restype = i
-    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp,
+                           ctypes.c_size_t, vp]
     L.attn_bwd.restype = i
+    L.attn_bwd_workspace_size.argtypes = [i, i, i]
+    L.attn_bwd_workspace_size.restype = ctypes.c_size_t
     L.attn_fwd_decode_workspace_size.argtypes = [i, i, i, i]
     L.attn_fwd_decode_workspace_size.restype = ctypes.c_size_t
     L.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp,
@@ -127,10 +131,15 @@ def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, total_q, tot
 
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, causal, scale,
-             stream=None):
+             workspace, workspace_bytes, stream=None):
     _check(load().attn_bwd(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse), _addr(dout),
                            _addr(dq), _addr(dk), _addr(dv), int(B), int(Hq), int(Hkv), int(Sq),
-                           int(Sk), int(d), int(bool(causal)), float(scale), _stream(stream)))
+                           int(Sk), int(d), int(bool(causal)), float(scale), _addr(workspace),
+                           int(workspace_bytes), _stream(stream)))
+
+
+def attn_bwd_workspace_size(B, Hq, Sq) -> int:
+    return int(load().attn_bwd_workspace_size(int(B), int(Hq), int(Sq)))
 
 
 def attn_fwd_decode_workspace_size(B, Hq, d, num_splits) -> int:

@@ -95,8 +95,10 @@ def run_bwd(q, k, v, o_bits, lse, do, causal, scale):
     dk, _ = nan_out(nk, 1)
     dv, _ = nan_out(nk, 1)
     ld = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32).reshape(-1)).to("cuda")
+    wsb = miattn.attn_bwd_workspace_size(B, Hq, Sq)
+    ws = torch.full((max(wsb // 4, 1),), float("nan"), dtype=torch.float32, device="cuda")
     miattn.attn_bwd(dev_bits(q), dev_bits(k), dev_bits(v), dev_bits(o_bits), ld, dev_bits(do),
-                    dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, causal, scale)
+                    dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, causal, scale, ws, wsb)
     torch.cuda.synchronize()
     out = []
     guards = True

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_workspace_size():
-    assert M.miattn_version() == 600
+    assert M.miattn_version() == 700
     assert M.attn_fwd_decode_workspace_size(32, 32, 128, 16) == 32 * 32 * 16 * 130 * 4
     assert M.attn_fwd_decode_workspace_size(0, 32, 128, 16) == 0
     assert M.attn_fwd_decode_workspace_size(1, 0, 128, 16) == 0
@@ -129,6 +129,24 @@ def test_attn_fwd_varlen_rejects():
         assert L.attn_fwd_varlen(*args(**kw)) == status, kw
         assert needle in M.miattn_last_error()
     assert L.attn_fwd_varlen(*args(q=0, k=0, v=0, o=0, lse=0, cq=0, ck=0, B=0)) == M.MIATTN_OK
+
+
+def test_attn_bwd_rejects():
+    L = M.load()
+    wsb = M.attn_bwd_workspace_size(1, 2, 8)
+    assert wsb == 1 * 2 * 8 * 4 and M.attn_bwd_workspace_size(-1, 2, 8) == 0
+    base = [FAKE] * 9 + [1, 2, 2, 8, 8, 128, 1, 0.125, FAKE, wsb, 0]
+    for idx, val, status, needle in [
+            (14, 256, M.MIATTN_ERR_UNSUPPORTED, "d = 64 and 128"),
+            (18, 16, M.MIATTN_ERR_INVALID_ARG, "workspace too small"),
+            (17, 0, M.MIATTN_ERR_INVALID_ARG, "workspace is NULL"),
+            (5, 0, M.MIATTN_ERR_INVALID_ARG, "dout is NULL"),
+            (8, FAKE + 2, M.MIATTN_ERR_INVALID_ARG, "aligned"),
+            (16, 0.0, M.MIATTN_ERR_INVALID_ARG, "scale")]:
+        args = list(base)
+        args[idx] = val
+        assert L.attn_bwd(*args) == status, (idx, val)
+        assert needle in M.miattn_last_error()
 
 
 def _dec(**kw):

@@ -130,7 +130,8 @@ __global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdArgs a, int n_ktiles)
     constexpr int KK = D / 16, DB = D / 32;
     __shared__ __attribute__((aligned(16))) uint16_t sQT[D * 32];
     __shared__ __attribute__((aligned(16))) uint16_t sDT[D * 32];
-    __shared__ float sL[32], sDv[32];
+    __shared__ __attribute__((aligned(16))) float sL[32];   // LSE_i log2(e), row i0 + i
+    __shared__ __attribute__((aligned(16))) float sDv[32];  // D_i
 
     const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
     int id = blockIdx.x;
@@ -186,7 +187,7 @@ __global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdArgs a, int n_ktiles)
         if (g == 0) {
             const int i = i0 + l32;
             sDv[l32] = i < Sq ? a.dsum[qrow0 + i] : 0.f;
-            sL[l32] = i < Sq ? a.lse[qrow0 + i] : -INFINITY;
+            sL[l32] = i < Sq ? a.lse[qrow0 + i] * kLog2e : -INFINITY;
         }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -206,17 +207,23 @@ __global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdArgs a, int n_ktiles)
         }
         if (t + 1 < n_steps)
             load_step(t + 1);  // in flight during the rest of this step
-        // lane: key my_key; register r: row i0 + 8(r/4) + 4g + r%4
+        // lane: key my_key; register r: row i0 + 8(r/4) + 4g + r%4 (rows
+        // 8(r/4) + 4g .. +3 are one 16-byte read of each statistic)
         f32x16 p, ds;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int ri = 8 * (r >> 2) + 4 * g + (r & 3);
-            const int i = i0 + ri;
-            const float L = sL[ri];
-            const bool vis = my_key < Sk && i < Sq && L > -INFINITY &&
-                             (!CAUSAL || my_key <= i + diag);
-            p[r] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -L * kLog2e)) : 0.f;
-            ds[r] = p[r] * (dp[r] - sDv[ri]);
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const float4 L4 = *(const float4 *)&sL[8 * r4 + 4 * g];
+            const float4 D4 = *(const float4 *)&sDv[8 * r4 + 4 * g];
+            const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = 4 * r4 + u;
+                const int i = i0 + 8 * r4 + 4 * g + u;
+                const bool vis = my_key < Sk && i < Sq && Lr[u] > -INFINITY &&
+                                 (!CAUSAL || my_key <= i + diag);
+                p[r] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -Lr[u])) : 0.f;
+                ds[r] = p[r] * (dp[r] - Dr[u]);
+            }
         }
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {

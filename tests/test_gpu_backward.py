@@ -89,3 +89,24 @@ def test_backward_after_the_gpu_forward():
     scale = inputs.default_scale(d)
     o_bits, lse, _ = H.run_fwd(q, k, v, True, scale)
     _check(q, k, v, do, True, scale, "bwd after gpu fwd", o_bits=o_bits, lse=lse)
+
+
+def test_backward_workload_full_size_sampled_heads():
+    """The bench's backward: the prefill workload (B2 H32 S4096 d128 causal),
+    the GPU forward's O and LSE feeding the backward, in the bench's launch
+    configuration; two (batch, head) slices checked against the oracle, which
+    computes them from Q, K, V and dO alone (one query head per kv-head)."""
+    w = inputs.WORKLOADS[3]
+    q, k, v = inputs.prefill_inputs(w)
+    do = _bits(w.seed + 11, (w.B, w.Hq, w.Sq, w.d))
+    _note("[gpu] backward workload: forward then backward on the GPU")
+    o_bits, lse, _ = H.run_fwd(q, k, v, True, w.scale)
+    dq, dk, dv, guards = H.run_bwd(q, k, v, o_bits, lse, do, True, w.scale)
+    assert guards
+    for b, h in ((0, 0), (1, 31)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = bw.attn_bwd(q[sl], k[sl], v[sl], do[sl], True, w.scale)
+        for name, got, ref in (("dq", dq[sl], rq), ("dk", dk[sl], rk), ("dv", dv[sl], rv)):
+            m = H.grad_metrics(got, ref)
+            _note(f"[gpu] backward workload b={b} h={h} {name}: {m}")
+            assert m["finite"] and m["rel_rms"] <= REL_RMS and m["max_abs_rel"] <= MAX_REL, m

@@ -157,3 +157,38 @@ def test_varlen_more_than_64_sequences():
     m = H.metrics(o, lse, o_ref, lse_ref)
     _note(f"[gpu] varlen 70 sequences: {m}")
     H.assert_parity(m, "varlen 70 sequences")
+
+
+def test_varlen_bench_configuration_sampled():
+    """The bench's packed chunked prefill (16 sequences of U[512, 4096]
+    queries against prefixes of U[0, 2048] keys, Hq 32, Hkv 8, d 128,
+    causal), in the bench's launch configuration; rows sampled per sequence
+    and head against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(7300))
+    lq = rng.integers(512, 4096, size=16, endpoint=True)
+    lk = lq + rng.integers(0, 2048, size=16, endpoint=True)
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    Hq, Hkv, d = 32, 8, 128
+    q, k, v = inputs.draw_prefill_bits(7301, 1, Hq, Hkv, int(lq.sum()), int(lk.sum()), d)
+    q, k, v = q[0], k[0], v[0]
+    scale = inputs.default_scale(d)
+    _note("[gpu] varlen bench configuration: running the HIP path")
+    o, lse, guards = _run(q, k, v, cu_q, cu_k, int(lq.max()), int(lk.max()), True, scale)
+    assert guards
+    pick = np.random.Generator(np.random.PCG64(7302))
+    o_ref, l_ref, o_got, l_got = [], [], [], []
+    for b in range(16):
+        q0, k0, k1, n = int(cu_q[b]), int(cu_k[b]), int(cu_k[b + 1]), int(lq[b])
+        rows_b = np.unique(np.concatenate([[0, n - 1], pick.integers(0, n, size=6)]))
+        rows = (np.arange(Hq)[:, None] * n + rows_b[None, :]).reshape(-1)
+        ob, lb = oracle.attn_fwd(q[None, :, q0:q0 + n], k[None, :, k0:k1], v[None, :, k0:k1],
+                                 True, scale, rows=rows)
+        o_ref.append(ob)
+        l_ref.append(lb)
+        o_got.append(o[:, q0 + rows_b].reshape(-1, d))
+        l_got.append(lse[:, q0 + rows_b].reshape(-1))
+    m = H.metrics(np.concatenate(o_got), np.concatenate(l_got), np.concatenate(o_ref),
+                  np.concatenate(l_ref))
+    _note(f"[gpu] varlen bench configuration: {m}")
+    H.assert_parity(m, "varlen bench configuration")

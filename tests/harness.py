@@ -114,7 +114,7 @@ def grad_metrics(bits, ref):
     against the f64 reference."""
     g = inputs.bf16_to_f32(bits).astype(np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    scale = max(float(np.abs(ref).max()), 1e-30)
+    scale = max(float(np.abs(ref).max()) if ref.size else 0.0, 1e-30)
     return {"finite": bool(np.all(np.isfinite(g))),
             "rel_rms": float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)),
             "max_abs_rel": float(np.abs(g - ref).max() / scale) if g.size else 0.0}

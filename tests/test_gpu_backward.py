@@ -110,3 +110,19 @@ def test_backward_workload_full_size_sampled_heads():
             m = H.grad_metrics(got, ref)
             _note(f"[gpu] backward workload b={b} h={h} {name}: {m}")
             assert m["finite"] and m["rel_rms"] <= REL_RMS and m["max_abs_rel"] <= MAX_REL, m
+
+
+@pytest.mark.parametrize("Sq,Sk", [(40, 0), (0, 40)])
+def test_backward_degenerate_lengths(Sq, Sk):
+    """No keys: dQ is exactly zero (no row sees a key). No queries: dK and dV
+    are exactly zero (no query sees a key)."""
+    B, Hq, Hkv, d = 1, 4, 2, 128
+    q = _bits(8200, (B, Hq, Sq, d))
+    k = _bits(8201, (B, Hkv, Sk, d))
+    v = _bits(8202, (B, Hkv, Sk, d))
+    do = _bits(8203, (B, Hq, Sq, d))
+    o_bits = np.zeros((B, Hq, Sq, d), dtype=np.uint16)
+    lse = np.full((B, Hq, Sq), -np.inf, dtype=np.float32)
+    dq, dk, dv, guards = H.run_bwd(q, k, v, o_bits, lse, do, True, inputs.default_scale(d))
+    assert guards
+    assert not dq.any() and not dk.any() and not dv.any()

@@ -37,7 +37,6 @@ PREFILL_WID, LONG_WID, DECODE_WID = 3, 4, 5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_b2_h32_s4096_d128_causal_traffic.txt")
 KERNEL_SOURCES = ("online_softmax_monoid_amd/csrc/prefill.hip",
                   "online_softmax_monoid_amd/csrc/prefill_q64.hip",
-                  "online_softmax_monoid_amd/csrc/prefill_pingpong.hip",
                   "online_softmax_monoid_amd/csrc/tile_order.h",
                   "online_softmax_monoid_amd/csrc/lds_copy.h",
                   "online_softmax_monoid_amd/csrc/resident.h",

@@ -23,7 +23,10 @@
  *     of how many prefill workgroups fit on the device at once.
  *   - Tensors are dense, row-major, contiguous. bf16 tensors are raw IEEE
  *     bfloat16 bit patterns (uint16); q, k, v, o and the workspace must be
- *     16-byte aligned, lse and kv_lens 4-byte aligned.
+ *     16-byte aligned. lse, kv_lens, block tables, prefix sums and ALiBi
+ *     slopes need only 4-byte alignment: they are read and written one
+ *     4-byte element at a time, so a view into a larger f32 or int32 tensor
+ *     can be passed directly.
  *   - Work is enqueued on `stream` and the call returns without waiting;
  *     nothing is synchronised. Calls on different streams are independent.
  *   - Every logical output element is written (including rows that see no
@@ -36,12 +39,11 @@
  *     that lies in a partially visible tile and is masked for some rows is
  *     multiplied by an exact zero weight, so its V row must hold finite
  *     values (NaN/inf there would propagate as 0 * NaN).
- *   - Accumulation is float32: scores and the monoid state in f32. In the
- *     prefill kernel the probabilities are rounded to bf16 (round to nearest
- *     even) before the value contraction, while the row sum l that
- *     normalises O and gives LSE adds the unrounded f32 probabilities.
- *     Decode keeps the probabilities in f32. O is rounded to bf16 (RNE) and
- *     LSE is stored as f32.
+ *   - Accumulation is float32: scores and the monoid state in f32. In both
+ *     the prefill and the decode kernels the probabilities are rounded to
+ *     bf16 (round to nearest even) before the value contraction, while the
+ *     row sum l that normalises O and gives LSE adds the unrounded f32
+ *     probabilities. O is rounded to bf16 (RNE) and LSE is stored as f32.
  *   - Return value: MIATTN_OK, or an error code with the message available
  *     from miattn_last_error(). Argument checks happen on the host before
  *     anything is enqueued; on error nothing is launched.

@@ -17,8 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmiattn.so")
-SOURCES = ["api.cpp", "prefill.hip", "prefill_q64.hip", "prefill_pingpong.hip", "decode.hip",
-           "backward.hip"]
+SOURCES = ["api.cpp", "prefill.hip", "prefill_q64.hip", "decode.hip", "backward.hip"]
 ARCH = "gfx950"
 
 
@@ -30,7 +29,7 @@ def hipcc() -> str:
 
 
 def flags(extra=()):
-    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # MFMA accumulators in VGPRs: the online-softmax rescale and the
             # epilogue touch them with VALU ops, which cannot address AGPRs
@@ -38,23 +37,46 @@ def flags(extra=()):
             "-fvisibility=hidden", "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC, *extra]
 
 
-def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
-    srcs = []
-    for s in SOURCES:
-        p = os.path.join(CSRC, s)
-        srcs += ["-x", "hip", p]
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *flags(extra), "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + msg)
-    if msg.strip() and verbose:
-        print(msg)
-    os.replace(tmp, out)
+    return res.returncode, msg
+
+
+def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the shared
+    library; the objects live in a build folder next to the sources."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    tag = "%d" % os.getpid()
+    cmds, objs = [], []
+    for s in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(s)[0] + "." + tag + ".o")
+        objs.append(obj)
+        cmds.append([hipcc(), *flags(extra), "-c", "-o", obj, "-x", "hip", os.path.join(CSRC, s)])
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+    try:
+        with ThreadPoolExecutor(workers) as pool:
+            results = list(pool.map(_run, cmds))
+        for cmd, (rc, msg) in zip(cmds, results):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            if rc != 0:
+                raise RuntimeError("hipcc failed:\n" + msg)
+            if msg.strip() and verbose:
+                print(msg)
+        tmp = out + ".tmp" + tag
+        rc, msg = _run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs])
+        if rc != 0:
+            raise RuntimeError("link failed:\n" + msg)
+        os.replace(tmp, out)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return out
 
 

@@ -487,7 +487,9 @@ decode_combine_kernel(DecodeArgs a)
             }
         }
     }
-    const bool empty = !(L > 0.f);
+    // no key at all (L = 0 exactly); a NaN sum (NaN in visible inputs)
+    // propagates to O and LSE instead of passing for an empty stream
+    const bool empty = L == 0.f;
     const float inv = empty ? 0.f : 1.f / L;
     uint16_t *orow = a.o + bh * D + PER * lane;
     if constexpr (PER == 1) {
@@ -511,10 +513,7 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
         const long long grid = (long long)a.B * a.Hkv * hchunks * a.splits;
         if (grid > 0x7fffffffLL)
             return hipErrorInvalidConfiguration;
-#ifndef MIATTN_DECODE_NW
-#define MIATTN_DECODE_NW 2  // waves per split: LDS (16 KB per wave) allows 10 waves per CU
-#endif
-        constexpr int NW = MIATTN_DECODE_NW;
+        constexpr int NW = 2;  // waves per split: LDS (16 KB per wave) allows 10 waves per CU
         hipLaunchKernelGGL((decode_mfma_kernel<D, NW, PAGED>), dim3((unsigned)grid), dim3(64 * NW), 0,
                            stream, a, hchunks);
         e = hipGetLastError();

@@ -65,9 +65,6 @@ hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream);
 // head dimensions 128 and 256: the software-pipelined kernel of
 // prefill_q64.hip, the default for both
 hipError_t launch_fwd_q64(const FwdArgs &a, int d, bool causal, hipStream_t stream);
-// head dimension 128: the two-wave ping-pong kernel of prefill_pingpong.hip
-// (built in, selected with -DMIATTN_D128_PINGPONG)
-hipError_t launch_fwd_pingpong(const FwdArgs &a, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t stream);
 // head dimensions 64 and 128: the backward kernels of backward.hip
 hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, hipStream_t stream);

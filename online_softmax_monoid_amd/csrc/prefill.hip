@@ -31,9 +31,7 @@
 // first; the query heads of one GQA group sharing a kv-head are adjacent.
 //
 // Head dimension 64 uses this kernel; head dimensions 128 and 256 the
-// software-pipelined kernel of prefill_q64.hip (this one with
-// -DMIATTN_D128_SIMPLE / -DMIATTN_D256_SIMPLE; at 128 the two-wave ping-pong
-// kernel of prefill_pingpong.hip with -DMIATTN_D128_PINGPONG).
+// software-pipelined persistent kernel of prefill_q64.hip.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -117,7 +115,7 @@ struct Cfg {
 // Score modifiers: none, soft cap, ALiBi
 enum { kModNone = 0, kModSoftcap = 1, kModAlibi = 2 };
 
-template <int D, int BN, int NW, bool PIPE, bool CAUSAL, int MOD>
+template <int D, int BN, int NW, bool CAUSAL, int MOD>
 __global__ void __launch_bounds__(NW * 64)
 fwd_kernel(FwdArgs a, int n_qtiles)
 {
@@ -179,10 +177,9 @@ fwd_kernel(FwdArgs a, int n_qtiles)
     }
 
     // ---- staging (a2) -----------------------------------------------------
-    // K runs one tile ahead of V: while tile j's softmax runs on the VALU, the
-    // MFMAs already compute tile j+1's scores. LDS holds K tiles j+1 (being
-    // read) and V tile j; the global loads of K tile j+2 and V tile j+1 are in
-    // flight in registers meanwhile and land in the buffers freed by tile j-1.
+    // K and V tiles travel together through registers into double buffers:
+    // while tile j computes from LDS, the global loads of tile j+1 are in
+    // flight in registers and land in the buffers freed by tile j-1.
     uint4 kreg[C::KPT];
     uint4 vreg[C::VPT][4];
 
@@ -380,7 +377,7 @@ fwd_kernel(FwdArgs a, int n_qtiles)
     // barriers; fully masked tiles of a wave are skipped).
     const int nwb = (max(0, wave_end - kofs) + BN - 1) / BN;
 
-    // ---- prologue: K tiles 0 and 1, V tile 0; scores of tile 0 -------------
+    // ---- prologue: K and V tile 0 -----------------------------------------
     // Staged on every path (an empty key range reads zeros), then all global
     // loads are drained, so none issued before the loop is still in flight in
     // it: the prefetch issued inside the loop is waited on only where its
@@ -389,55 +386,35 @@ fwd_kernel(FwdArgs a, int n_qtiles)
     load_v(0);
     store_k(0);
     store_v(0);
-    if (PIPE && nblk > 1) {
-        load_k(1);
-        store_k(1);
-    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
-    f32x16 sa[BN / 32], sb[BN / 32];
-    if (PIPE && nwb > 0)
-        scores(0, sa);
-
-    // one pipelined step: softmax + PV of tile j (scores in `cur`) while the
-    // MFMAs compute tile j+1's scores into `nxt`; then restage and sync.
-    // Without PIPE, K and V tiles travel together and the scores of tile j
-    // are computed at the start of step j.
-    auto step = [&](int j, f32x16 (&cur)[BN / 32], f32x16 (&nxt)[BN / 32]) {
-        constexpr int KA = PIPE ? 2 : 1;  // how far K is staged ahead
-        if (j + KA < nblk)
-            load_k(j + KA);
-        if (j + 1 < nblk)
+    // one step: the loads of tile j+1 go out, tile j's scores, softmax and PV
+    // run from LDS, then tile j+1 is stored into the other buffers and the
+    // workgroup syncs
+    f32x16 s[BN / 32];
+    for (int j = 0; j < nblk; ++j) {
+        if (j + 1 < nblk) {
+            load_k(j + 1);
             load_v(j + 1);
-        if (j < nwb) {
-            if (PIPE) {
-                if (j + 1 < nwb)
-                    scores((j + 1) & 1, nxt);
-            } else {
-                scores(j & 1, cur);
-            }
-            softmax_pv(j, cur);
         }
-        if (j + KA < nblk)
-            store_k((j + KA) & 1);
-        if (j + 1 < nblk)
+        if (j < nwb) {
+            scores(j & 1, s);
+            softmax_pv(j, s);
+        }
+        if (j + 1 < nblk) {
+            store_k((j + 1) & 1);
             store_v((j + 1) & 1);
+        }
         __syncthreads();
-    };
-
-    int j = 0;
-    for (; j + 1 < nblk; j += 2) {
-        step(j, sa, sb);
-        step(j + 1, sb, sa);
     }
-    if (j < nblk)
-        step(j, sa, sb);
 
     // ---- epilogue (a6) ----------------------------------------------------
     const float l_tot = halves_sum(l_half);
     if (my_q < Sq) {
-        const bool empty = !(l_tot > 0.f);
+        // a row that saw a key has l >= 1 relative to its reference; l = 0
+        // exactly means no key, and a NaN sum propagates
+        const bool empty = l_tot == 0.f;
         const float inv = empty ? 0.f : 1.f / l_tot;
         uint16_t *orow = a.o + (qrow0 + my_q) * D + 4 * g;
 #pragma unroll
@@ -458,7 +435,7 @@ fwd_kernel(FwdArgs a, int n_qtiles)
     }
 }
 
-template <int D, int BN, int NW, bool PIPE, bool CAUSAL, int MOD>
+template <int D, int BN, int NW, bool CAUSAL, int MOD>
 hipError_t launch_mod(const FwdArgs &a, hipStream_t stream)
 {
     constexpr int BM = NW * 32;
@@ -466,61 +443,36 @@ hipError_t launch_mod(const FwdArgs &a, hipStream_t stream)
     const long long n_tiles = (long long)a.B * a.Hq * n_qtiles;
     if (n_tiles > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_kernel<D, BN, NW, PIPE, CAUSAL, MOD>), dim3((unsigned)n_tiles), dim3(NW * 64),
+    hipLaunchKernelGGL((fwd_kernel<D, BN, NW, CAUSAL, MOD>), dim3((unsigned)n_tiles), dim3(NW * 64),
                        0, stream, a, n_qtiles);
     return hipGetLastError();
 }
 
-template <int D, int BN, int NW, bool PIPE, bool CAUSAL>
+template <int D, int BN, int NW, bool CAUSAL>
 hipError_t launch(const FwdArgs &a, hipStream_t stream)
 {
     if (a.softcap > 0.f)
-        return launch_mod<D, BN, NW, PIPE, CAUSAL, kModSoftcap>(a, stream);
+        return launch_mod<D, BN, NW, CAUSAL, kModSoftcap>(a, stream);
     if (a.alibi != nullptr)
-        return launch_mod<D, BN, NW, PIPE, CAUSAL, kModAlibi>(a, stream);
-    return launch_mod<D, BN, NW, PIPE, CAUSAL, kModNone>(a, stream);
+        return launch_mod<D, BN, NW, CAUSAL, kModAlibi>(a, stream);
+    return launch_mod<D, BN, NW, CAUSAL, kModNone>(a, stream);
 }
 
 }  // namespace
 
 // Tile configuration per head dimension: <BN keys per tile, NW waves,
 // K staged one tile ahead of V>.
-#ifndef MIATTN_FWD_D64
-#define MIATTN_FWD_D64 64, 4, false
-#endif
-#ifndef MIATTN_FWD_D128
-#define MIATTN_FWD_D128 64, 4, false
-#endif
-#ifndef MIATTN_FWD_D256
-#define MIATTN_FWD_D256 64, 4, false
-#endif
-
 hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
 {
     if (a.cu_q != nullptr)  // packed variable-length batches: the persistent kernel only
         return d == 64 ? hipErrorNotSupported : launch_fwd_q64(a, d, causal, stream);
     switch (d) {
-    case 64:
-        return causal ? launch<64, MIATTN_FWD_D64, true>(a, stream)
-                      : launch<64, MIATTN_FWD_D64, false>(a, stream);
+    case 64:  // 64-key tiles, four waves of 32 query rows
+        return causal ? launch<64, 64, 4, true>(a, stream)
+                      : launch<64, 64, 4, false>(a, stream);
     case 128:
-#if defined(MIATTN_D128_SIMPLE)
-        return causal ? launch<128, MIATTN_FWD_D128, true>(a, stream)
-                      : launch<128, MIATTN_FWD_D128, false>(a, stream);
-#elif defined(MIATTN_D128_PINGPONG)
-        if (a.window >= 0 || a.softcap > 0.f || a.alibi != nullptr)  // not in the ping-pong kernel
-            return launch_fwd_q64(a, 128, causal, stream);
-        return launch_fwd_pingpong(a, causal, stream);
-#else
-        return launch_fwd_q64(a, 128, causal, stream);
-#endif
     case 256:
-#if defined(MIATTN_D256_SIMPLE)
-        return causal ? launch<256, MIATTN_FWD_D256, true>(a, stream)
-                      : launch<256, MIATTN_FWD_D256, false>(a, stream);
-#else
-        return launch_fwd_q64(a, 256, causal, stream);
-#endif
+        return launch_fwd_q64(a, d, causal, stream);
     default:
         return hipErrorInvalidValue;
     }

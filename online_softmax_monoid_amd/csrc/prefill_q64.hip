@@ -5,9 +5,8 @@
 // two gfx950 limits measured on the simpler kernel:
 //
 //  * LDS read bandwidth (about 150-200 bytes/ns per CU): every 16-byte K or V
-//    fragment a wave reads from LDS feeds one 32x32x16 MFMA per 32-row query
-//    block the wave owns. The kernel is written for QB = 1 or 2 blocks per
-//    wave (32 or 64 query rows).
+//    fragment a wave reads from LDS feeds one 32x32x16 MFMA for the 32 query
+//    rows the wave owns.
 //  * VALU issue: the softmax costs about four VALU instructions and one
 //    v_exp_f32 per score, roughly what the score's MFMA share takes on the
 //    matrix unit. A wave can issue independent VALU work while its own MFMA
@@ -30,8 +29,8 @@
 //            tile j+1; LDS reads of K_{j+2}
 //
 // K and V tiles of 32 keys go global -> LDS by range-checked buffer DMA (keys
-// past the item's last visible key arrive as zeros) into rings of RING tiles
-// (four by default), one barrier per tile. Both are stored fragment-major:
+// past the item's last visible key arrive as zeros) into rings of four tiles,
+// one barrier per tile. Both are stored fragment-major:
 // each LDS read instruction
 // of a wave reads one contiguous 1 KB (K, ds_read_b128) or 512 B (V,
 // ds_read_b64_tr_b16) block, which is free of bank conflicts.
@@ -50,9 +49,8 @@
 //
 // The running maximum moves lazily: probabilities stay at most 2^8 above the
 // reference and the accumulator is rescaled only on the rare tiles that move
-// it. With two query blocks per wave the reference moves when a tile's row
-// maximum exceeds it by more than 8 in log2 units. With one block the check
-// uses the tile's row sums, which the softmax computes anyway: a lane whose
+// it. The check uses the tile's row sums, which the softmax computes anyway:
+// a lane whose
 // 16 probabilities sum to at most 2^8 has none above 2^8, and only a tile
 // that fails (or a wave with a row that has seen no key yet) takes the exact
 // maximum and recomputes its probabilities.
@@ -67,11 +65,6 @@
 #include "lds_copy.h"
 #include "resident.h"
 #include "tile_order.h"
-
-// Build switch: K/V ring depth (tiles, a power of two) at head dimension 128
-#ifndef MIATTN_Q64_D128_RING
-#define MIATTN_Q64_D128_RING 4
-#endif
 
 namespace miattn {
 namespace {
@@ -170,12 +163,13 @@ struct Item {
 // Score modifiers: none, soft cap, ALiBi
 enum { kModNone = 0, kModSoftcap = 1, kModAlibi = 2 };
 
-template <bool CAUSAL, int NWV, int D, int QB, int WPE, bool WIN, int MOD, bool VARLEN>
+template <bool CAUSAL, int NWV, int D, int WPE, bool WIN, int MOD, bool VARLEN>
 __global__ void __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 {
-    // D = 128 runs QB = 1 (32 rows, two waves per SIMD) or 2 (64 rows, one
-    // wave per SIMD) query blocks per wave, D = 256 one block
+    // one block of 32 query rows per wave (the state arrays below keep a
+    // query-block index of extent QB = 1)
+    constexpr int QB = 1;
     constexpr int BN = 32;             // keys per tile
     constexpr int BM = NWV * 32 * QB;  // query rows per work item
     constexpr int KKN = D / 16;        // 16-dim steps of QK = K fragments = copy instructions per tile
@@ -184,9 +178,9 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     constexpr int NG = QB * KKN / 4;   // groups of four MFMAs per stage
     constexpr int NPV = QB * DBN;      // PV MFMAs per 16-key chunk
     // K and V rings of RING tiles: K tile j+RING and V tile j+RING-1 are copied
-    // in step j (eight tiles of 8 KB each at head dimension 128, four of 16 KB
-    // at 256, within the 160 KB of LDS)
-    constexpr int RING = D == 128 ? MIATTN_Q64_D128_RING : 4;
+    // in step j (8 KB per tile at head dimension 128, 16 KB at 256: 64 or
+    // 128 KB of the 160 KB of LDS)
+    constexpr int RING = 4;
     constexpr int INFLIGHT = DPW + 2 * DPW * (RING - 3);  // copies newer than K tile j+3 at step j's end
     static_assert((RING & (RING - 1)) == 0 && RING >= 4, "ring of 2^n >= 4 tiles");
     static_assert((NG == 2 || NG == 4) && NWV * DPW == KKN && INFLIGHT < 64, "tile step shape");
@@ -503,13 +497,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
             e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * h + 4 * quad + i], c, nmc[qb]));
         p[qb][h].w[2 * quad] = pack_bf16x2(e[0], e[1]);
         p[qb][h].w[2 * quad + 1] = pack_bf16x2(e[2], e[3]);
-        if constexpr (QB == 1) {
-            tsum += (e[0] + e[1]) + (e[2] + e[3]);
-            pin(tsum);
-        } else {
-            l_half[qb] += (e[0] + e[1]) + (e[2] + e[3]);
-            pin(l_half[qb]);
-        }
+        tsum += (e[0] + e[1]) + (e[2] + e[3]);
+        pin(tsum);
         pin(p[qb][h].w[2 * quad]);
         pin(p[qb][h].w[2 * quad + 1]);
     };
@@ -517,7 +506,6 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // q.k before the scale): the soft cap keeps (cap / scale) tanh(s scale /
     // cap), tanh(x) = 1 - 2 / (exp(2x) + 1); ALiBi subtracts (slope / scale)
     // times the distance |i + Sk - Sq - key|. Applied before the mask.
-    static_assert(MOD == kModNone || QB == 1, "score modifiers need one query block per wave");
     const float sc_in = MOD == kModSoftcap ? 2.f * a.scale / a.softcap * kLog2e : 0.f;
     const float sc_out = MOD == kModSoftcap ? a.softcap / a.scale : 0.f;
     auto modify_tile = [&](Sc &s, int j) __attribute__((always_inline)) {
@@ -678,8 +666,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
             probs_quad(sA, pA, qb, 0, 1);
         }
         apply_alpha();  // the first reference moves consume their rescale here
-        if constexpr (QB == 1)
-            ref_unset = __any(m_ref[0] == -INFINITY);
+        ref_unset = __any(m_ref[0] == -INFINITY);
 #pragma unroll
         for (int kk = 0; kk < KKN; ++kk)
             read_k(kread_addr(ph + 1), kk);
@@ -731,15 +718,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         pin(kread);
         pin(vread);
         step_copies(j);
-        if constexpr (QB == 2)
-            apply_alpha();
         slot_end();
 
-        // Stage A, NG groups of four MFMAs (QK of tile j+1; with two query
-        // blocks, block 0 then block 1). Groups 0-1 read V_j; the groups
-        // compute chunk 1 of tile j's probabilities and, with two query
-        // blocks, in groups 2-3 the row maximum of block 0 of tile j+1 (its
-        // MFMAs finished in group 1).
+        // Stage A, NG groups of four MFMAs (QK of tile j+1). Groups 0-1 read
+        // V_j and compute chunk 1 of tile j's probabilities.
         constexpr int NRV = 2 * DBN;  // read_v calls per tile (two reads each)
 #pragma unroll
         for (int grp = 0; grp < NG; ++grp) {
@@ -752,16 +734,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
                     for (int c = sl * NRV / 8; c < (sl + 1) * NRV / 8; ++c)
                         read_v(vread, c >> 1, c & 1);
             }
-            if (grp < 2 * QB)
-                probs_quad(sc, pc, grp >> 1, 1, grp & 1);
-            if constexpr (QB == 2) {
-                if (grp == 2)
-                    row_max(sn, 0, 0, j + 1, MASK);
-                if (grp == 3) {
-                    row_max(sn, 0, 1, j + 1, MASK);
-                    row_max(sn, 0, 2, j + 1, MASK);
-                }
-            }
+            if (grp < 2)
+                probs_quad(sc, pc, 0, 1, grp);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -771,19 +745,12 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
             }
             slot_end();
         }
-        if constexpr (QB == 2) {
-            move_ref(0);
-            slot_end();
-        } else {
-            check_tile(sc, pc);  // tile j's probabilities are complete
-            slot_end();
-        }
+        check_tile(sc, pc);  // tile j's probabilities are complete
+        slot_end();
 
         // Stage B, NG groups of four MFMAs (PV of tile j). Each group reads
-        // D/64 K_{j+2} fragments. With two query blocks, groups 0-1 compute
-        // chunk 0 of tile j+1 for block 0 and the row maximum of block 1,
-        // groups 2-3 chunk 0 for block 1 after its reference update; with one,
-        // group 0 takes the row maximum and groups 1-2 chunk 0.
+        // KKN/NG K_{j+2} fragments. Group 0 applies the score modifier and the
+        // mask to tile j+1, the next groups compute its chunk 0.
         constexpr int KPG = KKN / NG;  // K reads per group
 #pragma unroll
         for (int grp = 0; grp < NG; ++grp) {
@@ -791,30 +758,20 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
             for (int i = 0; i < 4; ++i) {
                 const int sl = 4 * grp + i;
                 const int idx = sl % NPV;
-                pv_mfma(pc, idx % QB, idx / QB, sl / NPV);
+                pv_mfma(pc, 0, idx, sl / NPV);
                 if (i < KPG)
                     read_k(kread, KPG * grp + i);
             }
-            if constexpr (QB == 2) {
-                probs_quad(sn, pn, grp >> 1, 0, grp & 1);
-                if (grp == 0)
-                    row_max(sn, 1, 0, j + 1, MASK);
-                if (grp == 1) {
-                    row_max(sn, 1, 1, j + 1, MASK);
-                    row_max(sn, 1, 2, j + 1, MASK);
-                }
-            } else {
-                if (MOD != kModNone && grp == 0)
-                    modify_tile(sn, j + 1);
-                if (MASK && grp == 0)
-                    mask_tile(sn, 0, j + 1);
-                if (NG == 2 && grp == 1) {
-                    probs_quad(sn, pn, 0, 0, 0);
-                    probs_quad(sn, pn, 0, 0, 1);
-                }
-                if (NG == 4 && (grp == 1 || grp == 2))
-                    probs_quad(sn, pn, 0, 0, grp - 1);
+            if (MOD != kModNone && grp == 0)
+                modify_tile(sn, j + 1);
+            if (MASK && grp == 0)
+                mask_tile(sn, 0, j + 1);
+            if (NG == 2 && grp == 1) {
+                probs_quad(sn, pn, 0, 0, 0);
+                probs_quad(sn, pn, 0, 0, 1);
             }
+            if (NG == 4 && (grp == 1 || grp == 2))
+                probs_quad(sn, pn, 0, 0, grp - 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -823,10 +780,6 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
             }
             slot_end();
-            if (QB == 2 && grp == 1) {
-                move_ref(QB - 1);
-                slot_end();
-            }
         }
         step_end();
     };
@@ -855,7 +808,9 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         for (int qb = 0; qb < QB; ++qb) {
             const int my_q = q0 + 32 * qb + l32;
             const float l_tot = halves_sum(l_half[qb]);
-            const bool empty = !(l_tot > 0.f);
+            // l = 0 exactly only for a row that saw no key (otherwise l >= 1
+            // relative to the reference); a NaN sum propagates
+            const bool empty = l_tot == 0.f;
             const float inv = empty ? 0.f : __builtin_amdgcn_rcpf(l_tot);
             uint16_t *orow = a.o + (qrow0 + min(my_q, Sq - 1)) * D + 8 * g;
 #pragma unroll
@@ -1014,28 +969,12 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy may still target LDS
 }
 
-// Build switches for measuring other shapes: the number of waves per
-// workgroup at each head dimension, and 64 (QB=2, one wave per SIMD) or 32
-// (QB=1, two waves per SIMD) query rows per wave at head dimension 128.
-#ifndef MIATTN_Q64_D128_QB
-#define MIATTN_Q64_D128_QB 1
-#endif
-#ifndef MIATTN_Q64_D128_WAVES
-#define MIATTN_Q64_D128_WAVES 8
-#endif
-#ifndef MIATTN_Q64_D256_WAVES
-#define MIATTN_Q64_D256_WAVES 4
-#endif
-#ifndef MIATTN_Q64_D128_WPE  // waves per SIMD the d = 128 kernel is compiled for
-#define MIATTN_Q64_D128_WPE (2 * MIATTN_Q64_D128_WAVES / 8)
-#endif
-
 // One workgroup per resident slot (a multiple of 8, so that each XCD holds the
 // same number), each walking its share of the n_items work items.
-template <bool CAUSAL, int D, int QB, int NWV, int WPE, bool WIN, int MOD, bool VARLEN = false>
+template <bool CAUSAL, int D, int NWV, int WPE, bool WIN, int MOD, bool VARLEN = false>
 hipError_t launch_q64_t(const FwdArgs &a, int n_qtiles, int n_items, hipStream_t stream)
 {
-    const auto kernel = fwd_q64_kernel<CAUSAL, NWV, D, QB, WPE, WIN, MOD, VARLEN>;
+    const auto kernel = fwd_q64_kernel<CAUSAL, NWV, D, WPE, WIN, MOD, VARLEN>;
     const int resident = resident_workgroups(kernel, 64 * NWV);
     if (resident < 8)
         return hipErrorInvalidConfiguration;
@@ -1045,20 +984,21 @@ hipError_t launch_q64_t(const FwdArgs &a, int n_qtiles, int n_items, hipStream_t
     return hipGetLastError();
 }
 
-template <int D, int QB, int NWV, int WPE, int MOD>
+template <int D, int NWV, int WPE, int MOD>
 hipError_t dispatch_win(const FwdArgs &a, bool causal, int n_qtiles, int n, hipStream_t stream)
 {
     if (a.window >= 0)
-        return causal ? launch_q64_t<true, D, QB, NWV, WPE, true, MOD>(a, n_qtiles, n, stream)
-                      : launch_q64_t<false, D, QB, NWV, WPE, true, MOD>(a, n_qtiles, n, stream);
-    return causal ? launch_q64_t<true, D, QB, NWV, WPE, false, MOD>(a, n_qtiles, n, stream)
-                  : launch_q64_t<false, D, QB, NWV, WPE, false, MOD>(a, n_qtiles, n, stream);
+        return causal ? launch_q64_t<true, D, NWV, WPE, true, MOD>(a, n_qtiles, n, stream)
+                      : launch_q64_t<false, D, NWV, WPE, true, MOD>(a, n_qtiles, n, stream);
+    return causal ? launch_q64_t<true, D, NWV, WPE, false, MOD>(a, n_qtiles, n, stream)
+                  : launch_q64_t<false, D, NWV, WPE, false, MOD>(a, n_qtiles, n, stream);
 }
 
-template <int D, int QB, int NWV, int WPE>
+// NWV waves of 32 query rows per workgroup, WPE waves per SIMD
+template <int D, int NWV, int WPE>
 hipError_t launch_q64(const FwdArgs &a, bool causal, hipStream_t stream)
 {
-    constexpr int BM = NWV * 32 * QB;
+    constexpr int BM = NWV * 32;
     const int n_qtiles = (a.Sq + BM - 1) / BM;
     const long long n_items = (long long)a.B * a.Hq * n_qtiles;
     // item ids, and 8 GX per round past the last one, stay within int
@@ -1070,34 +1010,28 @@ hipError_t launch_q64(const FwdArgs &a, bool causal, hipStream_t stream)
     if (a.cu_q != nullptr) {  // packed variable-length batch: no window or modifier
         if (a.window >= 0 || a.softcap > 0.f || a.alibi != nullptr)
             return hipErrorNotSupported;
-        return causal ? launch_q64_t<true, D, QB, NWV, WPE, false, kModNone, true>(a, n_qtiles, n, stream)
-                      : launch_q64_t<false, D, QB, NWV, WPE, false, kModNone, true>(a, n_qtiles, n, stream);
+        return causal ? launch_q64_t<true, D, NWV, WPE, false, kModNone, true>(a, n_qtiles, n, stream)
+                      : launch_q64_t<false, D, NWV, WPE, false, kModNone, true>(a, n_qtiles, n, stream);
     }
-    if constexpr (QB == 1) {
-        if (a.softcap > 0.f)
-            return dispatch_win<D, QB, NWV, WPE, kModSoftcap>(a, causal, n_qtiles, n, stream);
-        if (a.alibi != nullptr)
-            return dispatch_win<D, QB, NWV, WPE, kModAlibi>(a, causal, n_qtiles, n, stream);
-    } else {
-        if (a.softcap > 0.f || a.alibi != nullptr)
-            return hipErrorNotSupported;
-    }
-    return dispatch_win<D, QB, NWV, WPE, kModNone>(a, causal, n_qtiles, n, stream);
+    if (a.softcap > 0.f)
+        return dispatch_win<D, NWV, WPE, kModSoftcap>(a, causal, n_qtiles, n, stream);
+    if (a.alibi != nullptr)
+        return dispatch_win<D, NWV, WPE, kModAlibi>(a, causal, n_qtiles, n, stream);
+    return dispatch_win<D, NWV, WPE, kModNone>(a, causal, n_qtiles, n, stream);
 }
 
 }  // namespace
 
+// Head dimension 128: eight waves (two per SIMD, 256 query rows per item);
+// 256: four waves (one per SIMD, the f32 accumulator alone takes 128
+// registers)
 hipError_t launch_fwd_q64(const FwdArgs &a, int d, bool causal, hipStream_t stream)
 {
     switch (d) {
     case 128:
-#if MIATTN_Q64_D128_QB == 1
-        return launch_q64<128, 1, MIATTN_Q64_D128_WAVES, MIATTN_Q64_D128_WPE>(a, causal, stream);
-#else
-        return launch_q64<128, 2, MIATTN_Q64_D128_WAVES, MIATTN_Q64_D128_WAVES / 4>(a, causal, stream);
-#endif
+        return launch_q64<128, 8, 2>(a, causal, stream);
     case 256:
-        return launch_q64<256, 1, MIATTN_Q64_D256_WAVES, MIATTN_Q64_D256_WAVES / 4>(a, causal, stream);
+        return launch_q64<256, 4, 1>(a, causal, stream);
     default:
         return hipErrorInvalidValue;
     }

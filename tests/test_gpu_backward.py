@@ -5,13 +5,18 @@ O and LSE, the backward's inputs from the forward, come from the oracle
 one case feeds it the GPU forward's outputs instead. The expected gradients
 are the oracle's f64 dQ, dK, dV from Q, K, V and dO alone.
 
-Tolerance, per gradient tensor: relative RMS error <= 2e-2 and max-abs error
-<= 5e-2 of the tensor's largest magnitude. The kernel rounds P and dS to
-bf16 for the MFMAs (2^-9 relative each), reads O in bf16 for D = dO.O, and
-rounds the results to bf16: each a 2^-9 relative error, and dS = P (dP - D)
-cancels where dP is close to D, so the relative error per element is larger
-than per tensor; the RMS bound allows for the sum of these four roundings
-with margin, the max bound for the cancellation.
+Tolerance, per gradient tensor: relative RMS error <= 8e-3 and max-abs error
+<= 1.2e-2 of the tensor's largest magnitude. The error budget: the kernels
+round four quantities to bf16 (RNE, relative error up to 2^-8 and about
+2^-9 / sqrt(3) = 1.1e-3 RMS each): P and dS before their MFMAs, O (read for
+D_i = dO_i . O_i) and the gradients themselves. Summed over many rows with
+independent signs these give about 1.6e-3 RMS for dV (P and the result) and
+about 2.2e-3 for dK and dQ (dS, O through D, the result), plus the f32
+accumulation (1e-6). dS = P (dP - D) cancels where dP is close to D, which
+scales one term's relative error up, so single elements reach a few times the
+RMS. Measured on every case: rel-RMS 2.1-2.9e-3, max 2.5-4.3e-3 of the tensor
+maximum; the bounds sit at about three times that, so an error one rounding
+larger than the budget fails.
 """
 from __future__ import annotations
 
@@ -26,7 +31,7 @@ from online_softmax_monoid_amd import inputs
 from tests import harness as H
 
 pytestmark = pytest.mark.gpu
-REL_RMS, MAX_REL = 2e-2, 5e-2
+REL_RMS, MAX_REL = 8e-3, 1.2e-2
 
 
 def _note(msg):
@@ -94,8 +99,9 @@ def test_backward_after_the_gpu_forward():
 def test_backward_workload_full_size_sampled_heads():
     """The bench's backward: the prefill workload (B2 H32 S4096 d128 causal),
     the GPU forward's O and LSE feeding the backward, in the bench's launch
-    configuration; two (batch, head) slices checked against the oracle, which
-    computes them from Q, K, V and dO alone (one query head per kv-head)."""
+    configuration; four (batch, head) slices checked against the oracle,
+    which computes them from Q, K, V and dO alone (one query head per
+    kv-head)."""
     w = inputs.WORKLOADS[3]
     q, k, v = inputs.prefill_inputs(w)
     do = _bits(w.seed + 11, (w.B, w.Hq, w.Sq, w.d))
@@ -103,13 +109,29 @@ def test_backward_workload_full_size_sampled_heads():
     o_bits, lse, _ = H.run_fwd(q, k, v, True, w.scale)
     dq, dk, dv, guards = H.run_bwd(q, k, v, o_bits, lse, do, True, w.scale)
     assert guards
-    for b, h in ((0, 0), (1, 31)):
+    for b, h in ((0, 0), (0, 17), (1, 6), (1, 31)):
         sl = (slice(b, b + 1), slice(h, h + 1))
         rq, rk, rv = bw.attn_bwd(q[sl], k[sl], v[sl], do[sl], True, w.scale)
         for name, got, ref in (("dq", dq[sl], rq), ("dk", dk[sl], rk), ("dv", dv[sl], rv)):
             m = H.grad_metrics(got, ref)
             _note(f"[gpu] backward workload b={b} h={h} {name}: {m}")
             assert m["finite"] and m["rel_rms"] <= REL_RMS and m["max_abs_rel"] <= MAX_REL, m
+
+
+@pytest.mark.parametrize("d", [128])
+def test_backward_gqa_full(d):
+    """Grouped-query heads at a size with many query tiles per key tile:
+    B1 Hq8 Hkv2 S2048 causal, forward and backward on the GPU, every element
+    of dQ, dK and dV against the oracle (dK and dV of a kv-head sum over its
+    four query heads)."""
+    B, Hq, Hkv, S = 1, 8, 2, 2048
+    q = _bits(8300 + d, (B, Hq, S, d), 0.5)
+    k = _bits(8301 + d, (B, Hkv, S, d), 0.5)
+    v = _bits(8302 + d, (B, Hkv, S, d))
+    do = _bits(8303 + d, (B, Hq, S, d))
+    scale = inputs.default_scale(d)
+    o_bits, lse, _ = H.run_fwd(q, k, v, True, scale)
+    _check(q, k, v, do, True, scale, f"bwd gqa full d={d}", o_bits=o_bits, lse=lse)
 
 
 @pytest.mark.parametrize("Sq,Sk", [(40, 0), (0, 40)])

@@ -4,8 +4,9 @@ Every case draws seeded bf16 inputs, runs libmiattn on the GPU with
 NaN-prefilled outputs and guard regions, and compares with the oracle on the
 same bits at O max-abs 1e-2, O rel-RMS 4e-3 and LSE max-abs 1e-3; rows with
 no visible key must be exactly (+0, -inf). The five workloads run at full
-size in the launch configuration the bench times; the two largest are checked
-on sampled rows, every row of the others is checked.
+size in the launch configuration the bench times; the long-context workload
+(B1 Hq16 Hkv2 S44032 d256) is checked on 512 sampled rows per head plus the
+first and last row, every row of the others is checked.
 """
 from __future__ import annotations
 
@@ -42,7 +43,7 @@ def _check_full(q, k, v, causal, scale, label):
     return o, lse
 
 
-@pytest.mark.parametrize("wid,causal", [(1, False), (2, True), (2, False)])
+@pytest.mark.parametrize("wid,causal", [(1, False), (2, True), (2, False), (3, True)])
 def test_workload_full_rows(wid, causal):
     w = inputs.WORKLOADS[wid]
     q, k, v = inputs.prefill_inputs(w)
@@ -68,7 +69,7 @@ def test_workload1_against_unrounded_fp32_draws():
     assert m["o_rel_rms"] <= H.O_REL_RMS and m["o_max_abs"] <= H.O_MAX_ABS
 
 
-@pytest.mark.parametrize("wid,rows_per_head", [(3, 64), (4, 512)])
+@pytest.mark.parametrize("wid,rows_per_head", [(4, 512)])
 def test_workload_sampled_rows(wid, rows_per_head):
     w = inputs.WORKLOADS[wid]
     _note(f"[gpu] workload {wid}: drawing inputs")

@@ -38,14 +38,32 @@ class MiattnError(RuntimeError):
 _lib = None
 
 
+def bind_to_torch_runtime():
+    """Import torch (when installed) before a HIP library is loaded.
+
+    torch ships its own HIP runtime (libamdhip64, soname .so.7, loaded by its
+    file name). A library that needs libamdhip64.so.7 and is loaded after
+    torch binds to that same runtime; loaded before torch, it brings in the
+    system runtime, torch then loads its own, and a process with two HIP
+    (and two HSA) runtimes sees the GPU in only one of them: streams and
+    device memory from torch would not belong to the runtime the kernels
+    are launched on."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+
+
 def load(path: str = LIB_PATH):
-    """Load the library (building it first if no build exists)."""
+    """Load the library (building it first if no build exists), after torch
+    so that both use one HIP runtime."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
         from . import build as _build
         _build.build(out=path)
+    bind_to_torch_runtime()
     L = ctypes.CDLL(path)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]

@@ -244,6 +244,33 @@ MIATTN_API int attn_fwd_decode(const void *q, const void *k_cache, const void *v
                     hipStream_t stream);
 
 /*
+ * Decode forward that allocates nothing and takes no workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. It is attn_fwd_decode (same
+ * arguments without the workspace, same kernels, bit-identical results) with
+ * the split partials in a fixed scratch array of 16 MiB that the library
+ * holds in device memory: each device the library runs on keeps its own copy
+ * from the first call on that device until the process ends (that first call
+ * looks up the array's device address, so make it before any graph
+ * capture).
+ *
+ *   q, k_cache, v_cache, kv_lens, o, lse, B, Hq, Hkv, S_cap, d, num_splits,
+ *   scale, stream: as for attn_fwd_decode.
+ *
+ * Limit: attn_fwd_decode_workspace_size(B, Hq, d, num_splits) must be at most
+ * 16 MiB (e.g. B = 32, Hq = 32, d = 128, 16 splits takes 8.5 MB), else
+ * MIATTN_ERR_UNSUPPORTED and nothing is launched. Every call on one device
+ * shares that device's scratch and needs no clearing (each call writes every
+ * partial it reads), but calls that may overlap on one device (different
+ * streams, or threads without ordering) race on it and must be serialised
+ * by the caller.
+ */
+MIATTN_API int attn_fwd_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                            const int *kv_lens, void *o, float *lse, int B, int Hq,
+                            int Hkv, int S_cap, int d, int num_splits, float scale,
+                            hipStream_t stream);
+
+/*
  * Decode forward over a paged KV cache: attn_fwd_decode with each stream's
  * cache rows read through a block table. A paged cache is the paper's gather
  * view (§2.1 "Views": one source coordinate of a read comes from an index

@@ -152,19 +152,24 @@ size_t attn_fwd_decode_workspace_size(int B, int Hq, int d, int num_splits)
     return (size_t)B * (size_t)Hq * (size_t)num_splits * (size_t)(d + 2) * sizeof(float);
 }
 
-int attn_fwd_decode(const void *q, const void *k_cache, const void *v_cache, const int *kv_lens,
-                    void *o, float *lse, int B, int Hq, int Hkv, int S_cap, int d,
-                    int num_splits, float scale, void *workspace, size_t workspace_bytes,
-                    hipStream_t stream)
+// Checks shared by the contiguous decode entry points; fills everything of
+// `a` but the partials' location. *done: nothing to launch (B == 0).
+static int decode_common(const void *q, const void *k_cache, const void *v_cache,
+                         const int *kv_lens, void *o, float *lse, int B, int Hq, int Hkv,
+                         int S_cap, int d, int num_splits, float scale, miattn::DecodeArgs &a,
+                         bool *done)
 {
+    *done = false;
     if (B < 0 || S_cap < 0)
         return fail(MIATTN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d, S_cap=%d)", B, S_cap);
     MIATTN_TRY(check_heads_dim(Hq, Hkv, d));
     MIATTN_TRY(check_scale(scale));
     if (num_splits < 1)
         return fail(MIATTN_ERR_INVALID_ARG, "num_splits must be >= 1 (got %d)", num_splits);
-    if (B == 0)
+    if (B == 0) {
+        *done = true;
         return MIATTN_OK;
+    }
     MIATTN_TRY(check_ptr(q, "q", 16));
     MIATTN_TRY(check_ptr(o, "o", 16));
     MIATTN_TRY(check_ptr(lse, "lse", 4));
@@ -173,29 +178,67 @@ int attn_fwd_decode(const void *q, const void *k_cache, const void *v_cache, con
         MIATTN_TRY(check_ptr(k_cache, "k_cache", 16));
         MIATTN_TRY(check_ptr(v_cache, "v_cache", 16));
     }
-    MIATTN_TRY(check_ptr(workspace, "workspace", 16));
-    const size_t need = attn_fwd_decode_workspace_size(B, Hq, d, num_splits);
-    if (workspace_bytes < need)
-        return fail(MIATTN_ERR_INVALID_ARG, "workspace too small: %zu bytes, need %zu",
-                    workspace_bytes, need);
-    miattn::DecodeArgs a;
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k_cache);
     a.v = static_cast<const uint16_t *>(v_cache);
     a.lens = kv_lens;
     a.o = static_cast<uint16_t *>(o);
     a.lse = lse;
-    // workspace layout: acc partials [B,Hq,S,d] first (16-byte aligned rows),
-    // then (m, l) pairs [B,Hq,S,2]
-    a.part_acc = static_cast<float *>(workspace);
-    a.part_ml = a.part_acc + (size_t)B * Hq * num_splits * d;
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
     a.S_cap = S_cap;
     a.splits = num_splits;
     a.scale = scale;
+    return MIATTN_OK;
+}
+
+int attn_fwd_decode(const void *q, const void *k_cache, const void *v_cache, const int *kv_lens,
+                    void *o, float *lse, int B, int Hq, int Hkv, int S_cap, int d,
+                    int num_splits, float scale, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream)
+{
+    miattn::DecodeArgs a;
+    bool done = false;
+    MIATTN_TRY(decode_common(q, k_cache, v_cache, kv_lens, o, lse, B, Hq, Hkv, S_cap, d,
+                             num_splits, scale, a, &done));
+    if (done)
+        return MIATTN_OK;
+    MIATTN_TRY(check_ptr(workspace, "workspace", 16));
+    const size_t need = attn_fwd_decode_workspace_size(B, Hq, d, num_splits);
+    if (workspace_bytes < need)
+        return fail(MIATTN_ERR_INVALID_ARG, "workspace too small: %zu bytes, need %zu",
+                    workspace_bytes, need);
+    // workspace layout: acc partials [B,Hq,S,d] first (16-byte aligned rows),
+    // then (m, l) pairs [B,Hq,S,2]
+    a.part_acc = static_cast<float *>(workspace);
+    a.part_ml = a.part_acc + (size_t)B * Hq * num_splits * d;
     return hip_status(miattn::launch_decode(a, d, stream), "attn_fwd_decode launch");
+}
+
+int attn_fwd_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                            const int *kv_lens, void *o, float *lse, int B, int Hq, int Hkv,
+                            int S_cap, int d, int num_splits, float scale, hipStream_t stream)
+{
+    miattn::DecodeArgs a;
+    bool done = false;
+    MIATTN_TRY(decode_common(q, k_cache, v_cache, kv_lens, o, lse, B, Hq, Hkv, S_cap, d,
+                             num_splits, scale, a, &done));
+    if (done)
+        return MIATTN_OK;
+    const size_t need = attn_fwd_decode_workspace_size(B, Hq, d, num_splits);
+    if (need > miattn::decode_scratch_bytes())
+        return fail(MIATTN_ERR_UNSUPPORTED,
+                    "attn_fwd_decode_noalloc needs %zu bytes of partials; its fixed scratch "
+                    "holds %zu (B * Hq * num_splits * (d + 2) * 4 must fit; "
+                    "attn_fwd_decode takes a caller workspace of any size)",
+                    need, miattn::decode_scratch_bytes());
+    float *ws = nullptr;
+    MIATTN_TRY(hip_status(miattn::decode_scratch(&ws), "attn_fwd_decode_noalloc scratch"));
+    // the same layout as the workspace of attn_fwd_decode
+    a.part_acc = ws;
+    a.part_ml = a.part_acc + (size_t)B * Hq * num_splits * d;
+    return hip_status(miattn::launch_decode(a, d, stream), "attn_fwd_decode_noalloc launch");
 }
 
 int attn_fwd_decode_paged(const void *q, const void *k_pages, const void *v_pages,

@@ -29,6 +29,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "launch.h"
 
 namespace miattn {
@@ -528,6 +531,53 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t stream)
 }
 
 }  // namespace
+
+namespace {
+
+// Split partials of the entry point for callers that cannot allocate
+// (attn_fwd_decode_noalloc): a fixed array in device memory instead of a
+// caller workspace. Every device the library runs on holds its own copy
+// until the process ends. Host code never passes the array's name to a
+// kernel: the name is a host-side stand-in, the device address comes from
+// hipGetSymbolAddress below.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+}  // namespace
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the first call on a device, with that device current) and kept.
+hipError_t decode_scratch(float **out)
+{
+    constexpr int kMaxDev = 64;
+    static std::atomic<float *> addr[kMaxDev];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDev)
+        return hipErrorInvalidDevice;
+    float *p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            void *sym = nullptr;
+            e = hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return e;
+            if (sym == nullptr)
+                return hipErrorInvalidSymbol;
+            p = static_cast<float *>(sym);
+            addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t stream)
 {

@@ -66,6 +66,10 @@ hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream);
 // prefill_q64.hip, the default for both
 hipError_t launch_fwd_q64(const FwdArgs &a, int d, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t stream);
+// The library's fixed decode scratch (decode.hip): its size in bytes, and its
+// address on the current device (looked up on the first call per device).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(float **out);
 // head dimensions 64 and 128: the backward kernels of backward.hip
 hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, hipStream_t stream);
 

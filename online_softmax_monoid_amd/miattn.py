@@ -24,7 +24,7 @@ MIATTN_ERR_HIP = 3
 EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_fwd_ext", "attn_fwd_varlen", "attn_bwd",
            "attn_bwd_workspace_size",
            "attn_fwd_decode_workspace_size",
-           "attn_fwd_decode",
+           "attn_fwd_decode", "attn_fwd_decode_noalloc",
            "attn_fwd_decode_paged", "miattn_last_error", "miattn_version")
 
 
@@ -84,6 +84,8 @@ def load(path: str = LIB_PATH):
     L.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp,
                                   ctypes.c_size_t, vp]
     L.attn_fwd_decode.restype = i
+    L.attn_fwd_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_decode_noalloc.restype = i
     L.attn_fwd_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f,
                                         vp, ctypes.c_size_t, vp]
     L.attn_fwd_decode_paged.restype = i
@@ -170,6 +172,14 @@ def attn_fwd_decode(q, k_cache, v_cache, kv_lens, o, lse, B, Hq, Hkv, S_cap, d, 
                                   _addr(o), _addr(lse), int(B), int(Hq), int(Hkv), int(S_cap),
                                   int(d), int(num_splits), float(scale), _addr(workspace),
                                   int(workspace_bytes), _stream(stream)))
+
+
+def attn_fwd_decode_noalloc(q, k_cache, v_cache, kv_lens, o, lse, B, Hq, Hkv, S_cap, d,
+                            num_splits, scale, stream=None):
+    _check(load().attn_fwd_decode_noalloc(_addr(q), _addr(k_cache), _addr(v_cache),
+                                          _addr(kv_lens), _addr(o), _addr(lse), int(B), int(Hq),
+                                          int(Hkv), int(S_cap), int(d), int(num_splits),
+                                          float(scale), _stream(stream)))
 
 
 def attn_fwd_decode_paged(q, k_pages, v_pages, block_table, kv_lens, o, lse, B, Hq, Hkv,

@@ -184,6 +184,34 @@ def test_decode_empty_batch_is_a_no_op():
     assert _dec(B=0, q=0, k=0, v=0, lens=0, o=0, lse=0, ws=0, wsb=0) == M.MIATTN_OK
 
 
+def _dec_noalloc(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, lens=FAKE, o=FAKE, lse=FAKE, B=2, Hq=4, Hkv=2, S_cap=16,
+                d=128, ns=4, scale=0.1, stream=0)
+    args.update(kw)
+    return M.load().attn_fwd_decode_noalloc(args["q"], args["k"], args["v"], args["lens"],
+                                            args["o"], args["lse"], args["B"], args["Hq"],
+                                            args["Hkv"], args["S_cap"], args["d"], args["ns"],
+                                            args["scale"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=0), M.MIATTN_ERR_INVALID_ARG, "q is NULL"),
+    (dict(lens=0), M.MIATTN_ERR_INVALID_ARG, "kv_lens is NULL"),
+    (dict(v=FAKE + 8), M.MIATTN_ERR_INVALID_ARG, "aligned"),
+    (dict(ns=0), M.MIATTN_ERR_INVALID_ARG, "num_splits"),
+    (dict(d=80), M.MIATTN_ERR_UNSUPPORTED, "head dimension"),
+    # 64 * 64 * 16 * (256 + 2) * 4 bytes of partials: more than the 16 MiB scratch
+    (dict(B=64, Hq=64, Hkv=8, d=256, ns=16), M.MIATTN_ERR_UNSUPPORTED, "scratch"),
+])
+def test_attn_fwd_decode_noalloc_rejects(kw, status, needle):
+    assert _dec_noalloc(**kw) == status
+    assert needle in M.miattn_last_error()
+
+
+def test_decode_noalloc_empty_batch_is_a_no_op():
+    assert _dec_noalloc(B=0, q=0, k=0, v=0, lens=0, o=0, lse=0) == M.MIATTN_OK
+
+
 def _paged(**kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, table=FAKE, lens=FAKE, o=FAKE, lse=FAKE, B=2, Hq=4,
                 Hkv=2, num_pages=8, page_size=16, max_pages=4, d=128, ns=4, scale=0.1, ws=FAKE,

@@ -15,7 +15,12 @@ HBM before the timed region starts. The f64 oracle, timed on a bounded row
 sample of the prefill workload on the host cores, is reported as a baseline.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
-    python bench.py --profile-pass   # short fixed launch sequence for rocprofv3
+    python bench.py --profile-pass   # every bench kernel a few times, for rocprofv3
+
+Every rate is reported from the mean launch over three rounds, with the
+median and the best round beside it. The machine probes (launch cost, DRAM
+latency, the MFMA ceiling and its shader clock, the streaming-read ceiling)
+come first; the decode's time floor is built from them.
 """
 from __future__ import annotations
 
@@ -318,8 +323,162 @@ def time_launches(fn, stream, torch, n):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+ROUNDS = 3
+
+
+def rounds_stats(rounds_ms):
+    """Timing summary of ROUNDS rounds of launches (ms per launch): the mean
+    over every launch, the median and the minimum of the round means, and the
+    fastest single launch."""
+    import statistics
+    means = [sum(r) / len(r) for r in rounds_ms]
+    allms = [x for r in rounds_ms for x in r]
+    return {"mean": sum(allms) / len(allms), "median": statistics.median(means),
+            "min": min(means), "min_launch": min(allms), "rounds": [round(m, 5) for m in means],
+            "launches": len(allms)}
+
+
+def measure(fn, stream, torch, per_round, warmup=2):
+    time_launches(fn, stream, torch, warmup)
+    return rounds_stats([time_launches(fn, stream, torch, per_round) for _ in range(ROUNDS)])
+
+
+def rate_entry(st, work, unit, peak, extra=None):
+    """Rates of one leg from its timing summary: `value` from the mean launch,
+    the median and best rounds beside it."""
+    div = 1e12 if unit == "TFLOP/s" else 1e9
+    v = work / (st["mean"] * 1e-3) / div
+    e = {"value": round(v, 2), "unit": unit, "ms": round(st["mean"], 5),
+         "ms_median_round": round(st["median"], 5), "ms_min_round": round(st["min"], 5),
+         "ms_min_launch": round(st["min_launch"], 5), "rounds_ms": st["rounds"],
+         "value_median_round": round(work / (st["median"] * 1e-3) / div, 2),
+         "value_best_round": round(work / (st["min"] * 1e-3) / div, 2),
+         "frac": round(v / peak, 4)}
+    if extra:
+        e.update(extra)
+    return e
+
+
+class Probes:
+    """Machine probes (libmiprobe.so): launch cost, DRAM latency, the MFMA
+    ceiling with its shader clock, and the streaming-read ceiling."""
+
+    def __init__(self, torch):
+        import ctypes
+        from online_softmax_monoid_amd import build, miattn
+        miattn.bind_to_torch_runtime()
+        if not os.path.exists(build.PROBE_LIB):
+            build._build_lib(build.PROBE_LIB, build.PROBE_SOURCES)
+        L = ctypes.CDLL(build.PROBE_LIB)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.probe_empty.argtypes = [i, vp]
+        L.probe_chase.argtypes = [vp, sz, ctypes.c_uint32, i, vp, vp]
+        L.probe_mfma.argtypes = [i, i, vp, vp, vp]
+        L.probe_read.argtypes = [vp, sz, i, vp, vp]
+        for f in (L.probe_empty, L.probe_chase, L.probe_mfma, L.probe_read):
+            f.restype = i
+        self.L, self.torch = L, torch
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: probe status {rc}")
+
+    def launch(self, stream):
+        """One empty launch (events around it, median of 200), and 2000
+        launches back to back (per launch)."""
+        import statistics
+        torch = self.torch
+        s = stream.cuda_stream
+        one = time_launches(lambda st: self._ok(self.L.probe_empty(1, s), "empty"), stream,
+                            torch, 200)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        self._ok(self.L.probe_empty(2000, s), "empty")
+        b.record(stream)
+        torch.cuda.synchronize()
+        return {"single_launch_us": round(statistics.median(one) * 1e3, 2),
+                "back_to_back_us": round(a.elapsed_time(b) * 1e3 / 2000, 3)}
+
+    def chase(self, stream, hops=20000):
+        """DRAM latency: a random cycle through 2^20 nodes 4 KiB apart in a
+        4 GiB buffer, built on the device; the last-level cache is flushed
+        by a 2 GiB read first, and each hop then reaches a line not read
+        before."""
+        torch = self.torch
+        n_elems = 1 << 30
+        stride = 1024
+        nodes = n_elems // stride
+        buf = torch.empty(n_elems, dtype=torch.int32, device="cuda")
+        g = torch.Generator().manual_seed(20261250)
+        perm = torch.randperm(nodes, generator=g).to("cuda")
+        idx = perm.to(torch.int64) * stride
+        nxt = (torch.roll(perm, -1).to(torch.int64) * stride).to(torch.int32)
+        buf[idx] = nxt
+        assert int(nxt.max()) < n_elems and int(idx.max()) < n_elems
+        out = torch.zeros(4, dtype=torch.int32, device="cuda")
+        flush = torch.empty(1 << 29, dtype=torch.float32, device="cuda")
+        sink = torch.empty(2048 * 4, dtype=torch.int32, device="cuda")
+        s = stream.cuda_stream
+        start = int(idx[0])
+        res = []
+        for _ in range(3):
+            self._ok(self.L.probe_read(flush.data_ptr(), flush.numel() * 4, 2048, sink.data_ptr(),
+                                       s), "read")
+            ms = time_launches(lambda st: self._ok(
+                self.L.probe_chase(buf.data_ptr(), n_elems, start, hops, out.data_ptr(), s),
+                "chase"), stream, torch, 1)[0]
+            res.append(ms * 1e6 / hops)
+        del buf, flush
+        torch.cuda.empty_cache()
+        return {"dram_latency_ns": round(min(res), 1), "hops": hops,
+                "runs_ns": [round(x, 1) for x in res]}
+
+    def mfma(self, stream, blocks=512, iters=6000):
+        """MFMA ceiling: 512 workgroups of four waves (two waves per SIMD on
+        256 CUs), each wave iters * 32 independent 32x32x16 bf16 MFMAs; the
+        shader clock from the cycle counter against the 100 MHz reference."""
+        import statistics
+        torch = self.torch
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        clk = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda")
+        s = stream.cuda_stream
+        fn = lambda st: self._ok(self.L.probe_mfma(blocks, iters, sink.data_ptr(), clk.data_ptr(),
+                                                   s), "mfma")
+        st = measure(fn, stream, torch, 3, warmup=1)
+        c = clk.cpu().numpy().reshape(blocks, 4).astype("float64")
+        ghz = (c[:, 1] - c[:, 0]) / ((c[:, 3] - c[:, 2]) / 1e8) / 1e9
+        flops = blocks * 4 * iters * 32 * 32768.0
+        return {"tflops": round(flops / (st["mean"] * 1e-3) / 1e12, 1),
+                "tflops_best": round(flops / (st["min_launch"] * 1e-3) / 1e12, 1),
+                "shader_clock_ghz": round(float(statistics.median(ghz)), 3),
+                "frac_of_spec": round(flops / (st["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+    def read(self, stream, nbytes=2 << 30, blocks=2048):
+        """Streaming-read ceiling over a 2 GiB buffer, and torch's device copy
+        of 1 GiB (read + write) beside it."""
+        torch = self.torch
+        buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        sink = torch.empty(blocks * 4, dtype=torch.int32, device="cuda")
+        s = stream.cuda_stream
+        st = measure(lambda x: self._ok(self.L.probe_read(buf.data_ptr(), nbytes, blocks,
+                                                          sink.data_ptr(), s), "read"),
+                     stream, torch, 5)
+        half = nbytes // 2
+        src = buf[:half // 4]
+        dst = torch.empty_like(src)
+        cst = measure(lambda x: dst.copy_(src), stream, torch, 5)
+        del buf, dst
+        torch.cuda.empty_cache()
+        return {"read_GBs": round(nbytes / (st["mean"] * 1e-3) / 1e9, 1),
+                "read_GBs_best": round(nbytes / (st["min_launch"] * 1e-3) / 1e9, 1),
+                "copy_GBs": round(2 * half / (cst["mean"] * 1e-3) / 1e9, 1),
+                "read_frac_of_spec": round(nbytes / (st["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(target_seconds: float = 12.0):
-    """The f64 oracle on a bounded random row sample of the prefill workload."""
+    """The f64 oracle on a bounded random row sample of the prefill workload,
+    on every host thread; then the tiny workload (B1 H2 S128 d64) on one
+    thread."""
     import numpy as np
     import oracle
     from online_softmax_monoid_amd import inputs
@@ -337,24 +496,59 @@ def cpu_baseline(target_seconds: float = 12.0):
 
     probe = np.sort(rng.choice(total_rows, size=2048, replace=False)).astype(np.int64)
     t0 = time.perf_counter()
-    oracle.attn_fwd(q, k, v, causal, w.scale, rows=probe)
+    oracle.attn_fwd(q, k, v, causal, w.scale, rows=probe, nthreads=threads)
     dt = time.perf_counter() - t0
     rate = row_flops(probe) / dt
     n = int(min(total_rows, max(2048, target_seconds * rate / (row_flops(probe) / 2048))))
     rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
     t0 = time.perf_counter()
-    oracle.attn_fwd(q, k, v, causal, w.scale, rows=rows)
+    oracle.attn_fwd(q, k, v, causal, w.scale, rows=rows, nthreads=threads)
     dt = time.perf_counter() - t0
     fl = row_flops(rows)
+    # the tiny workload, every row, on one thread
+    w1 = inputs.WORKLOADS[1]
+    q1, k1, v1 = inputs.prefill_inputs(w1)
+    t0 = time.perf_counter()
+    for _ in range(5):
+        oracle.attn_fwd(q1, k1, v1, False, w1.scale, nthreads=1)
+    dt1 = (time.perf_counter() - t0) / 5
+    oracle.attn_fwd(q1, k1, v1, False, w1.scale, nthreads=threads)  # restore the thread count
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} of {total_rows} query rows (uniform random, seed {w.seed + 7}) of "
                       f"the B2 H32 S4096 d128 causal prefill, f64 two-pass, {dt:.1f} s, "
-                      f"{fl / 1e9:.1f} GFLOP"}
+                      f"{fl / 1e9:.1f} GFLOP",
+            "one_thread_tiny": {"workload": "B1 H2 S128 d64 non-causal, all 256 rows",
+                                "seconds": round(dt1, 5), "cores": 1,
+                                "TFLOP/s": w1.flops(False) / dt1 / 1e12}}
+
+
+class PrefillCfg:
+    """A prefill workload at one causal setting (attn_fwd)."""
+
+    def __init__(self, w, torch, causal):
+        from online_softmax_monoid_amd import inputs
+        self.w = w
+        q, k, v = inputs.prefill_inputs(w)
+        self.q, self.k, self.v = dev_bits(q), dev_bits(k), dev_bits(v)
+        n = w.B * w.Hq * w.Sq
+        self.o = torch.empty(n * w.d, dtype=torch.int16, device="cuda")
+        self.lse = torch.empty(n, dtype=torch.float32, device="cuda")
+        self.causal = causal
+        self.flops = w.flops(causal)
+
+    def __call__(self, stream):
+        from online_softmax_monoid_amd import miattn
+        w = self.w
+        miattn.attn_fwd(self.q, self.k, self.v, self.o, self.lse, w.B, w.Hq, w.Hkv, w.Sq, w.Sk,
+                        w.d, self.causal, w.scale, stream)
 
 
 def profile_pass():
-    """A short fixed sequence for rocprofv3: a plain 1 GiB device copy (the
-    counter calibration), 3 prefill launches, 3 decode launches."""
+    """A short fixed sequence for rocprofv3 counter passes: a plain 1 GiB
+    device copy (the counter calibration), then every kernel the bench times:
+    3 launches each of the step's prefill and decode, the d = 64 workloads,
+    the window, score-modifier, packed, paged-decode and backward legs, and
+    one launch of the long-context d = 256 prefill."""
     import torch
     from online_softmax_monoid_amd import inputs
     stream = torch.cuda.current_stream()
@@ -362,13 +556,25 @@ def profile_pass():
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
-    pre = Prefill(inputs.WORKLOADS[PREFILL_WID], torch)
-    dec = Decode(inputs.WORKLOADS[DECODE_WID], torch)
     torch.cuda.synchronize()
-    for _ in range(3):
-        pre(stream)
-    for _ in range(3):
-        dec(stream)
+    del src, dst
+    legs = [Prefill(inputs.WORKLOADS[PREFILL_WID], torch), Decode(inputs.WORKLOADS[DECODE_WID], torch),
+            PrefillCfg(inputs.WORKLOADS[1], torch, False),
+            PrefillCfg(inputs.WORKLOADS[2], torch, True), PrefillCfg(inputs.WORKLOADS[2], torch, False)]
+    legs += [PrefillWindow(torch, **cfg) for _, cfg in WINDOW_LEGS]
+    legs += [PrefillScoreMod(torch, **cfg) for _, cfg in SCOREMOD_LEGS]
+    legs += [PrefillVarlen(torch), DecodePaged(inputs.WORKLOADS[DECODE_WID], torch)]
+    legs.append(Backward(legs[0], torch))
+    torch.cuda.synchronize()
+    for leg in legs:
+        for _ in range(3):
+            leg(stream)
+        torch.cuda.synchronize()
+        log(f"profile pass: {type(leg).__name__} done")
+    del legs
+    torch.cuda.empty_cache()
+    lng = Prefill(inputs.WORKLOADS[LONG_WID], torch)
+    lng(stream)
     torch.cuda.synchronize()
     log("profile pass done")
 
@@ -376,10 +582,12 @@ def profile_pass():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=60,
+                    help="timed steps, in three rounds (default 60: 3 x 20)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--long-steps", type=int, default=3)
+    ap.add_argument("--long-steps", type=int, default=2, help="long-context launches per round")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -396,109 +604,113 @@ def main():
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
 
+    machine = None
+    if not args.no_probes:
+        log("bench: machine probes")
+        pr = Probes(torch)
+        machine = {"launch": pr.launch(stream), "mfma_ceiling": pr.mfma(stream),
+                   "hbm": pr.read(stream), "latency": pr.chase(stream)}
+        log(f"bench: machine {json.dumps(machine)}")
+        del pr
+
     log("bench: drawing inputs")
     pre = Prefill(inputs.WORKLOADS[PREFILL_WID], torch)
     dec = Decode(inputs.WORKLOADS[DECODE_WID], torch)
     torch.cuda.synchronize()
 
-    def step(s):
-        pre(s)
-        dec(s)
-
     log(f"bench: warmup {args.warmup}")
     for _ in range(args.warmup):
-        step(stream)
+        pre(stream)
+        dec(stream)
     torch.cuda.synchronize()
 
-    log(f"bench: timing {args.steps} steps")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e in ev:
-        e[0].record(stream)
-        pre(stream)
-        e[1].record(stream)
-        dec(stream)
-        e[2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    pre_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    dec_ms = [b.elapsed_time(c) for _, b, c in ev]
-    pre_avg = sum(pre_ms) / len(pre_ms)
-    dec_avg = sum(dec_ms) / len(dec_ms)
-    tflops = pre.flops / (pre_avg * 1e-3) / 1e12
-    dec_gbs = dec.bytes / (dec_avg * 1e-3) / 1e9
-    log(f"bench: prefill {pre_avg:.4f} ms ({tflops:.1f} TFLOP/s), decode {dec_avg:.4f} ms "
-        f"({dec_gbs:.0f} GB/s)")
+    # the timed region: args.steps steps (prefill + decode) in three rounds,
+    # each round bracketed by a device synchronisation
+    per = [args.steps // ROUNDS + (1 if r < args.steps % ROUNDS else 0) for r in range(ROUNDS)]
+    log(f"bench: timing {args.steps} steps in rounds of {per}")
+    pre_rounds, dec_rounds, walls = [], [], []
+    for n in per:
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e in ev:
+            e[0].record(stream)
+            pre(stream)
+            e[1].record(stream)
+            dec(stream)
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+        pre_rounds.append([a.elapsed_time(b) for a, b, _ in ev])
+        dec_rounds.append([b.elapsed_time(c) for _, b, c in ev])
+    pst, dst_ = rounds_stats(pre_rounds), rounds_stats(dec_rounds)
+    tflops = pre.flops / (pst["mean"] * 1e-3) / 1e12
+    dec_gbs = dec.bytes / (dst_["mean"] * 1e-3) / 1e9
+    log(f"bench: prefill {pst['mean']:.4f} ms ({tflops:.1f} TFLOP/s; rounds {pst['rounds']}), "
+        f"decode {dst_['mean']:.4f} ms ({dec_gbs:.0f} GB/s; rounds {dst_['rounds']})")
+
+    legs = {}
     bwd = Backward(pre, torch)
-    time_launches(bwd, stream, torch, 2)
-    bms = time_launches(bwd, stream, torch, 5)
-    b_avg = sum(bms) / len(bms)
-    b_tf = bwd.flops / (b_avg * 1e-3) / 1e12
-    log(f"bench: backward d128 {b_avg:.4f} ms ({b_tf:.1f} TFLOP/s)")
+    legs["backward_d128"] = rate_entry(measure(bwd, stream, torch, 5), bwd.flops, "TFLOP/s",
+                                       PEAK_BF16_TFLOPS,
+                                       {"flops": "2.5 x the forward's (S, dP, dV, dK, dQ)"})
+    log(f"bench: backward_d128 {legs['backward_d128']['ms']} ms")
     del bwd, pre
     torch.cuda.empty_cache()
 
+    for wid, causal, per_round in ((1, False, 50), (2, True, 20), (2, False, 20)):
+        leg = PrefillCfg(inputs.WORKLOADS[wid], torch, causal)
+        name = f"workload{wid}_d64_{'causal' if causal else 'noncausal'}"
+        w = inputs.WORKLOADS[wid]
+        legs[name] = rate_entry(measure(leg, stream, torch, per_round), leg.flops, "TFLOP/s",
+                                PEAK_BF16_TFLOPS, {"shape": {"B": w.B, "Hq": w.Hq, "S": w.Sq,
+                                                             "d": w.d, "causal": causal}})
+        log(f"bench: {name} {legs[name]['ms']} ms ({legs[name]['value']} TFLOP/s)")
+        del leg
+    torch.cuda.empty_cache()
+
     log("bench: long-context GQA workload")
-    lw = inputs.WORKLOADS[LONG_WID]
-    lng = Prefill(lw, torch)
-    time_launches(lng, stream, torch, 1)
-    lms = time_launches(lng, stream, torch, args.long_steps)
-    l_avg = sum(lms) / len(lms)
-    l_tflops = lng.flops / (l_avg * 1e-3) / 1e12
-    log(f"bench: long-context {l_avg:.3f} ms ({l_tflops:.1f} TFLOP/s)")
+    lng = Prefill(inputs.WORKLOADS[LONG_WID], torch)
+    legs["long_context_gqa_d256"] = rate_entry(measure(lng, stream, torch, args.long_steps, 1),
+                                               lng.flops, "TFLOP/s", PEAK_BF16_TFLOPS)
+    log(f"bench: long-context {legs['long_context_gqa_d256']['ms']} ms")
     del lng
     torch.cuda.empty_cache()
 
-    windows = {}
     for name, cfg in WINDOW_LEGS:
         wl = PrefillWindow(torch, **cfg)
-        time_launches(wl, stream, torch, 3)
-        wms = time_launches(wl, stream, torch, 10)
-        w_avg = sum(wms) / len(wms)
-        w_tf = wl.flops / (w_avg * 1e-3) / 1e12
-        w_gbs = wl.bytes / (w_avg * 1e-3) / 1e9
-        log(f"bench: {name} {w_avg:.4f} ms ({w_tf:.1f} TFLOP/s, {w_gbs:.0f} GB/s)")
-        windows[name] = {"value": round(w_tf, 2), "unit": "TFLOP/s", "ms": round(w_avg, 4),
-                         "frac": round(w_tf / PEAK_BF16_TFLOPS, 4), "GB/s": round(w_gbs, 1),
-                         "hbm_frac": round(w_gbs / PEAK_HBM_GBS, 4),
-                         "shape": {k: v for k, v in cfg.items() if k != "seed"}}
+        st = measure(wl, stream, torch, 10)
+        legs[name] = rate_entry(st, wl.flops, "TFLOP/s", PEAK_BF16_TFLOPS,
+                                {"GB/s": round(wl.bytes / (st["mean"] * 1e-3) / 1e9, 1),
+                                 "hbm_frac": round(wl.bytes / (st["mean"] * 1e-3) / 1e9
+                                                   / PEAK_HBM_GBS, 4),
+                                 "shape": {k: v for k, v in cfg.items() if k != "seed"}})
+        log(f"bench: {name} {legs[name]['ms']} ms")
         del wl
         torch.cuda.empty_cache()
 
     for name, cfg in SCOREMOD_LEGS:
         sm = PrefillScoreMod(torch, **cfg)
-        time_launches(sm, stream, torch, 3)
-        sms = time_launches(sm, stream, torch, 10)
-        s_avg = sum(sms) / len(sms)
-        s_tf = sm.flops / (s_avg * 1e-3) / 1e12
-        log(f"bench: {name} {s_avg:.4f} ms ({s_tf:.1f} TFLOP/s)")
-        windows[name] = {"value": round(s_tf, 2), "unit": "TFLOP/s", "ms": round(s_avg, 4),
-                         "frac": round(s_tf / PEAK_BF16_TFLOPS, 4),
-                         "shape": {k: v for k, v in cfg.items() if k != "seed"}}
+        legs[name] = rate_entry(measure(sm, stream, torch, 10), sm.flops, "TFLOP/s",
+                                PEAK_BF16_TFLOPS,
+                                {"shape": {k: v for k, v in cfg.items() if k != "seed"}})
+        log(f"bench: {name} {legs[name]['ms']} ms")
         del sm
         torch.cuda.empty_cache()
 
     vl = PrefillVarlen(torch)
-    time_launches(vl, stream, torch, 3)
-    vms = time_launches(vl, stream, torch, 10)
-    v_avg = sum(vms) / len(vms)
-    v_tf = vl.flops / (v_avg * 1e-3) / 1e12
-    log(f"bench: varlen_chunked_d128 {v_avg:.4f} ms ({v_tf:.1f} TFLOP/s)")
-    windows["varlen_chunked_d128"] = {"value": round(v_tf, 2), "unit": "TFLOP/s",
-                                      "ms": round(v_avg, 4),
-                                      "frac": round(v_tf / PEAK_BF16_TFLOPS, 4),
-                                      "shape": vl.shape}
+    legs["varlen_chunked_d128"] = rate_entry(measure(vl, stream, torch, 10), vl.flops, "TFLOP/s",
+                                             PEAK_BF16_TFLOPS, {"shape": vl.shape})
+    log(f"bench: varlen_chunked_d128 {legs['varlen_chunked_d128']['ms']} ms")
     del vl
     torch.cuda.empty_cache()
 
     log("bench: paged decode (16-key pages)")
     dp = DecodePaged(inputs.WORKLOADS[DECODE_WID], torch)
-    time_launches(dp, stream, torch, args.warmup)
-    pms = time_launches(dp, stream, torch, args.steps)
-    p_avg = sum(pms) / len(pms)
-    p_gbs = dp.bytes / (p_avg * 1e-3) / 1e9
-    log(f"bench: paged decode {p_avg:.4f} ms ({p_gbs:.0f} GB/s)")
+    legs["decode_paged"] = rate_entry(measure(dp, stream, torch, 20, args.warmup), dp.bytes,
+                                      "GB/s", PEAK_HBM_GBS,
+                                      {"bound": "hbm", "page_size": DecodePaged.PAGE})
+    log(f"bench: paged decode {legs['decode_paged']['ms']} ms")
     del dp
     torch.cuda.empty_cache()
 
@@ -507,8 +719,23 @@ def main():
         log("bench: cpu baseline (f64 oracle on a row sample)")
         cpu = cpu_baseline()
 
+    # the decode's time floor (the tang paper, §9.2 "From traffic to time"):
+    # two dependent launches, one DRAM round trip, and the bytes at the
+    # bandwidth (the spec and the measured read ceiling)
+    floor = None
+    if machine is not None:
+        lat_ms = machine["latency"]["dram_latency_ns"] * 1e-6
+        launch_ms = machine["launch"]["back_to_back_us"] * 1e-3
+        floor = {"launches": 2, "launch_ms": round(launch_ms, 5), "latency_ms": round(lat_ms, 5),
+                 "bytes_ms_spec": round(dec.bytes / (PEAK_HBM_GBS * 1e6), 5),
+                 "bytes_ms_measured_read": round(dec.bytes / (machine["hbm"]["read_GBs"] * 1e6), 5)}
+        floor["floor_ms_spec"] = round(2 * launch_ms + lat_ms + floor["bytes_ms_spec"], 5)
+        floor["floor_ms_measured"] = round(2 * launch_ms + lat_ms + floor["bytes_ms_measured_read"], 5)
+        floor["decode_ms_over_floor_measured"] = round(dst_["mean"] / floor["floor_ms_measured"], 3)
+
     traffic = measured_traffic()
     pw, dw = inputs.WORKLOADS[PREFILL_WID], inputs.WORKLOADS[DECODE_WID]
+    wall = sum(walls)
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -531,6 +758,7 @@ def main():
             "decode": {"B": dw.B, "Hq": dw.Hq, "Hkv": dw.Hkv, "d": dw.d,
                        "kv_len_sum": int(dec.lens_host.sum()), "splits": dw.num_splits},
             "parallelism": "single GPU",
+            "rounds": per,
         },
         "roofline": {
             "bound": "mfma",
@@ -540,23 +768,19 @@ def main():
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
         },
-        "prefill_ms": round(pre_avg, 4),
-        "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "ms": round(dec_avg, 4),
-                   "frac": round(dec_gbs / PEAK_HBM_GBS, 4), "bound": "hbm",
-                   "algorithmic_bytes": dec.bytes},
-        "backward_d128": {"value": round(b_tf, 2), "unit": "TFLOP/s", "ms": round(b_avg, 4),
-                          "frac": round(b_tf / PEAK_BF16_TFLOPS, 4),
-                          "flops": "2.5 x the forward's (S, dP, dV, dK, dQ)"},
-        "long_context_gqa_d256": {"value": round(l_tflops, 2), "unit": "TFLOP/s",
-                                  "ms": round(l_avg, 3),
-                                  "frac": round(l_tflops / PEAK_BF16_TFLOPS, 4)},
-        **windows,
-        "decode_paged": {"value": round(p_gbs, 1), "unit": "GB/s", "ms": round(p_avg, 4),
-                         "frac": round(p_gbs / PEAK_HBM_GBS, 4), "bound": "hbm",
-                         "page_size": DecodePaged.PAGE},
+        "prefill": rate_entry(pst, pre_flops(pw), "TFLOP/s", PEAK_BF16_TFLOPS),
+        "decode": rate_entry(dst_, dec.bytes, "GB/s", PEAK_HBM_GBS,
+                             {"bound": "hbm", "algorithmic_bytes": dec.bytes,
+                              "floor": floor}),
+        **legs,
+        "machine": machine,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def pre_flops(w):
+    return w.flops(w.causal[0])
 
 
 if __name__ == "__main__":

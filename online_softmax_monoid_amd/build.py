@@ -1,4 +1,5 @@
-"""Build libmiattn.so in-tree with hipcc for gfx950.
+"""Build libmiattn.so (the attention library) and libmiprobe.so (the machine
+probes the benchmark reports beside it) in-tree with hipcc for gfx950.
 
     python -m online_softmax_monoid_amd.build
 
@@ -18,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmiattn.so")
 SOURCES = ["api.cpp", "prefill.hip", "prefill_q64.hip", "decode.hip", "backward.hip"]
+PROBE_LIB = os.path.join(PKG, "libmiprobe.so")
+PROBE_SOURCES = ["probes.hip"]
 ARCH = "gfx950"
 
 
@@ -44,7 +47,16 @@ def _run(cmd):
     return res.returncode, msg
 
 
-def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
+def build(out: str = LIB, extra=(), verbose: bool = False, probes: bool = True) -> str:
+    """Build the attention library at `out` and, unless probes is False, the
+    probe library beside the package; returns `out`."""
+    _build_lib(out, SOURCES, extra, verbose)
+    if probes:
+        _build_lib(PROBE_LIB, PROBE_SOURCES, extra, verbose)
+    return out
+
+
+def _build_lib(out, sources, extra=(), verbose: bool = False) -> str:
     """Compile every source to an object (in parallel), then link the shared
     library; the objects live in a build folder next to the sources."""
     from concurrent.futures import ThreadPoolExecutor
@@ -53,7 +65,7 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     os.makedirs(objdir, exist_ok=True)
     tag = "%d" % os.getpid()
     cmds, objs = [], []
-    for s in SOURCES:
+    for s in sources:
         obj = os.path.join(objdir, os.path.splitext(s)[0] + "." + tag + ".o")
         objs.append(obj)
         cmds.append([hipcc(), *flags(extra), "-c", "-o", obj, "-x", "hip", os.path.join(CSRC, s)])

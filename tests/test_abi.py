@@ -29,6 +29,20 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_probe_library_exports_every_declared_symbol():
+    """libmiprobe.so (the bench's machine probes) exports what include/miprobe.h
+    declares."""
+    from online_softmax_monoid_amd import build
+    text = open(os.path.join(ROOT, "include", "miprobe.h")).read()
+    names = sorted(set(re.findall(r"^MIPROBE_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.M)))
+    assert names == ["probe_chase", "probe_empty", "probe_mfma", "probe_read"]
+    if not os.path.exists(build.PROBE_LIB):
+        build._build_lib(build.PROBE_LIB, build.PROBE_SOURCES)
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
 def test_version_and_workspace_size():
     assert M.miattn_version() == 700
     assert M.attn_fwd_decode_workspace_size(32, 32, 128, 16) == 32 * 32 * 16 * 130 * 4

@@ -267,6 +267,39 @@ class Backward:
                         w.Hkv, w.Sq, w.Sk, w.d, p.causal, w.scale, self.ws, self.ws_bytes, stream)
 
 
+class BackwardShape:
+    """attn_bwd on seeded N(0, 1) * 0.5 inputs of a given shape, fed by the GPU
+    forward's O and LSE; the d = 256 leg takes the pages' backward regime
+    (head dimension 256, B * H * N = 131072: B2 H16 N4096, causal)."""
+
+    def __init__(self, torch, seed, B, H, S, d, causal):
+        from online_softmax_monoid_amd import inputs, miattn
+        q, k, v = inputs.draw_prefill_bits(seed, B, H, H, S, S, d, 0.5)
+        (do,) = inputs.draw_prefill_bits(seed + 1, B, H, H, S, S, d)[:1]
+        self.q, self.k, self.v, self.do = dev_bits(q), dev_bits(k), dev_bits(v), dev_bits(do)
+        n = B * H * S
+        self.o = torch.empty(n * d, dtype=torch.int16, device="cuda")
+        self.lse = torch.empty(n, dtype=torch.float32, device="cuda")
+        self.dq = torch.empty(n * d, dtype=torch.int16, device="cuda")
+        self.dk = torch.empty(n * d, dtype=torch.int16, device="cuda")
+        self.dv = torch.empty(n * d, dtype=torch.int16, device="cuda")
+        self.ws_bytes = miattn.attn_bwd_workspace_size(B, H, S)
+        self.ws = torch.empty(self.ws_bytes // 4, dtype=torch.float32, device="cuda")
+        self.shape = (B, H, S, d, causal)
+        self.scale = inputs.default_scale(d)
+        miattn.attn_fwd(self.q, self.k, self.v, self.o, self.lse, B, H, H, S, S, d, causal,
+                        self.scale, torch.cuda.current_stream())
+        fwd = 4.0 * B * H * S * S * d / (2 if causal else 1)
+        self.flops = 2.5 * fwd
+
+    def __call__(self, stream):
+        from online_softmax_monoid_amd import miattn
+        B, H, S, d, causal = self.shape
+        miattn.attn_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, self.dq, self.dk,
+                        self.dv, B, H, H, S, S, d, causal, self.scale, self.ws, self.ws_bytes,
+                        stream)
+
+
 class DecodePaged:
     """The decode workload with its cache in pages of ``page`` keys, pool
     pages in a seeded random order; two pool copies used alternately, as for
@@ -565,6 +598,7 @@ def profile_pass():
     legs += [PrefillScoreMod(torch, **cfg) for _, cfg in SCOREMOD_LEGS]
     legs += [PrefillVarlen(torch), DecodePaged(inputs.WORKLOADS[DECODE_WID], torch)]
     legs.append(Backward(legs[0], torch))
+    legs.append(BackwardShape(torch, 7400, 2, 16, 4096, 256, True))
     torch.cuda.synchronize()
     for leg in legs:
         for _ in range(3):
@@ -656,6 +690,15 @@ def main():
                                        {"flops": "2.5 x the forward's (S, dP, dV, dK, dQ)"})
     log(f"bench: backward_d128 {legs['backward_d128']['ms']} ms")
     del bwd, pre
+    torch.cuda.empty_cache()
+    b256 = BackwardShape(torch, 7400, 2, 16, 4096, 256, True)
+    legs["backward_d256"] = rate_entry(measure(b256, stream, torch, 3), b256.flops, "TFLOP/s",
+                                       PEAK_BF16_TFLOPS,
+                                       {"flops": "2.5 x the forward's (S, dP, dV, dK, dQ)",
+                                        "shape": {"B": 2, "H": 16, "S": 4096, "d": 256,
+                                                  "causal": True}})
+    log(f"bench: backward_d256 {legs['backward_d256']['ms']} ms")
+    del b256
     torch.cuda.empty_cache()
 
     for wid, causal, per_round in ((1, False, 50), (2, True, 20), (2, False, 20)):

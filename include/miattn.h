@@ -188,9 +188,9 @@ MIATTN_API int attn_fwd_varlen(const void *q, const void *k, const void *v, void
  *              bytes (f32 D_i per row, computed first); contents on entry do
  *              not matter. Two calls sharing one workspace must be ordered.
  *
- * f32 accumulation, bf16 results. Head dimensions 64 and 128 (256:
- * MIATTN_ERR_UNSUPPORTED). Keys no query sees get zero gradients; rows with
- * no visible key (LSE = -inf) contribute nothing.
+ * f32 accumulation, bf16 results; P and dS are rounded to bf16 for their
+ * matrix products. Head dimensions 64, 128 and 256. Keys no query sees get
+ * zero gradients; rows with no visible key (LSE = -inf) contribute nothing.
  */
 MIATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void *o,
              const float *lse, const void *dout, void *dq, void *dk, void *dv,

@@ -370,8 +370,6 @@ int attn_bwd(const void *q, const void *k, const void *v, const void *o, const f
     if (B < 0 || Sq < 0 || Sk < 0)
         return fail(MIATTN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d, Sq=%d, Sk=%d)", B, Sq, Sk);
     MIATTN_TRY(check_heads_dim(Hq, Hkv, d));
-    if (d == 256)
-        return fail(MIATTN_ERR_UNSUPPORTED, "the backward supports d = 64 and 128");
     MIATTN_TRY(check_scale(scale));
     if ((int64_t)Sq * d * 2 >= ((int64_t)1 << 31) || (int64_t)Sk * d * 2 >= ((int64_t)1 << 31))
         return fail(MIATTN_ERR_UNSUPPORTED,

@@ -354,6 +354,303 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdArgs a, int n_qtiles)
         }
 }
 
+// ---- head dimension 256: two cooperating waves per tile ---------------------------
+// At d = 256 one wave cannot hold a tile's operands and both gradient
+// accumulators (dK and dV alone are 256 registers per lane). Two waves share
+// a tile instead: wave 0 computes S from Q and K, wave 1 dP from dO and V
+// (each contraction runs once), P goes to wave 1 through LDS, dS comes back,
+// and each wave accumulates the gradients of one half of the head dimensions
+// from the packed P and dS. The fixed B operands of the S / dP contractions
+// (K or V rows, Q or dO rows) are kept in AGPRs, which the MFMAs read
+// directly; the accumulators and the softmax work stay in VGPRs.
+
+// pin a fragment in AGPRs: the MFMA reads it there and it leaves the 256
+// VGPRs to the accumulators
+__device__ __forceinline__ void to_agpr(bf16x8 &x) { asm volatile("" : "+a"(x)); }
+
+// dK, dV: one workgroup of two waves per (b, kv-head, 32-key tile)
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(128) bwd_dkdv2_kernel(BwdArgs a, int n_ktiles)
+{
+    constexpr int KK = D / 16, DBH = D / 64;  // 16-dim steps; 32-dim blocks per half
+    __shared__ __attribute__((aligned(16))) uint16_t sQT[D * 32];
+    __shared__ __attribute__((aligned(16))) uint16_t sDT[D * 32];
+    __shared__ __attribute__((aligned(16))) float sP[16 * 64];      // P in the S layout
+    __shared__ __attribute__((aligned(16))) uint32_t sPk[2][4 * 64];  // packed P chunks
+    __shared__ __attribute__((aligned(16))) uint32_t sSk[2][4 * 64];  // packed dS chunks
+    __shared__ __attribute__((aligned(16))) float sL[32];   // LSE_i log2(e), row i0 + i
+    __shared__ __attribute__((aligned(16))) float sDv[32];  // D_i
+
+    const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: S, 1: dP
+    int id = blockIdx.x;
+    const int kt = id % n_ktiles;
+    id /= n_ktiles;
+    const int kvh = id % a.Hkv;
+    const int b = id / a.Hkv;
+    const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq, G = a.Hq / a.Hkv;
+    const int j0 = 32 * kt;
+    const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
+    const float c = a.scale * kLog2e;
+
+    // wave 0: K rows (B operand of S = Q K^T); wave 1: V rows (of dP = dO V^T)
+    const __amdgpu_buffer_rsrc_t rkv =
+        make_rsrc((wave == 0 ? a.k : a.v) + krow0 * D, (uint32_t)Sk * D * 2);
+    bf16x8 bf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        bf[kk] = frag<D>(rkv, j0 + l32, kk, g);
+        to_agpr(bf[kk]);
+    }
+    f32x16 dk[DBH], dv[DBH];  // this wave's half: dims 32 (DBH wave + db) + l32
+#pragma unroll
+    for (int db = 0; db < DBH; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            dk[db][r] = dv[db][r] = 0.f;
+
+    const int i_first = CAUSAL ? max(0, j0 - diag) : 0;
+    const int qt0 = i_first / 32, nqt = (Sq + 31) / 32;
+    const int per_head = max(0, nqt - qt0), n_steps = G * per_head;
+    const int my_key = j0 + l32;
+    for (int t = 0; t < n_steps; ++t) {
+        const int hq = kvh * G + t / per_head, i0 = 32 * (qt0 + t % per_head);
+        const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
+        // wave 0: Q rows (A operand of S); wave 1: dO rows (of dP)
+        const __amdgpu_buffer_rsrc_t rqd =
+            make_rsrc((wave == 0 ? a.q : a.dout) + qrow0 * D, (uint32_t)Sq * D * 2);
+        bf16x8 af[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            af[kk] = frag<D>(rqd, i0 + l32, kk, g);
+        __syncthreads();  // both waves are done with the previous step's LDS
+        if (g == 0) {
+            const int i = i0 + l32;
+            if (wave == 0)
+                sL[l32] = i < Sq ? a.lse[qrow0 + i] * kLog2e : -INFINITY;
+            else
+                sDv[l32] = i < Sq ? a.dsum[qrow0 + i] : 0.f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            write_blk(wave == 0 ? sQT : sDT, af[kk], l32, kk, g);
+            to_agpr(af[kk]);
+        }
+        // S (wave 0) or dP (wave 1): lane key my_key, register r row
+        // i0 + 8(r/4) + 4g + r%4
+        f32x16 x;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            x[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], bf[kk], x, 0, 0, 0);
+        __syncthreads();  // the row statistics and transposed tiles are in LDS
+        if (wave == 0) {
+            f32x16 p;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float4 L4 = *(const float4 *)&sL[8 * r4 + 4 * g];
+                const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = 4 * r4 + u;
+                    const int i = i0 + 8 * r4 + 4 * g + u;
+                    const bool vis = my_key < Sk && i < Sq && Lr[u] > -INFINITY &&
+                                     (!CAUSAL || my_key <= i + diag);
+                    p[r] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c, -Lr[u])) : 0.f;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                sP[r * 64 + lane] = p[r];
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+                Frag8 f;
+                f.v = pack_chunk(p, ch);
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    sPk[ch][w * 64 + lane] = f.w[w];
+            }
+        }
+        __syncthreads();  // P is in LDS
+        if (wave == 1) {
+            f32x16 ds;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float4 D4 = *(const float4 *)&sDv[8 * r4 + 4 * g];
+                const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = 4 * r4 + u;
+                    ds[r] = sP[r * 64 + lane] * (x[r] - Dr[u]);
+                }
+            }
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+                Frag8 f;
+                f.v = pack_chunk(ds, ch);
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    sSk[ch][w * 64 + lane] = f.w[w];
+            }
+        }
+        __syncthreads();  // dS is in LDS
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+            Frag8 pa, sa;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                pa.w[w] = sPk[ch][w * 64 + lane];
+                sa.w[w] = sSk[ch][w * 64 + lane];
+            }
+#pragma unroll
+            for (int db = 0; db < DBH; ++db) {
+                const int dbg = DBH * wave + db;
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa.v, read_tr(sDT, dbg, ch, lane),
+                                                                 dv[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa.v, read_tr(sQT, dbg, ch, lane),
+                                                                 dk[db], 0, 0, 0);
+            }
+        }
+    }
+    // lane: dim 32 (DBH wave + db) + l32; register r: key j0 + 8(r/4) + 4g + r%4
+#pragma unroll
+    for (int db = 0; db < DBH; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const int dim = 32 * (DBH * wave + db) + l32;
+            if (j < Sk) {
+                a.dk[(krow0 + j) * D + dim] = to_bf16(dk[db][r] * a.scale);
+                a.dv[(krow0 + j) * D + dim] = to_bf16(dv[db][r]);
+            }
+        }
+}
+
+// dQ: one workgroup of two waves per (b, query head, 32-row query tile).
+// S^T = K Q^T (wave 0) and dP^T = V dO^T (wave 1) put the query row in the
+// lane and 16 keys in the registers; dS packed by registers is the A operand
+// of dQ += dS K, and each wave accumulates one half of the dimensions.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(128) bwd_dq2_kernel(BwdArgs a, int n_qtiles)
+{
+    constexpr int KK = D / 16, DBH = D / 64;
+    __shared__ __attribute__((aligned(16))) uint16_t sKT[D * 32];
+    __shared__ __attribute__((aligned(16))) float sP[16 * 64];
+    __shared__ __attribute__((aligned(16))) uint32_t sSk[2][4 * 64];
+
+    const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: S, 1: dP
+    int id = blockIdx.x;
+    const int qt = id % n_qtiles;
+    id /= n_qtiles;
+    const int hq = id % a.Hq;
+    const int b = id / a.Hq;
+    const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq, G = a.Hq / a.Hkv;
+    const int kvh = hq / G;
+    const int i0 = 32 * qt, my_q = i0 + l32;
+    const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
+    const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
+    const float c = a.scale * kLog2e;
+
+    // wave 0: Q rows (B operand of S^T); wave 1: dO rows (of dP^T)
+    const __amdgpu_buffer_rsrc_t rqd =
+        make_rsrc((wave == 0 ? a.q : a.dout) + qrow0 * D, (uint32_t)Sq * D * 2);
+    bf16x8 bf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        bf[kk] = frag<D>(rqd, my_q, kk, g);
+        to_agpr(bf[kk]);
+    }
+    const float Di = my_q < Sq ? a.dsum[qrow0 + my_q] : 0.f;
+    const float L = my_q < Sq ? a.lse[qrow0 + my_q] : -INFINITY;
+    const bool row_live = L > -INFINITY;
+
+    f32x16 dq[DBH];
+#pragma unroll
+    for (int db = 0; db < DBH; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            dq[db][r] = 0.f;
+
+    const int kv_end = CAUSAL ? min(Sk, max(0, min(i0 + 31, Sq - 1) + diag + 1)) : Sk;
+    const int nkt = (kv_end + 31) / 32;
+    // wave 0: K rows (A operand of S^T); wave 1: V rows (of dP^T)
+    const __amdgpu_buffer_rsrc_t rkv =
+        make_rsrc((wave == 0 ? a.k : a.v) + krow0 * D, (uint32_t)Sk * D * 2);
+    for (int kt = 0; kt < nkt; ++kt) {
+        const int j0 = 32 * kt;
+        bf16x8 af[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            af[kk] = frag<D>(rkv, j0 + l32, kk, g);
+        __syncthreads();  // both waves are done with the previous tile's LDS
+        if (wave == 0) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                write_blk(sKT, af[kk], l32, kk, g);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            to_agpr(af[kk]);
+        // S^T (wave 0) or dP^T (wave 1): lane row my_q, register r key
+        // j0 + 8(r/4) + 4g + r%4
+        f32x16 x;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            x[r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], bf[kk], x, 0, 0, 0);
+        if (wave == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                const bool vis = row_live && j < Sk && (!CAUSAL || j <= my_q + diag);
+                sP[r * 64 + lane] =
+                    vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c, -L * kLog2e)) : 0.f;
+            }
+        }
+        __syncthreads();  // P and the transposed K tile are in LDS
+        if (wave == 1) {
+            f32x16 ds;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                ds[r] = sP[r * 64 + lane] * (x[r] - Di);
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+                Frag8 f;
+                f.v = pack_chunk(ds, ch);
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    sSk[ch][w * 64 + lane] = f.w[w];
+            }
+        }
+        __syncthreads();  // dS is in LDS
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+            Frag8 sa;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                sa.w[w] = sSk[ch][w * 64 + lane];
+#pragma unroll
+            for (int db = 0; db < DBH; ++db)
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    sa.v, read_tr(sKT, DBH * wave + db, ch, lane), dq[db], 0, 0, 0);
+        }
+    }
+    // lane: dim 32 (DBH wave + db) + l32; register r: row i0 + 8(r/4) + 4g + r%4
+#pragma unroll
+    for (int db = 0; db < DBH; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (i < Sq)
+                a.dq[(qrow0 + i) * D + 32 * (DBH * wave + db) + l32] = to_bf16(dq[db][r] * a.scale);
+        }
+}
+
 // ---- D_i = dO_i . O_i for every row, once (the workspace) -----------------------
 // one wave per 32 rows of a (b, query head): lane l32 + 32 g takes dims
 // 16kk + 8g .. +7 of row l32
@@ -383,6 +680,8 @@ __global__ void __launch_bounds__(64) bwd_dsum_kernel(BwdArgs a, int n_qtiles)
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
 {
+    // head dimensions 64 and 128: one wave per tile; 256: two cooperating waves
+    constexpr bool TWO = D == 256;
     const int n_ktiles = (a.Sk + 31) / 32, n_qtiles = (a.Sq + 31) / 32;
     const long long g1 = (long long)a.B * a.Hkv * n_ktiles, g2 = (long long)a.B * a.Hq * n_qtiles;
     if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL)
@@ -394,15 +693,24 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
             return e;
     }
     if (g1 > 0) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g1), dim3(64), 0, stream, a,
-                           n_ktiles);
+        if constexpr (TWO)
+            hipLaunchKernelGGL((bwd_dkdv2_kernel<D, CAUSAL>), dim3((unsigned)g1), dim3(128), 0,
+                               stream, a, n_ktiles);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g1), dim3(64), 0,
+                               stream, a, n_ktiles);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
-    if (g2 > 0)
-        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)g2), dim3(64), 0, stream, a,
-                           n_qtiles);
+    if (g2 > 0) {
+        if constexpr (TWO)
+            hipLaunchKernelGGL((bwd_dq2_kernel<D, CAUSAL>), dim3((unsigned)g2), dim3(128), 0, stream,
+                               a, n_qtiles);
+        else
+            hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)g2), dim3(64), 0, stream,
+                               a, n_qtiles);
+    }
     return hipGetLastError();
 }
 
@@ -415,6 +723,8 @@ hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, hipStream_t stream)
         return causal ? launch_bwd_t<64, true>(a, stream) : launch_bwd_t<64, false>(a, stream);
     case 128:
         return causal ? launch_bwd_t<128, true>(a, stream) : launch_bwd_t<128, false>(a, stream);
+    case 256:
+        return causal ? launch_bwd_t<256, true>(a, stream) : launch_bwd_t<256, false>(a, stream);
     default:
         return hipErrorInvalidValue;
     }

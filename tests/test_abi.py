@@ -151,7 +151,7 @@ def test_attn_bwd_rejects():
     assert wsb == 1 * 2 * 8 * 4 and M.attn_bwd_workspace_size(-1, 2, 8) == 0
     base = [FAKE] * 9 + [1, 2, 2, 8, 8, 128, 1, 0.125, FAKE, wsb, 0]
     for idx, val, status, needle in [
-            (14, 256, M.MIATTN_ERR_UNSUPPORTED, "d = 64 and 128"),
+            (14, 96, M.MIATTN_ERR_UNSUPPORTED, "head dimension"),
             (18, 16, M.MIATTN_ERR_INVALID_ARG, "workspace too small"),
             (17, 0, M.MIATTN_ERR_INVALID_ARG, "workspace is NULL"),
             (5, 0, M.MIATTN_ERR_INVALID_ARG, "dout is NULL"),

@@ -70,6 +70,10 @@ BWD = [
     (1, 2, 2, 200, 77, 128, True),     # Sq > Sk: leading rows see no key
     (1, 4, 4, 190, 190, 128, False),
     (2, 6, 3, 257, 257, 64, True),
+    (1, 2, 2, 64, 64, 256, True),
+    (1, 4, 2, 130, 300, 256, False),   # GQA, Sq < Sk, ragged
+    (2, 4, 1, 257, 257, 256, True),    # GQA 4
+    (1, 2, 2, 200, 77, 256, True),     # Sq > Sk: leading rows see no key
 ]
 
 
@@ -84,16 +88,17 @@ def test_backward_parity(case):
     _check(q, k, v, do, causal, inputs.default_scale(d), f"bwd {case}")
 
 
-def test_backward_after_the_gpu_forward():
+@pytest.mark.parametrize("d", [128, 256])
+def test_backward_after_the_gpu_forward(d):
     """The whole step on the GPU: attn_fwd's O and LSE feed attn_bwd."""
-    B, Hq, Hkv, S, d = 1, 8, 2, 512, 128
-    q = _bits(8100, (B, Hq, S, d), 0.5)
-    k = _bits(8101, (B, Hkv, S, d), 0.5)
-    v = _bits(8102, (B, Hkv, S, d))
-    do = _bits(8103, (B, Hq, S, d))
+    B, Hq, Hkv, S = 1, 8, 2, 512
+    q = _bits(8100 + d, (B, Hq, S, d), 0.5)
+    k = _bits(8101 + d, (B, Hkv, S, d), 0.5)
+    v = _bits(8102 + d, (B, Hkv, S, d))
+    do = _bits(8103 + d, (B, Hq, S, d))
     scale = inputs.default_scale(d)
     o_bits, lse, _ = H.run_fwd(q, k, v, True, scale)
-    _check(q, k, v, do, True, scale, "bwd after gpu fwd", o_bits=o_bits, lse=lse)
+    _check(q, k, v, do, True, scale, f"bwd after gpu fwd d={d}", o_bits=o_bits, lse=lse)
 
 
 def test_backward_workload_full_size_sampled_heads():
@@ -118,7 +123,7 @@ def test_backward_workload_full_size_sampled_heads():
             assert m["finite"] and m["rel_rms"] <= REL_RMS and m["max_abs_rel"] <= MAX_REL, m
 
 
-@pytest.mark.parametrize("d", [128])
+@pytest.mark.parametrize("d", [128, 256])
 def test_backward_gqa_full(d):
     """Grouped-query heads at a size with many query tiles per key tile:
     B1 Hq8 Hkv2 S2048 causal, forward and backward on the GPU, every element
@@ -134,11 +139,11 @@ def test_backward_gqa_full(d):
     _check(q, k, v, do, True, scale, f"bwd gqa full d={d}", o_bits=o_bits, lse=lse)
 
 
-@pytest.mark.parametrize("Sq,Sk", [(40, 0), (0, 40)])
-def test_backward_degenerate_lengths(Sq, Sk):
+@pytest.mark.parametrize("Sq,Sk,d", [(40, 0, 128), (0, 40, 128), (40, 0, 256), (0, 40, 256)])
+def test_backward_degenerate_lengths(Sq, Sk, d):
     """No keys: dQ is exactly zero (no row sees a key). No queries: dK and dV
     are exactly zero (no query sees a key)."""
-    B, Hq, Hkv, d = 1, 4, 2, 128
+    B, Hq, Hkv = 1, 4, 2
     q = _bits(8200, (B, Hq, Sq, d))
     k = _bits(8201, (B, Hkv, Sk, d))
     v = _bits(8202, (B, Hkv, Sk, d))

@@ -282,7 +282,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
             to.gq = (x % xpu) * gsub + (pos - rank * gsub);
             to.qtile = CAUSAL ? n_qtiles - 1 - rank : rank;
         } else {
-            to = tile_order(id, n_units, G, n_qtiles, CAUSAL);
+            to = tile_order_grouped(id, n_units, G, n_qtiles, CAUSAL, GX);
         }
         const int b = to.unit / a.Hkv;
         const int kvh = to.unit - b * a.Hkv;

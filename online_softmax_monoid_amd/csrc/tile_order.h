@@ -42,4 +42,29 @@ __device__ __forceinline__ TileOrder tile_order(int id, int n_units, int G, int 
     return {unit, gq, causal ? n_qtiles - 1 - rank : rank};
 }
 
+// The order of the persistent kernels, which hold gx workgroups per XCD at
+// once. When the units split evenly over the XCDs, XCD x walks its units in
+// groups of U = gx / (query tiles per unit) units (at least one), whose items
+// fill the XCD's workgroups about once; within a group, heaviest query-tile
+// rank first, then unit, then query head. The workgroups in flight then read
+// the K and V of about U units, which fit the XCD's 4 MB L2, instead of all
+// of the XCD's units (measured at B2 H32 S4096 d128 causal: L2 misses fall
+// from 2.45x to 1.23x of the algorithmic reads). Otherwise the plain order
+// above.
+__device__ __forceinline__ TileOrder tile_order_grouped(int id, int n_units, int G, int n_qtiles,
+                                                        bool causal, int gx)
+{
+    constexpr int kXcds = 8;
+    if (n_units % kXcds != 0)
+        return tile_order(id, n_units, G, n_qtiles, causal);
+    const int upx = n_units / kXcds, per_unit = n_qtiles * G;
+    const int U = max(1, min(upx, gx / max(1, per_unit)));
+    const int gsize = U * per_unit;
+    const int x = id % kXcds, pos = id / kXcds;
+    const int grp = pos / gsize, u0 = grp * U, Ug = min(U, upx - u0);
+    const int rest = pos - grp * gsize;
+    const int rank = rest / (Ug * G), r2 = rest - rank * (Ug * G);
+    return {x * upx + u0 + r2 / G, r2 % G, causal ? n_qtiles - 1 - rank : rank};
+}
+
 }  // namespace miattn

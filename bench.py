@@ -40,8 +40,8 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU * 4096 flop/clk * 2
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PREFILL_WID, LONG_WID, DECODE_WID = 3, 4, 5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_b2_h32_s4096_d128_causal_traffic.txt")
-KERNEL_SOURCES = ("online_softmax_monoid_amd/csrc/prefill.hip",
-                  "online_softmax_monoid_amd/csrc/prefill_q64.hip",
+KERNEL_SOURCES = ("online_softmax_monoid_amd/csrc/prefill_kernel.h",
+                  "online_softmax_monoid_amd/csrc/prefill_d128.hip",
                   "online_softmax_monoid_amd/csrc/tile_order.h",
                   "online_softmax_monoid_amd/csrc/lds_copy.h",
                   "online_softmax_monoid_amd/csrc/resident.h",

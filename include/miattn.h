@@ -128,11 +128,11 @@ MIATTN_API int attn_fwd_window(const void *q, const void *k, const void *v, void
  *                 key j of query head h gets - alibi_slopes[h] * |i + Sk - Sq - j|
  *                 added (ALiBi, §7.3); the slopes are not inspected on the host
  *
- * applied in that order: the modifier to the scaled score, then the mask.
- * LSE is the log-sum-exp of the modified scores. Only the score changes, so
- * the reduction is the same online-softmax monoid (§2.3 "Rewrites").
- * softcap must be finite and >= 0; softcap > 0 together with alibi_slopes is
- * MIATTN_ERR_UNSUPPORTED. Every other argument, limit and error is attn_fwd's.
+ * applied in that order: the soft cap to the scaled score, then the ALiBi
+ * term (both may be given), then the mask. LSE is the log-sum-exp of the
+ * modified scores. Only the score changes, so the reduction is the same
+ * online-softmax monoid (§2.3 "Rewrites"). softcap must be finite and >= 0.
+ * Every other argument, limit and error is attn_fwd's.
  */
 MIATTN_API int attn_fwd_ext(const void *q, const void *k, const void *v, void *o, float *lse,
                  int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
@@ -162,7 +162,7 @@ MIATTN_API int attn_fwd_ext(const void *q, const void *k, const void *v, void *o
  * with attn_fwd's bottom-right causal alignment (a chunk of new queries
  * against its cached prefix plus itself when Sk > Sq). max_seqlen_q must be
  * at least the longest query count (it sizes the launch). Head dimensions
- * 128 and 256 (64: MIATTN_ERR_UNSUPPORTED); total_q * d * 2 and
+ * 64, 128 and 256; total_q * d * 2 and
  * total_k * d * 2 below 2^31. B == 0, total_q == 0 or max_seqlen_q == 0:
  * nothing to do.
  */

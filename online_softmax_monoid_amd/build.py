@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmiattn.so")
-SOURCES = ["api.cpp", "prefill.hip", "prefill_q64.hip", "decode.hip", "backward.hip"]
+SOURCES = ["api.cpp", "prefill_d64.hip", "prefill_d128.hip", "prefill_d256.hip", "decode.hip",
+           "backward.hip"]
 PROBE_LIB = os.path.join(PKG, "libmiprobe.so")
 PROBE_SOURCES = ["probes.hip"]
 ARCH = "gfx950"

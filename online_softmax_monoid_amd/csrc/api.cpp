@@ -137,8 +137,6 @@ int attn_fwd_ext(const void *q, const void *k, const void *v, void *o, float *ls
     if (!(softcap >= 0.f) || !isfinite(softcap))
         return fail(MIATTN_ERR_INVALID_ARG, "softcap must be finite and >= 0 (got %g)",
                     (double)softcap);
-    if (softcap > 0.f && alibi_slopes != nullptr)
-        return fail(MIATTN_ERR_UNSUPPORTED, "softcap and alibi_slopes together are not supported");
     if (alibi_slopes != nullptr && !aligned(alibi_slopes, 4))
         return fail(MIATTN_ERR_INVALID_ARG, "alibi_slopes is not 4-byte aligned");
     return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, window_left < 0 ? -1 : window_left,
@@ -318,8 +316,6 @@ int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float 
                     "sizes must be >= 0 (B=%d, total_q=%d, total_k=%d, max_seqlen_q=%d, "
                     "max_seqlen_k=%d)", B, total_q, total_k, max_seqlen_q, max_seqlen_k);
     MIATTN_TRY(check_heads_dim(Hq, Hkv, d));
-    if (d == 64)
-        return fail(MIATTN_ERR_UNSUPPORTED, "packed variable-length batches need d = 128 or 256");
     MIATTN_TRY(check_scale(scale));
     if ((int64_t)total_q * d * 2 >= ((int64_t)1 << 31) || (int64_t)total_k * d * 2 >= ((int64_t)1 << 31))
         return fail(MIATTN_ERR_UNSUPPORTED,

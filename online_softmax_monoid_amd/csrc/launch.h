@@ -61,10 +61,24 @@ struct BwdArgs {
 };
 
 // Each returns hipSuccess or the launch error.
-hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream);
-// head dimensions 128 and 256: the software-pipelined kernel of
-// prefill_q64.hip, the default for both
-hipError_t launch_fwd_q64(const FwdArgs &a, int d, bool causal, hipStream_t stream);
+// prefill: the software-pipelined persistent kernel of prefill_kernel.h, one
+// translation unit per head dimension
+hipError_t launch_fwd_d64(const FwdArgs &a, bool causal, hipStream_t stream);
+hipError_t launch_fwd_d128(const FwdArgs &a, bool causal, hipStream_t stream);
+hipError_t launch_fwd_d256(const FwdArgs &a, bool causal, hipStream_t stream);
+inline hipError_t launch_fwd(const FwdArgs &a, int d, bool causal, hipStream_t stream)
+{
+    switch (d) {
+    case 64:
+        return launch_fwd_d64(a, causal, stream);
+    case 128:
+        return launch_fwd_d128(a, causal, stream);
+    case 256:
+        return launch_fwd_d256(a, causal, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
 hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t stream);
 // The library's fixed decode scratch (decode.hip): its size in bytes, and its
 // address on the current device (looked up on the first call per device).

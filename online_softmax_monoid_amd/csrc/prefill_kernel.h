@@ -1,8 +1,23 @@
-// prefill_q64.hip -- fused attention forward on gfx950, head dimensions 128
-// and 256, software-pipelined.
+// prefill_kernel.h -- fused attention forward on gfx950 (head dimensions 64,
+// 128 and 256), software-pipelined, on a persistent grid. The kernel template
+// and its launcher; prefill_d64.hip, prefill_d128.hip and prefill_d256.hip
+// instantiate one head dimension each.
 //
-// Same operation and online-softmax monoid as prefill.hip. The design answers
-// two gfx950 limits measured on the simpler kernel:
+// For every (batch, query head, query row) it computes the softmax-weighted
+// sum of the visible value rows and the log-sum-exp of the scaled scores, as
+// one pass over the keys under the online-softmax monoid (the tang paper,
+// muni.works/research/tang, §2.2 "Comprehensions and monoids" and §2.3
+// "Rewrites": running max, sum rescaled to it, accumulator rescaled to it).
+// S^T = K Q^T runs on v_mfma_f32_32x32x16_bf16, so each lane owns one query
+// column and 16 keys of every 32x32 score block; masked keys are selected to
+// -inf (the identity of max); probabilities are rounded to bf16 in registers
+// and feed O^T += V^T P^T directly, V^T read in the accumulator's permuted
+// key order (the sum over keys is associative and commutative); the epilogue
+// O = acc / l, LSE = m scale + ln l runs on the lanes that hold the row
+// (§2.3: epilogues on the reducing thread), and a row with no visible key
+// gets (+0, -inf).
+//
+// The design answers two gfx950 limits measured on a simpler kernel:
 //
 //  * LDS read bandwidth (about 150-200 bytes/ns per CU): every 16-byte K or V
 //    fragment a wave reads from LDS feeds one 32x32x16 MFMA for the 32 query
@@ -17,9 +32,11 @@
 // faster than four waves of 64 rows: the second wave on the SIMD fills the
 // issue slots the first leaves idle while it waits on a dependent VALU chain.
 // Head dimension 256 runs four waves of 32 rows, one per SIMD: the f32
-// accumulator alone takes 128 registers. Each wave runs a two-stage software
-// pipeline per 32-key tile j, laid out in groups of four MFMAs with the VALU
-// and LDS work placed between them:
+// accumulator alone takes 128 registers. Head dimension 64 runs four waves of
+// 32 rows and two workgroups per CU (a tile step is then one group of four
+// MFMAs per stage). Each wave runs a two-stage software pipeline per 32-key
+// tile j, laid out in groups of four MFMAs with the VALU and LDS work placed
+// between them:
 //
 //   stage A: S_{j+1} = K_{j+1} Q^T                   | exp/pack/row-sum of the
 //            second 16 keys of tile j; row max of S_{j+1} for query block 0;
@@ -54,6 +71,8 @@
 // 16 probabilities sum to at most 2^8 has none above 2^8, and only a tile
 // that fails (or a wave with a row that has seen no key yet) takes the exact
 // maximum and recomputes its probabilities.
+
+#pragma once
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -150,7 +169,7 @@ __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint32_t &x) { asm volatile("" : "+v"(x)); }
 
 // One work item: the BM query rows of one (batch, query head) and the keys
-// they see (same tile order as prefill.hip)
+// they see
 struct Item {
     int64_t qrow0, krow0;  // first row of the query head / the item's first key row
     int q_wg, kv_end, nblk;
@@ -160,8 +179,8 @@ struct Item {
     bool live;    // the item has query rows (a packed batch has items past its sequences' ends)
 };
 
-// Score modifiers: none, soft cap, ALiBi
-enum { kModNone = 0, kModSoftcap = 1, kModAlibi = 2 };
+// Score modifiers: none, soft cap, ALiBi, or the soft cap and then ALiBi
+enum { kModNone = 0, kModSoftcap = 1, kModAlibi = 2, kModBoth = 3 };
 
 template <bool CAUSAL, int NWV, int D, int WPE, bool WIN, int MOD, bool VARLEN>
 __global__ void __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
@@ -183,7 +202,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     constexpr int RING = 4;
     constexpr int INFLIGHT = DPW + 2 * DPW * (RING - 3);  // copies newer than K tile j+3 at step j's end
     static_assert((RING & (RING - 1)) == 0 && RING >= 4, "ring of 2^n >= 4 tiles");
-    static_assert((NG == 2 || NG == 4) && NWV * DPW == KKN && INFLIGHT < 64, "tile step shape");
+    static_assert((NG == 1 || NG == 2 || NG == 4) && NWV * DPW == KKN && INFLIGHT < 64,
+                  "tile step shape");
     constexpr int TILE_CH = BN * D / 8;  // 16-byte chunks per tile
 
     __shared__ __attribute__((aligned(16))) uint4 sK_[RING * TILE_CH];  // K ring
@@ -312,7 +332,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
             kbase = ((int64_t)b * a.Hkv + kvh) * a.Sk;
         }
         const int dg = it.sk - it.sq;
-        it.slope = MOD == kModAlibi ? a.alibi[hq] / a.scale : 0.f;
+        it.slope = (MOD & kModAlibi) ? a.alibi[hq] / a.scale : 0.f;
         it.q_wg = to.qtile * BM;
         it.live = it.q_wg < it.sq;
         const int q_wg_last = min(it.q_wg + BM, it.sq) - 1;
@@ -505,22 +525,27 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // Score modifiers on the raw scores of tile j (the kernel's scores are
     // q.k before the scale): the soft cap keeps (cap / scale) tanh(s scale /
     // cap), tanh(x) = 1 - 2 / (exp(2x) + 1); ALiBi subtracts (slope / scale)
-    // times the distance |i + Sk - Sq - key|. Applied before the mask.
-    const float sc_in = MOD == kModSoftcap ? 2.f * a.scale / a.softcap * kLog2e : 0.f;
-    const float sc_out = MOD == kModSoftcap ? a.softcap / a.scale : 0.f;
+    // times the distance |i + Sk - Sq - key|; with both, the cap comes first.
+    // Applied before the mask.
+    const float sc_in = (MOD & kModSoftcap) ? 2.f * a.scale / a.softcap * kLog2e : 0.f;
+    const float sc_out = (MOD & kModSoftcap) ? a.softcap / a.scale : 0.f;
     auto modify_tile = [&](Sc &s, int j) __attribute__((always_inline)) {
-        if constexpr (MOD == kModSoftcap) {
+        if constexpr ((MOD & kModSoftcap) != 0) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float e = __builtin_amdgcn_exp2f(s[0][r] * sc_in);
                 s[0][r] = sc_out * __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f);
             }
-        } else if constexpr (MOD == kModAlibi) {
-            const int d0 = q0 + l32 + diag - kofs - j * BN - 4 * g;  // distance to key offset 0
+        }
+        if constexpr ((MOD & kModAlibi) != 0) {
+            // distance to key offset 0, in f32 (exact below 2^24): per score one
+            // subtraction of a constant and one FMA whose operand modifier
+            // takes the absolute value
+            const float d0 = (float)(q0 + l32 + diag - kofs - j * BN - 4 * g);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int dist = d0 - (8 * (r >> 2) + (r & 3));
-                s[0][r] = __builtin_fmaf(-slope, (float)abs(dist), s[0][r]);
+                const float dist = d0 - (float)(8 * (r >> 2) + (r & 3));
+                s[0][r] = __builtin_fmaf(-slope, __builtin_fabsf(dist), s[0][r]);
             }
         }
     };
@@ -720,28 +745,34 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         step_copies(j);
         slot_end();
 
-        // Stage A, NG groups of four MFMAs (QK of tile j+1). Groups 0-1 read
-        // V_j and compute chunk 1 of tile j's probabilities.
-        constexpr int NRV = 2 * DBN;  // read_v calls per tile (two reads each)
+        // Stage A, NG groups of four MFMAs (QK of tile j+1). The first (at
+        // most two) groups read V_j and compute chunk 1 of tile j's
+        // probabilities.
+        constexpr int NRV = 2 * DBN;          // read_v calls per tile (two reads each)
+        constexpr int VSL = NG >= 2 ? 8 : 4;  // MFMA slots that carry them
 #pragma unroll
         for (int grp = 0; grp < NG; ++grp) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int sl = 4 * grp + i;
                 qk_mfma(sn, sl / KKN, sl % KKN);
-                if (grp < 2)
+                if (sl < VSL)
 #pragma unroll
-                    for (int c = sl * NRV / 8; c < (sl + 1) * NRV / 8; ++c)
+                    for (int c = sl * NRV / VSL; c < (sl + 1) * NRV / VSL; ++c)
                         read_v(vread, c >> 1, c & 1);
             }
-            if (grp < 2)
+            if (NG == 1) {
+                probs_quad(sc, pc, 0, 1, 0);
+                probs_quad(sc, pc, 0, 1, 1);
+            } else if (grp < 2) {
                 probs_quad(sc, pc, 0, 1, grp);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 if (grp < 2)
-                    __builtin_amdgcn_sched_group_barrier(0x100, NRV / 4, 0);  // LDS reads
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NRV / VSL, 0);  // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x002, NG == 1 ? 8 : 4, 0);  // VALU
             }
             slot_end();
         }
@@ -766,6 +797,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
                 modify_tile(sn, j + 1);
             if (MASK && grp == 0)
                 mask_tile(sn, 0, j + 1);
+            if (NG == 1) {
+                probs_quad(sn, pn, 0, 0, 0);
+                probs_quad(sn, pn, 0, 0, 1);
+            }
             if (NG == 2 && grp == 1) {
                 probs_quad(sn, pn, 0, 0, 0);
                 probs_quad(sn, pn, 0, 0, 1);
@@ -777,7 +812,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 if (i < KPG)
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x002, NG == 1 ? 8 : 4, 0);  // VALU
             }
             slot_end();
         }
@@ -974,8 +1009,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
 template <bool CAUSAL, int D, int NWV, int WPE, bool WIN, int MOD, bool VARLEN = false>
 hipError_t launch_q64_t(const FwdArgs &a, int n_qtiles, int n_items, hipStream_t stream)
 {
-    const auto kernel = fwd_q64_kernel<CAUSAL, NWV, D, WPE, WIN, MOD, VARLEN>;
-    const int resident = resident_workgroups(kernel, 64 * NWV);
+    constexpr auto kernel = fwd_q64_kernel<CAUSAL, NWV, D, WPE, WIN, MOD, VARLEN>;
+    const int resident = resident_workgroups<kernel>(64 * NWV);
     if (resident < 8)
         return hipErrorInvalidConfiguration;
     const long long want = ((long long)n_items + 7) / 8 * 8;
@@ -1013,6 +1048,8 @@ hipError_t launch_q64(const FwdArgs &a, bool causal, hipStream_t stream)
         return causal ? launch_q64_t<true, D, NWV, WPE, false, kModNone, true>(a, n_qtiles, n, stream)
                       : launch_q64_t<false, D, NWV, WPE, false, kModNone, true>(a, n_qtiles, n, stream);
     }
+    if (a.softcap > 0.f && a.alibi != nullptr)
+        return dispatch_win<D, NWV, WPE, kModBoth>(a, causal, n_qtiles, n, stream);
     if (a.softcap > 0.f)
         return dispatch_win<D, NWV, WPE, kModSoftcap>(a, causal, n_qtiles, n, stream);
     if (a.alibi != nullptr)
@@ -1021,20 +1058,4 @@ hipError_t launch_q64(const FwdArgs &a, bool causal, hipStream_t stream)
 }
 
 }  // namespace
-
-// Head dimension 128: eight waves (two per SIMD, 256 query rows per item);
-// 256: four waves (one per SIMD, the f32 accumulator alone takes 128
-// registers)
-hipError_t launch_fwd_q64(const FwdArgs &a, int d, bool causal, hipStream_t stream)
-{
-    switch (d) {
-    case 128:
-        return launch_q64<128, 8, 2>(a, causal, stream);
-    case 256:
-        return launch_q64<256, 4, 1>(a, causal, stream);
-    default:
-        return hipErrorInvalidValue;
-    }
-}
-
 }  // namespace miattn

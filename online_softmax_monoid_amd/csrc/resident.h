@@ -8,10 +8,13 @@
 
 namespace miattn {
 
-// Compute units times the kernel's occupancy; cached per device and kernel
-// (one cache per instantiation). 0 if the runtime cannot tell.
-template <typename K>
-int resident_workgroups(K kernel, int threads)
+// Compute units times the kernel's occupancy; cached per device and per
+// kernel. The kernel is a template argument, so every kernel has a cache of
+// its own (keyed by its function type, kernels with one signature but
+// different occupancies -- head dimensions, waves per SIMD -- would share
+// one). 0 if the runtime cannot tell.
+template <auto Kernel>
+int resident_workgroups(int threads)
 {
     constexpr int kMaxDev = 64;
     static std::atomic<int> cache[kMaxDev];
@@ -25,7 +28,7 @@ int resident_workgroups(K kernel, int threads)
     }
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, threads, 0) != hipSuccess)
         return 0;
     const int v = cus * per_cu;
     if (v > 0 && dev >= 0 && dev < kMaxDev)

@@ -116,7 +116,7 @@ def test_attn_fwd_window_rejects_a_negative_window():
     (-1.0, 0, M.MIATTN_ERR_INVALID_ARG, "softcap"),
     (float("nan"), 0, M.MIATTN_ERR_INVALID_ARG, "softcap"),
     (float("inf"), 0, M.MIATTN_ERR_INVALID_ARG, "softcap"),
-    (5.0, FAKE, M.MIATTN_ERR_UNSUPPORTED, "together"),
+    (5.0, FAKE + 2, M.MIATTN_ERR_INVALID_ARG, "alibi_slopes"),
     (0.0, FAKE + 2, M.MIATTN_ERR_INVALID_ARG, "alibi_slopes"),
 ])
 def test_attn_fwd_ext_rejects(softcap, alibi, status, needle):
@@ -133,7 +133,7 @@ def test_attn_fwd_varlen_rejects():
         ("ck", FAKE), ("B", 2), ("tq", 100), ("tk", 120), ("mq", 60), ("mk", 70), ("Hq", 4),
         ("Hkv", 2), ("d", 128), ("causal", 1), ("scale", 0.1), ("stream", 0))]
     for kw, status, needle in [
-            (dict(d=64), M.MIATTN_ERR_UNSUPPORTED, "d = 128 or 256"),
+            (dict(d=96), M.MIATTN_ERR_UNSUPPORTED, "head dimension"),
             (dict(cq=0), M.MIATTN_ERR_INVALID_ARG, "cu_seqlens_q is NULL"),
             (dict(ck=FAKE + 2), M.MIATTN_ERR_INVALID_ARG, "aligned"),
             (dict(tq=-1), M.MIATTN_ERR_INVALID_ARG, "sizes"),

@@ -88,11 +88,21 @@ def test_alibi_parity(case):
            alibi_slopes(Hq), 0.5, f"alibi {case}")
 
 
-def test_softcap_and_alibi_together_rejected():
-    q = np.zeros((1, 1, 4, 64), np.uint16)
-    with pytest.raises(H.miattn.MiattnError) as e:
-        H.run_fwd_ext(q, q, q, True, 0.125, -1, 5.0, np.ones(1, np.float32))
-    assert e.value.status == H.miattn.MIATTN_ERR_UNSUPPORTED
+BOTH = [
+    # B, Hq, Hkv, Sq, Sk, d, causal, window, softcap
+    (1, 4, 2, 300, 300, 64, True, -1, 20.0),
+    (2, 4, 4, 190, 333, 128, False, -1, 30.0),
+    (1, 8, 2, 257, 257, 256, True, -1, 10.0),
+    (1, 4, 4, 500, 500, 128, True, 64, 15.0),
+]
+
+
+@pytest.mark.parametrize("case", BOTH)
+def test_softcap_and_alibi_together(case):
+    """Soft cap, then ALiBi, then the mask (and a window in the last case)."""
+    B, Hq, Hkv, Sq, Sk, d, causal, window, softcap = case
+    _check(7700 + BOTH.index(case), B, Hq, Hkv, Sq, Sk, d, causal, window, softcap,
+           alibi_slopes(Hq), 1.0, f"softcap+alibi {case}")
 
 
 # the two score-variant rows of the pages' table (§7.3: forward, n = 2k,

@@ -1,8 +1,8 @@
 """GPU: packed variable-length batches (attn_fwd_varlen) against the f64 oracle.
 
 Sequences of 0 to 1000 query rows and as many or more keys (a chunk of new
-queries against its cached prefix), causal and not, head dimensions 128 and
-256, GQA; max_seqlen_q above the longest sequence (the launch's items past a
+queries against its cached prefix), causal and not, head dimensions 64, 128
+and 256, GQA; max_seqlen_q above the longest sequence (the launch's items past a
 sequence's end are skipped); more work items than resident workgroups. A
 batch of equal lengths must match attn_fwd on the same data bit for bit.
 Tolerances as for attn_fwd.
@@ -55,6 +55,8 @@ VARLEN = [
     (2, [0, 1, 31, 32, 33, 257, 700], [0, 3, 0, 0, 0, 9, 0], 4, 2, 128, False),
     (3, [5, 300, 129, 1000], [0, 200, 0, 17], 4, 1, 256, True),
     (4, [64, 65, 190], [1, 0, 300], 2, 2, 256, False),
+    (5, [0, 1, 31, 33, 127, 129, 700], [0, 2, 0, 40, 0, 9, 64], 4, 2, 64, True),
+    (6, [5, 300, 129], [0, 200, 17], 6, 3, 64, False),
 ]
 
 
@@ -78,7 +80,7 @@ def test_varlen_parity(case):
     H.assert_parity(m, label)
 
 
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_varlen_equal_lengths_match_attn_fwd(d):
     B, Hq, Hkv, S = 3, 4, 2, 300
     q = _bits(40 + d, (B, Hq, S, d))

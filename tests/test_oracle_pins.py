@@ -189,6 +189,9 @@ MOD_CASES = [
     (1, 2, 1, 6, 6, 4, True, -1, 0.0, (0.5, 0.125)),
     (1, 2, 2, 5, 9, 3, False, -1, 0.0, (0.25, 1.0)),
     (1, 2, 1, 8, 8, 4, True, 3, 0.0, (0.75, 0.0)),
+    # both: the cap first, then the ALiBi term
+    (1, 2, 1, 6, 6, 4, True, -1, 0.75, (0.5, 0.125)),
+    (1, 2, 2, 5, 9, 3, False, 2, 3.0, (0.25, 1.0)),
 ]
 
 

@@ -618,7 +618,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60,
                     help="timed steps, in three rounds (default 60: 3 x 20)")
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first (the clock settles over the first tens of steps)")
     ap.add_argument("--long-steps", type=int, default=2, help="long-context launches per round")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true")

@@ -185,8 +185,9 @@ MIATTN_API int attn_fwd_varlen(const void *q, const void *k, const void *v, void
  *   dk    bf16 [B, Hkv, Sk, d]   written (summed over the Hq/Hkv query heads
  *   dv    bf16 [B, Hkv, Sk, d]   written  that read each kv-head)
  *   workspace  device scratch of at least attn_bwd_workspace_size(B, Hq, Sq)
- *              bytes (f32 D_i per row, computed first); contents on entry do
- *              not matter. Two calls sharing one workspace must be ordered.
+ *              bytes (per row the f32 pair D_i, LSE_i log2 e, computed
+ *              first); 4-byte aligned; contents on entry do not matter. Two
+ *              calls sharing one workspace must be ordered.
  *
  * f32 accumulation, bf16 results; P and dS are rounded to bf16 for their
  * matrix products. Head dimensions 64, 128 and 256. Keys no query sees get
@@ -198,7 +199,7 @@ MIATTN_API int attn_bwd(const void *q, const void *k, const void *v, const void 
              float scale, void *workspace, size_t workspace_bytes,
              hipStream_t stream);
 
-/* Bytes of workspace attn_bwd needs: B * Hq * Sq * 4. 0 for invalid sizes. */
+/* Bytes of workspace attn_bwd needs: B * Hq * Sq * 8. 0 for invalid sizes. */
 MIATTN_API size_t attn_bwd_workspace_size(int B, int Hq, int Sq);
 
 /*

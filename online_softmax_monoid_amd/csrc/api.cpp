@@ -355,7 +355,7 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Sq)
 {
     if (B < 0 || Hq < 1 || Sq < 0)
         return 0;
-    return (size_t)B * (size_t)Hq * (size_t)Sq * sizeof(float);
+    return (size_t)B * (size_t)Hq * (size_t)Sq * 2 * sizeof(float);
 }
 
 int attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,

@@ -27,6 +27,9 @@
 #include <stdint.h>
 
 #include "launch.h"
+#include "lds_copy.h"
+#include "resident.h"
+#include "tile_order.h"
 
 namespace miattn {
 namespace {
@@ -119,39 +122,114 @@ __device__ __forceinline__ bf16x8 read_tr(const uint16_t *t, int db, int c, int 
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// ---- dK, dV: one wave per (b, kv-head, 32-key tile) ----------------------------
-// S = Q K^T and dP = dO V^T put the key in the lane (column) and 16 query rows
-// in the registers; P and dS packed by registers are the A operands of
-// dV += P^T dO and dK += dS^T Q over those rows, with dO and Q read
-// transposed from LDS.
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdArgs a, int n_ktiles)
+// ---- head dimensions 64 and 128: workgroups of waves sharing a copy ring ---------
+// The operand tiles that every wave of a workgroup reads go global -> LDS by
+// buffer DMA (inline assembly, explicit waits) into a ring of RING stages, one
+// barrier per step: stage t is copied RING - 1 steps ahead, into the slot that
+// stage t - 1 used, which every wave has left once it passes step t's barrier.
+// Past the walk's end the copies cover no bytes (descriptors of length 0), so
+// every step issues the same number of copies and the waits stay fixed.
+// A tile read both ways is stored twice:
+//   fragment-major, block kk (1 KB): lane L's 16 bytes of row L%32, dims
+//     16kk + 8(L/32) .. +7 -- the operand of a product over the head dimension;
+//   transposing, the layout of read_tr above -- the operand of a product over
+//     the tile's rows.
+// Copy instruction i of a tile moves 1 KB, 16 bytes per lane from the offsets
+// below (rows past the descriptor's end read as zero).
+__device__ __forceinline__ uint32_t off_frag(int D, int i, int l32, int g)
 {
-    constexpr int KK = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t sQT[D * 32];
-    __shared__ __attribute__((aligned(16))) uint16_t sDT[D * 32];
-    __shared__ __attribute__((aligned(16))) float sL[32];   // LSE_i log2(e), row i0 + i
-    __shared__ __attribute__((aligned(16))) float sDv[32];  // D_i
+    return (uint32_t)(l32 * D + 16 * i + 8 * g) * 2;
+}
+__device__ __forceinline__ uint32_t off_tr(int D, int i, int l32, int g)
+{
+    const int db = i >> 1, kc = i & 1;
+    const int G4 = l32 >> 3, jj = (l32 >> 1) & 3, qh = l32 & 1;
+    const int row = 16 * kc + 8 * g + 4 * (G4 >> 1) + jj;
+    const int dim = 32 * db + 16 * (G4 & 1) + 8 * qh;
+    return (uint32_t)(row * D + dim) * 2;
+}
 
-    const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
-    int id = blockIdx.x;
-    const int kt = id % n_ktiles;
-    id /= n_ktiles;
-    const int kvh = id % a.Hkv;
-    const int b = id / a.Hkv;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+
+// 16 bytes at LDS byte address addr
+__device__ __forceinline__ u32x4 lds16(uint32_t addr) { return *(lds_u32x4 *)(uintptr_t)addr; }
+
+// read_tr from LDS byte addresses: addr = the tile's first byte + 8 lane
+__device__ __forceinline__ bf16x8 lds_tr(uint32_t addr, int db, int c)
+{
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const uint32_t p = addr + ((2 * db + c) * 2) * 512;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(p + 512));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Workgroup barrier that no memory access of the source crosses: the copies
+// into LDS are invisible to the compiler, so it must not move an LDS read
+// above the barrier that publishes the copied data.
+__device__ __forceinline__ void ring_barrier()
+{
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Wait for the fragments a wave loaded for itself and pin them there: the
+// compiler counts only its own loads, and with a use inside the loop it would
+// put the wait there, where it also drains every copy in flight.
+template <int N>
+__device__ __forceinline__ void settle(bf16x8 (&f)[N])
+{
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        u32x4 w = __builtin_bit_cast(u32x4, f[i]);
+        asm volatile("" : "+v"(w));
+        f[i] = __builtin_bit_cast(bf16x8, w);
+    }
+}
+
+// ---- dK, dV: one workgroup of four waves per (b, kv-head, 128-key block) -------------
+// Wave w holds keys j0 + 32w + l32 (K and V rows: the B operands of S = Q K^T
+// and dP = dO V^T, in registers). The workgroup walks the query tiles that see
+// any of its keys, over the kv-head's query heads, as one sequence of steps;
+// per step the ring holds the tile's Q and dO in both layouts and, per wave, its
+// rows' (D_i, LSE_i log2 e) pairs from the workspace. S and dP put the key in the
+// lane and 16 query rows in the registers; P and dS packed by registers are the
+// A operands of dV += P^T dO and dK += dS^T Q over those rows, with dO and Q
+// read transposed.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, int gx)
+{
+    constexpr int KK = D / 16, DB = D / 32, NW = 4, CPT = KK / NW;  // copies per tile and wave
+    constexpr int RING = 4;
+    constexpr int TILE_B = D * 64;         // one 32-row tile in one layout
+    constexpr int STAGE_B = 4 * TILE_B;    // Q frag, Q tr, dO frag, dO tr
+    constexpr int NCOPY = 4 * CPT + 1;     // copies per stage and wave
+    __shared__ __attribute__((aligned(1024))) uint4 sRing[RING * STAGE_B / 16];
+    __shared__ __attribute__((aligned(16))) float sStat[RING * NW * 64];
+
+    const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const TileOrder to = tile_order_grouped(blockIdx.x, a.B * a.Hkv, 1, nkb, false, gx);
+    const int kvh = to.unit % a.Hkv, b = to.unit / a.Hkv;
     const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq, G = a.Hq / a.Hkv;
-    const int j0 = 32 * kt;
+    const int j0 = 128 * to.qtile, jw0 = j0 + 32 * wave, my_key = jw0 + l32;
     const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
     const float c = a.scale * kLog2e;
 
+    // this wave's keys, loaded before the first copy is issued
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + krow0 * D, (uint32_t)Sk * D * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + krow0 * D, (uint32_t)Sk * D * 2);
-    bf16x8 kf[KK], vf[KK];  // B operands: key j0 + l32, dims 16kk + 8g
+    bf16x8 kf[KK], vf[KK];  // key my_key, dims 16kk + 8g
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-        kf[kk] = frag<D>(rk, j0 + l32, kk, g);
-        vf[kk] = frag<D>(rv, j0 + l32, kk, g);
+        kf[kk] = frag<D>(rk, my_key, kk, g);
+        vf[kk] = frag<D>(rv, my_key, kk, g);
     }
+    settle(kf);
+    settle(vf);
     f32x16 dk[DB], dv[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -159,90 +237,118 @@ __global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdArgs a, int n_ktiles)
         for (int r = 0; r < 16; ++r)
             dk[db][r] = dv[db][r] = 0.f;
 
-    // query tiles that see any key of this tile: rows i with j0 <= i + diag,
-    // walked as one sequence over the group's query heads; the next tile's
-    // fragments load while the current one computes
+    // query tiles that see any key of the block: rows i >= j0 - diag
     const int i_first = CAUSAL ? max(0, j0 - diag) : 0;
     const int qt0 = i_first / 32, nqt = (Sq + 31) / 32;
     const int per_head = max(0, nqt - qt0), n_steps = G * per_head;
-    const int my_key = j0 + l32;
-    bf16x8 qa[KK], da[KK];  // A operands: row i0 + l32, dims 16kk + 8g
-    auto load_step = [&](int t) __attribute__((always_inline)) {
-        const int hq = kvh * G + t / per_head, i0 = 32 * (qt0 + t % per_head);
-        const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0 * D, (uint32_t)Sq * D * 2);
-        const __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout + qrow0 * D, (uint32_t)Sq * D * 2);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            qa[kk] = frag<D>(rq, i0 + l32, kk, g);
-            da[kk] = frag<D>(rdo, i0 + l32, kk, g);
-        }
-    };
-    if (n_steps > 0)
-        load_step(0);
-    for (int t = 0; t < n_steps; ++t) {
-        const int hq = kvh * G + t / per_head, i0 = 32 * (qt0 + t % per_head);
-        const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
-        __syncthreads();  // the previous tile's LDS reads are done
-        if (g == 0) {
-            const int i = i0 + l32;
-            sDv[l32] = i < Sq ? a.dsum[qrow0 + i] : 0.f;
-            sL[l32] = i < Sq ? a.lse[qrow0 + i] * kLog2e : -INFINITY;
-        }
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            write_blk(sQT, qa[kk], l32, kk, g);
-            write_blk(sDT, da[kk], l32, kk, g);
-        }
-        __syncthreads();
 
+    uint32_t foff[CPT], toff[CPT];
+#pragma unroll
+    for (int h = 0; h < CPT; ++h) {
+        foff[h] = off_frag(D, CPT * wave + h, l32, g);
+        toff[h] = off_tr(D, CPT * wave + h, l32, g);
+    }
+    const uint32_t ring0 = lds_addr(sRing), stat0 = lds_addr(sStat);
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const uint16_t *qs = a.q, *dos = a.dout;
+        const float *ws = a.dsum;
+        uint32_t nq = 0, nw = 0;
+        if (t < n_steps) {
+            const int hq = kvh * G + t / per_head, i0 = 32 * (qt0 + t % per_head);
+            const int64_t r0 = ((int64_t)b * a.Hq + hq) * Sq + i0;
+            qs = a.q + r0 * D;
+            dos = a.dout + r0 * D;
+            ws = a.dsum + 2 * r0;
+            nq = (uint32_t)(Sq - i0) * (D * 2);
+            nw = (uint32_t)(Sq - i0) * 8;
+        }
+        const u32x4 dq_ = make_desc(qs, nq), dd = make_desc(dos, nq), dw = make_desc(ws, nw);
+        const uint32_t base = ring0 + (uint32_t)(t % RING) * STAGE_B + 1024 * CPT * wave;
+#pragma unroll
+        for (int h = 0; h < CPT; ++h) {
+            copy_to_lds(dq_, foff[h], base + 1024 * h);
+            copy_to_lds(dq_, toff[h], base + TILE_B + 1024 * h);
+            copy_to_lds(dd, foff[h], base + 2 * TILE_B + 1024 * h);
+            copy_to_lds(dd, toff[h], base + 3 * TILE_B + 1024 * h);
+        }
+        copy_to_lds_b32(dw, 4 * lane, stat0 + ((uint32_t)(t % RING) * NW + wave) * 256);
+    };
+
+#pragma unroll
+    for (int t = 0; t < RING - 1; ++t)
+        issue(t);
+    for (int t = 0; t < n_steps; ++t) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((RING - 2) * NCOPY));  // this wave's copies of stage t
+        ring_barrier();                                              // and every other wave's
+        issue(t + RING - 1);
+        const int i0 = 32 * (qt0 + t % per_head);
+        const bool any = jw0 < Sk && (!CAUSAL || i0 + 31 + diag >= jw0);
+        if (!any)
+            continue;
+        const bool full = (!CAUSAL || i0 + diag >= jw0 + 31) && jw0 + 31 < Sk && i0 + 31 < Sq;
+        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B;
         f32x16 s, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             s[r] = dp[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[kk], vf[kk], dp, 0, 0, 0);
+            const bf16x8 qa = __builtin_bit_cast(bf16x8, lds16(sb + 1024 * kk + 16 * lane));
+            const bf16x8 da = __builtin_bit_cast(bf16x8, lds16(sb + 2 * TILE_B + 1024 * kk + 16 * lane));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp, 0, 0, 0);
         }
-        if (t + 1 < n_steps)
-            load_step(t + 1);  // in flight during the rest of this step
-        // lane: key my_key; register r: row i0 + 8(r/4) + 4g + r%4 (rows
-        // 8(r/4) + 4g .. +3 are one 16-byte read of each statistic)
+        // lane: key my_key; register r: row i0 + 8(r/4) + 4g + r%4, whose (D, L)
+        // pair sits at byte 8 (8(r/4) + 4g + r%4) of the wave's statistics
+        const uint32_t st = stat0 + ((uint32_t)(t % RING) * NW + wave) * 256 + 32 * g;
         f32x16 p, ds;
+        float Dv[16];
+        bool live[16];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-            const float4 L4 = *(const float4 *)&sL[8 * r4 + 4 * g];
-            const float4 D4 = *(const float4 *)&sDv[8 * r4 + 4 * g];
-            const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
+            const u32x4 w0 = lds16(st + 64 * r4), w1 = lds16(st + 64 * r4 + 16);
+            const float Dr[4] = {__uint_as_float(w0.x), __uint_as_float(w0.z),
+                                 __uint_as_float(w1.x), __uint_as_float(w1.z)};
+            const float Lr[4] = {__uint_as_float(w0.y), __uint_as_float(w0.w),
+                                 __uint_as_float(w1.y), __uint_as_float(w1.w)};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int r = 4 * r4 + u;
-                const int i = i0 + 8 * r4 + 4 * g + u;
-                const bool vis = my_key < Sk && i < Sq && Lr[u] > -INFINITY &&
-                                 (!CAUSAL || my_key <= i + diag);
-                p[r] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -Lr[u])) : 0.f;
-                ds[r] = p[r] * (dp[r] - Dr[u]);
+                p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -Lr[u]));
+                Dv[r] = Dr[u];
+                live[r] = Lr[u] > -INFINITY;
             }
         }
+        if (!full) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                const bool vis = my_key < Sk && i < Sq && live[r] && (!CAUSAL || my_key <= i + diag);
+                p[r] = vis ? p[r] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            ds[r] = p[r] * (dp[r] - Dv[r]);
+        const uint32_t trd = sb + 3 * TILE_B + 8 * lane, trq = sb + TILE_B + 8 * lane;
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
             const bf16x8 pa = pack_chunk(p, ch), sa = pack_chunk(ds, ch);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, read_tr(sDT, db, ch, lane),
-                                                                 dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, read_tr(sQT, db, ch, lane),
-                                                                 dk[db], 0, 0, 0);
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, lds_tr(trd, db, ch), dv[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, lds_tr(trq, db, ch), dk[db], 0, 0, 0);
             }
         }
     }
-    // lane: dim 32 db + l32; register r: key j0 + 8(r/4) + 4g + r%4
+    // no copy may land in LDS after the workgroup has ended
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // lane: dim 32 db + l32; register r: key jw0 + 8(r/4) + 4g + r%4
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const int j = jw0 + 8 * (r >> 2) + 4 * g + (r & 3);
             if (j < Sk) {
                 a.dk[(krow0 + j) * D + 32 * db + l32] = to_bf16(dk[db][r] * a.scale);
                 a.dv[(krow0 + j) * D + 32 * db + l32] = to_bf16(dv[db][r]);
@@ -250,42 +356,51 @@ __global__ void __launch_bounds__(64) bwd_dkdv_kernel(BwdArgs a, int n_ktiles)
         }
 }
 
-// ---- dQ: one wave per (b, query head, 32-row query tile) -------------------------
-// S^T = K Q^T and dP^T = V dO^T put the query row in the lane and 16 keys in
-// the registers; dS packed by registers is the A operand of dQ += dS K over
-// those keys, with K read transposed from LDS.
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(64) bwd_dq_kernel(BwdArgs a, int n_qtiles)
+// ---- dQ: one workgroup of NW waves per (b, query head, 32 NW-row block) ------------
+// Wave w holds rows ib0 + 32w + l32 (Q and dO rows: the B operands of
+// S^T = K Q^T and dP^T = V dO^T, in registers, with the rows' D_i and
+// LSE_i log2 e). The workgroup walks the key tiles that any of its rows sees;
+// per step the ring holds the tile's K and V fragment-major and K transposing.
+// S^T and dP^T put the query row in the lane and 16 keys in the registers; dS
+// packed by registers is the A operand of dQ += dS K over those keys.
+template <int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb, int gx)
 {
     constexpr int KK = D / 16, DB = D / 32;
-    __shared__ __attribute__((aligned(16))) uint16_t sKT[D * 32];
+    static_assert((3 * KK) % NW == 0, "copies must split evenly over the waves");
+    constexpr int NCOPY = 3 * KK / NW;     // copies per stage and wave
+    constexpr int RING = 4;
+    constexpr int TILE_B = D * 64;
+    constexpr int STAGE_B = 3 * TILE_B;    // K frag, V frag, K tr
+    __shared__ __attribute__((aligned(1024))) uint4 sRing[RING * STAGE_B / 16];
 
-    const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
-    int id = blockIdx.x;
-    const int qt = id % n_qtiles;
-    id /= n_qtiles;
-    const int hq = id % a.Hq;
-    const int b = id / a.Hq;
-    const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq, G = a.Hq / a.Hkv;
-    const int kvh = hq / G;
-    const int i0 = 32 * qt, my_q = i0 + l32;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = a.Hq / a.Hkv;
+    const TileOrder to = tile_order_grouped(blockIdx.x, a.B * a.Hkv, G, nrb, CAUSAL, gx);
+    const int kvh = to.unit % a.Hkv, b = to.unit / a.Hkv, hq = kvh * G + to.gq;
+    const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq;
+    const int ib0 = 32 * NW * to.qtile, iw0 = ib0 + 32 * wave, my_q = iw0 + l32;
     const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
     const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
     const float c = a.scale * kLog2e;
 
+    // this wave's rows, loaded before the first copy is issued
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qrow0 * D, (uint32_t)Sq * D * 2);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout + qrow0 * D, (uint32_t)Sq * D * 2);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + krow0 * D, (uint32_t)Sk * D * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + krow0 * D, (uint32_t)Sk * D * 2);
-    bf16x8 qf[KK], df[KK];  // B operands: row my_q, dims 16kk + 8g
+    bf16x8 qf[KK], df[KK];  // row my_q, dims 16kk + 8g
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
         qf[kk] = frag<D>(rq, my_q, kk, g);
         df[kk] = frag<D>(rdo, my_q, kk, g);
     }
-    const float Di = my_q < Sq ? a.dsum[qrow0 + my_q] : 0.f;
-    const float L = my_q < Sq ? a.lse[qrow0 + my_q] : -INFINITY;
-    const bool row_live = L > -INFINITY;
+    const bool in = my_q < Sq;
+    float Di = in ? a.dsum[2 * (qrow0 + my_q)] : 0.f;
+    float L2 = in ? a.dsum[2 * (qrow0 + my_q) + 1] : -INFINITY;
+    settle(qf);
+    settle(df);
+    asm volatile("" : "+v"(Di), "+v"(L2));
+    const bool row_live = L2 > -INFINITY;
 
     f32x16 dq[DB];
 #pragma unroll
@@ -294,61 +409,94 @@ __global__ void __launch_bounds__(64) bwd_dq_kernel(BwdArgs a, int n_qtiles)
         for (int r = 0; r < 16; ++r)
             dq[db][r] = 0.f;
 
-    const int kv_end = CAUSAL ? min(Sk, max(0, min(i0 + 31, Sq - 1) + diag + 1)) : Sk;
+    // key tiles that any row of the block sees
+    const int i_last = min(ib0 + 32 * NW, Sq) - 1;
+    const int kv_end = CAUSAL ? min(Sk, max(0, i_last + diag + 1)) : Sk;
     const int nkt = (kv_end + 31) / 32;
-    bf16x8 ka[KK], va[KK];  // A operands: key j0 + l32, dims 16kk + 8g (loaded a tile ahead)
-    auto load_tile = [&](int kt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            ka[kk] = frag<D>(rk, 32 * kt + l32, kk, g);
-            va[kk] = frag<D>(rv, 32 * kt + l32, kk, g);
-        }
-    };
-    if (nkt > 0)
-        load_tile(0);
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int j0 = 32 * kt;
-        __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            write_blk(sKT, ka[kk], l32, kk, g);
-        __syncthreads();
 
+    // copy e = NCOPY w + h of a stage: tile e / KK (K frag, V frag, K tr),
+    // instruction e % KK
+    uint32_t coff[NCOPY], cdst[NCOPY];
+    bool cv[NCOPY];
+#pragma unroll
+    for (int h = 0; h < NCOPY; ++h) {
+        const int e = NCOPY * wave + h, x = e / KK, i = e % KK;
+        coff[h] = x == 2 ? off_tr(D, i, l32, g) : off_frag(D, i, l32, g);
+        cdst[h] = (uint32_t)(x * TILE_B + 1024 * i);
+        cv[h] = x == 1;
+    }
+    const uint32_t ring0 = lds_addr(sRing);
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const uint16_t *ks = a.k, *vs = a.v;
+        uint32_t n = 0;
+        if (t < nkt) {
+            ks = a.k + (krow0 + 32 * t) * D;
+            vs = a.v + (krow0 + 32 * t) * D;
+            n = (uint32_t)(kv_end - 32 * t) * (D * 2);
+        }
+        const u32x4 dk_ = make_desc(ks, n), dv_ = make_desc(vs, n);
+        const uint32_t base = ring0 + (uint32_t)(t % RING) * STAGE_B;
+#pragma unroll
+        for (int h = 0; h < NCOPY; ++h)
+            copy_to_lds(cv[h] ? dv_ : dk_, coff[h], base + cdst[h]);
+    };
+
+#pragma unroll
+    for (int t = 0; t < RING - 1; ++t)
+        issue(t);
+    for (int t = 0; t < nkt; ++t) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((RING - 2) * NCOPY));
+        ring_barrier();
+        issue(t + RING - 1);
+        const int j0 = 32 * t;
+        const bool any = iw0 < Sq && (!CAUSAL || iw0 + 31 + diag >= j0);
+        if (!any)
+            continue;
+        const bool full = (!CAUSAL || iw0 + diag >= j0 + 31) && j0 + 31 < Sk && iw0 + 31 < Sq;
+        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B;
         f32x16 s, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             s[r] = dp[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk], df[kk], dp, 0, 0, 0);
+            const bf16x8 ka = __builtin_bit_cast(bf16x8, lds16(sb + 1024 * kk + 16 * lane));
+            const bf16x8 va = __builtin_bit_cast(bf16x8, lds16(sb + TILE_B + 1024 * kk + 16 * lane));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kk], dp, 0, 0, 0);
         }
-        if (kt + 1 < nkt)
-            load_tile(kt + 1);  // in flight during the rest of this tile
         // lane: row my_q; register r: key j0 + 8(r/4) + 4g + r%4
         f32x16 ds;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool vis = row_live && j < Sk && (!CAUSAL || j <= my_q + diag);
-            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -L * kLog2e)) : 0.f;
-            ds[r] = p * (dp[r] - Di);
+        for (int r = 0; r < 16; ++r)
+            ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -L2));
+        if (!full) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                const bool vis = row_live && j < Sk && (!CAUSAL || j <= my_q + diag);
+                ds[r] = vis ? ds[r] : 0.f;
+            }
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            ds[r] = ds[r] * (dp[r] - Di);
+        const uint32_t trk = sb + 2 * TILE_B + 8 * lane;
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
             const bf16x8 sa = pack_chunk(ds, ch);
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, read_tr(sKT, db, ch, lane),
-                                                                 dq[db], 0, 0, 0);
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, lds_tr(trk, db, ch), dq[db], 0, 0, 0);
         }
     }
-    // lane: dim 32 db + l32; register r: row i0 + 8(r/4) + 4g + r%4
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // lane: dim 32 db + l32; register r: row iw0 + 8(r/4) + 4g + r%4
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const int i = iw0 + 8 * (r >> 2) + 4 * g + (r & 3);
             if (i < Sq)
                 a.dq[(qrow0 + i) * D + 32 * db + l32] = to_bf16(dq[db][r] * a.scale);
         }
@@ -429,7 +577,7 @@ __global__ void __launch_bounds__(128) bwd_dkdv2_kernel(BwdArgs a, int n_ktiles)
             if (wave == 0)
                 sL[l32] = i < Sq ? a.lse[qrow0 + i] * kLog2e : -INFINITY;
             else
-                sDv[l32] = i < Sq ? a.dsum[qrow0 + i] : 0.f;
+                sDv[l32] = i < Sq ? a.dsum[2 * (qrow0 + i)] : 0.f;
         }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -563,7 +711,7 @@ __global__ void __launch_bounds__(128) bwd_dq2_kernel(BwdArgs a, int n_qtiles)
         bf[kk] = frag<D>(rqd, my_q, kk, g);
         to_agpr(bf[kk]);
     }
-    const float Di = my_q < Sq ? a.dsum[qrow0 + my_q] : 0.f;
+    const float Di = my_q < Sq ? a.dsum[2 * (qrow0 + my_q)] : 0.f;
     const float L = my_q < Sq ? a.lse[qrow0 + my_q] : -INFINITY;
     const bool row_live = L > -INFINITY;
 
@@ -651,9 +799,10 @@ __global__ void __launch_bounds__(128) bwd_dq2_kernel(BwdArgs a, int n_qtiles)
         }
 }
 
-// ---- D_i = dO_i . O_i for every row, once (the workspace) -----------------------
-// one wave per 32 rows of a (b, query head): lane l32 + 32 g takes dims
-// 16kk + 8g .. +7 of row l32
+// ---- per-row statistics, once (the workspace) ------------------------------------
+// Row i's pair (D_i = dO_i . O_i, LSE_i log2 e) as two floats. One wave per 32
+// rows of a (b, query head): lane l32 + 32 g takes dims 16kk + 8g .. +7 of row
+// l32.
 template <int D>
 __global__ void __launch_bounds__(64) bwd_dsum_kernel(BwdArgs a, int n_qtiles)
 {
@@ -673,43 +822,56 @@ __global__ void __launch_bounds__(64) bwd_dsum_kernel(BwdArgs a, int n_qtiles)
             dot += (float)d[e] * (float)o[e];
     }
     dot += __shfl_xor(dot, 32, 64);
-    if (g == 0 && i < Sq)
-        a.dsum[qrow0 + i] = dot;
+    if (i < Sq) {
+        if (g == 0)
+            a.dsum[2 * (qrow0 + i)] = dot;
+        else
+            a.dsum[2 * (qrow0 + i) + 1] = a.lse[qrow0 + i] * kLog2e;
+    }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
 {
-    // head dimensions 64 and 128: one wave per tile; 256: two cooperating waves
+    // head dimensions 64 and 128: workgroups sharing a copy ring (dK/dV: 128
+    // keys of four waves; dQ: 32 NWQ rows); 256: two cooperating waves per tile
     constexpr bool TWO = D == 256;
+    constexpr int NWQ = D == 128 ? 8 : 4;
     const int n_ktiles = (a.Sk + 31) / 32, n_qtiles = (a.Sq + 31) / 32;
-    const long long g1 = (long long)a.B * a.Hkv * n_ktiles, g2 = (long long)a.B * a.Hq * n_qtiles;
-    if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL)
+    const int nkb = (a.Sk + 127) / 128, nrb = (a.Sq + 32 * NWQ - 1) / (32 * NWQ);
+    const long long g0 = (long long)a.B * a.Hq * n_qtiles;
+    const long long g1 = (long long)a.B * a.Hkv * (TWO ? n_ktiles : nkb);
+    const long long g2 = (long long)a.B * a.Hq * (TWO ? n_qtiles : nrb);
+    if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
-    if (g2 > 0) {
-        hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)g2), dim3(64), 0, stream, a, n_qtiles);
+    if (g0 > 0) {
+        hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)g0), dim3(64), 0, stream, a, n_qtiles);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
     if (g1 > 0) {
-        if constexpr (TWO)
+        if constexpr (TWO) {
             hipLaunchKernelGGL((bwd_dkdv2_kernel<D, CAUSAL>), dim3((unsigned)g1), dim3(128), 0,
                                stream, a, n_ktiles);
-        else
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)g1), dim3(64), 0,
-                               stream, a, n_ktiles);
+        } else {
+            constexpr auto kernel = bwd_dkdv_ring_kernel<D, CAUSAL>;
+            const int gx = max(1, resident_workgroups<kernel>(256) / 8);
+            hipLaunchKernelGGL(kernel, dim3((unsigned)g1), dim3(256), 0, stream, a, nkb, gx);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
     if (g2 > 0) {
-        if constexpr (TWO)
+        if constexpr (TWO) {
             hipLaunchKernelGGL((bwd_dq2_kernel<D, CAUSAL>), dim3((unsigned)g2), dim3(128), 0, stream,
                                a, n_qtiles);
-        else
-            hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)g2), dim3(64), 0, stream,
-                               a, n_qtiles);
+        } else {
+            constexpr auto kernel = bwd_dq_ring_kernel<D, CAUSAL, NWQ>;
+            const int gx = max(1, resident_workgroups<kernel>(64 * NWQ) / 8);
+            hipLaunchKernelGGL(kernel, dim3((unsigned)g2), dim3(64 * NWQ), 0, stream, a, nrb, gx);
+        }
     }
     return hipGetLastError();
 }

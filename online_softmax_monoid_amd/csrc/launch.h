@@ -55,7 +55,7 @@ struct BwdArgs {
     const uint16_t *q, *k, *v, *o, *dout;
     const float *lse;
     uint16_t *dq, *dk, *dv;
-    float *dsum;  // workspace: D_i = dO_i . O_i, f32 [B, Hq, Sq]
+    float *dsum;  // workspace: per row (D_i = dO_i . O_i, LSE_i log2 e), f32 [B, Hq, Sq, 2]
     int B, Hq, Hkv, Sq, Sk;
     float scale;
 };

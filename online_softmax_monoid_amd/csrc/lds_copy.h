@@ -41,6 +41,15 @@ __device__ __forceinline__ void copy_to_lds(u32x4 desc, uint32_t voffset, uint32
                  : "memory");
 }
 
+// The same for 4 bytes per lane, landing at lds_base + 4 * lane.
+__device__ __forceinline__ void copy_to_lds_b32(u32x4 desc, uint32_t voffset, uint32_t lds_base)
+{
+    asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voffset), "s"(desc), "{m0}"(lds_base)
+                 : "memory");
+}
+
 // LDS byte address of a __shared__ object (wave-uniform)
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {

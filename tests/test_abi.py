@@ -148,7 +148,7 @@ def test_attn_fwd_varlen_rejects():
 def test_attn_bwd_rejects():
     L = M.load()
     wsb = M.attn_bwd_workspace_size(1, 2, 8)
-    assert wsb == 1 * 2 * 8 * 4 and M.attn_bwd_workspace_size(-1, 2, 8) == 0
+    assert wsb == 1 * 2 * 8 * 8 and M.attn_bwd_workspace_size(-1, 2, 8) == 0
     base = [FAKE] * 9 + [1, 2, 2, 8, 8, 128, 1, 0.125, FAKE, wsb, 0]
     for idx, val, status, needle in [
             (14, 96, M.MIATTN_ERR_UNSUPPORTED, "head dimension"),

@@ -23,6 +23,7 @@
 // ends read as zeros.
 
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -178,14 +179,19 @@ __device__ __forceinline__ void ring_barrier()
 // Wait for the fragments a wave loaded for itself and pin them there: the
 // compiler counts only its own loads, and with a use inside the loop it would
 // put the wait there, where it also drains every copy in flight.
-template <int N>
+// AGPR: pin them in AGPRs instead (the MFMAs read their A/B operands there),
+// leaving the VGPRs to the softmax work.
+template <bool AGPR = false, int N>
 __device__ __forceinline__ void settle(bf16x8 (&f)[N])
 {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         u32x4 w = __builtin_bit_cast(u32x4, f[i]);
-        asm volatile("" : "+v"(w));
+        if constexpr (AGPR)
+            asm volatile("" : "+a"(w));
+        else
+            asm volatile("" : "+v"(w));
         f[i] = __builtin_bit_cast(bf16x8, w);
     }
 }
@@ -228,8 +234,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
         kf[kk] = frag<D>(rk, my_key, kk, g);
         vf[kk] = frag<D>(rv, my_key, kk, g);
     }
-    settle(kf);
-    settle(vf);
+    settle<true>(kf);
+    settle<true>(vf);
     f32x16 dk[DB], dv[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -249,20 +255,19 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
         toff[h] = off_tr(D, CPT * wave + h, l32, g);
     }
     const uint32_t ring0 = lds_addr(sRing), stat0 = lds_addr(sStat);
+    // stage t's copies; past the walk's end they cover no bytes (the index
+    // math is clamped and the lengths selected, so that no branch splits the
+    // step)
     auto issue = [&](int t) __attribute__((always_inline)) {
-        const uint16_t *qs = a.q, *dos = a.dout;
-        const float *ws = a.dsum;
-        uint32_t nq = 0, nw = 0;
-        if (t < n_steps) {
-            const int hq = kvh * G + t / per_head, i0 = 32 * (qt0 + t % per_head);
-            const int64_t r0 = ((int64_t)b * a.Hq + hq) * Sq + i0;
-            qs = a.q + r0 * D;
-            dos = a.dout + r0 * D;
-            ws = a.dsum + 2 * r0;
-            nq = (uint32_t)(Sq - i0) * (D * 2);
-            nw = (uint32_t)(Sq - i0) * 8;
-        }
-        const u32x4 dq_ = make_desc(qs, nq), dd = make_desc(dos, nq), dw = make_desc(ws, nw);
+        const int tc = min(t, max(n_steps - 1, 0));
+        const int hq = kvh * G + (per_head > 0 ? tc / per_head : 0);
+        const int i0 = 32 * (qt0 + (per_head > 0 ? tc % per_head : 0));
+        const int64_t r0 = ((int64_t)b * a.Hq + hq) * Sq + min(i0, Sq);
+        const bool live = t < n_steps;
+        const uint32_t nq = live ? (uint32_t)(Sq - i0) * (D * 2) : 0u;
+        const uint32_t nw = live ? (uint32_t)(Sq - i0) * 8 : 0u;
+        const u32x4 dq_ = make_desc(a.q + r0 * D, nq), dd = make_desc(a.dout + r0 * D, nq);
+        const u32x4 dw = make_desc(a.dsum + 2 * r0, nw);
         const uint32_t base = ring0 + (uint32_t)(t % RING) * STAGE_B + 1024 * CPT * wave;
 #pragma unroll
         for (int h = 0; h < CPT; ++h) {
@@ -273,37 +278,39 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
         }
         copy_to_lds_b32(dw, 4 * lane, stat0 + ((uint32_t)(t % RING) * NW + wave) * 256);
     };
-
-#pragma unroll
-    for (int t = 0; t < RING - 1; ++t)
-        issue(t);
-    for (int t = 0; t < n_steps; ++t) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((RING - 2) * NCOPY));  // this wave's copies of stage t
-        ring_barrier();                                              // and every other wave's
-        issue(t + RING - 1);
-        const int i0 = 32 * (qt0 + t % per_head);
-        const bool any = jw0 < Sk && (!CAUSAL || i0 + 31 + diag >= jw0);
-        if (!any)
-            continue;
-        const bool full = (!CAUSAL || i0 + diag >= jw0 + 31) && jw0 + 31 < Sk && i0 + 31 < Sq;
-        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B;
-        f32x16 s, dp;
+    // S and dP of stage t (16 query rows per lane, key my_key)
+    auto qk = [&](int t, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
+        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + 16 * lane;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             s[r] = dp[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            const bf16x8 qa = __builtin_bit_cast(bf16x8, lds16(sb + 1024 * kk + 16 * lane));
-            const bf16x8 da = __builtin_bit_cast(bf16x8, lds16(sb + 2 * TILE_B + 1024 * kk + 16 * lane));
+            const bf16x8 qa = __builtin_bit_cast(bf16x8, lds16(sb + 1024 * kk));
+            const bf16x8 da = __builtin_bit_cast(bf16x8, lds16(sb + 2 * TILE_B + 1024 * kk));
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp, 0, 0, 0);
         }
-        // lane: key my_key; register r: row i0 + 8(r/4) + 4g + r%4, whose (D, L)
-        // pair sits at byte 8 (8(r/4) + 4g + r%4) of the wave's statistics
+    };
+    // One step: the softmax gradient of step t (its S and dP in registers)
+    // alongside S and dP of step t+1, then dV and dK of step t. full: no
+    // (row, key) pair of the step is hidden (not diagonal, not a ragged end).
+    auto step = [&](int t, bool full, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
+        const int i0 = 32 * (qt0 + t % per_head);
+        // lane: key my_key; register r: row i0 + 8(r/4) + 4g + r%4. Hidden
+        // pairs get the score -inf, so that their probability is exactly 0.
+        if (!full) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                const bool vis = my_key < Sk && i < Sq && (!CAUSAL || my_key <= i + diag);
+                s[r] = vis ? s[r] : -INFINITY;
+            }
+        }
+        // row r's (D, L) pair sits at byte 8 (8(r/4) + 4g + r%4) of the wave's
+        // statistics
         const uint32_t st = stat0 + ((uint32_t)(t % RING) * NW + wave) * 256 + 32 * g;
         f32x16 p, ds;
-        float Dv[16];
-        bool live[16];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
             const u32x4 w0 = lds16(st + 64 * r4), w1 = lds16(st + 64 * r4 + 16);
@@ -315,31 +322,42 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
             for (int u = 0; u < 4; ++u) {
                 const int r = 4 * r4 + u;
                 p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -Lr[u]));
-                Dv[r] = Dr[u];
-                live[r] = Lr[u] > -INFINITY;
+                ds[r] = p[r] * (dp[r] - Dr[u]);
             }
         }
-        if (!full) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
-                const bool vis = my_key < Sk && i < Sq && live[r] && (!CAUSAL || my_key <= i + diag);
-                p[r] = vis ? p[r] : 0.f;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            ds[r] = p[r] * (dp[r] - Dv[r]);
-        const uint32_t trd = sb + 3 * TILE_B + 8 * lane, trq = sb + TILE_B + 8 * lane;
+        const bf16x8 pa0 = pack_chunk(p, 0), pa1 = pack_chunk(p, 1);
+        const bf16x8 sa0 = pack_chunk(ds, 0), sa1 = pack_chunk(ds, 1);
+        qk(t + 1, s, dp);
+        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + 8 * lane;
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-            const bf16x8 pa = pack_chunk(p, ch), sa = pack_chunk(ds, ch);
+            const bf16x8 pa = ch ? pa1 : pa0, sa = ch ? sa1 : sa0;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, lds_tr(trd, db, ch), dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, lds_tr(trq, db, ch), dk[db], 0, 0, 0);
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, lds_tr(sb + 3 * TILE_B, db, ch), dv[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, lds_tr(sb + TILE_B, db, ch), dk[db], 0, 0, 0);
             }
         }
+    };
+
+    // stage t is waited for at the top of step t - 1 (its S and dP are made
+    // there), copied at the top of step t - 3 into the slot of stage t - 4
+#pragma unroll
+    for (int t = 0; t < RING - 1; ++t)
+        issue(t);
+    f32x16 s, dp;
+    if (n_steps > 0) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((RING - 2) * NCOPY));
+        ring_barrier();
+        qk(0, s, dp);
+    }
+    for (int t = 0; t < n_steps; ++t) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((RING - 3) * NCOPY));  // this wave's copies of stage t+1
+        ring_barrier();                                              // and every other wave's
+        issue(t + RING - 1);
+        const int i0 = 32 * (qt0 + t % per_head);
+        const bool full = (!CAUSAL || i0 + diag >= jw0 + 31) && jw0 + 31 < Sk && i0 + 31 < Sq;
+        step(t, full, s, dp);
     }
     // no copy may land in LDS after the workgroup has ended
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -396,11 +414,10 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
     }
     const bool in = my_q < Sq;
     float Di = in ? a.dsum[2 * (qrow0 + my_q)] : 0.f;
-    float L2 = in ? a.dsum[2 * (qrow0 + my_q) + 1] : -INFINITY;
+    float L2 = in ? a.dsum[2 * (qrow0 + my_q) + 1] : 0.f;
     settle(qf);
     settle(df);
     asm volatile("" : "+v"(Di), "+v"(L2));
-    const bool row_live = L2 > -INFINITY;
 
     f32x16 dq[DB];
 #pragma unroll
@@ -467,20 +484,18 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
         }
         // lane: row my_q; register r: key j0 + 8(r/4) + 4g + r%4
         f32x16 ds;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -L2));
+        // hidden pairs get the score -inf, so that their probability is 0
         if (!full) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
-                const bool vis = row_live && j < Sk && (!CAUSAL || j <= my_q + diag);
-                ds[r] = vis ? ds[r] : 0.f;
+                const bool vis = in && j < Sk && (!CAUSAL || j <= my_q + diag);
+                s[r] = vis ? s[r] : -INFINITY;
             }
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            ds[r] = ds[r] * (dp[r] - Di);
+            ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -L2)) * (dp[r] - Di);
         const uint32_t trk = sb + 2 * TILE_B + 8 * lane;
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
@@ -825,8 +840,13 @@ __global__ void __launch_bounds__(64) bwd_dsum_kernel(BwdArgs a, int n_qtiles)
     if (i < Sq) {
         if (g == 0)
             a.dsum[2 * (qrow0 + i)] = dot;
-        else
-            a.dsum[2 * (qrow0 + i) + 1] = a.lse[qrow0 + i] * kLog2e;
+        else {
+            // a row that sees no key (LSE = -inf) gets the lowest finite value:
+            // every score of such a row is masked to -inf, and exp2 of
+            // -inf * c + FLT_MAX is exactly 0
+            const float L = a.lse[qrow0 + i] * kLog2e;
+            a.dsum[2 * (qrow0 + i) + 1] = L == -INFINITY ? -FLT_MAX : L;
+        }
     }
 }
 

@@ -533,7 +533,7 @@ __device__ __forceinline__ void to_agpr(bf16x8 &x) { asm volatile("" : "+a"(x));
 
 // dK, dV: one workgroup of two waves per (b, kv-head, 32-key tile)
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(128) bwd_dkdv2_kernel(BwdArgs a, int n_ktiles)
+__global__ void __launch_bounds__(128) bwd_dkdv2_kernel(BwdArgs a, int n_ktiles, int gx)
 {
     constexpr int KK = D / 16, DBH = D / 64;  // 16-dim steps; 32-dim blocks per half
     __shared__ __attribute__((aligned(16))) uint16_t sQT[D * 32];
@@ -546,13 +546,11 @@ __global__ void __launch_bounds__(128) bwd_dkdv2_kernel(BwdArgs a, int n_ktiles)
 
     const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: S, 1: dP
-    int id = blockIdx.x;
-    const int kt = id % n_ktiles;
-    id /= n_ktiles;
-    const int kvh = id % a.Hkv;
-    const int b = id / a.Hkv;
+    // XCD-grouped order: the tiles of a kv-head run on one XCD, heaviest first
+    const TileOrder to = tile_order_grouped(blockIdx.x, a.B * a.Hkv, 1, n_ktiles, false, gx);
+    const int kvh = to.unit % a.Hkv, b = to.unit / a.Hkv;
     const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq, G = a.Hq / a.Hkv;
-    const int j0 = 32 * kt;
+    const int j0 = 32 * to.qtile;
     const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
     const float c = a.scale * kLog2e;
 
@@ -696,7 +694,7 @@ __global__ void __launch_bounds__(128) bwd_dkdv2_kernel(BwdArgs a, int n_ktiles)
 // lane and 16 keys in the registers; dS packed by registers is the A operand
 // of dQ += dS K, and each wave accumulates one half of the dimensions.
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(128) bwd_dq2_kernel(BwdArgs a, int n_qtiles)
+__global__ void __launch_bounds__(128) bwd_dq2_kernel(BwdArgs a, int n_qtiles, int gx)
 {
     constexpr int KK = D / 16, DBH = D / 64;
     __shared__ __attribute__((aligned(16))) uint16_t sKT[D * 32];
@@ -705,14 +703,13 @@ __global__ void __launch_bounds__(128) bwd_dq2_kernel(BwdArgs a, int n_qtiles)
 
     const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: S, 1: dP
-    int id = blockIdx.x;
-    const int qt = id % n_qtiles;
-    id /= n_qtiles;
-    const int hq = id % a.Hq;
-    const int b = id / a.Hq;
-    const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq, G = a.Hq / a.Hkv;
-    const int kvh = hq / G;
-    const int i0 = 32 * qt, my_q = i0 + l32;
+    // XCD-grouped order: the row tiles of a kv-head's query heads run on one
+    // XCD, heaviest first
+    const int G = a.Hq / a.Hkv;
+    const TileOrder to = tile_order_grouped(blockIdx.x, a.B * a.Hkv, G, n_qtiles, CAUSAL, gx);
+    const int kvh = to.unit % a.Hkv, b = to.unit / a.Hkv, hq = kvh * G + to.gq;
+    const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq;
+    const int i0 = 32 * to.qtile, my_q = i0 + l32;
     const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
     const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
     const float c = a.scale * kLog2e;
@@ -872,8 +869,9 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
     }
     if (g1 > 0) {
         if constexpr (TWO) {
-            hipLaunchKernelGGL((bwd_dkdv2_kernel<D, CAUSAL>), dim3((unsigned)g1), dim3(128), 0,
-                               stream, a, n_ktiles);
+            constexpr auto kernel = bwd_dkdv2_kernel<D, CAUSAL>;
+            const int gx = max(1, resident_workgroups<kernel>(128) / 8);
+            hipLaunchKernelGGL(kernel, dim3((unsigned)g1), dim3(128), 0, stream, a, n_ktiles, gx);
         } else {
             constexpr auto kernel = bwd_dkdv_ring_kernel<D, CAUSAL>;
             const int gx = max(1, resident_workgroups<kernel>(256) / 8);
@@ -885,8 +883,9 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
     }
     if (g2 > 0) {
         if constexpr (TWO) {
-            hipLaunchKernelGGL((bwd_dq2_kernel<D, CAUSAL>), dim3((unsigned)g2), dim3(128), 0, stream,
-                               a, n_qtiles);
+            constexpr auto kernel = bwd_dq2_kernel<D, CAUSAL>;
+            const int gx = max(1, resident_workgroups<kernel>(128) / 8);
+            hipLaunchKernelGGL(kernel, dim3((unsigned)g2), dim3(128), 0, stream, a, n_qtiles, gx);
         } else {
             constexpr auto kernel = bwd_dq_ring_kernel<D, CAUSAL, NWQ>;
             const int gx = max(1, resident_workgroups<kernel>(64 * NWQ) / 8);

@@ -173,6 +173,25 @@ MIATTN_API int attn_fwd_varlen(const void *q, const void *k, const void *v, void
                     float scale, hipStream_t stream);
 
 /*
+ * A packed variable-length batch with the score and mask variants:
+ * attn_fwd_varlen with window_left, softcap and alibi_slopes as in
+ * attn_fwd_ext, each sequence taking them against its own lengths (its
+ * Sq, Sk: key j of the sequence is visible to its query i only if
+ * j >= i + Sk - Sq - window_left, and the ALiBi distance is
+ * |i + Sk - Sq - j|). Every sequence is an attention of its own, and a
+ * change of the score or the mask leaves the monoid alone (the tang paper,
+ * §2.3 "Rewrites"), so the kernel is the packed batch's with the variant's
+ * score and mask. softcap must be finite and >= 0; every other argument,
+ * limit and error is attn_fwd_varlen's.
+ */
+MIATTN_API int attn_fwd_varlen_ext(const void *q, const void *k, const void *v, void *o,
+                    float *lse, const int *cu_seqlens_q, const int *cu_seqlens_k,
+                    int B, int total_q, int total_k, int max_seqlen_q,
+                    int max_seqlen_k, int Hq, int Hkv, int d, int causal,
+                    int window_left, float softcap, const float *alibi_slopes,
+                    float scale, hipStream_t stream);
+
+/*
  * Prefill backward: the gradients of attn_fwd's O with respect to Q, K and V,
  * given the forward's O and LSE and the upstream gradient dout (the flash
  * backward: P is recomputed from LSE, and the softmax gradient uses

@@ -306,10 +306,11 @@ int attn_fwd_decode_paged(const void *q, const void *k_pages, const void *v_page
     return hip_status(miattn::launch_decode(a, d, stream), "attn_fwd_decode_paged launch");
 }
 
-int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
-                    const int *cu_seqlens_q, const int *cu_seqlens_k, int B, int total_q,
-                    int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int d,
-                    int causal, float scale, hipStream_t stream)
+static int varlen_impl(const void *q, const void *k, const void *v, void *o, float *lse,
+                       const int *cu_seqlens_q, const int *cu_seqlens_k, int B, int total_q,
+                       int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int d,
+                       int causal, int window, float softcap, const float *alibi, float scale,
+                       hipStream_t stream, const char *what)
 {
     if (B < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
         return fail(MIATTN_ERR_INVALID_ARG,
@@ -348,7 +349,37 @@ int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float 
     a.cu_k = cu_seqlens_k;
     a.total_q = total_q;
     a.total_k = total_k;
-    return hip_status(miattn::launch_fwd(a, d, causal != 0, stream), "attn_fwd_varlen launch");
+    a.window = window;
+    a.softcap = softcap;
+    a.alibi = alibi;
+    return hip_status(miattn::launch_fwd(a, d, causal != 0, stream), what);
+}
+
+int attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                    const int *cu_seqlens_q, const int *cu_seqlens_k, int B, int total_q,
+                    int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int d,
+                    int causal, float scale, hipStream_t stream)
+{
+    return varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, total_q, total_k,
+                       max_seqlen_q, max_seqlen_k, Hq, Hkv, d, causal, -1, 0.f, nullptr, scale,
+                       stream, "attn_fwd_varlen launch");
+}
+
+int attn_fwd_varlen_ext(const void *q, const void *k, const void *v, void *o, float *lse,
+                        const int *cu_seqlens_q, const int *cu_seqlens_k, int B, int total_q,
+                        int total_k, int max_seqlen_q, int max_seqlen_k, int Hq, int Hkv, int d,
+                        int causal, int window_left, float softcap, const float *alibi_slopes,
+                        float scale, hipStream_t stream)
+{
+    if (!(softcap >= 0.f) || !isfinite(softcap))
+        return fail(MIATTN_ERR_INVALID_ARG, "softcap must be finite and >= 0 (got %g)",
+                    (double)softcap);
+    if (alibi_slopes != nullptr && !aligned(alibi_slopes, 4))
+        return fail(MIATTN_ERR_INVALID_ARG, "alibi_slopes is not 4-byte aligned");
+    return varlen_impl(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, total_q, total_k,
+                       max_seqlen_q, max_seqlen_k, Hq, Hkv, d, causal,
+                       window_left < 0 ? -1 : window_left, softcap, alibi_slopes, scale, stream,
+                       "attn_fwd_varlen_ext launch");
 }
 
 size_t attn_bwd_workspace_size(int B, int Hq, int Sq)

@@ -1019,14 +1019,26 @@ hipError_t launch_q64_t(const FwdArgs &a, int n_qtiles, int n_items, hipStream_t
     return hipGetLastError();
 }
 
-template <int D, int NWV, int WPE, int MOD>
+template <int D, int NWV, int WPE, int MOD, bool VARLEN>
 hipError_t dispatch_win(const FwdArgs &a, bool causal, int n_qtiles, int n, hipStream_t stream)
 {
     if (a.window >= 0)
-        return causal ? launch_q64_t<true, D, NWV, WPE, true, MOD>(a, n_qtiles, n, stream)
-                      : launch_q64_t<false, D, NWV, WPE, true, MOD>(a, n_qtiles, n, stream);
-    return causal ? launch_q64_t<true, D, NWV, WPE, false, MOD>(a, n_qtiles, n, stream)
-                  : launch_q64_t<false, D, NWV, WPE, false, MOD>(a, n_qtiles, n, stream);
+        return causal ? launch_q64_t<true, D, NWV, WPE, true, MOD, VARLEN>(a, n_qtiles, n, stream)
+                      : launch_q64_t<false, D, NWV, WPE, true, MOD, VARLEN>(a, n_qtiles, n, stream);
+    return causal ? launch_q64_t<true, D, NWV, WPE, false, MOD, VARLEN>(a, n_qtiles, n, stream)
+                  : launch_q64_t<false, D, NWV, WPE, false, MOD, VARLEN>(a, n_qtiles, n, stream);
+}
+
+template <int D, int NWV, int WPE, bool VARLEN>
+hipError_t dispatch_mod(const FwdArgs &a, bool causal, int n_qtiles, int n, hipStream_t stream)
+{
+    if (a.softcap > 0.f && a.alibi != nullptr)
+        return dispatch_win<D, NWV, WPE, kModBoth, VARLEN>(a, causal, n_qtiles, n, stream);
+    if (a.softcap > 0.f)
+        return dispatch_win<D, NWV, WPE, kModSoftcap, VARLEN>(a, causal, n_qtiles, n, stream);
+    if (a.alibi != nullptr)
+        return dispatch_win<D, NWV, WPE, kModAlibi, VARLEN>(a, causal, n_qtiles, n, stream);
+    return dispatch_win<D, NWV, WPE, kModNone, VARLEN>(a, causal, n_qtiles, n, stream);
 }
 
 // NWV waves of 32 query rows per workgroup, WPE waves per SIMD
@@ -1042,19 +1054,9 @@ hipError_t launch_q64(const FwdArgs &a, bool causal, hipStream_t stream)
     if (n_items == 0)
         return hipSuccess;
     const int n = (int)n_items;
-    if (a.cu_q != nullptr) {  // packed variable-length batch: no window or modifier
-        if (a.window >= 0 || a.softcap > 0.f || a.alibi != nullptr)
-            return hipErrorNotSupported;
-        return causal ? launch_q64_t<true, D, NWV, WPE, false, kModNone, true>(a, n_qtiles, n, stream)
-                      : launch_q64_t<false, D, NWV, WPE, false, kModNone, true>(a, n_qtiles, n, stream);
-    }
-    if (a.softcap > 0.f && a.alibi != nullptr)
-        return dispatch_win<D, NWV, WPE, kModBoth>(a, causal, n_qtiles, n, stream);
-    if (a.softcap > 0.f)
-        return dispatch_win<D, NWV, WPE, kModSoftcap>(a, causal, n_qtiles, n, stream);
-    if (a.alibi != nullptr)
-        return dispatch_win<D, NWV, WPE, kModAlibi>(a, causal, n_qtiles, n, stream);
-    return dispatch_win<D, NWV, WPE, kModNone>(a, causal, n_qtiles, n, stream);
+    if (a.cu_q != nullptr)  // packed variable-length batch
+        return dispatch_mod<D, NWV, WPE, true>(a, causal, n_qtiles, n, stream);
+    return dispatch_mod<D, NWV, WPE, false>(a, causal, n_qtiles, n, stream);
 }
 
 }  // namespace

@@ -21,7 +21,8 @@ MIATTN_ERR_INVALID_ARG = 1
 MIATTN_ERR_UNSUPPORTED = 2
 MIATTN_ERR_HIP = 3
 
-EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_fwd_ext", "attn_fwd_varlen", "attn_bwd",
+EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_fwd_ext", "attn_fwd_varlen",
+           "attn_fwd_varlen_ext", "attn_bwd",
            "attn_bwd_workspace_size",
            "attn_fwd_decode_workspace_size",
            "attn_fwd_decode", "attn_fwd_decode_noalloc",
@@ -74,6 +75,9 @@ def load(path: str = LIB_PATH):
     L.attn_fwd_ext.restype = i
     L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, vp]
     L.attn_fwd_varlen.restype = i
+    L.attn_fwd_varlen_ext.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i,
+                                      i, f, vp, f, vp]
+    L.attn_fwd_varlen_ext.restype = i
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp,
                            ctypes.c_size_t, vp]
     L.attn_bwd.restype = i
@@ -148,6 +152,17 @@ def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, total_q, tot
                                   int(total_k), int(max_seqlen_q), int(max_seqlen_k), int(Hq),
                                   int(Hkv), int(d), int(bool(causal)), float(scale),
                                   _stream(stream)))
+
+
+def attn_fwd_varlen_ext(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, total_q, total_k,
+                        max_seqlen_q, max_seqlen_k, Hq, Hkv, d, causal, window_left, softcap,
+                        alibi_slopes, scale, stream=None):
+    _check(load().attn_fwd_varlen_ext(_addr(q), _addr(k), _addr(v), _addr(o), _addr(lse),
+                                      _addr(cu_seqlens_q), _addr(cu_seqlens_k), int(B),
+                                      int(total_q), int(total_k), int(max_seqlen_q),
+                                      int(max_seqlen_k), int(Hq), int(Hkv), int(d),
+                                      int(bool(causal)), int(window_left), float(softcap),
+                                      _addr(alibi_slopes), float(scale), _stream(stream)))
 
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, causal, scale,

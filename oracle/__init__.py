@@ -157,11 +157,12 @@ def attn_decode(q_bits, kc_bits, vc_bits, lens, scale: float, nthreads: int = 0)
 
 
 def attn_fwd_varlen(q_bits, k_bits, v_bits, cu_q, cu_k, causal: bool, scale: float,
-                    nthreads: int = 0):
+                    nthreads: int = 0, window: int = -1, softcap: float = 0.0, alibi=None):
     """A packed batch of sequences: q [Hq, total_q, d], k / v [Hkv, total_k, d];
     sequence b is rows cu_q[b] .. cu_q[b+1]-1 against keys cu_k[b] .. cu_k[b+1]-1,
-    each the plain attention of attn_fwd on its own. Returns o [Hq, total_q, d]
-    and lse [Hq, total_q] (f64)."""
+    each the attention of attn_fwd on its own (with the same window, soft cap
+    and ALiBi slopes, taken against the sequence's own lengths). Returns
+    o [Hq, total_q, d] and lse [Hq, total_q] (f64)."""
     q = _u16(q_bits)
     k = _u16(k_bits)
     v = _u16(v_bits)
@@ -174,7 +175,7 @@ def attn_fwd_varlen(q_bits, k_bits, v_bits, cu_q, cu_k, causal: bool, scale: flo
         if q1 == q0:
             continue
         ob, lb = attn_fwd(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1], causal,
-                          scale, nthreads=nthreads)
+                          scale, nthreads=nthreads, window=window, softcap=softcap, alibi=alibi)
         o[:, q0:q1] = ob[0]
         lse[:, q0:q1] = lb[0]
     return o, lse

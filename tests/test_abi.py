@@ -145,6 +145,28 @@ def test_attn_fwd_varlen_rejects():
     assert L.attn_fwd_varlen(*args(q=0, k=0, v=0, o=0, lse=0, cq=0, ck=0, B=0)) == M.MIATTN_OK
 
 
+def test_attn_fwd_varlen_ext_rejects():
+    """The packed batch with variants: attn_fwd_varlen's checks, plus the soft
+    cap and ALiBi slope checks of attn_fwd_ext."""
+    L = M.load()
+    args = lambda **kw: [kw.get(n, dv) for n, dv in (
+        ("q", FAKE), ("k", FAKE), ("v", FAKE), ("o", FAKE), ("lse", FAKE), ("cq", FAKE),
+        ("ck", FAKE), ("B", 2), ("tq", 100), ("tk", 120), ("mq", 60), ("mk", 70), ("Hq", 4),
+        ("Hkv", 2), ("d", 128), ("causal", 1), ("window", -1), ("softcap", 0.0),
+        ("alibi", 0), ("scale", 0.1), ("stream", 0))]
+    for kw, status, needle in [
+            (dict(softcap=-1.0), M.MIATTN_ERR_INVALID_ARG, "softcap"),
+            (dict(softcap=float("nan")), M.MIATTN_ERR_INVALID_ARG, "softcap"),
+            (dict(alibi=FAKE + 2), M.MIATTN_ERR_INVALID_ARG, "alibi_slopes"),
+            (dict(d=96), M.MIATTN_ERR_UNSUPPORTED, "head dimension"),
+            (dict(cq=0), M.MIATTN_ERR_INVALID_ARG, "cu_seqlens_q is NULL"),
+            (dict(tq=-1), M.MIATTN_ERR_INVALID_ARG, "sizes"),
+            (dict(Hq=3), M.MIATTN_ERR_INVALID_ARG, "multiple")]:
+        assert L.attn_fwd_varlen_ext(*args(**kw)) == status, kw
+        assert needle in M.miattn_last_error()
+    assert L.attn_fwd_varlen_ext(*args(q=0, k=0, v=0, o=0, lse=0, cq=0, ck=0, B=0)) == M.MIATTN_OK
+
+
 def test_attn_bwd_rejects():
     L = M.load()
     wsb = M.attn_bwd_workspace_size(1, 2, 8)

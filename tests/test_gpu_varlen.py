@@ -1,4 +1,5 @@
-"""GPU: packed variable-length batches (attn_fwd_varlen) against the f64 oracle.
+"""GPU: packed variable-length batches (attn_fwd_varlen, and attn_fwd_varlen_ext
+with windows, soft caps and ALiBi) against the f64 oracle.
 
 Sequences of 0 to 1000 query rows and as many or more keys (a chunk of new
 queries against its cached prefix), causal and not, head dimensions 64, 128
@@ -194,3 +195,89 @@ def test_varlen_bench_configuration_sampled():
                   np.concatenate(l_ref))
     _note(f"[gpu] varlen bench configuration: {m}")
     H.assert_parity(m, "varlen bench configuration")
+
+
+# ---- packed batches with the score and mask variants (attn_fwd_varlen_ext) ----------
+
+def _run_ext(q, k, v, cu_q, cu_k, max_q, max_k, causal, scale, window, softcap, alibi):
+    torch = H.torch_mod()
+    Hq, total_q, d = q.shape
+    Hkv, total_k, _ = k.shape
+    n = Hq * total_q
+    o, lse = H.nan_out(n * d, n)
+    cq = torch.tensor(cu_q, dtype=torch.int32, device="cuda")
+    ck = torch.tensor(cu_k, dtype=torch.int32, device="cuda")
+    ad = None if alibi is None else torch.from_numpy(np.ascontiguousarray(alibi, np.float32)).cuda()
+    H.miattn.attn_fwd_varlen_ext(H.dev_bits(q), H.dev_bits(k), H.dev_bits(v), o, lse, cq, ck,
+                                 len(cu_q) - 1, total_q, total_k, max_q, max_k, Hq, Hkv, d,
+                                 causal, window, softcap, ad, scale)
+    torch.cuda.synchronize()
+    ob = H.host_bits(o)
+    lh = lse.cpu().numpy()
+    guards = bool(np.all(ob[n * d:] == H.NAN_BF16) and np.all(np.isnan(lh[n:])))
+    return ob[:n * d].reshape(Hq, total_q, d), lh[:n].reshape(Hq, total_q), guards
+
+
+def _slopes(Hq):
+    return (2.0 ** (-8.0 * (np.arange(Hq) + 1) / Hq)).astype(np.float32)
+
+
+VARLEN_EXT = [
+    # seed, query lengths, extra cached keys, Hq, Hkv, d, causal, window, softcap, ALiBi
+    (11, [0, 1, 31, 33, 257, 700], [0, 0, 5, 100, 0, 64], 4, 2, 128, True, 64, 0.0, False),
+    (12, [5, 300, 129], [0, 200, 17], 4, 2, 128, False, 100, 0.0, False),
+    (13, [1, 33, 300, 0], [0, 9, 40, 3], 4, 2, 128, True, -1, 30.0, False),
+    (14, [1, 33, 300], [3, 0, 100], 4, 1, 64, True, -1, 0.0, True),
+    (15, [64, 190, 513], [1, 0, 300], 2, 2, 256, False, -1, 20.0, True),
+    (16, [31, 257, 700], [0, 64, 5], 6, 3, 64, True, 128, 50.0, True),
+    (17, [129, 0, 400], [20, 7, 0], 4, 2, 256, True, 32, 0.0, True),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_EXT)
+def test_varlen_ext_parity(case):
+    """Windows, soft caps and ALiBi on packed batches: each sequence takes the
+    variant against its own lengths; against the f64 oracle per sequence."""
+    seed, lq, extra, Hq, Hkv, d, causal, window, softcap, use_alibi = case
+    lk = [a + b for a, b in zip(lq, extra)]
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q = _bits(seed * 10, (Hq, int(cu_q[-1]), d))
+    k = _bits(seed * 10 + 1, (Hkv, int(cu_k[-1]), d))
+    v = _bits(seed * 10 + 2, (Hkv, int(cu_k[-1]), d))
+    al = _slopes(Hq) if use_alibi else None
+    scale = inputs.default_scale(d)
+    label = f"varlen ext {case}"
+    _note(f"[gpu] {label}: running the HIP path")
+    o, lse, guards = _run_ext(q, k, v, cu_q, cu_k, max(lq) + 40, max(lk) + 40, causal, scale,
+                              window, softcap, al)
+    assert guards, f"{label}: write outside the logical outputs"
+    o_ref, lse_ref = oracle.attn_fwd_varlen(q, k, v, cu_q, cu_k, causal, scale, window=window,
+                                            softcap=softcap, alibi=al)
+    m = H.metrics(o, lse, o_ref, lse_ref)
+    _note(f"[gpu] {label}: {m}")
+    H.assert_parity(m, label)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_varlen_ext_equal_lengths_match_attn_fwd_ext(d):
+    """A packed batch of equal lengths under every variant at once gives
+    attn_fwd_ext's outputs bit for bit."""
+    B, Hq, Hkv, S = 3, 4, 2, 300
+    q = _bits(50 + d, (B, Hq, S, d))
+    k = _bits(51 + d, (B, Hkv, S, d))
+    v = _bits(52 + d, (B, Hkv, S, d))
+    pack = lambda x: np.ascontiguousarray(x.transpose(1, 0, 2, 3).reshape(x.shape[1], -1, d))
+    cu = (np.arange(B + 1) * S).astype(np.int32)
+    scale = inputs.default_scale(d)
+    al = _slopes(Hq)
+    for causal, window, softcap in ((True, 77, 30.0), (False, 40, 0.0)):
+        _note(f"[gpu] varlen ext equal lengths d={d} causal={causal}: running the HIP path")
+        o0, l0, _ = H.run_fwd_ext(q, k, v, causal, scale, window=window, softcap=softcap,
+                                  alibi=al)
+        o1, l1, guards = _run_ext(pack(q), pack(k), pack(v), cu, cu, S, S, causal, scale, window,
+                                  softcap, al)
+        assert guards
+        assert np.array_equal(o1, o0.transpose(1, 0, 2, 3).reshape(Hq, B * S, d))
+        assert np.array_equal(l1.view(np.uint32),
+                              l0.transpose(1, 0, 2).reshape(Hq, B * S).view(np.uint32))

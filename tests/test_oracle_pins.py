@@ -180,6 +180,38 @@ def test_varlen_brute_force_tiny():
                     _close(lse[h, i], bl[0][h][n])
 
 
+def test_varlen_with_window_and_modifiers_brute_force_tiny():
+    """A packed batch under a window, a soft cap and ALiBi slopes: each
+    sequence against brute force on its own rows and keys, the window and the
+    ALiBi distance taken against that sequence's lengths."""
+    rng = np.random.Generator(np.random.PCG64(33))
+    Hq, Hkv, d = 2, 1, 3
+    cu_q = [0, 4, 4, 9, 11]
+    cu_k = [0, 6, 8, 11, 11]
+    q = _rand_bits(rng, (Hq, cu_q[-1], d))
+    k = _rand_bits(rng, (Hkv, cu_k[-1], d))
+    v = _rand_bits(rng, (Hkv, cu_k[-1], d))
+    al = np.array([0.5, 0.125], dtype=np.float32)
+    for causal, window, softcap, alibi in ((True, 2, 0.75, al), (False, 1, 0.0, al),
+                                           (True, -1, 3.0, None), (False, 3, 1.5, None)):
+        o, lse = oracle.attn_fwd_varlen(q, k, v, cu_q, cu_k, causal, 0.5, window=window,
+                                        softcap=softcap, alibi=alibi)
+        for b in range(4):
+            rows = range(cu_q[b], cu_q[b + 1])
+            keys = range(cu_k[b], cu_k[b + 1])
+            if not rows:
+                continue
+            qq = [[[[int(x) for x in q[h, i]] for i in rows] for h in range(Hq)]]
+            kk = [[[[int(x) for x in k[g, j]] for j in keys] for g in range(Hkv)]]
+            vv = [[[[int(x) for x in v[g, j]] for j in keys] for g in range(Hkv)]]
+            bo, bl = brute.attention(qq, kk, vv, causal, 0.5, window=window, softcap=softcap,
+                                     alibi=None if alibi is None else alibi.tolist())
+            for h in range(Hq):
+                for n, i in enumerate(rows):
+                    _close(o[h, i], bo[0][h][n])
+                    _close(lse[h, i], bl[0][h][n])
+
+
 # ------------------------------------------------------- score modifiers --
 MOD_CASES = [
     # B, Hq, Hkv, Sq, Sk, d, causal, window, softcap, alibi slopes (or None)

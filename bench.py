@@ -371,7 +371,9 @@ def rounds_stats(rounds_ms):
             "launches": len(allms)}
 
 
-def measure(fn, stream, torch, per_round, warmup=2):
+def measure(fn, stream, torch, per_round, warmup=10):
+    """Launches of one leg after `warmup` untimed ones (the clock settles over
+    the first few after a change of kernel), in ROUNDS rounds."""
     time_launches(fn, stream, torch, warmup)
     return rounds_stats([time_launches(fn, stream, torch, per_round) for _ in range(ROUNDS)])
 
@@ -693,7 +695,7 @@ def main():
     del bwd, pre
     torch.cuda.empty_cache()
     b256 = BackwardShape(torch, 7400, 2, 16, 4096, 256, True)
-    legs["backward_d256"] = rate_entry(measure(b256, stream, torch, 3), b256.flops, "TFLOP/s",
+    legs["backward_d256"] = rate_entry(measure(b256, stream, torch, 5), b256.flops, "TFLOP/s",
                                        PEAK_BF16_TFLOPS,
                                        {"flops": "2.5 x the forward's (S, dP, dV, dK, dQ)",
                                         "shape": {"B": 2, "H": 16, "S": 4096, "d": 256,

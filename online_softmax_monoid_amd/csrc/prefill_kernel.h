@@ -200,14 +200,26 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // in step j (8 KB per tile at head dimension 128, 16 KB at 256: 64 or
     // 128 KB of the 160 KB of LDS)
     constexpr int RING = 4;
-    constexpr int INFLIGHT = DPW + 2 * DPW * (RING - 3);  // copies newer than K tile j+3 at step j's end
+    // ROWPAIR (head dimension 256): copy i of a tile takes two whole 512-byte
+    // rows, keys i and i+16, into a 1 KB block; the blocks lie KPB (K) or VPB
+    // (V) bytes apart. Otherwise fragment-major (see the copies below). At 256
+    // the workgroup's 128 query rows need twice the copy bandwidth per MFMA of
+    // d = 128, and fragment-major copies (32 keys x 32 bytes each) kept the
+    // L1 busy with four times the cache lines.
+    constexpr bool ROWCOPY = D == 256;
+    constexpr int CPT = DPW;  // copy instructions per wave per tile, each of K and V
+    constexpr int INFLIGHT = CPT + 2 * CPT * (RING - 3);  // copies newer than K tile j+3 at step j's end
     static_assert((RING & (RING - 1)) == 0 && RING >= 4, "ring of 2^n >= 4 tiles");
     static_assert((NG == 1 || NG == 2 || NG == 4) && NWV * DPW == KKN && INFLIGHT < 64,
                   "tile step shape");
+    static_assert(!ROWCOPY || (D == 256 && BN == 32), "row pairs: 512-byte rows, 32-key tiles");
     constexpr int TILE_CH = BN * D / 8;  // 16-byte chunks per tile
+    constexpr int KPB = 1040, VPB = 1088;  // block strides of ROWPAIR (bytes)
+    constexpr uint32_t KTILE_B = ROWCOPY ? 16 * KPB : TILE_CH * 16;
+    constexpr uint32_t VTILE_B = ROWCOPY ? 16 * VPB : TILE_CH * 16;
 
-    __shared__ __attribute__((aligned(16))) uint4 sK_[RING * TILE_CH];  // K ring
-    __shared__ __attribute__((aligned(16))) uint4 sV_[RING * TILE_CH];  // V ring
+    __shared__ __attribute__((aligned(16))) uint4 sK_[RING * KTILE_B / 16];  // K ring
+    __shared__ __attribute__((aligned(16))) uint4 sV_[RING * VTILE_B / 16];  // V ring
     uint4 *const sK = sK_;  // the lambdas below may not name __shared__ variables
     uint4 *const sV = sV_;
 
@@ -360,37 +372,49 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // L = 16G + 4jj + q, the four values V[16kc + 8hh + 4(G/2) + jj]
     // [32db + 16(G%2) + 4q .. +3]; a transposing 8-byte read of the block
     // gives lane L the values of dim 32db + L%32 at four consecutive keys.
-    uint32_t koff[DPW], voff[DPW];
+    //
+    // ROWPAIR layout: key r at byte (r % 16) * PB + (r / 16) * 512 of the tile
+    // (PB = KPB or VPB); wave w issues copies CPT w .. CPT w + CPT - 1, lane
+    // L of copy i taking 16 bytes of key i + 16 (L / 32). The strides keep both
+    // kinds of read free of bank conflicts: K fragments (lane l: key l%32)
+    // start 16 (mod 256) bytes apart, and the transposing V reads of a key
+    // quad 64 bytes apart.
+    uint32_t koff[CPT], voff[CPT];
 #pragma unroll
-    for (int h = 0; h < DPW; ++h) {
-        const int i = DPW * wave + h;
-        koff[h] = (uint32_t)(l32 * D + 16 * i + 8 * g) * 2;
-        const int db = i >> 1, kc = i & 1, tt = l32;
-        const int G4 = tt >> 3, jj = (tt >> 1) & 3, qh = tt & 1;
-        const int key = 16 * kc + 8 * g + 4 * (G4 >> 1) + jj;
-        const int dim = 32 * db + 16 * (G4 & 1) + 8 * qh;
-        voff[h] = (uint32_t)(key * D + dim) * 2;
+    for (int h = 0; h < CPT; ++h) {
+        if constexpr (ROWCOPY) {
+            koff[h] = voff[h] = (uint32_t)((CPT * wave + h) * 512 + 8192 * g + 16 * l32);
+        } else {
+            const int i = DPW * wave + h;
+            koff[h] = (uint32_t)(l32 * D + 16 * i + 8 * g) * 2;
+            const int db = i >> 1, kc = i & 1, tt = l32;
+            const int G4 = tt >> 3, jj = (tt >> 1) & 3, qh = tt & 1;
+            const int key = 16 * kc + 8 * g + 4 * (G4 >> 1) + jj;
+            const int dim = 32 * db + 16 * (G4 & 1) + 8 * qh;
+            voff[h] = (uint32_t)(key * D + dim) * 2;
+        }
     }
-    // LDS byte addresses (M0 values) of this wave's share of ring slot 0
-    constexpr uint32_t TILE_B = TILE_CH * 16;
-    const uint32_t m0k = lds_addr(sK) + 1024 * DPW * wave;
-    const uint32_t m0v = lds_addr(sV) + 1024 * DPW * wave;
+    // LDS byte addresses (M0 values) of this wave's share of ring slot 0, and
+    // the distance between its consecutive copies
+    const uint32_t m0k = lds_addr(sK) + (ROWCOPY ? KPB * CPT * wave : 1024 * DPW * wave);
+    const uint32_t m0v = lds_addr(sV) + (ROWCOPY ? VPB * CPT * wave : 1024 * DPW * wave);
+    constexpr uint32_t KSTEP = ROWCOPY ? KPB : 1024, VSTEP = ROWCOPY ? VPB : 1024;
     // copy of the BN keys from src on, of which `keys` exist (none if keys <=
     // 0), into ring slot s. The descriptor ends at the last key that exists:
     // keys past it read as zero, and a copy of no key moves no data.
     auto dma_k = [&](int s, const uint16_t *src, int keys) __attribute__((always_inline)) {
         const u32x4 d = make_desc(src, (uint32_t)max(keys, 0) * (D * 2));
-        const uint32_t m0 = m0k + (uint32_t)(s & (RING - 1)) * TILE_B;
+        const uint32_t m0 = m0k + (uint32_t)(s & (RING - 1)) * KTILE_B;
 #pragma unroll
-        for (int h = 0; h < DPW; ++h)
-            copy_to_lds(d, koff[h], m0 + 1024 * h);
+        for (int h = 0; h < CPT; ++h)
+            copy_to_lds(d, koff[h], m0 + KSTEP * h);
     };
     auto dma_v = [&](int s, const uint16_t *src, int keys) __attribute__((always_inline)) {
         const u32x4 d = make_desc(src, (uint32_t)max(keys, 0) * (D * 2));
-        const uint32_t m0 = m0v + (uint32_t)(s & (RING - 1)) * TILE_B;
+        const uint32_t m0 = m0v + (uint32_t)(s & (RING - 1)) * VTILE_B;
 #pragma unroll
-        for (int h = 0; h < DPW; ++h)
-            copy_to_lds(d, voff[h], m0 + 1024 * h);
+        for (int h = 0; h < CPT; ++h)
+            copy_to_lds(d, voff[h], m0 + VSTEP * h);
     };
     // ---- fragments from LDS -------------------------------------------------------
     Frag8 kf[KKN];      // A fragments of the K tile the next QK uses
@@ -398,24 +422,37 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // Reads take a lane's LDS byte address in the slot (K: slot + 16 lane, V:
     // slot + 8 lane), computed once per step ahead of everything else so that
     // the reads can start with the step's first MFMA.
+    // (ROWPAIR: K lane l reads key l%32 at dims 16kk + 8(l/32), 32 bytes per
+    // kk further; V lane 16m + 4e + c supplies key 16kc + 8hh + 4(m/2) + e at
+    // dims 32db + 16(m%2) + 4c .. +3 to the transposing read of its group)
     auto read_k = [&](uint32_t addr, int kk) __attribute__((always_inline)) {
         typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-        kf[kk].u = __builtin_bit_cast(uint4, *(lds_u32x4 *)(uintptr_t)(addr + 1024 * kk));
+        kf[kk].u = __builtin_bit_cast(uint4, *(lds_u32x4 *)(uintptr_t)(addr + (ROWCOPY ? 32 : 1024) * kk));
+    };
+    auto vimm = [](int db, int kc, int hh) {
+        return ROWCOPY ? (uint32_t)(8 * hh * VPB + 512 * kc + 64 * db)
+                       : (uint32_t)(((2 * db + kc) * 2 + hh) * 512);
     };
     auto read_v = [&](uint32_t addr, int db, int kc) __attribute__((always_inline)) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)(uintptr_t)(addr + ((2 * db + kc) * 2 + 0) * 512));
+            (lds_i16x4 *)(uintptr_t)(addr + vimm(db, kc, 0)));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4 *)(uintptr_t)(addr + ((2 * db + kc) * 2 + 1) * 512));
+            (lds_i16x4 *)(uintptr_t)(addr + vimm(db, kc, 1)));
         const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         vf[db][kc] = __builtin_bit_cast(bf16x8, both);
     };
     const uint32_t lds_k = lds_addr(sK), lds_v = lds_addr(sV);
+    const uint32_t klane =
+        ROWCOPY ? (uint32_t)((l32 & 15) * KPB + 512 * (l32 >> 4) + 16 * g) : (uint32_t)(16 * lane);
+    const uint32_t vlane =
+        ROWCOPY ? (uint32_t)((4 * (lane >> 5) + ((lane & 15) >> 2)) * VPB + 32 * ((lane >> 4) & 1) +
+                             16 * ((lane & 3) >> 1) + 8 * (lane & 1))
+                : (uint32_t)(8 * lane);
     auto kread_addr = [&](int s) __attribute__((always_inline)) {
-        return lds_k + (uint32_t)(s & (RING - 1)) * TILE_B + 16 * lane;
+        return lds_k + (uint32_t)(s & (RING - 1)) * KTILE_B + klane;
     };
     auto vread_addr = [&](int s) __attribute__((always_inline)) {
-        return lds_v + (uint32_t)(s & (RING - 1)) * TILE_B + 8 * lane;
+        return lds_v + (uint32_t)(s & (RING - 1)) * VTILE_B + vlane;
     };
 
     // ---- monoid state per query block -------------------------------------------

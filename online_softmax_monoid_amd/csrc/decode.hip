@@ -166,19 +166,23 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
     // K and V blocks go global -> LDS by buffer DMA, each instruction four
     // (head dim 128) whole key rows, so every read is a contiguous 1 KB. A
     // row's 16-byte chunk c sits at slot c ^ swz(row) of the row, which keeps
-    // the fragment reads below free of (K) or low in (V) bank conflicts.
+    // the fragment reads below free of bank conflicts.
     // Instruction i, lane l: row RPI i + l / CPR, slot (l % CPR) ^ swz(row).
     constexpr int CPR = D / 8;     // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;  // rows per DMA instruction
     constexpr int NI = BK / RPI;   // DMA instructions per block
-    // Row key of the swizzle. At head dimension 128 it is the row index
-    // (mod 16) rotated left by one bit: the 16 rows of a K read still get 16
-    // different keys, and the 32 lanes of a transposing V read (rows
-    // 4G + j, G in {0, 1} or {2, 3}, two chunks each) then reach 16 different
-    // slots instead of 8, which halves their bank conflicts.
+    // Row key of the swizzle. LDS serves a 16-byte read in four passes of 16
+    // lanes: lanes l % 16 < 8 of one lane row with lanes l % 16 >= 8 of
+    // another, the two rows differing in bit 0 (measured: the bank-conflict
+    // counter of every layout tried matches this grouping), and a
+    // transposing 8-byte read in two passes of 32 lanes. From head
+    // dimension 128 on, key 2 row (mod chunks per row) makes both reads
+    // conflict-free: a V read's 32 lanes (rows 4G + j, G in {0, 1} or {2, 3},
+    // two chunks each) reach 16 different slots, and in a K read the
+    // lanes of the two lane rows reach slots of opposite parity. At head
+    // dimension 64 (two rows per 256 bytes) the row index itself does that.
     auto swz = [](int row) __attribute__((always_inline)) {
-        const int m = row % CPR;
-        return D == 128 ? (((2 * m) & 15) | (m >> 3)) : m;
+        return D == 64 ? row % CPR : (2 * row) % CPR;
     };
     auto dma = [&](uint4 *buf, const uint16_t *base, int kb) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t r = block_rsrc(base, kb);

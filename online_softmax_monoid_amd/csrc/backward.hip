@@ -9,18 +9,19 @@
 //   dQ_i  = scale sum_j dS_ij k_j
 //
 // D_i is computed once per row into the caller's workspace by a first small
-// kernel. Then two kernels, no atomics: one wave per 32-key tile accumulates dK and dV over
-// the query heads of its kv-head and their query tiles; one wave per 32-row
-// query tile accumulates dQ over the key tiles. Every product is a
-// v_mfma_f32_32x32x16_bf16 with f32 accumulation. As in the forward, a score
-// accumulator holds, in lane l, one column (l % 32) and the 16 rows
-// 8(r/4) + 4(l/32) + r%4 of its registers r; its registers packed to bf16
-// are then directly the A operand of the next product over those rows, with
-// the other operand read in the same permuted row order. Only the operands
-// that need a transpose (Q and dO for dK/dV, K for dQ) pass through LDS, in
-// the forward's V layout and by transposing reads.
-// Fragments are read from global memory by buffer loads, so rows past the
-// ends read as zeros.
+// kernel. Then two kernels, no atomics: a workgroup per 128-key block
+// accumulates dK and dV over the query heads of its kv-head and their query
+// tiles; a workgroup per block of query rows accumulates dQ over the key
+// tiles. Every product is a v_mfma_f32_32x32x16_bf16 with f32 accumulation.
+// As in the forward, a score accumulator holds, in lane l, one column (l % 32)
+// and the 16 rows 8(r/4) + 4(l/32) + r%4 of its registers r; its registers
+// packed to bf16 are then directly the A operand of the next product over
+// those rows, with the other operand read in the same permuted row order.
+// The streamed operand tiles go through LDS, copied once per workgroup; the
+// ones that need a transpose (Q and dO for dK/dV, K for dQ) are also stored in
+// the forward's V layout and read by transposing reads. A wave's fixed rows
+// are read from global memory by buffer loads, so rows past the ends read as
+// zeros.
 
 #include <hip/hip_runtime.h>
 #include <float.h>
@@ -89,41 +90,7 @@ __device__ __forceinline__ bf16x8 pack_chunk(const f32x16 &x, int c)
     return f.v;
 }
 
-// A 32-row tile in LDS for transposing reads, the forward's V layout: 512-byte
-// blocks b = (2 db + c) 2 + hh, and in block b at byte 8L, for
-// L = 16 G + 4 jj + q, the four values of row 16c + 8hh + 4(G/2) + jj at dims
-// 32 db + 16 (G%2) + 4q .. +3. (D * 64 bytes per tile.)
-//
-// A lane holding row `row`, dims 16kk + 8g .. +7, writes them as two 8-byte
-// groups.
-__device__ __forceinline__ void write_blk(uint16_t *t, bf16x8 v, int row, int kk, int g)
-{
-    Frag8 f;
-    f.v = v;
-    const int c = row >> 4, hh = (row >> 3) & 1, G2 = (row >> 2) & 1, jj = row & 3;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-        const int dim = 16 * kk + 8 * g + 4 * h2;
-        const int db = dim >> 5, dp = dim & 31;
-        const int L = 16 * (2 * G2 + (dp >> 4)) + 4 * jj + ((dp & 15) >> 2);
-        *(uint2 *)((char *)t + ((2 * db + c) * 2 + hh) * 512 + 8 * L) =
-            make_uint2(f.w[2 * h2], f.w[2 * h2 + 1]);
-    }
-}
-
-// B operand over the permuted rows of pack_chunk: a transposing 8-byte read of
-// each block gives lane l dim 32 db + l%32 at rows 16c + 8hh + 4(l/32) .. +3
-__device__ __forceinline__ bf16x8 read_tr(const uint16_t *t, int db, int c, int lane)
-{
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const char *p = (const char *)t + ((2 * db + c) * 2) * 512 + 8 * lane;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const_cast<char *>(p)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const_cast<char *>(p + 512)));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// ---- head dimensions 64 and 128: workgroups of waves sharing a copy ring ---------
+// ---- workgroups of waves sharing a copy ring -------------------------------------
 // The operand tiles that every wave of a workgroup reads go global -> LDS by
 // buffer DMA (inline assembly, explicit waits) into a ring of RING stages, one
 // barrier per step: stage t is copied RING - 1 steps ahead, into the slot that
@@ -133,8 +100,11 @@ __device__ __forceinline__ bf16x8 read_tr(const uint16_t *t, int db, int c, int 
 // A tile read both ways is stored twice:
 //   fragment-major, block kk (1 KB): lane L's 16 bytes of row L%32, dims
 //     16kk + 8(L/32) .. +7 -- the operand of a product over the head dimension;
-//   transposing, the layout of read_tr above -- the operand of a product over
-//     the tile's rows.
+//   transposing, the forward's V layout -- the operand of a product over the
+//     tile's rows: 512-byte blocks b = (2 db + c) 2 + hh, and in block b at
+//     byte 8L, for L = 16 G + 4 jj + q, the four values of row
+//     16c + 8hh + 4(G/2) + jj at dims 32 db + 16 (G%2) + 4q .. +3 (64 bytes
+//     per dimension).
 // Copy instruction i of a tile moves 1 KB, 16 bytes per lane from the offsets
 // below (rows past the descriptor's end read as zero).
 __device__ __forceinline__ uint32_t off_frag(int D, int i, int l32, int g)
@@ -155,7 +125,9 @@ typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 // 16 bytes at LDS byte address addr
 __device__ __forceinline__ u32x4 lds16(uint32_t addr) { return *(lds_u32x4 *)(uintptr_t)addr; }
 
-// read_tr from LDS byte addresses: addr = the tile's first byte + 8 lane
+// B operand over the permuted rows of pack_chunk, from a transposing tile: a
+// transposing 8-byte read of each block gives lane l dim 32 db + l%32 at rows
+// 16c + 8hh + 4(l/32) .. +3. addr = the tile's first LDS byte + 8 lane.
 __device__ __forceinline__ bf16x8 lds_tr(uint32_t addr, int db, int c)
 {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -205,21 +177,30 @@ __device__ __forceinline__ void settle(bf16x8 (&f)[N])
 // lane and 16 query rows in the registers; P and dS packed by registers are the
 // A operands of dV += P^T dO and dK += dS^T Q over those rows, with dO and Q
 // read transposed.
+// At head dimension 256 the dK and dV accumulators of all dimensions do not fit
+// a wave's registers beside its K and V rows: a key block is then two
+// workgroups, each accumulating one half of the dimensions (both compute the
+// block's S and dP, which contract over all of them).
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, int gx)
 {
-    constexpr int KK = D / 16, DB = D / 32, NW = 4, CPT = KK / NW;  // copies per tile and wave
-    constexpr int RING = 4;
-    constexpr int TILE_B = D * 64;         // one 32-row tile in one layout
-    constexpr int STAGE_B = 4 * TILE_B;    // Q frag, Q tr, dO frag, dO tr
-    constexpr int NCOPY = 4 * CPT + 1;     // copies per stage and wave
+    constexpr int NH = D == 256 ? 2 : 1;  // dimension halves per key block
+    constexpr int DH = D / NH;            // dK / dV dimensions of a workgroup
+    constexpr int KK = D / 16, DB = DH / 32, NW = 4;
+    constexpr int CPF = KK / NW, CPT = DH / 16 / NW;  // fragment / transposing copies per tile and wave
+    constexpr int RING = D == 256 ? 3 : 4;            // 48 KB stages at 256
+    constexpr int TILE_F = D * 64;        // one 32-row tile, fragment-major
+    constexpr int TILE_T = DH * 64;       // its dims of the half, transposing
+    constexpr int STAGE_B = 2 * (TILE_F + TILE_T);  // Q frag, Q tr, dO frag, dO tr
+    constexpr int NCOPY = 2 * (CPF + CPT) + 1;      // copies per stage and wave
     __shared__ __attribute__((aligned(1024))) uint4 sRing[RING * STAGE_B / 16];
     __shared__ __attribute__((aligned(16))) float sStat[RING * NW * 64];
 
     const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const TileOrder to = tile_order_grouped(blockIdx.x, a.B * a.Hkv, 1, nkb, false, gx);
-    const int kvh = to.unit % a.Hkv, b = to.unit / a.Hkv;
+    // the two halves of a key block are neighbours in the order (same XCD)
+    const TileOrder to = tile_order_grouped(blockIdx.x, a.B * a.Hkv, NH, nkb, false, gx);
+    const int kvh = to.unit % a.Hkv, b = to.unit / a.Hkv, half = to.gq;
     const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq, G = a.Hq / a.Hkv;
     const int j0 = 128 * to.qtile, jw0 = j0 + 32 * wave, my_key = jw0 + l32;
     const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
@@ -248,12 +229,13 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     const int qt0 = i_first / 32, nqt = (Sq + 31) / 32;
     const int per_head = max(0, nqt - qt0), n_steps = G * per_head;
 
-    uint32_t foff[CPT], toff[CPT];
+    uint32_t foff[CPF], toff[CPT];
 #pragma unroll
-    for (int h = 0; h < CPT; ++h) {
-        foff[h] = off_frag(D, CPT * wave + h, l32, g);
-        toff[h] = off_tr(D, CPT * wave + h, l32, g);
-    }
+    for (int h = 0; h < CPF; ++h)
+        foff[h] = off_frag(D, CPF * wave + h, l32, g);
+#pragma unroll
+    for (int h = 0; h < CPT; ++h)
+        toff[h] = off_tr(D, CPT * wave + h, l32, g) + 2 * DH * half;
     const uint32_t ring0 = lds_addr(sRing), stat0 = lds_addr(sStat);
     // stage t's copies; past the walk's end they cover no bytes (the index
     // math is clamped and the lengths selected, so that no branch splits the
@@ -268,13 +250,17 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
         const uint32_t nw = live ? (uint32_t)(Sq - i0) * 8 : 0u;
         const u32x4 dq_ = make_desc(a.q + r0 * D, nq), dd = make_desc(a.dout + r0 * D, nq);
         const u32x4 dw = make_desc(a.dsum + 2 * r0, nw);
-        const uint32_t base = ring0 + (uint32_t)(t % RING) * STAGE_B + 1024 * CPT * wave;
+        const uint32_t base = ring0 + (uint32_t)(t % RING) * STAGE_B;
+        const uint32_t fb = base + 1024 * CPF * wave, tb = base + TILE_F + 1024 * CPT * wave;
+#pragma unroll
+        for (int h = 0; h < CPF; ++h) {
+            copy_to_lds(dq_, foff[h], fb + 1024 * h);
+            copy_to_lds(dd, foff[h], fb + TILE_F + TILE_T + 1024 * h);
+        }
 #pragma unroll
         for (int h = 0; h < CPT; ++h) {
-            copy_to_lds(dq_, foff[h], base + 1024 * h);
-            copy_to_lds(dq_, toff[h], base + TILE_B + 1024 * h);
-            copy_to_lds(dd, foff[h], base + 2 * TILE_B + 1024 * h);
-            copy_to_lds(dd, toff[h], base + 3 * TILE_B + 1024 * h);
+            copy_to_lds(dq_, toff[h], tb + 1024 * h);
+            copy_to_lds(dd, toff[h], tb + TILE_F + TILE_T + 1024 * h);
         }
         copy_to_lds_b32(dw, 4 * lane, stat0 + ((uint32_t)(t % RING) * NW + wave) * 256);
     };
@@ -287,7 +273,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             const bf16x8 qa = __builtin_bit_cast(bf16x8, lds16(sb + 1024 * kk));
-            const bf16x8 da = __builtin_bit_cast(bf16x8, lds16(sb + 2 * TILE_B + 1024 * kk));
+            const bf16x8 da = __builtin_bit_cast(bf16x8, lds16(sb + TILE_F + TILE_T + 1024 * kk));
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp, 0, 0, 0);
         }
@@ -334,8 +320,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
             const bf16x8 pa = ch ? pa1 : pa0, sa = ch ? sa1 : sa0;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, lds_tr(sb + 3 * TILE_B, db, ch), dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, lds_tr(sb + TILE_B, db, ch), dk[db], 0, 0, 0);
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, lds_tr(sb + 2 * TILE_F + TILE_T, db, ch), dv[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, lds_tr(sb + TILE_F, db, ch), dk[db], 0, 0, 0);
             }
         }
     };
@@ -361,15 +347,15 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     }
     // no copy may land in LDS after the workgroup has ended
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    // lane: dim 32 db + l32; register r: key jw0 + 8(r/4) + 4g + r%4
+    // lane: dim DH half + 32 db + l32; register r: key jw0 + 8(r/4) + 4g + r%4
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int j = jw0 + 8 * (r >> 2) + 4 * g + (r & 3);
             if (j < Sk) {
-                a.dk[(krow0 + j) * D + 32 * db + l32] = to_bf16(dk[db][r] * a.scale);
-                a.dv[(krow0 + j) * D + 32 * db + l32] = to_bf16(dv[db][r]);
+                a.dk[(krow0 + j) * D + DH * half + 32 * db + l32] = to_bf16(dk[db][r] * a.scale);
+                a.dv[(krow0 + j) * D + DH * half + 32 * db + l32] = to_bf16(dv[db][r]);
             }
         }
 }
@@ -387,7 +373,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
     constexpr int KK = D / 16, DB = D / 32;
     static_assert((3 * KK) % NW == 0, "copies must split evenly over the waves");
     constexpr int NCOPY = 3 * KK / NW;     // copies per stage and wave
-    constexpr int RING = 4;
+    constexpr int RING = D == 256 ? 3 : 4;  // 48 KB stages at 256
     constexpr int TILE_B = D * 64;
     constexpr int STAGE_B = 3 * TILE_B;    // K frag, V frag, K tr
     __shared__ __attribute__((aligned(1024))) uint4 sRing[RING * STAGE_B / 16];
@@ -415,8 +401,10 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
     const bool in = my_q < Sq;
     float Di = in ? a.dsum[2 * (qrow0 + my_q)] : 0.f;
     float L2 = in ? a.dsum[2 * (qrow0 + my_q) + 1] : 0.f;
-    settle(qf);
-    settle(df);
+    // at 256 (one wave per SIMD) the fixed operands go to AGPRs, the VGPRs to
+    // the accumulator
+    settle<D == 256>(qf);
+    settle<D == 256>(df);
     asm volatile("" : "+v"(Di), "+v"(L2));
 
     f32x16 dq[DB];
@@ -517,300 +505,6 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
         }
 }
 
-// ---- head dimension 256: two cooperating waves per tile ---------------------------
-// At d = 256 one wave cannot hold a tile's operands and both gradient
-// accumulators (dK and dV alone are 256 registers per lane). Two waves share
-// a tile instead: wave 0 computes S from Q and K, wave 1 dP from dO and V
-// (each contraction runs once), P goes to wave 1 through LDS, dS comes back,
-// and each wave accumulates the gradients of one half of the head dimensions
-// from the packed P and dS. The fixed B operands of the S / dP contractions
-// (K or V rows, Q or dO rows) are kept in AGPRs, which the MFMAs read
-// directly; the accumulators and the softmax work stay in VGPRs.
-
-// pin a fragment in AGPRs: the MFMA reads it there and it leaves the 256
-// VGPRs to the accumulators
-__device__ __forceinline__ void to_agpr(bf16x8 &x) { asm volatile("" : "+a"(x)); }
-
-// dK, dV: one workgroup of two waves per (b, kv-head, 32-key tile)
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(128) bwd_dkdv2_kernel(BwdArgs a, int n_ktiles, int gx)
-{
-    constexpr int KK = D / 16, DBH = D / 64;  // 16-dim steps; 32-dim blocks per half
-    __shared__ __attribute__((aligned(16))) uint16_t sQT[D * 32];
-    __shared__ __attribute__((aligned(16))) uint16_t sDT[D * 32];
-    __shared__ __attribute__((aligned(16))) float sP[16 * 64];      // P in the S layout
-    __shared__ __attribute__((aligned(16))) uint32_t sPk[2][4 * 64];  // packed P chunks
-    __shared__ __attribute__((aligned(16))) uint32_t sSk[2][4 * 64];  // packed dS chunks
-    __shared__ __attribute__((aligned(16))) float sL[32];   // LSE_i log2(e), row i0 + i
-    __shared__ __attribute__((aligned(16))) float sDv[32];  // D_i
-
-    const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: S, 1: dP
-    // XCD-grouped order: the tiles of a kv-head run on one XCD, heaviest first
-    const TileOrder to = tile_order_grouped(blockIdx.x, a.B * a.Hkv, 1, n_ktiles, false, gx);
-    const int kvh = to.unit % a.Hkv, b = to.unit / a.Hkv;
-    const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq, G = a.Hq / a.Hkv;
-    const int j0 = 32 * to.qtile;
-    const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
-    const float c = a.scale * kLog2e;
-
-    // wave 0: K rows (B operand of S = Q K^T); wave 1: V rows (of dP = dO V^T)
-    const __amdgpu_buffer_rsrc_t rkv =
-        make_rsrc((wave == 0 ? a.k : a.v) + krow0 * D, (uint32_t)Sk * D * 2);
-    bf16x8 bf[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        bf[kk] = frag<D>(rkv, j0 + l32, kk, g);
-        to_agpr(bf[kk]);
-    }
-    f32x16 dk[DBH], dv[DBH];  // this wave's half: dims 32 (DBH wave + db) + l32
-#pragma unroll
-    for (int db = 0; db < DBH; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            dk[db][r] = dv[db][r] = 0.f;
-
-    const int i_first = CAUSAL ? max(0, j0 - diag) : 0;
-    const int qt0 = i_first / 32, nqt = (Sq + 31) / 32;
-    const int per_head = max(0, nqt - qt0), n_steps = G * per_head;
-    const int my_key = j0 + l32;
-    for (int t = 0; t < n_steps; ++t) {
-        const int hq = kvh * G + t / per_head, i0 = 32 * (qt0 + t % per_head);
-        const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
-        // wave 0: Q rows (A operand of S); wave 1: dO rows (of dP)
-        const __amdgpu_buffer_rsrc_t rqd =
-            make_rsrc((wave == 0 ? a.q : a.dout) + qrow0 * D, (uint32_t)Sq * D * 2);
-        bf16x8 af[KK];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            af[kk] = frag<D>(rqd, i0 + l32, kk, g);
-        __syncthreads();  // both waves are done with the previous step's LDS
-        if (g == 0) {
-            const int i = i0 + l32;
-            if (wave == 0)
-                sL[l32] = i < Sq ? a.lse[qrow0 + i] * kLog2e : -INFINITY;
-            else
-                sDv[l32] = i < Sq ? a.dsum[2 * (qrow0 + i)] : 0.f;
-        }
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            write_blk(wave == 0 ? sQT : sDT, af[kk], l32, kk, g);
-            to_agpr(af[kk]);
-        }
-        // S (wave 0) or dP (wave 1): lane key my_key, register r row
-        // i0 + 8(r/4) + 4g + r%4
-        f32x16 x;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            x[r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], bf[kk], x, 0, 0, 0);
-        __syncthreads();  // the row statistics and transposed tiles are in LDS
-        if (wave == 0) {
-            f32x16 p;
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const float4 L4 = *(const float4 *)&sL[8 * r4 + 4 * g];
-                const float Lr[4] = {L4.x, L4.y, L4.z, L4.w};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = 4 * r4 + u;
-                    const int i = i0 + 8 * r4 + 4 * g + u;
-                    const bool vis = my_key < Sk && i < Sq && Lr[u] > -INFINITY &&
-                                     (!CAUSAL || my_key <= i + diag);
-                    p[r] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c, -Lr[u])) : 0.f;
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                sP[r * 64 + lane] = p[r];
-#pragma unroll
-            for (int ch = 0; ch < 2; ++ch) {
-                Frag8 f;
-                f.v = pack_chunk(p, ch);
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    sPk[ch][w * 64 + lane] = f.w[w];
-            }
-        }
-        __syncthreads();  // P is in LDS
-        if (wave == 1) {
-            f32x16 ds;
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const float4 D4 = *(const float4 *)&sDv[8 * r4 + 4 * g];
-                const float Dr[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = 4 * r4 + u;
-                    ds[r] = sP[r * 64 + lane] * (x[r] - Dr[u]);
-                }
-            }
-#pragma unroll
-            for (int ch = 0; ch < 2; ++ch) {
-                Frag8 f;
-                f.v = pack_chunk(ds, ch);
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    sSk[ch][w * 64 + lane] = f.w[w];
-            }
-        }
-        __syncthreads();  // dS is in LDS
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-            Frag8 pa, sa;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                pa.w[w] = sPk[ch][w * 64 + lane];
-                sa.w[w] = sSk[ch][w * 64 + lane];
-            }
-#pragma unroll
-            for (int db = 0; db < DBH; ++db) {
-                const int dbg = DBH * wave + db;
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa.v, read_tr(sDT, dbg, ch, lane),
-                                                                 dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa.v, read_tr(sQT, dbg, ch, lane),
-                                                                 dk[db], 0, 0, 0);
-            }
-        }
-    }
-    // lane: dim 32 (DBH wave + db) + l32; register r: key j0 + 8(r/4) + 4g + r%4
-#pragma unroll
-    for (int db = 0; db < DBH; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const int dim = 32 * (DBH * wave + db) + l32;
-            if (j < Sk) {
-                a.dk[(krow0 + j) * D + dim] = to_bf16(dk[db][r] * a.scale);
-                a.dv[(krow0 + j) * D + dim] = to_bf16(dv[db][r]);
-            }
-        }
-}
-
-// dQ: one workgroup of two waves per (b, query head, 32-row query tile).
-// S^T = K Q^T (wave 0) and dP^T = V dO^T (wave 1) put the query row in the
-// lane and 16 keys in the registers; dS packed by registers is the A operand
-// of dQ += dS K, and each wave accumulates one half of the dimensions.
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(128) bwd_dq2_kernel(BwdArgs a, int n_qtiles, int gx)
-{
-    constexpr int KK = D / 16, DBH = D / 64;
-    __shared__ __attribute__((aligned(16))) uint16_t sKT[D * 32];
-    __shared__ __attribute__((aligned(16))) float sP[16 * 64];
-    __shared__ __attribute__((aligned(16))) uint32_t sSk[2][4 * 64];
-
-    const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0: S, 1: dP
-    // XCD-grouped order: the row tiles of a kv-head's query heads run on one
-    // XCD, heaviest first
-    const int G = a.Hq / a.Hkv;
-    const TileOrder to = tile_order_grouped(blockIdx.x, a.B * a.Hkv, G, n_qtiles, CAUSAL, gx);
-    const int kvh = to.unit % a.Hkv, b = to.unit / a.Hkv, hq = kvh * G + to.gq;
-    const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq;
-    const int i0 = 32 * to.qtile, my_q = i0 + l32;
-    const int64_t qrow0 = ((int64_t)b * a.Hq + hq) * Sq;
-    const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
-    const float c = a.scale * kLog2e;
-
-    // wave 0: Q rows (B operand of S^T); wave 1: dO rows (of dP^T)
-    const __amdgpu_buffer_rsrc_t rqd =
-        make_rsrc((wave == 0 ? a.q : a.dout) + qrow0 * D, (uint32_t)Sq * D * 2);
-    bf16x8 bf[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        bf[kk] = frag<D>(rqd, my_q, kk, g);
-        to_agpr(bf[kk]);
-    }
-    const float Di = my_q < Sq ? a.dsum[2 * (qrow0 + my_q)] : 0.f;
-    const float L = my_q < Sq ? a.lse[qrow0 + my_q] : -INFINITY;
-    const bool row_live = L > -INFINITY;
-
-    f32x16 dq[DBH];
-#pragma unroll
-    for (int db = 0; db < DBH; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            dq[db][r] = 0.f;
-
-    const int kv_end = CAUSAL ? min(Sk, max(0, min(i0 + 31, Sq - 1) + diag + 1)) : Sk;
-    const int nkt = (kv_end + 31) / 32;
-    // wave 0: K rows (A operand of S^T); wave 1: V rows (of dP^T)
-    const __amdgpu_buffer_rsrc_t rkv =
-        make_rsrc((wave == 0 ? a.k : a.v) + krow0 * D, (uint32_t)Sk * D * 2);
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int j0 = 32 * kt;
-        bf16x8 af[KK];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            af[kk] = frag<D>(rkv, j0 + l32, kk, g);
-        __syncthreads();  // both waves are done with the previous tile's LDS
-        if (wave == 0) {
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                write_blk(sKT, af[kk], l32, kk, g);
-        }
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            to_agpr(af[kk]);
-        // S^T (wave 0) or dP^T (wave 1): lane row my_q, register r key
-        // j0 + 8(r/4) + 4g + r%4
-        f32x16 x;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            x[r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk], bf[kk], x, 0, 0, 0);
-        if (wave == 0) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
-                const bool vis = row_live && j < Sk && (!CAUSAL || j <= my_q + diag);
-                sP[r * 64 + lane] =
-                    vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[r], c, -L * kLog2e)) : 0.f;
-            }
-        }
-        __syncthreads();  // P and the transposed K tile are in LDS
-        if (wave == 1) {
-            f32x16 ds;
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                ds[r] = sP[r * 64 + lane] * (x[r] - Di);
-#pragma unroll
-            for (int ch = 0; ch < 2; ++ch) {
-                Frag8 f;
-                f.v = pack_chunk(ds, ch);
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    sSk[ch][w * 64 + lane] = f.w[w];
-            }
-        }
-        __syncthreads();  // dS is in LDS
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-            Frag8 sa;
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                sa.w[w] = sSk[ch][w * 64 + lane];
-#pragma unroll
-            for (int db = 0; db < DBH; ++db)
-                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    sa.v, read_tr(sKT, DBH * wave + db, ch, lane), dq[db], 0, 0, 0);
-        }
-    }
-    // lane: dim 32 (DBH wave + db) + l32; register r: row i0 + 8(r/4) + 4g + r%4
-#pragma unroll
-    for (int db = 0; db < DBH; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = i0 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (i < Sq)
-                a.dq[(qrow0 + i) * D + 32 * (DBH * wave + db) + l32] = to_bf16(dq[db][r] * a.scale);
-        }
-}
-
 // ---- per-row statistics, once (the workspace) ------------------------------------
 // Row i's pair (D_i = dO_i . O_i, LSE_i log2 e) as two floats. One wave per 32
 // rows of a (b, query head): lane l32 + 32 g takes dims 16kk + 8g .. +7 of row
@@ -850,15 +544,14 @@ __global__ void __launch_bounds__(64) bwd_dsum_kernel(BwdArgs a, int n_qtiles)
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
 {
-    // head dimensions 64 and 128: workgroups sharing a copy ring (dK/dV: 128
-    // keys of four waves; dQ: 32 NWQ rows); 256: two cooperating waves per tile
-    constexpr bool TWO = D == 256;
+    // workgroups sharing a copy ring: dK/dV per 128-key block (two, one per
+    // half of the dimensions, at 256), dQ per block of 32 NWQ rows
     constexpr int NWQ = D == 128 ? 8 : 4;
-    const int n_ktiles = (a.Sk + 31) / 32, n_qtiles = (a.Sq + 31) / 32;
+    const int n_qtiles = (a.Sq + 31) / 32;
     const int nkb = (a.Sk + 127) / 128, nrb = (a.Sq + 32 * NWQ - 1) / (32 * NWQ);
     const long long g0 = (long long)a.B * a.Hq * n_qtiles;
-    const long long g1 = (long long)a.B * a.Hkv * (TWO ? n_ktiles : nkb);
-    const long long g2 = (long long)a.B * a.Hq * (TWO ? n_qtiles : nrb);
+    const long long g1 = (long long)a.B * a.Hkv * nkb * (D == 256 ? 2 : 1);
+    const long long g2 = (long long)a.B * a.Hq * nrb;
     if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
     if (g0 > 0) {
@@ -868,29 +561,17 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
             return e;
     }
     if (g1 > 0) {
-        if constexpr (TWO) {
-            constexpr auto kernel = bwd_dkdv2_kernel<D, CAUSAL>;
-            const int gx = max(1, resident_workgroups<kernel>(128) / 8);
-            hipLaunchKernelGGL(kernel, dim3((unsigned)g1), dim3(128), 0, stream, a, n_ktiles, gx);
-        } else {
-            constexpr auto kernel = bwd_dkdv_ring_kernel<D, CAUSAL>;
-            const int gx = max(1, resident_workgroups<kernel>(256) / 8);
-            hipLaunchKernelGGL(kernel, dim3((unsigned)g1), dim3(256), 0, stream, a, nkb, gx);
-        }
+        constexpr auto kernel = bwd_dkdv_ring_kernel<D, CAUSAL>;
+        const int gx = max(1, resident_workgroups<kernel>(256) / 8);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)g1), dim3(256), 0, stream, a, nkb, gx);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
     if (g2 > 0) {
-        if constexpr (TWO) {
-            constexpr auto kernel = bwd_dq2_kernel<D, CAUSAL>;
-            const int gx = max(1, resident_workgroups<kernel>(128) / 8);
-            hipLaunchKernelGGL(kernel, dim3((unsigned)g2), dim3(128), 0, stream, a, n_qtiles, gx);
-        } else {
-            constexpr auto kernel = bwd_dq_ring_kernel<D, CAUSAL, NWQ>;
-            const int gx = max(1, resident_workgroups<kernel>(64 * NWQ) / 8);
-            hipLaunchKernelGGL(kernel, dim3((unsigned)g2), dim3(64 * NWQ), 0, stream, a, nrb, gx);
-        }
+        constexpr auto kernel = bwd_dq_ring_kernel<D, CAUSAL, NWQ>;
+        const int gx = max(1, resident_workgroups<kernel>(64 * NWQ) / 8);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)g2), dim3(64 * NWQ), 0, stream, a, nrb, gx);
     }
     return hipGetLastError();
 }

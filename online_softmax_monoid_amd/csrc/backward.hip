@@ -172,35 +172,37 @@ __device__ __forceinline__ void settle(bf16x8 (&f)[N])
 // Wave w holds keys j0 + 32w + l32 (K and V rows: the B operands of S = Q K^T
 // and dP = dO V^T, in registers). The workgroup walks the query tiles that see
 // any of its keys, over the kv-head's query heads, as one sequence of steps;
-// per step the ring holds the tile's Q and dO in both layouts and, per wave, its
-// rows' (D_i, LSE_i log2 e) pairs from the workspace. S and dP put the key in the
-// lane and 16 query rows in the registers; P and dS packed by registers are the
-// A operands of dV += P^T dO and dK += dS^T Q over those rows, with dO and Q
-// read transposed.
-// At head dimension 256 the dK and dV accumulators of all dimensions do not fit
-// a wave's registers beside its K and V rows: a key block is then two
-// workgroups, each accumulating one half of the dimensions (both compute the
-// block's S and dP, which contract over all of them).
-template <int D, bool CAUSAL>
+// per step the ring holds the tile's Q and dO in the layouts its products read
+// and, per wave, its rows' (D_i, LSE_i log2 e) pairs from the workspace. S and
+// dP put the key in the lane and 16 query rows in the registers; P and dS
+// packed by registers are the A operands of dV += P^T dO and dK += dS^T Q over
+// those rows, with dO and Q read transposed.
+// PART 0 makes both gradients. At head dimension 256 the dK and dV
+// accumulators of all dimensions do not fit a wave's registers beside its K and
+// V rows, so two launches share the work: PART 1 makes dV (S and P only: no V
+// rows, no dP, Q fragment-major and dO transposing), PART 2 makes dK (S, dP and
+// dS: Q both ways and dO fragment-major).
+template <int D, bool CAUSAL, int PART>
 __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, int gx)
 {
-    constexpr int NH = D == 256 ? 2 : 1;  // dimension halves per key block
-    constexpr int DH = D / NH;            // dK / dV dimensions of a workgroup
-    constexpr int KK = D / 16, DB = DH / 32, NW = 4;
-    constexpr int CPF = KK / NW, CPT = DH / 16 / NW;  // fragment / transposing copies per tile and wave
-    constexpr int RING = D == 256 ? 3 : 4;            // 48 KB stages at 256
-    constexpr int TILE_F = D * 64;        // one 32-row tile, fragment-major
-    constexpr int TILE_T = DH * 64;       // its dims of the half, transposing
-    constexpr int STAGE_B = 2 * (TILE_F + TILE_T);  // Q frag, Q tr, dO frag, dO tr
-    constexpr int NCOPY = 2 * (CPF + CPT) + 1;      // copies per stage and wave
+    constexpr bool DODV = PART != 2, DODK = PART != 1;  // DODK: dP, dS and V rows too
+    constexpr int KK = D / 16, DB = D / 32, NW = 4;
+    constexpr int CPF = KK / NW, CPT = KK / NW;  // fragment / transposing copies per tile and wave
+    constexpr int TILE_F = D * 64;               // one 32-row tile, fragment-major
+    constexpr int TILE_T = D * 64;               // transposing
+    constexpr int OFF_QT = TILE_F;               // stage: Q frag, [Q tr], [dO frag], [dO tr]
+    constexpr int OFF_OF = OFF_QT + (DODK ? TILE_T : 0);
+    constexpr int OFF_OT = OFF_OF + (DODK ? TILE_F : 0);
+    constexpr int STAGE_B = OFF_OT + (DODV ? TILE_T : 0);
+    constexpr int RING = STAGE_B > 32768 ? 3 : 4;  // 48 KB stages (dK at 256): 3
+    constexpr int NCOPY = CPF + (DODK ? CPT + CPF : 0) + (DODV ? CPT : 0) + 1;  // per stage and wave
     __shared__ __attribute__((aligned(1024))) uint4 sRing[RING * STAGE_B / 16];
     __shared__ __attribute__((aligned(16))) float sStat[RING * NW * 64];
 
     const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // the two halves of a key block are neighbours in the order (same XCD)
-    const TileOrder to = tile_order_grouped(blockIdx.x, a.B * a.Hkv, NH, nkb, false, gx);
-    const int kvh = to.unit % a.Hkv, b = to.unit / a.Hkv, half = to.gq;
+    const TileOrder to = tile_order_grouped(blockIdx.x, a.B * a.Hkv, 1, nkb, false, gx);
+    const int kvh = to.unit % a.Hkv, b = to.unit / a.Hkv;
     const int Sq = a.Sq, Sk = a.Sk, diag = Sk - Sq, G = a.Hq / a.Hkv;
     const int j0 = 128 * to.qtile, jw0 = j0 + 32 * wave, my_key = jw0 + l32;
     const int64_t krow0 = ((int64_t)b * a.Hkv + kvh) * Sk;
@@ -209,20 +211,26 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     // this wave's keys, loaded before the first copy is issued
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + krow0 * D, (uint32_t)Sk * D * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + krow0 * D, (uint32_t)Sk * D * 2);
-    bf16x8 kf[KK], vf[KK];  // key my_key, dims 16kk + 8g
+    bf16x8 kf[KK], vf[DODK ? KK : 1];  // key my_key, dims 16kk + 8g
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
         kf[kk] = frag<D>(rk, my_key, kk, g);
-        vf[kk] = frag<D>(rv, my_key, kk, g);
+        if constexpr (DODK)
+            vf[kk] = frag<D>(rv, my_key, kk, g);
     }
     settle<true>(kf);
-    settle<true>(vf);
-    f32x16 dk[DB], dv[DB];
+    if constexpr (DODK)
+        settle<true>(vf);
+    f32x16 dk[DODK ? DB : 1], dv[DODV ? DB : 1];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            dk[db][r] = dv[db][r] = 0.f;
+        for (int r = 0; r < 16; ++r) {
+            if constexpr (DODK)
+                dk[db][r] = 0.f;
+            if constexpr (DODV)
+                dv[db][r] = 0.f;
+        }
 
     // query tiles that see any key of the block: rows i >= j0 - diag
     const int i_first = CAUSAL ? max(0, j0 - diag) : 0;
@@ -235,7 +243,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
         foff[h] = off_frag(D, CPF * wave + h, l32, g);
 #pragma unroll
     for (int h = 0; h < CPT; ++h)
-        toff[h] = off_tr(D, CPT * wave + h, l32, g) + 2 * DH * half;
+        toff[h] = off_tr(D, CPT * wave + h, l32, g);
     const uint32_t ring0 = lds_addr(sRing), stat0 = lds_addr(sStat);
     // stage t's copies; past the walk's end they cover no bytes (the index
     // math is clamped and the lengths selected, so that no branch splits the
@@ -251,20 +259,23 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
         const u32x4 dq_ = make_desc(a.q + r0 * D, nq), dd = make_desc(a.dout + r0 * D, nq);
         const u32x4 dw = make_desc(a.dsum + 2 * r0, nw);
         const uint32_t base = ring0 + (uint32_t)(t % RING) * STAGE_B;
-        const uint32_t fb = base + 1024 * CPF * wave, tb = base + TILE_F + 1024 * CPT * wave;
+        const uint32_t fb = base + 1024 * CPF * wave, tb = base + 1024 * CPT * wave;
 #pragma unroll
         for (int h = 0; h < CPF; ++h) {
             copy_to_lds(dq_, foff[h], fb + 1024 * h);
-            copy_to_lds(dd, foff[h], fb + TILE_F + TILE_T + 1024 * h);
+            if constexpr (DODK)
+                copy_to_lds(dd, foff[h], fb + OFF_OF + 1024 * h);
         }
 #pragma unroll
         for (int h = 0; h < CPT; ++h) {
-            copy_to_lds(dq_, toff[h], tb + 1024 * h);
-            copy_to_lds(dd, toff[h], tb + TILE_F + TILE_T + 1024 * h);
+            if constexpr (DODK)
+                copy_to_lds(dq_, toff[h], tb + OFF_QT + 1024 * h);
+            if constexpr (DODV)
+                copy_to_lds(dd, toff[h], tb + OFF_OT + 1024 * h);
         }
         copy_to_lds_b32(dw, 4 * lane, stat0 + ((uint32_t)(t % RING) * NW + wave) * 256);
     };
-    // S and dP of stage t (16 query rows per lane, key my_key)
+    // S (and dP) of stage t (16 query rows per lane, key my_key)
     auto qk = [&](int t, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
         const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + 16 * lane;
 #pragma unroll
@@ -273,12 +284,14 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             const bf16x8 qa = __builtin_bit_cast(bf16x8, lds16(sb + 1024 * kk));
-            const bf16x8 da = __builtin_bit_cast(bf16x8, lds16(sb + TILE_F + TILE_T + 1024 * kk));
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp, 0, 0, 0);
+            if constexpr (DODK) {
+                const bf16x8 da = __builtin_bit_cast(bf16x8, lds16(sb + OFF_OF + 1024 * kk));
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp, 0, 0, 0);
+            }
         }
     };
-    // One step: the softmax gradient of step t (its S and dP in registers)
+    // One step: the softmax (gradient) of step t (its S and dP in registers)
     // alongside S and dP of step t+1, then dV and dK of step t. full: no
     // (row, key) pair of the step is hidden (not diagonal, not a ragged end).
     auto step = [&](int t, bool full, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
@@ -308,26 +321,38 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
             for (int u = 0; u < 4; ++u) {
                 const int r = 4 * r4 + u;
                 p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -Lr[u]));
-                ds[r] = p[r] * (dp[r] - Dr[u]);
+                if constexpr (DODK)
+                    ds[r] = p[r] * (dp[r] - Dr[u]);
             }
         }
-        const bf16x8 pa0 = pack_chunk(p, 0), pa1 = pack_chunk(p, 1);
-        const bf16x8 sa0 = pack_chunk(ds, 0), sa1 = pack_chunk(ds, 1);
+        bf16x8 pa0, pa1, sa0, sa1;
+        if constexpr (DODV) {
+            pa0 = pack_chunk(p, 0);
+            pa1 = pack_chunk(p, 1);
+        }
+        if constexpr (DODK) {
+            sa0 = pack_chunk(ds, 0);
+            sa1 = pack_chunk(ds, 1);
+        }
         qk(t + 1, s, dp);
         const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + 8 * lane;
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-            const bf16x8 pa = ch ? pa1 : pa0, sa = ch ? sa1 : sa0;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, lds_tr(sb + 2 * TILE_F + TILE_T, db, ch), dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, lds_tr(sb + TILE_F, db, ch), dk[db], 0, 0, 0);
+                if constexpr (DODV)
+                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch ? pa1 : pa0, lds_tr(sb + OFF_OT, db, ch),
+                                                                     dv[db], 0, 0, 0);
+                if constexpr (DODK)
+                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch ? sa1 : sa0, lds_tr(sb + OFF_QT, db, ch),
+                                                                     dk[db], 0, 0, 0);
             }
         }
     };
 
     // stage t is waited for at the top of step t - 1 (its S and dP are made
-    // there), copied at the top of step t - 3 into the slot of stage t - 4
+    // there), copied at the top of step t + 1 - RING into the slot of stage
+    // t - RING
 #pragma unroll
     for (int t = 0; t < RING - 1; ++t)
         issue(t);
@@ -347,15 +372,17 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     }
     // no copy may land in LDS after the workgroup has ended
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    // lane: dim DH half + 32 db + l32; register r: key jw0 + 8(r/4) + 4g + r%4
+    // lane: dim 32 db + l32; register r: key jw0 + 8(r/4) + 4g + r%4
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int j = jw0 + 8 * (r >> 2) + 4 * g + (r & 3);
             if (j < Sk) {
-                a.dk[(krow0 + j) * D + DH * half + 32 * db + l32] = to_bf16(dk[db][r] * a.scale);
-                a.dv[(krow0 + j) * D + DH * half + 32 * db + l32] = to_bf16(dv[db][r]);
+                if constexpr (DODK)
+                    a.dk[(krow0 + j) * D + 32 * db + l32] = to_bf16(dk[db][r] * a.scale);
+                if constexpr (DODV)
+                    a.dv[(krow0 + j) * D + 32 * db + l32] = to_bf16(dv[db][r]);
             }
         }
 }
@@ -541,16 +568,24 @@ __global__ void __launch_bounds__(64) bwd_dsum_kernel(BwdArgs a, int n_qtiles)
     }
 }
 
+template <auto Kernel>
+hipError_t launch_dkdv(const BwdArgs &a, long long grid, int nkb, hipStream_t stream)
+{
+    const int gx = max(1, resident_workgroups<Kernel>(256) / 8);
+    hipLaunchKernelGGL(Kernel, dim3((unsigned)grid), dim3(256), 0, stream, a, nkb, gx);
+    return hipGetLastError();
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
 {
-    // workgroups sharing a copy ring: dK/dV per 128-key block (two, one per
-    // half of the dimensions, at 256), dQ per block of 32 NWQ rows
+    // workgroups sharing a copy ring: dK/dV per 128-key block, dQ per block of
+    // 32 NWQ rows
     constexpr int NWQ = D == 128 ? 8 : 4;
     const int n_qtiles = (a.Sq + 31) / 32;
     const int nkb = (a.Sk + 127) / 128, nrb = (a.Sq + 32 * NWQ - 1) / (32 * NWQ);
     const long long g0 = (long long)a.B * a.Hq * n_qtiles;
-    const long long g1 = (long long)a.B * a.Hkv * nkb * (D == 256 ? 2 : 1);
+    const long long g1 = (long long)a.B * a.Hkv * nkb;
     const long long g2 = (long long)a.B * a.Hq * nrb;
     if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
@@ -561,10 +596,15 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
             return e;
     }
     if (g1 > 0) {
-        constexpr auto kernel = bwd_dkdv_ring_kernel<D, CAUSAL>;
-        const int gx = max(1, resident_workgroups<kernel>(256) / 8);
-        hipLaunchKernelGGL(kernel, dim3((unsigned)g1), dim3(256), 0, stream, a, nkb, gx);
-        const hipError_t e = hipGetLastError();
+        // dK and dV: one launch, or at 256 one for dK and one for dV
+        hipError_t e;
+        if constexpr (D == 256) {
+            e = launch_dkdv<bwd_dkdv_ring_kernel<D, CAUSAL, 2>>(a, g1, nkb, stream);
+            if (e == hipSuccess)
+                e = launch_dkdv<bwd_dkdv_ring_kernel<D, CAUSAL, 1>>(a, g1, nkb, stream);
+        } else {
+            e = launch_dkdv<bwd_dkdv_ring_kernel<D, CAUSAL, 0>>(a, g1, nkb, stream);
+        }
         if (e != hipSuccess)
             return e;
     }

@@ -138,6 +138,61 @@ __device__ __forceinline__ bf16x8 lds_tr(uint32_t addr, int db, int c)
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Row-major tiles (head dimension 256): a 32-row tile as its rows of
+// 2D bytes, the 16-byte chunk c of row r at chunk c ^ rm_swz(r) of the row.
+// One copy of the tile serves both reads, and a copy instruction reads whole
+// rows (1 KB = 1024 / 2D rows): 16 L1 accesses per KB where a fragment-shaped
+// copy takes 64, and 2.3 times the copy rate (measured). The key keeps both
+// reads free of bank conflicts under the way LDS serves them (measured with a
+// probe kernel and the bank-conflict counter): a 16-byte read goes in four
+// passes of 16 lanes (lanes l % 16 < 8 of one 16-lane row with lanes
+// l % 16 >= 8 of another, the two rows' indices differing in bit 0), a
+// transposing 8-byte read in two passes of 32 lanes. Every pass of every read
+// below (checked at head dimensions 128 and 256) then reaches 16 different
+// 16-byte bank groups (a transposing read: four rows 4m + jj, whose keys differ in bits
+// 2-3, times four consecutive chunks).
+__device__ __forceinline__ int rm_swz(int r) { return 4 * (r & 3) | ((r >> 2) & 1) | 2 * ((r >> 4) & 1); }
+
+// copy instruction i of a row-major tile: the offset of lane l's 16 bytes in
+// the tile's rows in global memory (row 1024 i / 2D + l / (D/8)); the copy puts
+// them at byte 1024 i + 16 l of the LDS tile, slot l % (D/8) of that row
+__device__ __forceinline__ uint32_t off_rm(int D, int i, int lane)
+{
+    const int cpr = D / 8, row = (64 / cpr) * i + lane / cpr, c = lane % cpr;
+    return (uint32_t)(row * 2 * D + 16 * (c ^ rm_swz(row)));
+}
+
+// a lane's fragment-read offsets in a row-major tile: row l % 32, chunk
+// 2 k8 + l / 32 (k8 < 8; 16-dim step kk = k8 + 8 h adds 256 h bytes)
+__device__ __forceinline__ uint32_t rm_frag_off(int D, int k8, int lane)
+{
+    const int r = lane & 31, g = lane >> 5;
+    return (uint32_t)(r * 2 * D + 16 * ((2 * k8 + g) ^ rm_swz(r)));
+}
+
+// a lane's transposing-read offsets in a row-major tile, for 16-row chunk ch and
+// 32-dim block db % 4 (db / 4 adds 256 bytes): lane L = 16 G + 4 jj + q reads
+// dims 32 db + 16 (G % 2) + 4 q .. +3 of row 16 ch + 4 (G / 2) + jj, which is
+// chunk 4 db + 2 (G % 2) + q / 2 of the row; the rows + 8 (hh = 1) are 16 D
+// bytes further
+__device__ __forceinline__ uint32_t rm_tr_off(int D, int ch, int db4, int lane)
+{
+    const int G = lane >> 4, jj = (lane >> 2) & 3, q = lane & 3;
+    const int R = 16 * ch + 4 * (G >> 1) + jj;
+    return (uint32_t)(R * 2 * D + 64 * (db4 ^ jj) + 16 * ((2 * (G & 1) + (q >> 1)) ^ ((G >> 1) + 2 * ch)) +
+                      8 * (q & 1));
+}
+
+// the B operand of lds_tr from a row-major tile; p = tile + the lane's offset
+__device__ __forceinline__ bf16x8 lds_tr_rm(uint32_t p, int D)
+{
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(p + 16 * D));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Workgroup barrier that no memory access of the source crosses: the copies
 // into LDS are invisible to the compiler, so it must not move an LDS read
 // above the barrier that publishes the copied data.
@@ -186,16 +241,21 @@ template <int D, bool CAUSAL, int PART>
 __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, int gx)
 {
     constexpr bool DODV = PART != 2, DODK = PART != 1;  // DODK: dP, dS and V rows too
+    // row-major tiles at 256; at 64 and 128 fragment-major and transposing
+    // copies (at 128 the row-major reads' per-lane addresses cost more issue
+    // time than the cheaper copies save: 1.226 against 1.177 ms)
+    constexpr bool RM = D == 256;
     constexpr int KK = D / 16, DB = D / 32, NW = 4;
-    constexpr int CPF = KK / NW, CPT = KK / NW;  // fragment / transposing copies per tile and wave
-    constexpr int TILE_F = D * 64;               // one 32-row tile, fragment-major
-    constexpr int TILE_T = D * 64;               // transposing
-    constexpr int OFF_QT = TILE_F;               // stage: Q frag, [Q tr], [dO frag], [dO tr]
-    constexpr int OFF_OF = OFF_QT + (DODK ? TILE_T : 0);
-    constexpr int OFF_OT = OFF_OF + (DODK ? TILE_F : 0);
-    constexpr int STAGE_B = OFF_OT + (DODV ? TILE_T : 0);
-    constexpr int RING = STAGE_B > 32768 ? 3 : 4;  // 48 KB stages (dK at 256): 3
-    constexpr int NCOPY = CPF + (DODK ? CPT + CPF : 0) + (DODV ? CPT : 0) + 1;  // per stage and wave
+    constexpr int CPF = KK / NW, CPT = KK / NW;  // copies per tile and wave
+    constexpr int TILE_F = D * 64;               // one 32-row tile
+    constexpr int TILE_T = D * 64;
+    // stage: Q, dO (row-major), or Q frag, [Q tr], [dO frag], [dO tr]
+    constexpr int OFF_QT = RM ? 0 : TILE_F;
+    constexpr int OFF_OF = RM ? TILE_F : OFF_QT + (DODK ? TILE_T : 0);
+    constexpr int OFF_OT = RM ? TILE_F : OFF_OF + (DODK ? TILE_F : 0);
+    constexpr int STAGE_B = RM ? 2 * TILE_F : OFF_OT + (DODV ? TILE_T : 0);
+    constexpr int RING = STAGE_B > 32768 ? 3 : 4;
+    constexpr int NCOPY = (RM ? 2 * CPF : CPF + (DODK ? CPT + CPF : 0) + (DODV ? CPT : 0)) + 1;  // per stage and wave
     __shared__ __attribute__((aligned(1024))) uint4 sRing[RING * STAGE_B / 16];
     __shared__ __attribute__((aligned(16))) float sStat[RING * NW * 64];
 
@@ -240,10 +300,18 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     uint32_t foff[CPF], toff[CPT];
 #pragma unroll
     for (int h = 0; h < CPF; ++h)
-        foff[h] = off_frag(D, CPF * wave + h, l32, g);
+        foff[h] = RM ? off_rm(D, CPF * wave + h, lane) : off_frag(D, CPF * wave + h, l32, g);
 #pragma unroll
     for (int h = 0; h < CPT; ++h)
-        toff[h] = off_tr(D, CPT * wave + h, l32, g);
+        toff[h] = RM ? 0u : off_tr(D, CPT * wave + h, l32, g);
+    // row-major read offsets: fragments by 16-dim step % 8, transposing reads by
+    // (16-row chunk, 32-dim block % 4)
+    uint32_t fro[8], tro[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        fro[i] = RM ? rm_frag_off(D, i, lane) : 0u;
+        tro[i] = RM ? rm_tr_off(D, i >> 2, i & 3, lane) : 0u;
+    }
     const uint32_t ring0 = lds_addr(sRing), stat0 = lds_addr(sStat);
     // stage t's copies; past the walk's end they cover no bytes (the index
     // math is clamped and the lengths selected, so that no branch splits the
@@ -263,32 +331,36 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
 #pragma unroll
         for (int h = 0; h < CPF; ++h) {
             copy_to_lds(dq_, foff[h], fb + 1024 * h);
-            if constexpr (DODK)
+            if constexpr (DODK || RM)
                 copy_to_lds(dd, foff[h], fb + OFF_OF + 1024 * h);
         }
+        if constexpr (!RM) {
 #pragma unroll
-        for (int h = 0; h < CPT; ++h) {
-            if constexpr (DODK)
-                copy_to_lds(dq_, toff[h], tb + OFF_QT + 1024 * h);
-            if constexpr (DODV)
-                copy_to_lds(dd, toff[h], tb + OFF_OT + 1024 * h);
+            for (int h = 0; h < CPT; ++h) {
+                if constexpr (DODK)
+                    copy_to_lds(dq_, toff[h], tb + OFF_QT + 1024 * h);
+                if constexpr (DODV)
+                    copy_to_lds(dd, toff[h], tb + OFF_OT + 1024 * h);
+            }
         }
         copy_to_lds_b32(dw, 4 * lane, stat0 + ((uint32_t)(t % RING) * NW + wave) * 256);
     };
     // S (and dP) of stage t (16 query rows per lane, key my_key)
     auto qk = [&](int t, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
-        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + 16 * lane;
+        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + (RM ? 0 : 16 * lane);
+        // fragment kk of the tile at byte o
+        auto fr = [&](uint32_t o, int kk) __attribute__((always_inline)) {
+            return __builtin_bit_cast(bf16x8, RM ? lds16(sb + o + fro[kk & 7] + 256 * (kk >> 3))
+                                                 : lds16(sb + o + 1024 * kk));
+        };
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             s[r] = dp[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            const bf16x8 qa = __builtin_bit_cast(bf16x8, lds16(sb + 1024 * kk));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], s, 0, 0, 0);
-            if constexpr (DODK) {
-                const bf16x8 da = __builtin_bit_cast(bf16x8, lds16(sb + OFF_OF + 1024 * kk));
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp, 0, 0, 0);
-            }
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr(0, kk), kf[kk], s, 0, 0, 0);
+            if constexpr (DODK)
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr(OFF_OF, kk), vf[kk], dp, 0, 0, 0);
         }
     };
     // One step: the softmax (gradient) of step t (its S and dP in registers)
@@ -335,17 +407,21 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
             sa1 = pack_chunk(ds, 1);
         }
         qk(t + 1, s, dp);
-        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + 8 * lane;
+        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + (RM ? 0 : 8 * lane);
+        // block (ch, db) of the transposing operand in the tile at byte o
+        auto tr = [&](uint32_t o, int db, int ch) __attribute__((always_inline)) {
+            return RM ? lds_tr_rm(sb + o + tro[4 * ch + (db & 3)] + 256 * (db >> 2), D) : lds_tr(sb + o, db, ch);
+        };
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 if constexpr (DODV)
-                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch ? pa1 : pa0, lds_tr(sb + OFF_OT, db, ch),
-                                                                     dv[db], 0, 0, 0);
+                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch ? pa1 : pa0, tr(OFF_OT, db, ch), dv[db],
+                                                                     0, 0, 0);
                 if constexpr (DODK)
-                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch ? sa1 : sa0, lds_tr(sb + OFF_QT, db, ch),
-                                                                     dk[db], 0, 0, 0);
+                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch ? sa1 : sa0, tr(OFF_QT, db, ch), dk[db],
+                                                                     0, 0, 0);
             }
         }
     };
@@ -391,18 +467,21 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
 // Wave w holds rows ib0 + 32w + l32 (Q and dO rows: the B operands of
 // S^T = K Q^T and dP^T = V dO^T, in registers, with the rows' D_i and
 // LSE_i log2 e). The workgroup walks the key tiles that any of its rows sees;
-// per step the ring holds the tile's K and V fragment-major and K transposing.
+// per step the ring holds the tile's K and V fragment-major and K transposing
+// (at head dimension 256: K and V row-major).
 // S^T and dP^T put the query row in the lane and 16 keys in the registers; dS
 // packed by registers is the A operand of dQ += dS K over those keys.
 template <int D, bool CAUSAL, int NW>
 __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb, int gx)
 {
     constexpr int KK = D / 16, DB = D / 32;
-    static_assert((3 * KK) % NW == 0, "copies must split evenly over the waves");
-    constexpr int NCOPY = 3 * KK / NW;     // copies per stage and wave
-    constexpr int RING = D == 256 ? 3 : 4;  // 48 KB stages at 256
+    constexpr bool RM = D == 256;          // row-major tiles (K read both ways)
+    constexpr int NT = RM ? 2 : 3;         // tiles per stage: K, V or K frag, V frag, K tr
+    static_assert((NT * KK) % NW == 0, "copies must split evenly over the waves");
+    constexpr int NCOPY = NT * KK / NW;    // copies per stage and wave
     constexpr int TILE_B = D * 64;
-    constexpr int STAGE_B = 3 * TILE_B;    // K frag, V frag, K tr
+    constexpr int STAGE_B = NT * TILE_B;
+    constexpr int RING = 4;
     __shared__ __attribute__((aligned(1024))) uint4 sRing[RING * STAGE_B / 16];
 
     const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
@@ -453,9 +532,16 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
 #pragma unroll
     for (int h = 0; h < NCOPY; ++h) {
         const int e = NCOPY * wave + h, x = e / KK, i = e % KK;
-        coff[h] = x == 2 ? off_tr(D, i, l32, g) : off_frag(D, i, l32, g);
+        coff[h] = RM ? off_rm(D, i, lane) : x == 2 ? off_tr(D, i, l32, g) : off_frag(D, i, l32, g);
         cdst[h] = (uint32_t)(x * TILE_B + 1024 * i);
         cv[h] = x == 1;
+    }
+    // row-major read offsets (see the dK/dV kernel)
+    uint32_t fro[8], tro[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        fro[i] = RM ? rm_frag_off(D, i, lane) : 0u;
+        tro[i] = RM ? rm_tr_off(D, i >> 2, i & 3, lane) : 0u;
     }
     const uint32_t ring0 = lds_addr(sRing);
     auto issue = [&](int t) __attribute__((always_inline)) {
@@ -490,12 +576,15 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             s[r] = dp[r] = 0.f;
+        // fragment kk of the tile at byte o
+        auto fr = [&](uint32_t o, int kk) __attribute__((always_inline)) {
+            return __builtin_bit_cast(bf16x8, RM ? lds16(sb + o + fro[kk & 7] + 256 * (kk >> 3))
+                                                 : lds16(sb + o + 1024 * kk + 16 * lane));
+        };
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            const bf16x8 ka = __builtin_bit_cast(bf16x8, lds16(sb + 1024 * kk + 16 * lane));
-            const bf16x8 va = __builtin_bit_cast(bf16x8, lds16(sb + TILE_B + 1024 * kk + 16 * lane));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kk], dp, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr(0, kk), qf[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr(TILE_B, kk), df[kk], dp, 0, 0, 0);
         }
         // lane: row my_q; register r: key j0 + 8(r/4) + 4g + r%4
         f32x16 ds;
@@ -511,13 +600,15 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -L2)) * (dp[r] - Di);
-        const uint32_t trk = sb + 2 * TILE_B + 8 * lane;
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
             const bf16x8 sa = pack_chunk(ds, ch);
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, lds_tr(trk, db, ch), dq[db], 0, 0, 0);
+            for (int db = 0; db < DB; ++db) {
+                const bf16x8 kt = RM ? lds_tr_rm(sb + tro[4 * ch + (db & 3)] + 256 * (db >> 2), D)
+                                     : lds_tr(sb + 2 * TILE_B + 8 * lane, db, ch);
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, kt, dq[db], 0, 0, 0);
+            }
         }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));

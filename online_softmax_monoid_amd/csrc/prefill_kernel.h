@@ -208,11 +208,16 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // L1 busy with four times the cache lines.
     constexpr bool ROWCOPY = D == 256;
     constexpr int CPT = DPW;  // copy instructions per wave per tile, each of K and V
+    // SPREAD (at 256, one wave per SIMD): a step's copies go one after each
+    // group of four MFMAs instead of all at its start, where the four waves'
+    // 32 copies queued at once in the CU's address unit (about 12 ns each)
+    constexpr bool SPREAD = ROWCOPY;
     constexpr int INFLIGHT = CPT + 2 * CPT * (RING - 3);  // copies newer than K tile j+3 at step j's end
     static_assert((RING & (RING - 1)) == 0 && RING >= 4, "ring of 2^n >= 4 tiles");
     static_assert((NG == 1 || NG == 2 || NG == 4) && NWV * DPW == KKN && INFLIGHT < 64,
                   "tile step shape");
     static_assert(!ROWCOPY || (D == 256 && BN == 32), "row pairs: 512-byte rows, 32-key tiles");
+    static_assert(!SPREAD || NG == CPT, "one copy of K and one of V per group");
     constexpr int TILE_CH = BN * D / 8;  // 16-byte chunks per tile
     constexpr int KPB = 1040, VPB = 1088;  // block strides of ROWPAIR (bytes)
     constexpr uint32_t KTILE_B = ROWCOPY ? 16 * KPB : TILE_CH * 16;
@@ -740,9 +745,20 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // Copies of step j of an item: K of stream position j+RING and V of
     // j+RING-1, which are the item's own tiles, the next item's first tiles (K
     // 0 .. RING-1, V 0 .. RING-2), or nothing.
-    auto step_copies = [&](int j) __attribute__((always_inline)) {
-        dma_k(ph + j, kp, krem);
-        dma_v(ph + j + RING - 1, vp, vrem);
+    // (SPREAD: descriptors and LDS addresses only; the step issues copy h of K
+    // after its stage-A group h and copy h of V after its stage-B group h)
+    u32x4 cdk, cdv;
+    uint32_t cmk = 0, cmv = 0;
+    auto step_copies = [&](int j, auto SPREADc) __attribute__((always_inline)) {
+        if constexpr (decltype(SPREADc)::value) {
+            cdk = make_desc(kp, (uint32_t)max(krem, 0) * (D * 2));
+            cdv = make_desc(vp, (uint32_t)max(vrem, 0) * (D * 2));
+            cmk = m0k + (uint32_t)((ph + j) & (RING - 1)) * KTILE_B;
+            cmv = m0v + (uint32_t)((ph + j + RING - 1) & (RING - 1)) * VTILE_B;
+        } else {
+            dma_k(ph + j, kp, krem);
+            dma_v(ph + j + RING - 1, vp, vrem);
+        }
         // after the item's last tile, the next item's first ones
         if (j + RING + 1 == nblk) {
             kp = kn;
@@ -779,7 +795,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         uint32_t vread = vread_addr(ph + j);      // V tile j
         pin(kread);
         pin(vread);
-        step_copies(j);
+        step_copies(j, IntC<SPREAD>{});
         slot_end();
 
         // Stage A, NG groups of four MFMAs (QK of tile j+1). The first (at
@@ -812,6 +828,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
                 __builtin_amdgcn_sched_group_barrier(0x002, NG == 1 ? 8 : 4, 0);  // VALU
             }
             slot_end();
+            if constexpr (SPREAD) {
+                copy_to_lds(cdk, koff[grp], cmk + KSTEP * grp);
+                slot_end();
+            }
         }
         check_tile(sc, pc);  // tile j's probabilities are complete
         slot_end();
@@ -852,6 +872,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
                 __builtin_amdgcn_sched_group_barrier(0x002, NG == 1 ? 8 : 4, 0);  // VALU
             }
             slot_end();
+            if constexpr (SPREAD) {
+                copy_to_lds(cdv, voff[grp], cmv + VSTEP * grp);
+                slot_end();
+            }
         }
         step_end();
     };
@@ -865,7 +889,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         if (j < nwb) {
             step(IntC<1>{}, j, sc, sn, pc, pn);
         } else {
-            step_copies(j);
+            step_copies(j, IntC<0>{});
             step_end();
         }
     };

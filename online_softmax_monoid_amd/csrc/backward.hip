@@ -316,7 +316,13 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     // stage t's copies; past the walk's end they cover no bytes (the index
     // math is clamped and the lengths selected, so that no branch splits the
     // step)
-    auto issue = [&](int t) __attribute__((always_inline)) {
+    // A stage's copies in three parts, issued at three points of a step (its
+    // start, before the next S/dP products, before the dV/dK products) rather
+    // than at once, where every wave's copies would queue together in the
+    // CU's address unit. The descriptors of stage t come first.
+    u32x4 cq, cd, cw;
+    uint32_t cslot = 0;
+    auto prep = [&](int t) __attribute__((always_inline)) {
         const int tc = min(t, max(n_steps - 1, 0));
         const int hq = kvh * G + (per_head > 0 ? tc / per_head : 0);
         const int i0 = 32 * (qt0 + (per_head > 0 ? tc % per_head : 0));
@@ -324,26 +330,37 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
         const bool live = t < n_steps;
         const uint32_t nq = live ? (uint32_t)(Sq - i0) * (D * 2) : 0u;
         const uint32_t nw = live ? (uint32_t)(Sq - i0) * 8 : 0u;
-        const u32x4 dq_ = make_desc(a.q + r0 * D, nq), dd = make_desc(a.dout + r0 * D, nq);
-        const u32x4 dw = make_desc(a.dsum + 2 * r0, nw);
-        const uint32_t base = ring0 + (uint32_t)(t % RING) * STAGE_B;
+        cq = make_desc(a.q + r0 * D, nq);
+        cd = make_desc(a.dout + r0 * D, nq);
+        cw = make_desc(a.dsum + 2 * r0, nw);
+        cslot = (uint32_t)(t % RING);
+    };
+    // part p of NP of the prepared stage's copies (copy e goes in part e NP / NCOPY)
+    auto issue = [&](int p, int np) __attribute__((always_inline)) {
+        const uint32_t base = ring0 + cslot * STAGE_B;
         const uint32_t fb = base + 1024 * CPF * wave, tb = base + 1024 * CPT * wave;
+        int e = 0;
+        auto one = [&](auto &&f) __attribute__((always_inline)) {
+            if (e * np / NCOPY == p)
+                f();
+            ++e;
+        };
 #pragma unroll
         for (int h = 0; h < CPF; ++h) {
-            copy_to_lds(dq_, foff[h], fb + 1024 * h);
+            one([&] { copy_to_lds(cq, foff[h], fb + 1024 * h); });
             if constexpr (DODK || RM)
-                copy_to_lds(dd, foff[h], fb + OFF_OF + 1024 * h);
+                one([&] { copy_to_lds(cd, foff[h], fb + OFF_OF + 1024 * h); });
         }
         if constexpr (!RM) {
 #pragma unroll
             for (int h = 0; h < CPT; ++h) {
                 if constexpr (DODK)
-                    copy_to_lds(dq_, toff[h], tb + OFF_QT + 1024 * h);
+                    one([&] { copy_to_lds(cq, toff[h], tb + OFF_QT + 1024 * h); });
                 if constexpr (DODV)
-                    copy_to_lds(dd, toff[h], tb + OFF_OT + 1024 * h);
+                    one([&] { copy_to_lds(cd, toff[h], tb + OFF_OT + 1024 * h); });
             }
         }
-        copy_to_lds_b32(dw, 4 * lane, stat0 + ((uint32_t)(t % RING) * NW + wave) * 256);
+        one([&] { copy_to_lds_b32(cw, 4 * lane, stat0 + (cslot * NW + wave) * 256); });
     };
     // S (and dP) of stage t (16 query rows per lane, key my_key)
     auto qk = [&](int t, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
@@ -406,12 +423,14 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
             sa0 = pack_chunk(ds, 0);
             sa1 = pack_chunk(ds, 1);
         }
+        issue(1, 3);
         qk(t + 1, s, dp);
         const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + (RM ? 0 : 8 * lane);
         // block (ch, db) of the transposing operand in the tile at byte o
         auto tr = [&](uint32_t o, int db, int ch) __attribute__((always_inline)) {
             return RM ? lds_tr_rm(sb + o + tro[4 * ch + (db & 3)] + 256 * (db >> 2), D) : lds_tr(sb + o, db, ch);
         };
+        issue(2, 3);
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
@@ -430,8 +449,10 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     // there), copied at the top of step t + 1 - RING into the slot of stage
     // t - RING
 #pragma unroll
-    for (int t = 0; t < RING - 1; ++t)
-        issue(t);
+    for (int t = 0; t < RING - 1; ++t) {
+        prep(t);
+        issue(0, 1);
+    }
     f32x16 s, dp;
     if (n_steps > 0) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((RING - 2) * NCOPY));
@@ -441,7 +462,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     for (int t = 0; t < n_steps; ++t) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((RING - 3) * NCOPY));  // this wave's copies of stage t+1
         ring_barrier();                                              // and every other wave's
-        issue(t + RING - 1);
+        prep(t + RING - 1);
+        issue(0, 3);
         const int i0 = 32 * (qt0 + t % per_head);
         const bool full = (!CAUSAL || i0 + diag >= jw0 + 31) && jw0 + 31 < Sk && i0 + 31 < Sq;
         step(t, full, s, dp);
@@ -482,6 +504,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
     constexpr int TILE_B = D * 64;
     constexpr int STAGE_B = NT * TILE_B;
     constexpr int RING = 4;
+    constexpr int NP = RM ? 3 : 1;         // parts a stage's copies are issued in
     __shared__ __attribute__((aligned(1024))) uint4 sRing[RING * STAGE_B / 16];
 
     const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
@@ -544,7 +567,9 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
         tro[i] = RM ? rm_tr_off(D, i >> 2, i & 3, lane) : 0u;
     }
     const uint32_t ring0 = lds_addr(sRing);
-    auto issue = [&](int t) __attribute__((always_inline)) {
+    u32x4 cdk, cdv;
+    uint32_t cbase = 0;
+    auto prep = [&](int t) __attribute__((always_inline)) {
         const uint16_t *ks = a.k, *vs = a.v;
         uint32_t n = 0;
         if (t < nkt) {
@@ -552,24 +577,38 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
             vs = a.v + (krow0 + 32 * t) * D;
             n = (uint32_t)(kv_end - 32 * t) * (D * 2);
         }
-        const u32x4 dk_ = make_desc(ks, n), dv_ = make_desc(vs, n);
-        const uint32_t base = ring0 + (uint32_t)(t % RING) * STAGE_B;
+        cdk = make_desc(ks, n);
+        cdv = make_desc(vs, n);
+        cbase = ring0 + (uint32_t)(t % RING) * STAGE_B;
+    };
+    // part p of NP of the prepared stage's copies (copy h goes in part h NP / NCOPY)
+    auto issue = [&](int p, int np) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < NCOPY; ++h)
-            copy_to_lds(cv[h] ? dv_ : dk_, coff[h], base + cdst[h]);
+            if (h * np / NCOPY == p)
+                copy_to_lds(cv[h] ? cdv : cdk, coff[h], cbase + cdst[h]);
     };
 
 #pragma unroll
-    for (int t = 0; t < RING - 1; ++t)
-        issue(t);
+    for (int t = 0; t < RING - 1; ++t) {
+        prep(t);
+        issue(0, 1);
+    }
     for (int t = 0; t < nkt; ++t) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((RING - 2) * NCOPY));
         ring_barrier();
-        issue(t + RING - 1);
+        // at 256 the stage's copies go in three parts: here, after the S/dP
+        // products, before the dQ products (every wave issues all three; at 64
+        // and 128 the two waves of a SIMD hide a burst: no gain)
+        prep(t + RING - 1);
+        issue(0, NP);
         const int j0 = 32 * t;
         const bool any = iw0 < Sq && (!CAUSAL || iw0 + 31 + diag >= j0);
-        if (!any)
+        if (!any) {
+            issue(1, NP);
+            issue(2, NP);
             continue;
+        }
         const bool full = (!CAUSAL || iw0 + diag >= j0 + 31) && j0 + 31 < Sk && iw0 + 31 < Sq;
         const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B;
         f32x16 s, dp;
@@ -586,6 +625,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr(0, kk), qf[kk], s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr(TILE_B, kk), df[kk], dp, 0, 0, 0);
         }
+        issue(1, NP);
         // lane: row my_q; register r: key j0 + 8(r/4) + 4g + r%4
         f32x16 ds;
         // hidden pairs get the score -inf, so that their probability is 0
@@ -600,6 +640,7 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             ds[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -L2)) * (dp[r] - Di);
+        issue(2, NP);
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
             const bf16x8 sa = pack_chunk(ds, ch);

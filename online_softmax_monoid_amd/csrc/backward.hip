@@ -316,10 +316,11 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     // stage t's copies; past the walk's end they cover no bytes (the index
     // math is clamped and the lengths selected, so that no branch splits the
     // step)
-    // A stage's copies in three parts, issued at three points of a step (its
-    // start, before the next S/dP products, before the dV/dK products) rather
-    // than at once, where every wave's copies would queue together in the
-    // CU's address unit. The descriptors of stage t come first.
+    // A stage's copies in four parts, issued at four points of a step (its
+    // start, before the next S/dP products, before the dV/dK products, between
+    // their two 16-row chunks) rather than at once, where every wave's copies
+    // would queue together in the CU's address unit. The descriptors of stage
+    // t come first.
     u32x4 cq, cd, cw;
     uint32_t cslot = 0;
     auto prep = [&](int t) __attribute__((always_inline)) {
@@ -423,14 +424,14 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
             sa0 = pack_chunk(ds, 0);
             sa1 = pack_chunk(ds, 1);
         }
-        issue(1, 3);
+        issue(1, 4);
         qk(t + 1, s, dp);
         const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + (RM ? 0 : 8 * lane);
         // block (ch, db) of the transposing operand in the tile at byte o
         auto tr = [&](uint32_t o, int db, int ch) __attribute__((always_inline)) {
             return RM ? lds_tr_rm(sb + o + tro[4 * ch + (db & 3)] + 256 * (db >> 2), D) : lds_tr(sb + o, db, ch);
         };
-        issue(2, 3);
+        issue(2, 4);
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
@@ -442,6 +443,8 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
                     dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ch ? sa1 : sa0, tr(OFF_QT, db, ch), dk[db],
                                                                      0, 0, 0);
             }
+            if (ch == 0)
+                issue(3, 4);
         }
     };
 
@@ -463,7 +466,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
         __builtin_amdgcn_s_waitcnt(vmcnt_imm((RING - 3) * NCOPY));  // this wave's copies of stage t+1
         ring_barrier();                                              // and every other wave's
         prep(t + RING - 1);
-        issue(0, 3);
+        issue(0, 4);
         const int i0 = 32 * (qt0 + t % per_head);
         const bool full = (!CAUSAL || i0 + diag >= jw0 + 31) && jw0 + 31 < Sk && i0 + 31 < Sq;
         step(t, full, s, dp);

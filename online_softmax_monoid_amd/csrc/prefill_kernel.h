@@ -208,12 +208,13 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // L1 busy with four times the cache lines.
     constexpr bool ROWCOPY = D == 256;
     constexpr int CPT = DPW;  // copy instructions per wave per tile, each of K and V
-    // A step's copies go one after each group of four MFMAs (copy h of K after
-    // stage-A group h, of V after stage-B group h) instead of all at the step's
-    // start, where every wave's copies queued at once in the CU's address unit
-    // (12 to 27 ns per 1 KB copy, by shape) and held the waves at issue:
-    // 2.9% at head dimension 256, 2.2% at 128, 1-2% at 64, outputs
-    // bit-identical. (The masked steps still issue theirs at once.)
+    // A step's copies go one after each group of four MFMAs (the K copies
+    // after the last CPT groups of stage A, the V copies after the first CPT of
+    // stage B) instead of all at the step's start, where every wave's copies
+    // queued at once in the CU's address unit (12 to 27 ns per 1 KB copy, by
+    // shape) and held the waves at issue: 2.9% at head dimension 256, 3.5% at
+    // 128, 1-2% at 64, outputs bit-identical. (The masked steps still issue
+    // theirs at once.)
     constexpr bool SPREAD = true;
     constexpr int INFLIGHT = CPT + 2 * CPT * (RING - 3);  // copies newer than K tile j+3 at step j's end
     static_assert((RING & (RING - 1)) == 0 && RING >= 4, "ring of 2^n >= 4 tiles");
@@ -832,8 +833,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
             }
             slot_end();
             if constexpr (SPREAD) {
-                if (grp < CPT) {
-                    copy_to_lds(cdk, koff[grp], cmk + KSTEP * grp);
+                if (grp >= NG - CPT) {
+                    copy_to_lds(cdk, koff[grp - (NG - CPT)], cmk + KSTEP * (grp - (NG - CPT)));
                     slot_end();
                 }
             }

@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import math
 import os
+import zlib
 
 import numpy as np
 import pytest
@@ -24,11 +25,28 @@ from online_softmax_monoid_amd import inputs
 from tests import brute
 
 RTOL_EXACT = 1e-13
+# an LSE that lands near zero keeps an absolute error of a few ulps of the
+# scores it was summed from
+LSE_ATOL = 1e-14
 
 
 def _rand_bits(rng, shape, std=1.0):
     x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
     return inputs.bf16_bits(x)
+
+
+def _seed(case):
+    """A seed fixed by the case's text (hash() of a tuple holding None
+    changes from process to process)."""
+    return zlib.crc32(repr(case).encode())
+
+
+def _o_atol(v):
+    """Absolute floor for comparing two f64 evaluations of O = sum p_j v_j:
+    an element that cancels to near zero keeps an absolute rounding error of
+    a few ulps of max|v|, which a purely relative bound would reject."""
+    vf = inputs.bf16_to_f32(v).astype(np.float64)
+    return 1e-15 * max(1.0, float(np.abs(vf).max()) if vf.size else 1.0)
 
 
 def _close(a, b, rtol=RTOL_EXACT, atol=1e-300):
@@ -39,7 +57,8 @@ def _close(a, b, rtol=RTOL_EXACT, atol=1e-300):
     fa, fb = np.where(same_inf, 0, a), np.where(same_inf, 0, b)
     err = np.abs(fa - fb)
     bound = atol + rtol * np.maximum(np.abs(fa), np.abs(fb))
-    assert np.all(err <= bound), f"max err {err.max()} (bound {bound[err.argmax()]})"
+    worst = int(np.argmax(np.ravel(err - bound))) if err.size else 0
+    assert np.all(err <= bound), f"err {np.ravel(err)[worst]} above bound {np.ravel(bound)[worst]}"
 
 
 # --------------------------------------------------------------------- T1 --
@@ -58,19 +77,19 @@ TINY_CASES = [
 @pytest.mark.parametrize("case", TINY_CASES)
 def test_brute_force_tiny(case):
     B, Hq, Hkv, Sq, Sk, d, causal = case
-    rng = np.random.Generator(np.random.PCG64(hash(case) % (2 ** 32)))
+    rng = np.random.Generator(np.random.PCG64(_seed(case)))
     q = _rand_bits(rng, (B, Hq, Sq, d))
     k = _rand_bits(rng, (B, Hkv, Sk, d))
     v = _rand_bits(rng, (B, Hkv, Sk, d))
     scale = 0.5
     o, lse = oracle.attn_fwd(q, k, v, causal, scale)
     bo, blse = brute.attention(q.tolist(), k.tolist(), v.tolist(), causal, scale)
-    _close(o, np.array(bo, dtype=np.float64).reshape(o.shape))
-    _close(lse, np.array(blse, dtype=np.float64))
+    _close(o, np.array(bo, dtype=np.float64).reshape(o.shape), atol=_o_atol(v))
+    _close(lse, np.array(blse, dtype=np.float64), atol=LSE_ATOL)
     mo, mlse = brute.mp_attention(q.tolist(), k.tolist(), v.tolist(), causal, scale)
     _close(o, np.array([[[[float(x) for x in r] for r in h] for h in b] for b in mo],
-                       dtype=np.float64).reshape(o.shape))
-    _close(lse, np.array([[[float(x) for x in h] for h in b] for b in mlse]))
+                       dtype=np.float64).reshape(o.shape), atol=_o_atol(v))
+    _close(lse, np.array([[[float(x) for x in h] for h in b] for b in mlse]), atol=LSE_ATOL)
     # empty rows: O = +0 exactly and LSE = -inf
     if causal:
         for i in range(Sq):
@@ -93,14 +112,14 @@ WINDOW_CASES = [
 @pytest.mark.parametrize("case", WINDOW_CASES)
 def test_window_brute_force_tiny(case):
     B, Hq, Hkv, Sq, Sk, d, causal, window = case
-    rng = np.random.Generator(np.random.PCG64(hash(case) % (2 ** 32)))
+    rng = np.random.Generator(np.random.PCG64(_seed(case)))
     q = _rand_bits(rng, (B, Hq, Sq, d))
     k = _rand_bits(rng, (B, Hkv, Sk, d))
     v = _rand_bits(rng, (B, Hkv, Sk, d))
     o, lse = oracle.attn_fwd(q, k, v, causal, 0.5, window=window)
     bo, blse = brute.attention(q.tolist(), k.tolist(), v.tolist(), causal, 0.5, window=window)
-    _close(o, np.array(bo, dtype=np.float64).reshape(o.shape))
-    _close(lse, np.array(blse, dtype=np.float64))
+    _close(o, np.array(bo, dtype=np.float64).reshape(o.shape), atol=_o_atol(v))
+    _close(lse, np.array(blse, dtype=np.float64), atol=LSE_ATOL)
     for i in range(Sq):  # a row with no key in its window: (+0, -inf) exactly
         lo = i + Sk - Sq - window
         hi = min(Sk - 1, i + Sk - Sq) if causal else Sk - 1
@@ -230,7 +249,7 @@ MOD_CASES = [
 @pytest.mark.parametrize("case", MOD_CASES)
 def test_score_modifiers_brute_force_tiny(case):
     B, Hq, Hkv, Sq, Sk, d, causal, window, softcap, alibi = case
-    rng = np.random.Generator(np.random.PCG64(hash(case) % (2 ** 32)))
+    rng = np.random.Generator(np.random.PCG64(_seed(case)))
     q = _rand_bits(rng, (B, Hq, Sq, d))
     k = _rand_bits(rng, (B, Hkv, Sk, d))
     v = _rand_bits(rng, (B, Hkv, Sk, d))
@@ -238,8 +257,8 @@ def test_score_modifiers_brute_force_tiny(case):
     o, lse = oracle.attn_fwd(q, k, v, causal, 0.5, window=window, softcap=softcap, alibi=al)
     bo, blse = brute.attention(q.tolist(), k.tolist(), v.tolist(), causal, 0.5, window=window,
                                softcap=softcap, alibi=None if al is None else al.tolist())
-    _close(o, np.array(bo, dtype=np.float64).reshape(o.shape))
-    _close(lse, np.array(blse, dtype=np.float64))
+    _close(o, np.array(bo, dtype=np.float64).reshape(o.shape), atol=_o_atol(v))
+    _close(lse, np.array(blse, dtype=np.float64), atol=LSE_ATOL)
 
 
 def test_alibi_steep_slope_keeps_the_aligned_key():

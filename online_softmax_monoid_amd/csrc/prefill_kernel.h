@@ -273,6 +273,9 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // item of the list is past a sequence's end, and the heavy tiles come
     // first.
     const bool compact = VARLEN && a.B <= 64;
+    const int xpu_v = a.Hkv < 8 && 8 % a.Hkv == 0 ? 8 / a.Hkv : 0;  // XCDs per kv-head
+    const bool heads_by_xcd =
+        compact && a.Hq % 8 == 0 && (a.Hkv % 8 == 0 || (xpu_v > 0 && G % xpu_v == 0));
     int v_qlo = 0, v_sq = 0, v_klo = 0, v_sk = 0, v_nq = 0, v_pos = 0;  // lane b: sequence b
     int n_live = n_items;
     if constexpr (VARLEN) {
@@ -310,7 +313,18 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
                 rank_c0 += n;
                 ++rank_r;
             }
-            const int idx = id - rank_c0, k = idx / a.Hq, hq_c = idx - k * a.Hq;
+            const int idx = id - rank_c0, k = idx / a.Hq, pq = idx - k * a.Hq;
+            // A (sequence, rank) block of Hq items starts at a multiple of Hq,
+            // so with Hq % 8 == 0 item pq runs on XCD pq % 8. The G query heads
+            // of a kv-head then go to one XCD (or, with fewer than 8 kv-heads,
+            // to an equal share of XCDs), where they read its K and V through
+            // one L2 instead of one L2 each.
+            int hq_c = pq;
+            if (heads_by_xcd) {
+                const int x = pq & 7, t = pq >> 3;
+                hq_c = a.Hkv % 8 == 0 ? (x + 8 * (t / G)) * G + t % G
+                                      : (x / xpu_v) * G + (x % xpu_v) * (G / xpu_v) + t;
+            }
             const unsigned long long hit = __ballot(lane < a.B && v_pos == k);
             b_c = hit ? (int)__builtin_ctzll(hit) : 0;  // exactly one lane matches
             to.unit = b_c * a.Hkv + hq_c / G;

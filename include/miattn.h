@@ -204,9 +204,10 @@ MIATTN_API int attn_fwd_varlen_ext(const void *q, const void *k, const void *v, 
  *   dk    bf16 [B, Hkv, Sk, d]   written (summed over the Hq/Hkv query heads
  *   dv    bf16 [B, Hkv, Sk, d]   written  that read each kv-head)
  *   workspace  device scratch of at least attn_bwd_workspace_size(B, Hq, Sq)
- *              bytes (per row the f32 pair D_i, LSE_i log2 e, computed
- *              first); 4-byte aligned; contents on entry do not matter. Two
- *              calls sharing one workspace must be ordered.
+ *              bytes (per row the f32 pair D_i, LSE_i log2 e, written by the
+ *              dQ kernel and read by the dK/dV kernel that follows it);
+ *              4-byte aligned; contents on entry do not matter. Two calls
+ *              sharing one workspace must be ordered.
  *
  * f32 accumulation, bf16 results; P and dS are rounded to bf16 for their
  * matrix products. Head dimensions 64, 128 and 256. Keys no query sees get

@@ -8,11 +8,12 @@
 //   dV_j  = sum_i P_ij dO_i      dK_j = scale sum_i dS_ij q_i
 //   dQ_i  = scale sum_j dS_ij k_j
 //
-// D_i is computed once per row into the caller's workspace by a first small
-// kernel. Then two kernels, no atomics: a workgroup per 128-key block
-// accumulates dK and dV over the query heads of its kv-head and their query
-// tiles; a workgroup per block of query rows accumulates dQ over the key
-// tiles. Every product is a v_mfma_f32_32x32x16_bf16 with f32 accumulation.
+// Two kernels, no atomics. First a workgroup per block of query rows
+// accumulates dQ over the key tiles; its waves, which hold their rows' dO
+// anyway, also compute each row's D_i and write it (with LSE_i log2 e) to the
+// caller's workspace. Then a workgroup per 128-key block accumulates dK and
+// dV over the query heads of its kv-head and their query tiles, reading those
+// row statistics. Every product is a v_mfma_f32_32x32x16_bf16 with f32 accumulation.
 // As in the forward, a score accumulator holds, in lane l, one column (l % 32)
 // and the 16 rows 8(r/4) + 4(l/32) + r%4 of its registers r; its registers
 // packed to bf16 are then directly the A operand of the next product over
@@ -531,8 +532,30 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
         df[kk] = frag<D>(rdo, my_q, kk, g);
     }
     const bool in = my_q < Sq;
-    float Di = in ? a.dsum[2 * (qrow0 + my_q)] : 0.f;
-    float L2 = in ? a.dsum[2 * (qrow0 + my_q) + 1] : 0.f;
+    // the row's statistics (D_i = dO_i . O_i, LSE_i log2 e), computed here and
+    // written to the workspace for the dK/dV launch that follows; each row
+    // belongs to exactly one wave of one workgroup
+    float Di, L2;
+    {
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o + qrow0 * D, (uint32_t)Sq * D * 2);
+        float dot = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const bf16x8 o = frag<D>(ro, my_q, kk, g);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                dot += (float)df[kk][e] * (float)o[e];
+        }
+        dot += __shfl_xor(dot, 32, 64);
+        // a row that sees no key (LSE = -inf) gets the lowest finite value:
+        // every score of such a row is masked to -inf, and exp2 of
+        // -inf * c + FLT_MAX is exactly 0
+        const float L = in ? a.lse[qrow0 + my_q] * kLog2e : 0.f;
+        Di = in ? dot : 0.f;
+        L2 = L == -INFINITY ? -FLT_MAX : L;
+        if (in)
+            a.dsum[2 * (qrow0 + my_q) + g] = g == 0 ? Di : L2;
+    }
     // at 256 (one wave per SIMD) the fixed operands go to AGPRs, the VGPRs to
     // the accumulator
     settle<D == 256>(qf);
@@ -667,42 +690,6 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
         }
 }
 
-// ---- per-row statistics, once (the workspace) ------------------------------------
-// Row i's pair (D_i = dO_i . O_i, LSE_i log2 e) as two floats. One wave per 32
-// rows of a (b, query head): lane l32 + 32 g takes dims 16kk + 8g .. +7 of row
-// l32.
-template <int D>
-__global__ void __launch_bounds__(64) bwd_dsum_kernel(BwdArgs a, int n_qtiles)
-{
-    constexpr int KK = D / 16;
-    const int lane = threadIdx.x, l32 = lane & 31, g = lane >> 5;
-    const int qt = blockIdx.x % n_qtiles, bh = blockIdx.x / n_qtiles;
-    const int Sq = a.Sq, i = 32 * qt + l32;
-    const int64_t qrow0 = (int64_t)bh * Sq;
-    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(a.dout + qrow0 * D, (uint32_t)Sq * D * 2);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.o + qrow0 * D, (uint32_t)Sq * D * 2);
-    float dot = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 d = frag<D>(rdo, i, kk, g), o = frag<D>(ro, i, kk, g);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            dot += (float)d[e] * (float)o[e];
-    }
-    dot += __shfl_xor(dot, 32, 64);
-    if (i < Sq) {
-        if (g == 0)
-            a.dsum[2 * (qrow0 + i)] = dot;
-        else {
-            // a row that sees no key (LSE = -inf) gets the lowest finite value:
-            // every score of such a row is masked to -inf, and exp2 of
-            // -inf * c + FLT_MAX is exactly 0
-            const float L = a.lse[qrow0 + i] * kLog2e;
-            a.dsum[2 * (qrow0 + i) + 1] = L == -INFINITY ? -FLT_MAX : L;
-        }
-    }
-}
-
 template <auto Kernel>
 hipError_t launch_dkdv(const BwdArgs &a, long long grid, int nkb, hipStream_t stream)
 {
@@ -717,15 +704,17 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
     // workgroups sharing a copy ring: dK/dV per 128-key block, dQ per block of
     // 32 NWQ rows
     constexpr int NWQ = D == 128 ? 8 : 4;
-    const int n_qtiles = (a.Sq + 31) / 32;
     const int nkb = (a.Sk + 127) / 128, nrb = (a.Sq + 32 * NWQ - 1) / (32 * NWQ);
-    const long long g0 = (long long)a.B * a.Hq * n_qtiles;
     const long long g1 = (long long)a.B * a.Hkv * nkb;
     const long long g2 = (long long)a.B * a.Hq * nrb;
-    if (g0 > 0x7fffffffLL || g1 > 0x7fffffffLL || g2 > 0x7fffffffLL)
+    if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
-    if (g0 > 0) {
-        hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)g0), dim3(64), 0, stream, a, n_qtiles);
+    // dQ first: its workgroups also write every row's (D_i, LSE_i log2 e),
+    // which the dK/dV launch reads
+    if (g2 > 0) {
+        constexpr auto kernel = bwd_dq_ring_kernel<D, CAUSAL, NWQ>;
+        const int gx = max(1, resident_workgroups<kernel>(64 * NWQ) / 8);
+        hipLaunchKernelGGL(kernel, dim3((unsigned)g2), dim3(64 * NWQ), 0, stream, a, nrb, gx);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -742,11 +731,6 @@ hipError_t launch_bwd_t(const BwdArgs &a, hipStream_t stream)
         }
         if (e != hipSuccess)
             return e;
-    }
-    if (g2 > 0) {
-        constexpr auto kernel = bwd_dq_ring_kernel<D, CAUSAL, NWQ>;
-        const int gx = max(1, resident_workgroups<kernel>(64 * NWQ) / 8);
-        hipLaunchKernelGGL(kernel, dim3((unsigned)g2), dim3(64 * NWQ), 0, stream, a, nrb, gx);
     }
     return hipGetLastError();
 }

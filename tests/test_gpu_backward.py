@@ -153,3 +153,25 @@ def test_backward_degenerate_lengths(Sq, Sk, d):
     dq, dk, dv, guards = H.run_bwd(q, k, v, o_bits, lse, do, True, inputs.default_scale(d))
     assert guards
     assert not dq.any() and not dk.any() and not dv.any()
+
+
+def test_backward_d256_bench_shape_sampled_heads():
+    """The bench's head-dimension-256 backward (B2 H16 S4096 d256 causal, the
+    same seeded draws), the GPU forward's O and LSE feeding it, in that launch
+    configuration; two (batch, head) slices against the oracle."""
+    B, NH, S, d = 2, 16, 4096, 256
+    q, k, v = inputs.draw_prefill_bits(7400, B, NH, NH, S, S, d, 0.5)
+    (do,) = inputs.draw_prefill_bits(7401, B, NH, NH, S, S, d)[:1]
+    scale = inputs.default_scale(d)
+    _note("[gpu] backward d256 bench shape: forward then backward on the GPU")
+    o_bits, lse, _ = H.run_fwd(q, k, v, True, scale)
+    dq, dk, dv, guards = H.run_bwd(q, k, v, o_bits, lse, do, True, scale)
+    assert guards
+    for b, h in ((0, 3), (1, 12)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = bw.attn_bwd(q[sl], k[sl], v[sl], do[sl], True, scale)
+        for name, got, ref in (("dq", dq[sl], rq), ("dk", dk[sl], rk), ("dv", dv[sl], rv)):
+            m = H.grad_metrics(got, ref)
+            _note(f"[gpu] backward d256 bench shape b={b} h={h} {name}: {m}")
+            assert m["finite"] and m["rel_rms"] <= REL_RMS and m["max_abs_rel"] <= MAX_REL, m
+

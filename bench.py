@@ -805,6 +805,9 @@ def main():
                        "kv_len_sum": int(dec.lens_host.sum()), "splits": dw.num_splits},
             "parallelism": "single GPU",
             "rounds": per,
+            "seeds": {"prefill": inputs.WORKLOADS[PREFILL_WID].seed,
+                      "decode": inputs.WORKLOADS[DECODE_WID].seed,
+                      "long_context": inputs.WORKLOADS[LONG_WID].seed},
         },
         "roofline": {
             "bound": "mfma",
@@ -822,6 +825,17 @@ def main():
         "machine": machine,
         "cpu_baseline": cpu,
     }
+    # the same rates against the ceilings measured on this machine (the MFMA and
+    # streaming-read probes), beside the spec peaks
+    if machine is not None:
+        mf, rd = machine["mfma_ceiling"]["tflops"], machine["hbm"]["read_GBs"]
+        for key in ("prefill", "long_context_gqa_d256", "backward_d128", "backward_d256",
+                    "window_d128_w4096", "varlen_chunked_d128"):
+            if isinstance(out.get(key), dict) and mf > 0:
+                out[key]["frac_of_measured_mfma"] = round(out[key]["value"] / mf, 4)
+        for key in ("decode", "decode_paged"):
+            if isinstance(out.get(key), dict) and rd > 0:
+                out[key]["frac_of_measured_read"] = round(out[key]["value"] / rd, 4)
     print(json.dumps(out), flush=True)
 
 

@@ -58,6 +58,12 @@ VARLEN = [
     (4, [64, 65, 190], [1, 0, 300], 2, 2, 256, False),
     (5, [0, 1, 31, 33, 127, 129, 700], [0, 2, 0, 40, 0, 9, 64], 4, 2, 64, True),
     (6, [5, 300, 129], [0, 200, 17], 6, 3, 64, False),
+    # Hq a multiple of 8: the walk gives a kv-head's query heads one XCD
+    # (Hkv a multiple of 8) or an equal share of the XCDs (Hkv dividing 8)
+    (7, [33, 300, 129, 5], [0, 64, 17, 0], 8, 1, 128, True),
+    (8, [190, 64, 257], [3, 0, 40], 16, 2, 128, True),
+    (9, [77, 300], [0, 100], 16, 16, 64, False),
+    (10, [129, 31, 400], [9, 0, 0], 8, 4, 256, True),
 ]
 
 

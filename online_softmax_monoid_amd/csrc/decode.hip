@@ -208,16 +208,20 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
     // table row and to the pool, so that no entry can send a copy outside
     // it). Rows past the split repeat its last row instead of reading zeros:
     // their scores are masked and their probabilities are exactly 0.
-    auto paged_offsets = [&](int kb, int64_t (&off)[NI]) __attribute__((always_inline)) {
+    auto table_pages = [&](int kb, int (&pg)[3]) __attribute__((always_inline)) {
+        const int lp0 = kb >> a.page_shift;
+        const int *trow = a.table + (int64_t)b * a.max_pages;
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+            pg[t] = trow[min(lp0 + t, a.max_pages - 1)];
+    };
+    auto paged_offsets = [&](int kb, const int (&pe)[3], int64_t (&off)[NI]) __attribute__((always_inline)) {
         const int sh = a.page_shift;
         const int lp0 = kb >> sh;
-        const int *trow = a.table + (int64_t)b * a.max_pages;
         int pg[3];
 #pragma unroll
-        for (int t = 0; t < 3; ++t) {
-            const int e = trow[min(lp0 + t, a.max_pages - 1)];
-            pg[t] = min(max(e, 0), a.num_pages - 1);
-        }
+        for (int t = 0; t < 3; ++t)
+            pg[t] = min(max(pe[t], 0), a.num_pages - 1);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int rb = RPI * i + lane / CPR;  // row in the block
@@ -235,10 +239,11 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
             __builtin_amdgcn_global_load_lds((const void *)(pool + off[i]), (lds_void *)(buf + 64 * i),
                                              16, 0, kNT);
     };
-    auto copy_block = [&](int kb) __attribute__((always_inline)) {
+    // (paged: the block's table entries pe, read beforehand by table_pages)
+    auto copy_block = [&](int kb, const int (&pe)[3]) __attribute__((always_inline)) {
         if constexpr (PAGED) {
             int64_t off[NI];
-            paged_offsets(kb, off);
+            paged_offsets(kb, pe, off);
             dma_paged(sK, a.k, off);
             dma_paged(sV, a.v, off);
         } else {
@@ -285,10 +290,19 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
     for (int i = 0; i < DB; ++i)
         acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (wave < nb)
-        copy_block(k_lo + BK * wave);
+    int pe[3] = {0, 0, 0};  // paged: table entries of the wave's next block
+    if (wave < nb) {
+        if constexpr (PAGED)
+            table_pages(k_lo + BK * wave, pe);
+        copy_block(k_lo + BK * wave, pe);
+    }
     for (int n = wave; n < nb; n += NW) {
         const int kb = k_lo + BK * n;
+        // paged: the next block's table entries are read now, so that they
+        // land with this block's copies instead of costing a memory round
+        // trip of their own before the next copies can be issued
+        if (PAGED && n + NW < nb)
+            table_pages(kb + BK * NW, pe);
         // this block's copies have landed (nothing newer is in flight); take
         // it into registers, then start the copies of this wave's next block
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -296,7 +310,7 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
         read_v();
         if (n + NW < nb) {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the block is in registers
-            copy_block(kb + BK * NW);
+            copy_block(kb + BK * NW, pe);
         }
         // S^T for the two 16-key halves: lane l holds keys 16 half + 4(l/16) + i
         // for the query head in column l%16

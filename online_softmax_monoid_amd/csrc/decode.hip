@@ -61,10 +61,14 @@ __device__ __forceinline__ int clamped_len(const DecodeArgs &a, int b)
 // splits running alone at the end. Up to 64 streams every wave ranks them
 // itself (lane i holds stream i's length); beyond that streams go in index
 // order.
-__device__ __forceinline__ int stream_by_rank(const DecodeArgs &a, int rank, int lane)
+// The stream's clamped length comes back in len (read from the lane that
+// ranked it, so that no second load of the lengths delays the first copies).
+__device__ __forceinline__ int stream_by_rank(const DecodeArgs &a, int rank, int lane, int &len)
 {
-    if (a.B > 64)
+    if (a.B > 64) {
+        len = __builtin_amdgcn_readfirstlane(clamped_len(a, rank));
         return rank;
+    }
     const int mine = lane < a.B ? clamped_len(a, lane) : -1;
     int my_rank = 0;
     for (int o = 0; o < a.B; ++o) {
@@ -72,7 +76,9 @@ __device__ __forceinline__ int stream_by_rank(const DecodeArgs &a, int rank, int
         my_rank += (lo > mine) || (lo == mine && o < lane);
     }
     const unsigned long long hit = __ballot(lane < a.B && my_rank == rank);
-    return hit ? (int)__builtin_ctzll(hit) : rank;  // exactly one lane matches
+    const int b = hit ? (int)__builtin_ctzll(hit) : rank;  // exactly one lane matches
+    len = __builtin_amdgcn_readlane(mine, b);
+    return b;
 }
 
 // ---- split kernel on MFMA ----------------------------------------------------
@@ -133,12 +139,12 @@ decode_mfma_kernel(DecodeArgs a, int hchunks)
     id /= hchunks;
     const int kvh = id % a.Hkv;
     const int sr = id / a.Hkv;  // stream rank
-    const int b = stream_by_rank(a, sr, lane);
+    int len;
+    const int b = stream_by_rank(a, sr, lane, len);
     const int G = a.Hq / a.Hkv;
     const int h0 = kvh * G + 16 * hc;
     const int GH = min(16, G - 16 * hc);  // query heads of this chunk
 
-    const int len = __builtin_amdgcn_readfirstlane(clamped_len(a, b));
     const int k_lo = (int)(((int64_t)split * len) / a.splits);
     const int k_hi = (int)(((int64_t)(split + 1) * len) / a.splits);
     const int nb = (k_hi - k_lo + BK - 1) / BK;

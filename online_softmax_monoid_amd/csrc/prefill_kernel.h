@@ -568,8 +568,11 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // them towards their uses); inside the group its independent chains
     // overlap one another.
     //
-    // probabilities of scores r = 8h + 4quad .. +3 -> two packed bf16 pairs
-    auto probs_quad = [&](const Sc &s, Pc &p, int qb, int h, int quad)
+    // probabilities of scores r = 8h + 4quad .. +3 -> two packed bf16 pairs;
+    // init: the tile's first quad, whose sum starts tsum (an add to the zero
+    // it was reset to would cost one VALU instruction per tile: x + 0 is not
+    // x for x = -0, so the compiler keeps it)
+    auto probs_quad = [&](const Sc &s, Pc &p, int qb, int h, int quad, bool init = false)
         __attribute__((always_inline)) {
         float e[4];
 #pragma unroll
@@ -577,7 +580,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
             e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * h + 4 * quad + i], c, nmc[qb]));
         p[qb][h].w[2 * quad] = pack_bf16x2(e[0], e[1]);
         p[qb][h].w[2 * quad + 1] = pack_bf16x2(e[2], e[3]);
-        tsum += (e[0] + e[1]) + (e[2] + e[3]);
+        const float q4 = (e[0] + e[1]) + (e[2] + e[3]);
+        tsum = init ? q4 : tsum + q4;
         pin(tsum);
         pin(p[qb][h].w[2 * quad]);
         pin(p[qb][h].w[2 * quad + 1]);
@@ -695,8 +699,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         row_max(s, 0, 2, 0, false);
         move_ref(0);
         apply_alpha();
-        tsum = 0.f;
-        probs_quad(s, p, 0, 0, 0);
+        probs_quad(s, p, 0, 0, 0, true);
         probs_quad(s, p, 0, 0, 1);
         probs_quad(s, p, 0, 1, 0);
         probs_quad(s, p, 0, 1, 1);
@@ -747,7 +750,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
             row_max(sA, qb, 1, 0, true);
             row_max(sA, qb, 2, 0, true);
             move_ref(qb);
-            probs_quad(sA, pA, qb, 0, 0);
+            probs_quad(sA, pA, qb, 0, 0, qb == 0);
             probs_quad(sA, pA, qb, 0, 1);
         }
         apply_alpha();  // the first reference moves consume their rescale here
@@ -875,15 +878,15 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
             if (MASK && grp == 0)
                 mask_tile(sn, 0, j + 1);
             if (NG == 1) {
-                probs_quad(sn, pn, 0, 0, 0);
+                probs_quad(sn, pn, 0, 0, 0, true);
                 probs_quad(sn, pn, 0, 0, 1);
             }
             if (NG == 2 && grp == 1) {
-                probs_quad(sn, pn, 0, 0, 0);
+                probs_quad(sn, pn, 0, 0, 0, true);
                 probs_quad(sn, pn, 0, 0, 1);
             }
             if (NG == 4 && (grp == 1 || grp == 2))
-                probs_quad(sn, pn, 0, 0, grp - 1);
+                probs_quad(sn, pn, 0, 0, grp - 1, grp == 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA

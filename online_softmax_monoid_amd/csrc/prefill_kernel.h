@@ -200,13 +200,14 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // in step j (8 KB per tile at head dimension 128, 16 KB at 256: 64 or
     // 128 KB of the 160 KB of LDS)
     constexpr int RING = 4;
-    // ROWPAIR (head dimension 256): copy i of a tile takes two whole 512-byte
-    // rows, keys i and i+16, into a 1 KB block; the blocks lie KPB (K) or VPB
-    // (V) bytes apart. Otherwise fragment-major (see the copies below). At 256
-    // the workgroup's 128 query rows need twice the copy bandwidth per MFMA of
-    // d = 128, and fragment-major copies (32 keys x 32 bytes each) kept the
-    // L1 busy with four times the cache lines.
-    constexpr bool ROWCOPY = D == 256;
+    // ROWCOPY (head dimensions 128 and 256): copy i of a tile takes RPB whole
+    // rows of 2D bytes, keys i, i + NBLK, .., into a 1 KB block; the blocks lie
+    // KPB (K) or VPB (V) bytes apart. Otherwise (64) fragment-major (see the
+    // copies below). A fragment-major copy (32 keys x 32 bytes) touches four
+    // times the cache lines of a copy of whole rows and kept the L1 busy.
+    constexpr bool ROWCOPY = D == 128 || D == 256;
+    constexpr int RPB = 512 / D;      // rows per 1 KB block (ROWCOPY)
+    constexpr int NBLK = 32 / RPB;    // blocks per tile (ROWCOPY)
     constexpr int CPT = DPW;  // copy instructions per wave per tile, each of K and V
     // A step's copies go one after each group of four MFMAs (the K copies
     // after the last CPT groups of stage A, the V copies after the first CPT of
@@ -220,12 +221,12 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     static_assert((RING & (RING - 1)) == 0 && RING >= 4, "ring of 2^n >= 4 tiles");
     static_assert((NG == 1 || NG == 2 || NG == 4) && NWV * DPW == KKN && INFLIGHT < 64,
                   "tile step shape");
-    static_assert(!ROWCOPY || (D == 256 && BN == 32), "row pairs: 512-byte rows, 32-key tiles");
+    static_assert(!ROWCOPY || (BN == 32 && NBLK == KKN), "row copies: 32-key tiles, one block per copy");
     static_assert(!SPREAD || CPT <= NG, "at most one copy of K and one of V per group");
     constexpr int TILE_CH = BN * D / 8;  // 16-byte chunks per tile
-    constexpr int KPB = 1040, VPB = 1088;  // block strides of ROWPAIR (bytes)
-    constexpr uint32_t KTILE_B = ROWCOPY ? 16 * KPB : TILE_CH * 16;
-    constexpr uint32_t VTILE_B = ROWCOPY ? 16 * VPB : TILE_CH * 16;
+    constexpr int KPB = D == 256 ? 1040 : 1056, VPB = 1088;  // block strides of ROWCOPY (bytes)
+    constexpr uint32_t KTILE_B = ROWCOPY ? NBLK * KPB : TILE_CH * 16;
+    constexpr uint32_t VTILE_B = ROWCOPY ? NBLK * VPB : TILE_CH * 16;
 
     __shared__ __attribute__((aligned(16))) uint4 sK_[RING * KTILE_B / 16];  // K ring
     __shared__ __attribute__((aligned(16))) uint4 sV_[RING * VTILE_B / 16];  // V ring
@@ -396,17 +397,26 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // [32db + 16(G%2) + 4q .. +3]; a transposing 8-byte read of the block
     // gives lane L the values of dim 32db + L%32 at four consecutive keys.
     //
-    // ROWPAIR layout: key r at byte (r % 16) * PB + (r / 16) * 512 of the tile
-    // (PB = KPB or VPB); wave w issues copies CPT w .. CPT w + CPT - 1, lane
-    // L of copy i taking 16 bytes of key i + 16 (L / 32). The strides keep both
-    // kinds of read free of bank conflicts: K fragments (lane l: key l%32)
-    // start 16 (mod 256) bytes apart, and the transposing V reads of a key
-    // quad 64 bytes apart.
+    // ROWCOPY layout: key r at byte (r % NBLK) * PB + (r / NBLK) * 2D of the
+    // tile (PB = KPB or VPB); wave w issues copies CPT w .. CPT w + CPT - 1,
+    // lane L of copy i taking 16 bytes of key i + NBLK (L / (D/8)). At 128 the
+    // K rows of odd r / NBLK hold their 16-byte chunks in pairs swapped (chunk
+    // c at c ^ 1). Strides and swap keep both kinds of read free of bank
+    // conflicts under the way LDS serves them (16-byte reads in passes of 16
+    // lanes: l % 16 < 8 of one 16-lane row with l % 16 >= 8 of its neighbour;
+    // transposing 8-byte reads in passes of 32 lanes): each pass of a K
+    // fragment read reaches 16 different 16-byte bank groups, and the
+    // transposing V reads of a key quad start 64 bytes apart.
+    const auto kswap = [](int quarter) { return D == 128 ? (quarter & 1) : 0; };
     uint32_t koff[CPT], voff[CPT];
 #pragma unroll
     for (int h = 0; h < CPT; ++h) {
         if constexpr (ROWCOPY) {
-            koff[h] = voff[h] = (uint32_t)((CPT * wave + h) * 512 + 8192 * g + 16 * l32);
+            constexpr int CPR = D / 8;  // 16-byte chunks per row
+            const int quarter = lane / CPR, chunk = lane % CPR;
+            const int key = CPT * wave + h + NBLK * quarter;
+            koff[h] = (uint32_t)(key * 2 * D + 16 * (chunk ^ kswap(quarter)));
+            voff[h] = (uint32_t)(key * 2 * D + 16 * chunk);
         } else {
             const int i = DPW * wave + h;
             koff[h] = (uint32_t)(l32 * D + 16 * i + 8 * g) * 2;
@@ -445,7 +455,7 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     // Reads take a lane's LDS byte address in the slot (K: slot + 16 lane, V:
     // slot + 8 lane), computed once per step ahead of everything else so that
     // the reads can start with the step's first MFMA.
-    // (ROWPAIR: K lane l reads key l%32 at dims 16kk + 8(l/32), 32 bytes per
+    // (ROWCOPY: K lane l reads key l%32 at dims 16kk + 8(l/32), 32 bytes per
     // kk further; V lane 16m + 4e + c supplies key 16kc + 8hh + 4(m/2) + e at
     // dims 32db + 16(m%2) + 4c .. +3 to the transposing read of its group)
     auto read_k = [&](uint32_t addr, int kk) __attribute__((always_inline)) {
@@ -453,8 +463,10 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
         kf[kk].u = __builtin_bit_cast(uint4, *(lds_u32x4 *)(uintptr_t)(addr + (ROWCOPY ? 32 : 1024) * kk));
     };
     auto vimm = [](int db, int kc, int hh) {
-        return ROWCOPY ? (uint32_t)(8 * hh * VPB + 512 * kc + 64 * db)
-                       : (uint32_t)(((2 * db + kc) * 2 + hh) * 512);
+        if constexpr (ROWCOPY)
+            return D == 256 ? (uint32_t)(8 * hh * VPB + 512 * kc + 64 * db)
+                            : (uint32_t)(512 * kc + 256 * hh + 64 * db);
+        return (uint32_t)(((2 * db + kc) * 2 + hh) * 512);
     };
     auto read_v = [&](uint32_t addr, int db, int kc) __attribute__((always_inline)) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -466,7 +478,8 @@ fwd_q64_kernel(FwdArgs a, int n_qtiles, int n_items)
     };
     const uint32_t lds_k = lds_addr(sK), lds_v = lds_addr(sV);
     const uint32_t klane =
-        ROWCOPY ? (uint32_t)((l32 & 15) * KPB + 512 * (l32 >> 4) + 16 * g) : (uint32_t)(16 * lane);
+        ROWCOPY ? (uint32_t)((l32 % NBLK) * KPB + 2 * D * (l32 / NBLK) + 16 * (g ^ kswap(l32 / NBLK)))
+                : (uint32_t)(16 * lane);
     const uint32_t vlane =
         ROWCOPY ? (uint32_t)((4 * (lane >> 5) + ((lane & 15) >> 2)) * VPB + 32 * ((lane >> 4) & 1) +
                              16 * ((lane & 3) >> 1) + 8 * (lane & 1))

@@ -194,6 +194,70 @@ __device__ __forceinline__ bf16x8 lds_tr_rm(uint32_t p, int D)
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Both-ways tiles (head dimension 128): one copy of a 32-row tile serves the
+// fragment reads and the transposing reads. Block i (FT_PB bytes apart) holds
+// the rows i, i + 8, i + 16, i + 24 whole (256 bytes each), the 16-byte chunk c
+// of row r at chunk c ^ ft_swz(r) of its row. A copy instruction reads four
+// whole rows (8 cache lines per KB, against 32 for a fragment-shaped copy),
+// and under the way LDS serves reads (as above) every pass of both kinds of
+// read reaches all banks once, with each read's step (16-dim step kk, 16-row
+// chunk, 32-dim block) in the instruction's offset field.
+constexpr int FT_PB = 1088;
+__device__ __forceinline__ int ft_swz(int r) { return 2 * ((r & 7) >> 2) + ((r >> 3) & 1); }
+
+// copy instruction i of a both-ways tile: lane l's 16 bytes in global memory
+// (row i + 8 (l / 16), the chunk stored at slot l % 16)
+__device__ __forceinline__ uint32_t off_ft(int i, int lane)
+{
+    const int r = i + 8 * (lane >> 4), p = lane & 15;
+    return (uint32_t)(r * 256 + 16 * (p ^ ft_swz(r)));
+}
+
+// a lane's fragment-read offset in a both-ways tile for even (odd = 0) or odd
+// 16-dim steps kk; the read of step kk is at this offset + 32 kk (row l % 32,
+// chunk 2 kk + l / 32)
+__device__ __forceinline__ uint32_t ft_frag_off(int lane, int odd)
+{
+    const int r = lane & 31, g = lane >> 5, sw = ft_swz(r);
+    const int flip = 32 * (sw >> 1);  // chunk bit 1 swapped: kk ^ 1
+    return (uint32_t)((r & 7) * FT_PB + 256 * (r >> 3) + 16 * (g ^ (sw & 1)) + (odd ? -flip : flip));
+}
+
+// a lane's transposing-read offset in a both-ways tile for row half hh: lane
+// L = 16 m + 4 e + c supplies row 16 ch + 8 hh + 4 (m / 2) + e at dims
+// 32 db + 16 (m % 2) + 4 c .. +3, at this offset + 512 ch + 64 db
+__device__ __forceinline__ uint32_t ft_tr_off(int lane, int hh)
+{
+    const int m = lane >> 4, e = (lane >> 2) & 3, c = lane & 3, a2 = m >> 1;
+    const int r = 8 * hh + 4 * a2 + e;  // the row's place in its 16-row chunk
+    return (uint32_t)((r & 7) * FT_PB + 256 * hh + 16 * ((2 * (m & 1) + (c >> 1)) ^ ft_swz(r)) +
+                      8 * (c & 1));
+}
+
+// a tile's LDS byte address plus a lane's offset, opaque to the compiler:
+// the reads from it then carry their constant steps in the instruction's
+// offset field (otherwise the compiler keeps offset + step per read in a
+// register, hoisted out of the loop, and adds the tile address before every
+// read)
+__device__ __forceinline__ uint32_t lane_addr(uint32_t tile, uint32_t off)
+{
+    uint32_t a = tile + off;
+    asm volatile("" : "+v"(a));
+    return a;
+}
+
+// the B operand of lds_tr from a both-ways tile: p0, p1 = the tile's address
+// plus the lane's offsets of ft_tr_off (lane_addr)
+__device__ __forceinline__ bf16x8 lds_tr_ft(uint32_t p0, uint32_t p1, int db, int ch)
+{
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const uint32_t step = 512 * ch + 64 * db;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(p0 + step));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(uintptr_t)(p1 + step));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Workgroup barrier that no memory access of the source crosses: the copies
 // into LDS are invisible to the compiler, so it must not move an LDS read
 // above the barrier that publishes the copied data.
@@ -246,17 +310,20 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     // copies (at 128 the row-major reads' per-lane addresses cost more issue
     // time than the cheaper copies save: 1.226 against 1.177 ms)
     constexpr bool RM = D == 256;
+    constexpr bool FT = D == 128;  // both-ways tiles
+    constexpr bool ONE = RM || FT;  // one copy of Q and of dO serves both reads
     constexpr int KK = D / 16, DB = D / 32, NW = 4;
     constexpr int CPF = KK / NW, CPT = KK / NW;  // copies per tile and wave
-    constexpr int TILE_F = D * 64;               // one 32-row tile
+    constexpr int TILE_F = FT ? 8 * FT_PB : D * 64;  // one 32-row tile
     constexpr int TILE_T = D * 64;
-    // stage: Q, dO (row-major), or Q frag, [Q tr], [dO frag], [dO tr]
-    constexpr int OFF_QT = RM ? 0 : TILE_F;
-    constexpr int OFF_OF = RM ? TILE_F : OFF_QT + (DODK ? TILE_T : 0);
-    constexpr int OFF_OT = RM ? TILE_F : OFF_OF + (DODK ? TILE_F : 0);
-    constexpr int STAGE_B = RM ? 2 * TILE_F : OFF_OT + (DODV ? TILE_T : 0);
+    constexpr uint32_t BLK = FT ? FT_PB : 1024;  // distance of a tile's copy blocks
+    // stage: Q, dO (row-major or both-ways), or Q frag, [Q tr], [dO frag], [dO tr]
+    constexpr int OFF_QT = ONE ? 0 : TILE_F;
+    constexpr int OFF_OF = ONE ? TILE_F : OFF_QT + (DODK ? TILE_T : 0);
+    constexpr int OFF_OT = ONE ? TILE_F : OFF_OF + (DODK ? TILE_F : 0);
+    constexpr int STAGE_B = ONE ? 2 * TILE_F : OFF_OT + (DODV ? TILE_T : 0);
     constexpr int RING = STAGE_B > 32768 ? 3 : 4;
-    constexpr int NCOPY = (RM ? 2 * CPF : CPF + (DODK ? CPT + CPF : 0) + (DODV ? CPT : 0)) + 1;  // per stage and wave
+    constexpr int NCOPY = (ONE ? 2 * CPF : CPF + (DODK ? CPT + CPF : 0) + (DODV ? CPT : 0)) + 1;  // per stage and wave
     __shared__ __attribute__((aligned(1024))) uint4 sRing[RING * STAGE_B / 16];
     __shared__ __attribute__((aligned(16))) float sStat[RING * NW * 64];
 
@@ -301,10 +368,11 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     uint32_t foff[CPF], toff[CPT];
 #pragma unroll
     for (int h = 0; h < CPF; ++h)
-        foff[h] = RM ? off_rm(D, CPF * wave + h, lane) : off_frag(D, CPF * wave + h, l32, g);
+        foff[h] = RM ? off_rm(D, CPF * wave + h, lane)
+                     : FT ? off_ft(CPF * wave + h, lane) : off_frag(D, CPF * wave + h, l32, g);
 #pragma unroll
     for (int h = 0; h < CPT; ++h)
-        toff[h] = RM ? 0u : off_tr(D, CPT * wave + h, l32, g);
+        toff[h] = ONE ? 0u : off_tr(D, CPT * wave + h, l32, g);
     // row-major read offsets: fragments by 16-dim step % 8, transposing reads by
     // (16-row chunk, 32-dim block % 4)
     uint32_t fro[8], tro[8];
@@ -313,6 +381,9 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
         fro[i] = RM ? rm_frag_off(D, i, lane) : 0u;
         tro[i] = RM ? rm_tr_off(D, i >> 2, i & 3, lane) : 0u;
     }
+    // both-ways read offsets: fragments by kk % 2, transposing reads by row half
+    const uint32_t fto[2] = {FT ? ft_frag_off(lane, 0) : 0u, FT ? ft_frag_off(lane, 1) : 0u};
+    const uint32_t tto[2] = {FT ? ft_tr_off(lane, 0) : 0u, FT ? ft_tr_off(lane, 1) : 0u};
     const uint32_t ring0 = lds_addr(sRing), stat0 = lds_addr(sStat);
     // stage t's copies; past the walk's end they cover no bytes (the index
     // math is clamped and the lengths selected, so that no branch splits the
@@ -340,7 +411,7 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     // part p of NP of the prepared stage's copies (copy e goes in part e NP / NCOPY)
     auto issue = [&](int p, int np) __attribute__((always_inline)) {
         const uint32_t base = ring0 + cslot * STAGE_B;
-        const uint32_t fb = base + 1024 * CPF * wave, tb = base + 1024 * CPT * wave;
+        const uint32_t fb = base + BLK * CPF * wave, tb = base + 1024 * CPT * wave;
         int e = 0;
         auto one = [&](auto &&f) __attribute__((always_inline)) {
             if (e * np / NCOPY == p)
@@ -349,11 +420,11 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
         };
 #pragma unroll
         for (int h = 0; h < CPF; ++h) {
-            one([&] { copy_to_lds(cq, foff[h], fb + 1024 * h); });
-            if constexpr (DODK || RM)
-                one([&] { copy_to_lds(cd, foff[h], fb + OFF_OF + 1024 * h); });
+            one([&] { copy_to_lds(cq, foff[h], fb + BLK * h); });
+            if constexpr (DODK || ONE)
+                one([&] { copy_to_lds(cd, foff[h], fb + OFF_OF + BLK * h); });
         }
-        if constexpr (!RM) {
+        if constexpr (!ONE) {
 #pragma unroll
             for (int h = 0; h < CPT; ++h) {
                 if constexpr (DODK)
@@ -366,11 +437,17 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
     };
     // S (and dP) of stage t (16 query rows per lane, key my_key)
     auto qk = [&](int t, f32x16 &s, f32x16 &dp) __attribute__((always_inline)) {
-        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + (RM ? 0 : 16 * lane);
+        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + (ONE ? 0 : 16 * lane);
+        const uint32_t fa0 = FT ? lane_addr(sb, fto[0]) : 0u, fa1 = FT ? lane_addr(sb, fto[1]) : 0u;
+        uint32_t fra[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            fra[i] = RM ? lane_addr(sb, fro[i]) : 0u;
         // fragment kk of the tile at byte o
         auto fr = [&](uint32_t o, int kk) __attribute__((always_inline)) {
-            return __builtin_bit_cast(bf16x8, RM ? lds16(sb + o + fro[kk & 7] + 256 * (kk >> 3))
-                                                 : lds16(sb + o + 1024 * kk));
+            return __builtin_bit_cast(bf16x8, RM ? lds16(fra[kk & 7] + o + 256 * (kk >> 3))
+                                              : FT ? lds16((kk & 1 ? fa1 : fa0) + o + 32 * kk)
+                                                   : lds16(sb + o + 1024 * kk));
         };
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -427,10 +504,17 @@ __global__ void __launch_bounds__(256) bwd_dkdv_ring_kernel(BwdArgs a, int nkb, 
         }
         issue(1, 4);
         qk(t + 1, s, dp);
-        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + (RM ? 0 : 8 * lane);
+        const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B + (ONE ? 0 : 8 * lane);
+        const uint32_t ta0 = FT ? lane_addr(sb, tto[0]) : 0u, ta1 = FT ? lane_addr(sb, tto[1]) : 0u;
+        uint32_t tra[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            tra[i] = RM ? lane_addr(sb, tro[i]) : 0u;
         // block (ch, db) of the transposing operand in the tile at byte o
         auto tr = [&](uint32_t o, int db, int ch) __attribute__((always_inline)) {
-            return RM ? lds_tr_rm(sb + o + tro[4 * ch + (db & 3)] + 256 * (db >> 2), D) : lds_tr(sb + o, db, ch);
+            return RM   ? lds_tr_rm(tra[4 * ch + (db & 3)] + o + 256 * (db >> 2), D)
+                   : FT ? lds_tr_ft(ta0 + o, ta1 + o, db, ch)
+                        : lds_tr(sb + o, db, ch);
         };
         issue(2, 4);
 #pragma unroll
@@ -502,10 +586,12 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
 {
     constexpr int KK = D / 16, DB = D / 32;
     constexpr bool RM = D == 256;          // row-major tiles (K read both ways)
-    constexpr int NT = RM ? 2 : 3;         // tiles per stage: K, V or K frag, V frag, K tr
+    constexpr bool FT = D == 128;          // both-ways tiles (K read both ways)
+    constexpr int NT = RM || FT ? 2 : 3;   // tiles per stage: K, V or K frag, V frag, K tr
     static_assert((NT * KK) % NW == 0, "copies must split evenly over the waves");
     constexpr int NCOPY = NT * KK / NW;    // copies per stage and wave
-    constexpr int TILE_B = D * 64;
+    constexpr int TILE_B = FT ? 8 * FT_PB : D * 64;
+    constexpr uint32_t BLK = FT ? FT_PB : 1024;  // distance of a tile's copy blocks
     constexpr int STAGE_B = NT * TILE_B;
     constexpr int RING = 4;
     constexpr int NP = RM ? 3 : 1;         // parts a stage's copies are issued in
@@ -581,8 +667,9 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
 #pragma unroll
     for (int h = 0; h < NCOPY; ++h) {
         const int e = NCOPY * wave + h, x = e / KK, i = e % KK;
-        coff[h] = RM ? off_rm(D, i, lane) : x == 2 ? off_tr(D, i, l32, g) : off_frag(D, i, l32, g);
-        cdst[h] = (uint32_t)(x * TILE_B + 1024 * i);
+        coff[h] = RM ? off_rm(D, i, lane)
+                     : FT ? off_ft(i, lane) : x == 2 ? off_tr(D, i, l32, g) : off_frag(D, i, l32, g);
+        cdst[h] = (uint32_t)(x * TILE_B + BLK * i);
         cv[h] = x == 1;
     }
     // row-major read offsets (see the dK/dV kernel)
@@ -592,6 +679,8 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
         fro[i] = RM ? rm_frag_off(D, i, lane) : 0u;
         tro[i] = RM ? rm_tr_off(D, i >> 2, i & 3, lane) : 0u;
     }
+    const uint32_t fto[2] = {FT ? ft_frag_off(lane, 0) : 0u, FT ? ft_frag_off(lane, 1) : 0u};
+    const uint32_t tto[2] = {FT ? ft_tr_off(lane, 0) : 0u, FT ? ft_tr_off(lane, 1) : 0u};
     const uint32_t ring0 = lds_addr(sRing);
     u32x4 cdk, cdv;
     uint32_t cbase = 0;
@@ -637,14 +726,23 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
         }
         const bool full = (!CAUSAL || iw0 + diag >= j0 + 31) && j0 + 31 < Sk && iw0 + 31 < Sq;
         const uint32_t sb = ring0 + (uint32_t)(t % RING) * STAGE_B;
+        const uint32_t fa0 = FT ? lane_addr(sb, fto[0]) : 0u, fa1 = FT ? lane_addr(sb, fto[1]) : 0u;
+        const uint32_t ta0 = FT ? lane_addr(sb, tto[0]) : 0u, ta1 = FT ? lane_addr(sb, tto[1]) : 0u;
+        uint32_t fra[8], tra[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            fra[i] = RM ? lane_addr(sb, fro[i]) : 0u;
+            tra[i] = RM ? lane_addr(sb, tro[i]) : 0u;
+        }
         f32x16 s, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             s[r] = dp[r] = 0.f;
         // fragment kk of the tile at byte o
         auto fr = [&](uint32_t o, int kk) __attribute__((always_inline)) {
-            return __builtin_bit_cast(bf16x8, RM ? lds16(sb + o + fro[kk & 7] + 256 * (kk >> 3))
-                                                 : lds16(sb + o + 1024 * kk + 16 * lane));
+            return __builtin_bit_cast(bf16x8, RM ? lds16(fra[kk & 7] + o + 256 * (kk >> 3))
+                                              : FT ? lds16((kk & 1 ? fa1 : fa0) + o + 32 * kk)
+                                                   : lds16(sb + o + 1024 * kk + 16 * lane));
         };
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -672,8 +770,9 @@ __global__ void __launch_bounds__(64 * NW) bwd_dq_ring_kernel(BwdArgs a, int nrb
             const bf16x8 sa = pack_chunk(ds, ch);
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const bf16x8 kt = RM ? lds_tr_rm(sb + tro[4 * ch + (db & 3)] + 256 * (db >> 2), D)
-                                     : lds_tr(sb + 2 * TILE_B + 8 * lane, db, ch);
+                const bf16x8 kt = RM   ? lds_tr_rm(tra[4 * ch + (db & 3)] + 256 * (db >> 2), D)
+                                  : FT ? lds_tr_ft(ta0, ta1, db, ch)
+                                       : lds_tr(sb + 2 * TILE_B + 8 * lane, db, ch);
                 dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa, kt, dq[db], 0, 0, 0);
             }
         }

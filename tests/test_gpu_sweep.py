@@ -1,5 +1,5 @@
-"""GPU: a seeded sweep of small random shapes, forward and backward, against
-the f64 oracles.
+"""GPU: a seeded sweep of small random shapes, forward, backward and decode
+(contiguous and paged), against the f64 oracles.
 
 The shape lists are drawn once from a fixed PCG64 stream, so the cases (and
 their test ids) are the same on every run. The lengths are drawn so that most
@@ -9,7 +9,8 @@ include 1: every ragged end of the tile and copy layouts at head dimensions
 heads. Bounds as in the parity tests: forward O max-abs 1e-2, O rel-RMS 4e-3,
 LSE max-abs 1e-3, rows that see no key exactly (+0, -inf); backward per
 gradient tensor rel-RMS <= 8e-3 and max-abs <= 1.2e-2 of its largest
-magnitude.
+magnitude. The paged decode must also equal the contiguous decode bit for bit
+(pool pages no stream owns hold NaN bits).
 """
 from __future__ import annotations
 
@@ -54,6 +55,31 @@ def _draw_shapes(seed, n, max_len):
 
 FWD = _draw_shapes(20261211, 30, 300)
 BWD = _draw_shapes(20261212, 12, 160)
+
+
+def _draw_decode(seed, n):
+    """(seed, lens, Hq, Hkv, d, page size, splits): lengths from 0 to 700,
+    with an empty stream or a one-row stream forced into two of every three
+    cases, and 1 to 16 query heads per kv-head."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 7))
+        lens = rng.integers(0, 701, size=B)
+        if i % 3 == 0:
+            lens[0] = 0
+        if i % 3 == 1:
+            lens[-1] = 1
+        hkv = int(rng.integers(1, 5))
+        g = int(rng.choice([1, 2, 4, 8, 16]))
+        d = int(rng.choice([64, 128, 256]))
+        P = int(rng.choice([16, 32, 64]))
+        splits = int(rng.integers(1, 25))
+        out.append((seed + 7 * i, [int(x) for x in lens], hkv * g, hkv, d, P, splits))
+    return out
+
+
+DEC = _draw_decode(20261213, 16)
 
 
 @pytest.mark.parametrize("i", range(len(FWD)))
@@ -102,3 +128,32 @@ def test_backward_sweep(i):
             continue
         assert m["rel_rms"] <= REL_RMS, f"{label} {name}: {m}"
         assert m["max_abs_rel"] <= MAX_REL, f"{label} {name}: {m}"
+
+
+@pytest.mark.parametrize("i", range(len(DEC)))
+def test_decode_sweep(i):
+    seed, lens, Hq, Hkv, d, P, splits = DEC[i]
+    lens = np.asarray(lens, dtype=np.int32)
+    label = f"decode sweep {i} B={len(lens)} Hq={Hq} Hkv={Hkv} d={d} P={P} splits={splits}"
+    nan = int(inputs.BF16_NAN)
+    max_pages = max(1, int((lens.max() + P - 1) // P))
+    S_cap = max_pages * P
+    _, q, kc, vc = inputs.draw_decode_bits(seed, len(lens), Hq, Hkv, d, 0, 0, S_cap, lens=lens,
+                                           pad_bits=nan)
+    scale = inputs.default_scale(d)
+    _note(f"[gpu] {label} lens={lens.tolist()}")
+    o, lse, guards = H.run_decode(q, kc, vc, lens, scale, splits)
+    assert guards, f"{label}: write outside the logical outputs"
+    o_ref, lse_ref = oracle.attn_decode(q, kc, vc, lens, scale)
+    m = H.metrics(o, lse, o_ref, lse_ref)
+    _note(f"[gpu] {label}: {m}")
+    H.assert_parity(m, label)
+    assert m["empty_rows"] == Hq * int((lens == 0).sum())
+    # the same rows in a page pool, in a seeded random page order
+    table, npg = inputs.paged_layout(seed + 1, lens, P, max_pages, spare_pages=3)
+    kp = inputs.scatter_to_pages(kc, table, npg, P, fill_bits=nan)
+    vp = inputs.scatter_to_pages(vc, table, npg, P, fill_bits=nan)
+    op, lp, guards = H.run_decode_paged(q, kp, vp, table, lens, P, scale, splits)
+    assert guards, f"{label} paged: write outside the logical outputs"
+    assert np.array_equal(op, o), f"{label}: paged O differs from the contiguous decode"
+    assert np.array_equal(lp.view(np.uint32), lse.view(np.uint32)), f"{label}: paged LSE differs"

@@ -1,4 +1,5 @@
-"""GPU: a seeded sweep of small random shapes, forward, backward and decode
+"""GPU: a seeded sweep of small random shapes, forward (plain, and with a
+sliding window, soft cap and ALiBi drawn at random), backward and decode
 (contiguous and paged), against the f64 oracles.
 
 The shape lists are drawn once from a fixed PCG64 stream, so the cases (and
@@ -82,6 +83,25 @@ def _draw_decode(seed, n):
 DEC = _draw_decode(20261213, 16)
 
 
+def _draw_ext(seed, n):
+    """Forward shapes with a sliding window, a soft cap and ALiBi slopes,
+    each present or not at random (at least one of them in every case)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for b, hq, hkv, sq, sk, d, causal in _draw_shapes(seed + 1, n, 300):
+        while True:
+            window = int(rng.integers(0, 200)) if rng.random() < 0.5 else -1
+            softcap = float(rng.uniform(5.0, 50.0)) if rng.random() < 0.5 else 0.0
+            alibi = bool(rng.random() < 0.5)
+            if window >= 0 or softcap > 0.0 or alibi:
+                break
+        out.append((b, hq, hkv, sq, sk, d, causal, window, round(softcap, 3), alibi))
+    return out
+
+
+EXT = _draw_ext(20261214, 16)
+
+
 @pytest.mark.parametrize("i", range(len(FWD)))
 def test_forward_sweep(i):
     B, Hq, Hkv, Sq, Sk, d, causal = FWD[i]
@@ -157,3 +177,24 @@ def test_decode_sweep(i):
     assert guards, f"{label} paged: write outside the logical outputs"
     assert np.array_equal(op, o), f"{label}: paged O differs from the contiguous decode"
     assert np.array_equal(lp.view(np.uint32), lse.view(np.uint32)), f"{label}: paged LSE differs"
+
+
+@pytest.mark.parametrize("i", range(len(EXT)))
+def test_forward_variants_sweep(i):
+    B, Hq, Hkv, Sq, Sk, d, causal, window, softcap, alibi = EXT[i]
+    label = f"fwd variant sweep {i} {EXT[i]}"
+    seed = 9800 + 10 * i
+    std = 0.5 if alibi else 1.0
+    q = _bits(seed, (B, Hq, Sq, d), std)
+    k = _bits(seed + 1, (B, Hkv, Sk, d), std)
+    v = _bits(seed + 2, (B, Hkv, Sk, d))
+    slopes = (2.0 ** (-8.0 * (np.arange(Hq) + 1) / Hq)).astype(np.float32) if alibi else None
+    scale = inputs.default_scale(d)
+    _note(f"[gpu] {label}")
+    o, lse, guards = H.run_fwd_ext(q, k, v, causal, scale, window, softcap, slopes)
+    assert guards, f"{label}: write outside the logical outputs"
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal, scale, window=window, softcap=softcap,
+                                     alibi=slopes)
+    m = H.metrics(o, lse, o_ref, lse_ref)
+    _note(f"[gpu] {label}: {m}")
+    H.assert_parity(m, label)

@@ -1,6 +1,7 @@
-"""GPU: a seeded sweep of small random shapes, forward (plain, and with a
-sliding window, soft cap and ALiBi drawn at random), backward and decode
-(contiguous and paged), against the f64 oracles.
+"""GPU: a seeded sweep of small random shapes, forward (plain, with a
+sliding window, soft cap and ALiBi drawn at random, and packed variable-length
+batches), backward and decode (contiguous and paged), against the f64
+oracles.
 
 The shape lists are drawn once from a fixed PCG64 stream, so the cases (and
 their test ids) are the same on every run. The lengths are drawn so that most
@@ -102,6 +103,30 @@ def _draw_ext(seed, n):
 EXT = _draw_ext(20261214, 16)
 
 
+def _draw_varlen(seed, n):
+    """Packed batches: 1-8 sequences of 0-400 query rows, each with 0-200
+    more keys than rows (a chunk against its cache), and the variants drawn
+    as in _draw_ext (any of them may be absent here)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for i in range(n):
+        nseq = int(rng.integers(1, 9))
+        lq = [int(x) for x in rng.integers(0, 401, size=nseq)]
+        extra = [int(x) for x in rng.integers(0, 201, size=nseq)]
+        hkv = int(rng.integers(1, 3))
+        g = int(rng.choice([1, 2, 4]))
+        d = int(rng.choice([64, 128, 256]))
+        causal = bool(rng.random() < 0.6)
+        window = int(rng.integers(0, 200)) if rng.random() < 0.3 else -1
+        softcap = round(float(rng.uniform(5.0, 50.0)), 3) if rng.random() < 0.3 else 0.0
+        alibi = bool(rng.random() < 0.3)
+        out.append((seed + 11 * i, lq, extra, hkv * g, hkv, d, causal, window, softcap, alibi))
+    return out
+
+
+VARLEN = _draw_varlen(20261215, 10)
+
+
 @pytest.mark.parametrize("i", range(len(FWD)))
 def test_forward_sweep(i):
     B, Hq, Hkv, Sq, Sk, d, causal = FWD[i]
@@ -195,6 +220,32 @@ def test_forward_variants_sweep(i):
     assert guards, f"{label}: write outside the logical outputs"
     o_ref, lse_ref = oracle.attn_fwd(q, k, v, causal, scale, window=window, softcap=softcap,
                                      alibi=slopes)
+    m = H.metrics(o, lse, o_ref, lse_ref)
+    _note(f"[gpu] {label}: {m}")
+    H.assert_parity(m, label)
+
+
+@pytest.mark.parametrize("i", range(len(VARLEN)))
+def test_varlen_sweep(i):
+    from tests.test_gpu_varlen import _run_ext
+
+    seed, lq, extra, Hq, Hkv, d, causal, window, softcap, alibi = VARLEN[i]
+    lk = [a + b for a, b in zip(lq, extra)]
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    std = 0.5 if alibi else 1.0
+    q = _bits(seed, (Hq, int(cu_q[-1]), d), std)
+    k = _bits(seed + 1, (Hkv, int(cu_k[-1]), d), std)
+    v = _bits(seed + 2, (Hkv, int(cu_k[-1]), d))
+    slopes = (2.0 ** (-8.0 * (np.arange(Hq) + 1) / Hq)).astype(np.float32) if alibi else None
+    scale = inputs.default_scale(d)
+    label = f"varlen sweep {i} {VARLEN[i]}"
+    _note(f"[gpu] {label}")
+    o, lse, guards = _run_ext(q, k, v, cu_q, cu_k, max(lq), max(lk), causal, scale, window,
+                              softcap, slopes)
+    assert guards, f"{label}: write outside the logical outputs"
+    o_ref, lse_ref = oracle.attn_fwd_varlen(q, k, v, cu_q, cu_k, causal, scale, window=window,
+                                            softcap=softcap, alibi=slopes)
     m = H.metrics(o, lse, o_ref, lse_ref)
     _note(f"[gpu] {label}: {m}")
     H.assert_parity(m, label)
